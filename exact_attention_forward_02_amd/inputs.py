@@ -1,0 +1,101 @@
+"""Seeded synthetic inputs and the named workloads.
+
+This module holds no attention arithmetic.  It is the only code that both the
+GPU path and the CPU oracle are fed from: tests, the benchmark and the smoke
+check draw Q, K, V here and hand the same tensors to both sides.
+
+Recipe: a CPU ``torch.Generator`` seeded with the workload's seed draws Q,
+then K, then V as float32 N(0, 1) (Q optionally multiplied by a constant in
+float32), each rounded to bfloat16 with round-to-nearest-even.  Layout is
+[B, H, L, d], contiguous.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, asdict
+
+import torch
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    Lq: int
+    Lk: int
+    dqk: int
+    dv: int
+    causal: bool
+    seed: int
+    q_mult: float = 1.0
+
+    def flops(self) -> float:
+        """Algorithmic FLOPs: 2*B*Hq*Lq*Lk*(dqk+dv), halved under the causal mask."""
+        f = 2.0 * self.B * self.Hq * self.Lq * self.Lk * (self.dqk + self.dv)
+        return f / 2.0 if self.causal else f
+
+    def valid_pairs(self) -> int:
+        """Exact count of visible (query, key) pairs per (b, h)."""
+        if not self.causal:
+            return self.Lq * self.Lk
+        off = self.Lk - self.Lq
+        total = 0
+        for i in range(self.Lq):
+            total += max(0, min(self.Lk, i + off + 1))
+        return total
+
+    def min_hbm_bytes(self) -> int:
+        """Q, K, V read once and O, lse written once."""
+        q = self.B * self.Hq * self.Lq * self.dqk * 2
+        k = self.B * self.Hkv * self.Lk * self.dqk * 2
+        v = self.B * self.Hkv * self.Lk * self.dv * 2
+        o = self.B * self.Hq * self.Lq * self.dv * 2
+        lse = self.B * self.Hq * self.Lq * 4
+        return q + k + v + o + lse
+
+    def as_dict(self) -> dict:
+        return asdict(self)
+
+
+# The five workloads of the study (sizes as the attention-forward benchmark
+# grid describes them: 32k total tokens at hidden 2048, long causal sequences,
+# a grouped-query case and the (192, 128) head shape).
+WORKLOADS = {
+    "tiny": Workload("tiny", 1, 1, 1, 256, 256, 64, 64, False, seed=1),
+    "tiny_q6": Workload("tiny_q6", 1, 1, 1, 256, 256, 64, 64, False, seed=1, q_mult=6.0),
+    "mha_l2k": Workload("mha_l2k", 16, 16, 16, 2048, 2048, 128, 128, False, seed=2),
+    "causal_l8k": Workload("causal_l8k", 4, 16, 16, 8192, 8192, 128, 128, True, seed=3),
+    "gqa_l16k": Workload("gqa_l16k", 2, 32, 8, 16384, 16384, 128, 128, True, seed=4),
+    "dsv3_l32k": Workload("dsv3_l32k", 1, 16, 16, 32768, 32768, 192, 128, True, seed=5),
+}
+
+
+def make_qkv(B: int, Hq: int, Hkv: int, Lq: int, Lk: int, dqk: int, dv: int,
+             seed: int, q_mult: float = 1.0):
+    """Seeded bf16 CPU tensors q [B,Hq,Lq,dqk], k [B,Hkv,Lk,dqk], v [B,Hkv,Lk,dv]."""
+    g = torch.Generator(device="cpu").manual_seed(int(seed))
+    q = torch.randn((B, Hq, Lq, dqk), generator=g, dtype=torch.float32)
+    if q_mult != 1.0:
+        q.mul_(float(q_mult))
+    q = q.to(torch.bfloat16)
+    k = torch.randn((B, Hkv, Lk, dqk), generator=g, dtype=torch.float32).to(torch.bfloat16)
+    v = torch.randn((B, Hkv, Lk, dv), generator=g, dtype=torch.float32).to(torch.bfloat16)
+    return q, k, v
+
+
+def workload_qkv(w: Workload):
+    return make_qkv(w.B, w.Hq, w.Hkv, w.Lq, w.Lk, w.dqk, w.dv, w.seed, w.q_mult)
+
+
+def sample_rows(B: int, Hq: int, Lq: int, n: int, seed: int = 0):
+    """n distinct flat row indices (b*Hq + h)*Lq + i, always including the first
+    and last position of the first and last head, drawn with a fixed seed."""
+    total = B * Hq * Lq
+    if n >= total:
+        return torch.arange(total, dtype=torch.int64)
+    g = torch.Generator(device="cpu").manual_seed(int(seed))
+    picked = torch.randperm(total, generator=g)[:n]
+    fixed = torch.tensor([0, Lq - 1, total - Lq, total - 1], dtype=torch.int64)
+    rows = torch.unique(torch.cat([fixed, picked]))
+    return rows

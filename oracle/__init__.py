@@ -1,0 +1,163 @@
+"""CPU fp64 oracle for exact attention forward -- TEST INFRASTRUCTURE ONLY.
+
+Only the test suite, the smoke check and the benchmark's CPU-baseline leg may
+import this package.  It shares no code with the GPU library and never imports
+it; the two meet only through the seeded inputs both are fed.
+
+The arithmetic lives in ``attn_oracle.c`` (plain C, double precision, OpenMP
+over query rows).  This module compiles it with gcc when no built library is
+present and marshals arguments through ctypes.
+
+Functions
+---------
+attn_rows      the definition, materialised one score row at a time
+online_rows    the tiled method (always-rescale Algorithm 1, or conditional
+               base-2 rescaling per row or per row group), for checking the
+               algorithm against the definition
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+SOURCE = os.path.join(_HERE, "attn_oracle.c")
+LIBRARY = os.path.join(_HERE, "liboracle.so")
+
+_i64 = ctypes.c_int64
+_ptr = ctypes.c_void_p
+
+
+def build(source: str = SOURCE, output: str = LIBRARY, extra_flags=()) -> str:
+    """Compile the oracle with gcc into a shared library and return its path."""
+    cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-Wall", "-Wextra",
+           *extra_flags, "-o", output + ".tmp", source, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(output + ".tmp", output)
+    return output
+
+
+def _as_bits(t) -> np.ndarray:
+    """bf16 tensor (torch, any device) or uint16 array -> contiguous uint16."""
+    if isinstance(t, np.ndarray):
+        if t.dtype != np.uint16:
+            raise TypeError("numpy inputs must hold bf16 bit patterns as uint16")
+        return np.ascontiguousarray(t)
+    import torch
+
+    if t.dtype != torch.bfloat16:
+        raise TypeError(f"expected a bfloat16 tensor, got {t.dtype}")
+    return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+class Oracle:
+    """ctypes handle on one built copy of attn_oracle.c."""
+
+    def __init__(self, path: str = LIBRARY):
+        self.path = path
+        lib = ctypes.CDLL(path)
+        lib.oracle_attn_rows.restype = ctypes.c_int
+        lib.oracle_attn_rows.argtypes = [
+            _ptr, _ptr, _ptr, _i64, _i64, _i64, _i64, _i64, _i64, _i64,
+            ctypes.c_int, ctypes.c_double, _ptr, _i64, _ptr, _ptr, ctypes.c_int]
+        lib.oracle_online_rows.restype = ctypes.c_int
+        lib.oracle_online_rows.argtypes = [
+            _ptr, _ptr, _ptr, _i64, _i64, _i64, _i64, _i64, _i64, _i64,
+            ctypes.c_int, ctypes.c_double, _i64, ctypes.c_int, ctypes.c_double,
+            _i64, _ptr, _i64, _ptr, _ptr, _ptr, _ptr, ctypes.c_int]
+        self._lib = lib
+
+    @staticmethod
+    def _shapes(q, k, v):
+        if q.ndim != 4 or k.ndim != 4 or v.ndim != 4:
+            raise ValueError("q, k, v must be [B, H, L, d]")
+        B, Hq, Lq, dqk = q.shape
+        Bk, Hkv, Lk, dk = k.shape
+        Bv, Hv, Lv, dv = v.shape
+        if (Bk, dk) != (B, dqk) or (Bv, Hv, Lv) != (B, Hkv, Lk):
+            raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} "
+                             f"v{tuple(v.shape)}")
+        return B, Hq, Hkv, Lq, Lk, dqk, dv
+
+    @staticmethod
+    def _rows(rows, total):
+        if rows is None:
+            return None, total
+        r = np.ascontiguousarray(np.asarray(rows, dtype=np.int64).ravel())
+        return r, r.size
+
+    def attn_rows(self, q, k, v, causal: bool, scale: float | None = None,
+                  rows=None, threads: int = 0):
+        """Exact O [n, dv] and lse [n] (float64) for the requested query rows.
+
+        A row index is (b*Hq + h)*Lq + i; rows=None means every row in order.
+        """
+        qb, kb, vb = _as_bits(q), _as_bits(k), _as_bits(v)
+        B, Hq, Hkv, Lq, Lk, dqk, dv = self._shapes(qb, kb, vb)
+        if scale is None:
+            scale = 1.0 / math.sqrt(dqk)
+        r, n = self._rows(rows, B * Hq * Lq)
+        o = np.empty((n, dv), dtype=np.float64)
+        lse = np.empty((n,), dtype=np.float64)
+        rc = self._lib.oracle_attn_rows(
+            qb.ctypes.data, kb.ctypes.data, vb.ctypes.data,
+            B, Hq, Hkv, Lq, Lk, dqk, dv, int(bool(causal)), float(scale),
+            None if r is None else r.ctypes.data, n,
+            o.ctypes.data, lse.ctypes.data, int(threads))
+        if rc != 0:
+            raise ValueError(f"oracle_attn_rows rejected its arguments (code {rc})")
+        return o, lse
+
+    def online_rows(self, q, k, v, causal: bool, scale: float | None = None,
+                    bn: int = 64, mode: int = 1, tau: float = 8.0, group: int = 1,
+                    rows=None, threads: int = 0):
+        """Tiled method; returns (O, lse, state[n, 2], n_rescale_events).
+
+        mode 0: always rescale, natural exponent; mode 1: conditional base-2
+        rescale decided per row; mode 2: decision shared by `group` rows.
+        state[:, 0] is the final reference, state[:, 1] the final denominator.
+        """
+        qb, kb, vb = _as_bits(q), _as_bits(k), _as_bits(v)
+        B, Hq, Hkv, Lq, Lk, dqk, dv = self._shapes(qb, kb, vb)
+        if scale is None:
+            scale = 1.0 / math.sqrt(dqk)
+        r, n = self._rows(rows, B * Hq * Lq)
+        o = np.empty((n, dv), dtype=np.float64)
+        lse = np.empty((n,), dtype=np.float64)
+        state = np.empty((n, 2), dtype=np.float64)
+        events = ctypes.c_int64(0)
+        rc = self._lib.oracle_online_rows(
+            qb.ctypes.data, kb.ctypes.data, vb.ctypes.data,
+            B, Hq, Hkv, Lq, Lk, dqk, dv, int(bool(causal)), float(scale),
+            int(bn), int(mode), float(tau), int(group),
+            None if r is None else r.ctypes.data, n,
+            o.ctypes.data, lse.ctypes.data, state.ctypes.data,
+            ctypes.addressof(events), int(threads))
+        if rc != 0:
+            raise ValueError(f"oracle_online_rows rejected its arguments (code {rc})")
+        return o, lse, state, int(events.value)
+
+
+_default: Oracle | None = None
+
+
+def load() -> Oracle:
+    """The oracle built from this directory (compiled on first use if absent)."""
+    global _default
+    if _default is None:
+        if not os.path.exists(LIBRARY):
+            build()
+        _default = Oracle(LIBRARY)
+    return _default
+
+
+def attn_rows(*args, **kwargs):
+    return load().attn_rows(*args, **kwargs)
+
+
+def online_rows(*args, **kwargs):
+    return load().online_rows(*args, **kwargs)

@@ -1,0 +1,458 @@
+/*
+ * attn_oracle.c -- plain, slow, obviously-correct CPU oracle for exact
+ * attention forward, in IEEE double precision.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path links, loads or
+ * calls this file; only the test suite, the smoke check and the benchmark's
+ * CPU-baseline leg do.  It shares no code, header, table or helper with the
+ * GPU library.
+ *
+ * Inputs are bf16 bit patterns (uint16).  Each is widened exactly to double
+ * (a bf16 value is the top half of an IEEE binary32), so the oracle works on
+ * the exact values the GPU receives.
+ *
+ * Layouts (all contiguous, row-major):
+ *   q   [B, Hq,  Lq, dqk]      k [B, Hkv, Lk, dqk]      v [B, Hkv, Lk, dv]
+ *   o   [n_rows, dv]  (double) lse [n_rows]  (double)
+ * A "row" is one query vector, flat index r = (b*Hq + h)*Lq + i.
+ *
+ * Definitions followed (sources are the three pages on FlashAttention):
+ *  - exact attention O = softmax(scale * Q K^T) V per head, softmax along keys:
+ *    "Infra: Flash Attention", opening section (S = QK^T/sqrt d, P = softmax S,
+ *    O = PV) and "Flash Attention 4 ..." (fangpin gpu-hpc-book ch. 13), section
+ *    on the real bottleneck of attention.
+ *  - safe softmax (subtract the row max): "Infra: Flash Attention", section on
+ *    computing softmax in segments.
+ *  - logsumexp L_i = m_i + log l_i = log sum_j e^{S_ij}: "Infra: Flash
+ *    Attention", Algorithm 1 (output step) and the backward-recompute section.
+ *  - causal mask aligned bottom-right (query i sees keys j <= i + Lk - Lq) and
+ *    GQA head mapping (query head h reads K/V head h / (Hq/Hkv)): "Flash
+ *    Attention 4 ..." ch. 13, section on causal attention and GQA.
+ *  - a row with no valid key has no defined softmax; the pages leave its
+ *    output to the operator.  Reading adopted: O = 0, lse = -inf.
+ *
+ * The online (tiled) variants in the second half follow the algorithms the
+ * pages describe step by step; they exist to check that the tiled method
+ * reaches the same result as the definition.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* Exact widening of a bf16 bit pattern: bf16 is binary32 with the low 16
+ * mantissa bits dropped, so shifting the pattern into the top half of a
+ * 32-bit word gives the identical binary32 value. */
+static double bf16_bits_to_double(uint16_t bits)
+{
+    uint32_t word = ((uint32_t)bits) << 16;
+    float f;
+    memcpy(&f, &word, sizeof f);
+    return (double)f;
+}
+
+typedef struct {
+    int64_t B, Hq, Hkv, Lq, Lk, dqk, dv;
+    int causal;
+    double scale;
+} dims_t;
+
+static int check_dims(const dims_t* d)
+{
+    if (d->B < 1 || d->Hq < 1 || d->Hkv < 1 || d->Lq < 1 || d->Lk < 1 ||
+        d->dqk < 1 || d->dv < 1)
+        return 1;
+    if (d->Hq % d->Hkv != 0)
+        return 2;
+    if (!(d->scale > 0.0) || !isfinite(d->scale))
+        return 3;
+    return 0;
+}
+
+/* Number of keys row i may attend: all Lk keys, or, with the bottom-right
+ * causal mask, keys 0 .. i + Lk - Lq (clamped to [0, Lk]). */
+static int64_t valid_keys(const dims_t* d, int64_t i)
+{
+    if (!d->causal)
+        return d->Lk;
+    int64_t last = i + d->Lk - d->Lq; /* last visible key index */
+    if (last < 0)
+        return 0;
+    return last + 1 < d->Lk ? last + 1 : d->Lk;
+}
+
+typedef struct {
+    const uint16_t* qrow; /* dqk */
+    const uint16_t* kh;   /* [Lk, dqk] of the row's K/V head */
+    const uint16_t* vh;   /* [Lk, dv] */
+    int64_t i;            /* query position */
+} row_ref_t;
+
+static row_ref_t locate_row(const dims_t* d, const uint16_t* q, const uint16_t* k,
+                            const uint16_t* v, int64_t r)
+{
+    row_ref_t rr;
+    int64_t i = r % d->Lq;
+    int64_t bh = r / d->Lq;
+    int64_t h = bh % d->Hq;
+    int64_t b = bh / d->Hq;
+    int64_t group = d->Hq / d->Hkv;
+    int64_t hk = h / group;
+    rr.qrow = q + ((b * d->Hq + h) * d->Lq + i) * d->dqk;
+    rr.kh = k + (b * d->Hkv + hk) * d->Lk * d->dqk;
+    rr.vh = v + (b * d->Hkv + hk) * d->Lk * d->dv;
+    rr.i = i;
+    return rr;
+}
+
+/* ------------------------------------------------------------------------ */
+/* 1. The definition, materialised: one full score row at a time.           */
+/* ------------------------------------------------------------------------ */
+
+static void exact_row(const dims_t* d, row_ref_t rr, double* qd, double* s,
+                      double* o_row, double* lse_out)
+{
+    int64_t n = valid_keys(d, rr.i);
+    for (int64_t c = 0; c < d->dv; ++c)
+        o_row[c] = 0.0;
+    if (n == 0) {
+        *lse_out = -INFINITY;
+        return;
+    }
+    for (int64_t c = 0; c < d->dqk; ++c)
+        qd[c] = bf16_bits_to_double(rr.qrow[c]);
+
+    /* S_i,j = scale * q_i . k_j for every visible key j */
+    double m = -INFINITY;
+    for (int64_t j = 0; j < n; ++j) {
+        const uint16_t* kj = rr.kh + j * d->dqk;
+        double dot = 0.0;
+        for (int64_t c = 0; c < d->dqk; ++c)
+            dot += qd[c] * bf16_bits_to_double(kj[c]);
+        s[j] = d->scale * dot;
+        if (s[j] > m)
+            m = s[j];
+    }
+    /* P_i,j = e^{S_i,j - m} / l with l = sum_j e^{S_i,j - m} */
+    double l = 0.0;
+    for (int64_t j = 0; j < n; ++j) {
+        s[j] = exp(s[j] - m);
+        l += s[j];
+    }
+    /* O_i = sum_j P_i,j V_j */
+    for (int64_t j = 0; j < n; ++j) {
+        const uint16_t* vj = rr.vh + j * d->dv;
+        double p = s[j] / l;
+        for (int64_t c = 0; c < d->dv; ++c)
+            o_row[c] += p * bf16_bits_to_double(vj[c]);
+    }
+    *lse_out = m + log(l);
+}
+
+/*
+ * oracle_attn_rows: exact attention for a list of query rows (or all rows
+ * when rows == NULL, in which case n_rows must equal B*Hq*Lq).
+ * Returns 0 on success, nonzero on bad arguments.
+ */
+int oracle_attn_rows(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                     int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk,
+                     int64_t dqk, int64_t dv, int causal, double scale,
+                     const int64_t* rows, int64_t n_rows,
+                     double* o, double* lse, int n_threads)
+{
+    dims_t d = {B, Hq, Hkv, Lq, Lk, dqk, dv, causal, scale};
+    int rc = check_dims(&d);
+    if (rc)
+        return rc;
+    if (!q || !k || !v || !o || !lse)
+        return 4;
+    int64_t total = B * Hq * Lq;
+    if (!rows && n_rows != total)
+        return 5;
+    if (rows)
+        for (int64_t t = 0; t < n_rows; ++t)
+            if (rows[t] < 0 || rows[t] >= total)
+                return 6;
+#ifdef _OPENMP
+    if (n_threads > 0)
+        omp_set_num_threads(n_threads);
+#else
+    (void)n_threads;
+#endif
+
+    int failed = 0;
+#pragma omp parallel
+    {
+        double* qd = (double*)malloc(sizeof(double) * (size_t)dqk);
+        double* s = (double*)malloc(sizeof(double) * (size_t)Lk);
+        int ok = qd && s;
+        /* every thread reaches the worksharing loop, even after a failed
+         * allocation, so the loop's barrier cannot deadlock */
+#pragma omp for schedule(dynamic, 16)
+        for (int64_t t = 0; t < n_rows; ++t) {
+            if (!ok) {
+#pragma omp atomic write
+                failed = 1;
+                continue;
+            }
+            int64_t r = rows ? rows[t] : t;
+            row_ref_t rr = locate_row(&d, q, k, v, r);
+            exact_row(&d, rr, qd, s, o + t * dv, lse + t);
+        }
+        free(qd);
+        free(s);
+    }
+    return failed ? 7 : 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* 2. The tiled method, block by block over K/V, for checking the algorithm. */
+/* ------------------------------------------------------------------------ */
+/*
+ * mode 0 -- always rescale, natural exponent ("Infra: Flash Attention",
+ *           Algorithm 1, FlashAttention-2 form):
+ *             m' = max(m, rowmax S);  alpha = e^{m - m'};  W = e^{S - m'}
+ *             l = alpha*l + rowsum W;  U = alpha*U + W V;  m = m'
+ *           finally O = U / l and L = m + log l.  A row whose whole tile is
+ *           masked skips the update (the pages' boundary conditions).
+ * mode 1 -- conditional rescaling in base 2 ("Flash Attention 4 ..." ch. 13,
+ *           section on online softmax and conditional rescaling):
+ *           the reference r is kept in raw-score units (unscaled q.k);
+ *           scale_log2 = log2(e) * scale;  the first block with a visible key
+ *           adopts its own max with acc_scale = 1; afterwards
+ *             cand = max(r, rowmax X);  delta = (r - cand) * scale_log2
+ *             delta >= -tau : keep r, acc_scale = 1
+ *             delta <  -tau : r = cand, acc_scale = 2^delta (a rescale event)
+ *           l = acc_scale*l + sum 2^{(x - r)*scale_log2};  U likewise with V.
+ *           Finally O = U / l and lse = scale*r + ln l (natural log; equal to
+ *           the definition because u(r)/l(r) does not depend on r, "Infra:
+ *           Flash Attention", section on why the exponent reference may lag).
+ * mode 2 -- as mode 1, but the switch decision is shared by a group of
+ *           `group` consecutive query rows of one head: if any row in the
+ *           group needs a rescale, every row of the group moves its reference
+ *           to its own candidate max (the FA4 review's wording that the whole
+ *           warp rescales when any thread needs it).
+ *
+ * Inputs as for oracle_attn_rows; bn = keys per block.  rows lists query
+ * rows (NULL = all).  Optional outputs: state[2*t] = final reference (mode 0:
+ * m in scaled units; modes 1/2: r in raw units), state[2*t+1] = final l;
+ * n_rescale (one counter for the whole call) counts rescale events.
+ */
+
+typedef struct {
+    double ref;  /* running reference (-inf before the first visible key) */
+    double l;    /* running denominator relative to ref */
+    double* u;   /* running numerator, dv values */
+    int64_t n;   /* visible keys of this row */
+    int64_t i;   /* query position */
+    int64_t events; /* blocks after the first at which the state was rescaled */
+    row_ref_t rr;
+    double* qd;
+} online_state_t;
+
+static void online_rows_group(const dims_t* d, int mode, int64_t bn, double tau,
+                              online_state_t* st, int64_t g, double* x,
+                              double* bmax, int* wants)
+{
+    const double scale_log2 = d->scale / M_LN2; /* = log2(e) * scale */
+    int64_t nmax = 0;
+    for (int64_t a = 0; a < g; ++a)
+        if (st[a].n > nmax)
+            nmax = st[a].n;
+
+    for (int64_t j0 = 0; j0 < nmax; j0 += bn) {
+        int64_t j1 = j0 + bn < d->Lk ? j0 + bn : d->Lk;
+        int any_switch = 0;
+        /* pass 1: raw scores x_ij of this block and the per-row decision */
+        for (int64_t a = 0; a < g; ++a) {
+            online_state_t* s = &st[a];
+            bmax[a] = -INFINITY;
+            wants[a] = 0;
+            for (int64_t j = j0; j < j1; ++j) {
+                double* xj = &x[a * bn + (j - j0)];
+                if (j >= s->n) {
+                    *xj = -INFINITY; /* masked (future key or past the end) */
+                    continue;
+                }
+                const uint16_t* kj = s->rr.kh + j * d->dqk;
+                double dot = 0.0;
+                for (int64_t c = 0; c < d->dqk; ++c)
+                    dot += s->qd[c] * bf16_bits_to_double(kj[c]);
+                *xj = (mode == 0) ? d->scale * dot : dot;
+                if (*xj > bmax[a])
+                    bmax[a] = *xj;
+            }
+            if (mode != 0 && bmax[a] > -INFINITY && s->ref > -INFINITY) {
+                double cand = bmax[a] > s->ref ? bmax[a] : s->ref;
+                double delta = (s->ref - cand) * scale_log2;
+                if (delta < -tau)
+                    wants[a] = 1;
+            }
+            any_switch |= wants[a];
+        }
+        /* pass 2: update each row's state */
+        for (int64_t a = 0; a < g; ++a) {
+            online_state_t* s = &st[a];
+            if (bmax[a] == -INFINITY)
+                continue; /* the whole tile row is masked: skip the update */
+            double acc_scale;
+            double* xa = &x[a * bn];
+            if (mode == 0) {
+                double m_new = bmax[a] > s->ref ? bmax[a] : s->ref;
+                acc_scale = exp(s->ref - m_new); /* e^{-inf} = 0 at the start */
+                s->ref = m_new;
+                s->l *= acc_scale;
+                for (int64_t c = 0; c < d->dv; ++c)
+                    s->u[c] *= acc_scale;
+                for (int64_t j = j0; j < j1; ++j) {
+                    double w = exp(xa[j - j0] - s->ref); /* e^{-inf} = 0 */
+                    if (w == 0.0)
+                        continue;
+                    s->l += w;
+                    const uint16_t* vj = s->rr.vh + j * d->dv;
+                    for (int64_t c = 0; c < d->dv; ++c)
+                        s->u[c] += w * bf16_bits_to_double(vj[c]);
+                }
+                continue;
+            }
+            if (s->ref == -INFINITY) {
+                /* first block with a visible key: adopt its max */
+                s->ref = bmax[a];
+                acc_scale = 1.0;
+            } else {
+                double cand = bmax[a] > s->ref ? bmax[a] : s->ref;
+                int do_switch = (mode == 1) ? wants[a] : any_switch;
+                if (do_switch) {
+                    acc_scale = exp2((s->ref - cand) * scale_log2);
+                    s->ref = cand;
+                    ++s->events;
+                } else {
+                    acc_scale = 1.0;
+                }
+            }
+            s->l *= acc_scale;
+            for (int64_t c = 0; c < d->dv; ++c)
+                s->u[c] *= acc_scale;
+            for (int64_t j = j0; j < j1; ++j) {
+                double xv = xa[j - j0];
+                if (xv == -INFINITY)
+                    continue;
+                double w = exp2((xv - s->ref) * scale_log2);
+                s->l += w;
+                const uint16_t* vj = s->rr.vh + j * d->dv;
+                for (int64_t c = 0; c < d->dv; ++c)
+                    s->u[c] += w * bf16_bits_to_double(vj[c]);
+            }
+        }
+    }
+}
+
+int oracle_online_rows(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                       int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk,
+                       int64_t dqk, int64_t dv, int causal, double scale,
+                       int64_t bn, int mode, double tau, int64_t group,
+                       const int64_t* rows, int64_t n_rows,
+                       double* o, double* lse, double* state,
+                       int64_t* n_rescale, int n_threads)
+{
+    dims_t d = {B, Hq, Hkv, Lq, Lk, dqk, dv, causal, scale};
+    int rc = check_dims(&d);
+    if (rc)
+        return rc;
+    if (!q || !k || !v || !o || !lse)
+        return 4;
+    if (bn < 1 || mode < 0 || mode > 2 || !(tau >= 0.0) || (mode == 2 && group < 1))
+        return 8;
+    if (mode != 2)
+        group = 1;
+    int64_t total = B * Hq * Lq;
+    if (!rows && n_rows != total)
+        return 5;
+    if (rows)
+        for (int64_t t = 0; t < n_rows; ++t)
+            if (rows[t] < 0 || rows[t] >= total)
+                return 6;
+#ifdef _OPENMP
+    if (n_threads > 0)
+        omp_set_num_threads(n_threads);
+#else
+    (void)n_threads;
+#endif
+
+    int64_t events = 0;
+    int failed = 0;
+#pragma omp parallel reduction(+ : events)
+    {
+        online_state_t* st = (online_state_t*)calloc((size_t)group, sizeof *st);
+        double* ubuf = (double*)malloc(sizeof(double) * (size_t)(group * dv));
+        double* qbuf = (double*)malloc(sizeof(double) * (size_t)(group * dqk));
+        double* x = (double*)malloc(sizeof(double) * (size_t)(group * bn));
+        double* bmax = (double*)malloc(sizeof(double) * (size_t)group);
+        int* wants = (int*)malloc(sizeof(int) * (size_t)group);
+        int ok = st && ubuf && qbuf && x && bmax && wants;
+#pragma omp for schedule(dynamic, 4)
+        for (int64_t t = 0; t < n_rows; ++t) {
+            if (!ok) {
+#pragma omp atomic write
+                failed = 1;
+                continue;
+            }
+            {
+                int64_t r = rows ? rows[t] : t;
+                /* The group holding row r: rows of the same (b, h) whose
+                 * positions share i / group.  Every member is computed so the
+                 * shared decision is taken over the whole group. */
+                int64_t i = r % Lq;
+                int64_t first = r - (i % group);
+                int64_t g = group;
+                if ((i - i % group) + g > Lq)
+                    g = Lq - (i - i % group);
+                int64_t mine = r - first;
+                for (int64_t a = 0; a < g; ++a) {
+                    st[a].rr = locate_row(&d, q, k, v, first + a);
+                    st[a].i = st[a].rr.i;
+                    st[a].n = valid_keys(&d, st[a].i);
+                    st[a].ref = -INFINITY;
+                    st[a].l = 0.0;
+                    st[a].events = 0;
+                    st[a].u = ubuf + a * dv;
+                    st[a].qd = qbuf + a * dqk;
+                    for (int64_t c = 0; c < dv; ++c)
+                        st[a].u[c] = 0.0;
+                    for (int64_t c = 0; c < dqk; ++c)
+                        st[a].qd[c] = bf16_bits_to_double(st[a].rr.qrow[c]);
+                }
+                online_rows_group(&d, mode, bn, tau, st, g, x, bmax, wants);
+                online_state_t* s = &st[mine];
+                double* orow = o + t * dv;
+                if (s->l > 0.0) {
+                    for (int64_t c = 0; c < dv; ++c)
+                        orow[c] = s->u[c] / s->l;
+                    lse[t] = (mode == 0) ? s->ref + log(s->l)
+                                         : scale * s->ref + log(s->l);
+                } else {
+                    for (int64_t c = 0; c < dv; ++c)
+                        orow[c] = 0.0;
+                    lse[t] = -INFINITY;
+                }
+                if (state) {
+                    state[2 * t] = s->ref;
+                    state[2 * t + 1] = s->l;
+                }
+                events += s->events; /* events of the requested row only */
+            }
+        }
+        free(st);
+        free(ubuf);
+        free(qbuf);
+        free(x);
+        free(bmax);
+        free(wants);
+    }
+    if (n_rescale)
+        *n_rescale = events;
+    return failed ? 7 : 0;
+}

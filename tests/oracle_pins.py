@@ -1,0 +1,396 @@
+"""Pins that tie the CPU oracle to facts fixed outside itself.
+
+Every ``pin_*`` function takes an oracle handle (``oracle.Oracle``) and raises
+AssertionError when the oracle disagrees with:
+  * values the pages print for their worked example (tests/golden/),
+  * closed forms (uniform weights, a single visible key, powers of two computed
+    with exact rationals),
+  * a library routine for the same special case (torch's float64
+    scaled_dot_product_attention and logsumexp on the CPU),
+  * invariants (permutation, GQA == repeated K/V, zero padding, a constant
+    score shift, value rows of ones),
+  * the tiled method's own algebra (always-rescale and conditional variants
+    agree with the definition; the rescale-event count behaves as the pages
+    describe).
+They run unchanged against deliberately broken copies of the oracle in
+test_oracle_mutations.py, which checks that each planted mistake trips at
+least one pin.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import torch
+import torch.nn.functional as F
+
+from exact_attention_forward_02_amd.inputs import make_qkv
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+LN2 = math.log(2.0)
+
+
+def _bf(values, shape):
+    """Small exactly-representable values -> bf16 tensor of the given shape."""
+    t = torch.tensor(values, dtype=torch.float32).reshape(shape)
+    back = t.to(torch.bfloat16).to(torch.float32)
+    assert torch.equal(back, t), "fixture value not exact in bf16"
+    return t.to(torch.bfloat16)
+
+
+def _close(a, b, tol, what):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    assert a.shape == b.shape, f"{what}: shape {a.shape} != {b.shape}"
+    same_inf = np.isinf(a) & np.isinf(b) & (np.sign(a) == np.sign(b))
+    with np.errstate(invalid="ignore"):
+        err = np.where(same_inf, 0.0, np.abs(a - b))  # NaN stays NaN and fails
+    worst = float(np.max(err)) if err.size else 0.0
+    assert worst <= tol, f"{what}: max error {worst:.3e} > {tol:.1e}"
+
+
+def _visible(Lq, Lk, causal):
+    """Boolean [Lq, Lk]: key j visible to query i (bottom-right causal)."""
+    i = torch.arange(Lq)[:, None]
+    j = torch.arange(Lk)[None, :]
+    return (j <= i + (Lk - Lq)) if causal else torch.ones(Lq, Lk, dtype=torch.bool)
+
+
+# --------------------------------------------------------------------------
+# Worked example printed on the pages, and the conditional cases derived from it
+# --------------------------------------------------------------------------
+
+def _example_tensors(key_exponents, values):
+    n = len(key_exponents)
+    q = _bf([1.0], (1, 1, 1, 1))
+    k = _bf([float(e) for e in key_exponents], (1, 1, n, 1))
+    v = _bf([float(x) for x in values], (1, 1, n, 1))
+    return q, k, v
+
+
+def pin_worked_example(orc):
+    with open(os.path.join(GOLDEN, "online_merge_example.json"), encoding="utf-8") as f:
+        fx = json.load(f)
+    exps = fx["exp_scores"]
+    keys = [round(math.log2(e)) for e in exps]
+    assert [2 ** e for e in keys] == exps
+    q, k, v = _example_tensors(keys, fx["values"])
+    want_o = fx["output"]["num"] / fx["output"]["den"]
+    want_lse = math.log(sum(exps))
+
+    o, lse = orc.attn_rows(q, k, v, causal=False, scale=LN2)
+    _close(o[0, 0], want_o, 1e-14, "worked example O")
+    _close(lse[0], want_lse, 1e-14, "worked example lse")
+
+    # the pages' two-block merge, always rescaling (natural exponent)
+    o, lse, st, _ = orc.online_rows(q, k, v, causal=False, scale=LN2, bn=2, mode=0)
+    _close(st[0, 1], fx["merge"]["l"], 1e-14, "merged l")
+    _close(o[0, 0] * st[0, 1], fx["merge"]["u"], 1e-14, "merged u")
+    _close(st[0, 0], math.log(8.0), 1e-14, "merged m")
+    _close(o[0, 0], want_o, 1e-14, "online O")
+
+    # each block on its own
+    for name, ref_m in (("block_a", math.log(2.0)), ("block_b", math.log(8.0))):
+        sel = fx[name]["keys"]
+        ob, _, sb, _ = orc.online_rows(q, k[:, :, sel], v[:, :, sel], causal=False,
+                                       scale=LN2, bn=2, mode=0)
+        _close(sb[0, 1], fx[name]["l"], 1e-14, f"{name} l")
+        _close(ob[0, 0] * sb[0, 1], fx[name]["u"], 1e-14, f"{name} u")
+        _close(sb[0, 0], ref_m, 1e-14, f"{name} m")
+
+
+def _exact_weighted_mean(exponents, values):
+    w = [Fraction(2) ** e for e in exponents]
+    num = sum(wi * Fraction(vi) for wi, vi in zip(w, values))
+    return num / sum(w), sum(w)
+
+
+def pin_conditional_cases(orc):
+    """Threshold 8 in base 2 with scale = ln 2 (so scale*log2(e) = 1):
+    a jump of 2 keeps the reference, 10 moves it, exactly 8 keeps it."""
+    values = [1, 2, 3, 4]
+    cases = [
+        # exponents, expect_events, final ref (raw units), final l
+        ([0, 1, 2, 3], 0, 1.0, 7.5),
+        ([0, 1, 10, 11], 1, 11.0, 1.5 / 1024 + 1.5),
+        ([0, 1, 8, 9], 0, 1.0, 385.5),
+    ]
+    for exps, want_events, want_ref, want_l in cases:
+        q, k, v = _example_tensors(exps, values)
+        frac, total = _exact_weighted_mean(exps, values)
+        want_lse = math.log(float(total))
+        o, lse, st, ev = orc.online_rows(q, k, v, causal=False, scale=LN2, bn=2,
+                                         mode=1, tau=8.0)
+        assert ev == want_events, f"exponents {exps}: {ev} rescale events, want {want_events}"
+        _close(st[0, 0], want_ref, 0.0, f"exponents {exps}: final reference")
+        _close(st[0, 1], want_l, 1e-12, f"exponents {exps}: final l")
+        _close(o[0, 0], float(frac), 1e-14, f"exponents {exps}: O")
+        _close(lse[0], want_lse, 1e-14, f"exponents {exps}: lse")
+        om, lm = orc.attn_rows(q, k, v, causal=False, scale=LN2)
+        _close(om[0, 0], float(frac), 1e-14, f"exponents {exps}: definition O")
+        _close(lm[0], want_lse, 1e-14, f"exponents {exps}: definition lse")
+    # the same firing case under the shared (group) decision and always-rescale
+    q, k, v = _example_tensors([0, 1, 10, 11], values)
+    for mode in (0, 2):
+        o, _, _, _ = orc.online_rows(q, k, v, causal=False, scale=LN2, bn=2, mode=mode,
+                                     tau=8.0, group=1)
+        _close(o[0, 0], 11269 / 3075, 1e-14, f"firing case mode {mode}")
+
+
+# --------------------------------------------------------------------------
+# Closed forms
+# --------------------------------------------------------------------------
+
+def pin_zero_query(orc):
+    """Q = 0 makes every visible score 0: O_i is the mean of the visible V rows
+    and lse_i = ln(number of visible keys); a row with none gives 0 / -inf."""
+    for causal, Lq, Lk in ((False, 5, 5), (True, 5, 5), (True, 3, 7), (True, 6, 4),
+                           (False, 4, 9)):
+        _, k, v = make_qkv(1, 2, 1, Lq, Lk, 8, 6, seed=11 + Lq * 31 + Lk)
+        q = torch.zeros((1, 2, Lq, 8), dtype=torch.bfloat16)
+        o, lse = orc.attn_rows(q, k, v, causal=causal, scale=0.3)
+        vis = _visible(Lq, Lk, causal)
+        vd = v.double()[0, 0]
+        want_o = np.zeros((2 * Lq, 6))
+        want_lse = np.zeros(2 * Lq)
+        for h in range(2):
+            for i in range(Lq):
+                n = int(vis[i].sum())
+                r = h * Lq + i
+                if n == 0:
+                    want_lse[r] = -math.inf
+                    continue
+                want_o[r] = vd[vis[i]].mean(0).numpy()
+                want_lse[r] = math.log(n)
+        _close(o, want_o, 1e-14, f"Q=0 O (causal={causal}, Lq={Lq}, Lk={Lk})")
+        _close(lse, want_lse, 1e-14, f"Q=0 lse (causal={causal}, Lq={Lq}, Lk={Lk})")
+
+
+def pin_causal_first_row(orc):
+    """With Lq = Lk and the causal mask, query 0 sees key 0 only:
+    O_0 = V_0 and lse_0 = scale * q_0 . k_0."""
+    q, k, v = make_qkv(2, 2, 2, 7, 7, 16, 8, seed=5)
+    scale = 0.37
+    rows = [0, 7, 14, 21]  # position 0 of every (b, h)
+    o, lse = orc.attn_rows(q, k, v, causal=True, scale=scale, rows=rows)
+    for t, r in enumerate(rows):
+        b, h = divmod(r // 7, 2)
+        qd = [float(x) for x in q[b, h, 0].double()]
+        kd = [float(x) for x in k[b, h, 0].double()]
+        want = scale * math.fsum(a * c for a, c in zip(qd, kd))
+        _close(o[t], v[b, h, 0].double().numpy(), 0.0, f"causal row 0 O (row {r})")
+        _close(lse[t], want, 1e-12, f"causal row 0 lse (row {r})")
+
+
+def pin_powers_of_two(orc):
+    """scale = ln 2, q = e_0, k_j = n_j e_0: weights are exactly 2^{n_j}, so O and
+    lse follow from exact rational arithmetic."""
+    rng = np.random.default_rng(7)
+    for causal in (False, True):
+        L = 12
+        n = rng.integers(-30, 31, size=L)
+        q = torch.zeros((1, 1, L, 4), dtype=torch.float32)
+        q[..., 0] = 1.0
+        q = q.to(torch.bfloat16)
+        kf = torch.from_numpy(rng.standard_normal((1, 1, L, 4))).float()
+        kf[..., 0] = torch.from_numpy(n.astype(np.float32))
+        k = kf.to(torch.bfloat16)
+        assert torch.equal(k[0, 0, :, 0].float(), torch.from_numpy(n.astype(np.float32)))
+        v = torch.from_numpy(rng.standard_normal((1, 1, L, 3))).float().to(torch.bfloat16)
+        o, lse = orc.attn_rows(q, k, v, causal=causal, scale=LN2)
+        vv = v[0, 0].double().numpy()
+        for i in range(L):
+            last = i if causal else L - 1
+            w = [Fraction(2) ** int(e) for e in n[: last + 1]]
+            tot = sum(w)
+            for c in range(3):
+                num = sum(wi * Fraction(float(vv[j, c])) for j, wi in enumerate(w))
+                _close(o[i, c], float(num / tot), 1e-13, f"powers of two O[{i},{c}]")
+            _close(lse[i], math.log(float(tot)), 1e-13, f"powers of two lse[{i}]")
+
+
+# --------------------------------------------------------------------------
+# Library routine on the same special cases (torch float64 CPU)
+# --------------------------------------------------------------------------
+
+SDPA_SHAPES = [
+    # B, Hq, Hkv, Lq, Lk, dqk, dv, causal
+    (1, 1, 1, 9, 9, 8, 8, False),
+    (2, 4, 2, 13, 21, 16, 8, False),
+    (2, 4, 1, 17, 17, 8, 12, True),
+    (1, 6, 3, 11, 29, 24, 16, True),
+    (1, 2, 2, 19, 10, 8, 8, True),   # Lq > Lk: leading rows see no key
+    (3, 2, 2, 1, 33, 64, 64, False),
+]
+
+
+def _library_reference(q, k, v, causal, scale):
+    """torch SDPA (float64, CPU) for O and torch.logsumexp for lse."""
+    B, Hq, Lq, _ = q.shape
+    Hkv, Lk = k.shape[1], k.shape[2]
+    qd, kd, vd = q.double(), k.double(), v.double()
+    vis = _visible(Lq, Lk, causal)
+    o = F.scaled_dot_product_attention(qd, kd, vd, attn_mask=vis, scale=scale,
+                                       enable_gqa=(Hq != Hkv))
+    kr = kd.repeat_interleave(Hq // Hkv, dim=1)
+    s = scale * torch.matmul(qd, kr.transpose(-1, -2))
+    s = s.masked_fill(~vis, -math.inf)
+    lse = torch.logsumexp(s, dim=-1)
+    empty = ~vis.any(dim=1)  # rows with no visible key
+    o[:, :, empty] = 0.0
+    return o.reshape(B * Hq * Lq, -1).numpy(), lse.reshape(-1).numpy()
+
+
+def pin_library_sdpa(orc):
+    for idx, (B, Hq, Hkv, Lq, Lk, dqk, dv, causal) in enumerate(SDPA_SHAPES):
+        q, k, v = make_qkv(B, Hq, Hkv, Lq, Lk, dqk, dv, seed=100 + idx)
+        scale = 1.0 / math.sqrt(dqk)
+        o, lse = orc.attn_rows(q, k, v, causal=causal, scale=scale)
+        want_o, want_lse = _library_reference(q, k, v, causal, scale)
+        tag = f"shape {idx} {(B, Hq, Hkv, Lq, Lk, dqk, dv, causal)}"
+        _close(o, want_o, 1e-12, f"{tag} O vs torch SDPA")
+        _close(lse, want_lse, 1e-12, f"{tag} lse vs torch logsumexp")
+
+
+# --------------------------------------------------------------------------
+# Invariants
+# --------------------------------------------------------------------------
+
+def pin_value_ones(orc):
+    """V rows of ones: O is 1 wherever a key is visible (each P row sums to 1)."""
+    q, k, _ = make_qkv(1, 3, 1, 10, 14, 8, 5, seed=21, q_mult=4.0)
+    v = torch.ones((1, 1, 14, 5), dtype=torch.bfloat16)
+    for causal in (False, True):
+        o, _ = orc.attn_rows(q, k, v, causal=causal, scale=0.9)
+        _close(o, np.ones_like(o), 1e-13, f"V = 1 (causal={causal})")
+
+
+def pin_permutation(orc):
+    """Non-causal: permuting K and V rows together changes nothing."""
+    q, k, v = make_qkv(2, 2, 2, 6, 15, 16, 8, seed=31, q_mult=3.0)
+    perm = torch.from_numpy(np.random.default_rng(3).permutation(15))
+    o1, l1 = orc.attn_rows(q, k, v, causal=False)
+    o2, l2 = orc.attn_rows(q, k[:, :, perm].contiguous(), v[:, :, perm].contiguous(),
+                           causal=False)
+    _close(o1, o2, 1e-13, "permuted K/V: O")
+    _close(l1, l2, 1e-13, "permuted K/V: lse")
+
+
+def pin_gqa_repeat(orc):
+    """GQA equals MHA with each K/V head repeated for its group of query heads."""
+    q, k, v = make_qkv(2, 6, 2, 9, 12, 8, 8, seed=41)
+    kr = k.repeat_interleave(3, dim=1).contiguous()
+    vr = v.repeat_interleave(3, dim=1).contiguous()
+    for causal in (False, True):
+        o1, l1 = orc.attn_rows(q, k, v, causal=causal)
+        o2, l2 = orc.attn_rows(q, kr, vr, causal=causal)
+        _close(o1, o2, 0.0, f"GQA vs repeated K/V O (causal={causal})")
+        _close(l1, l2, 0.0, f"GQA vs repeated K/V lse (causal={causal})")
+
+
+def pin_zero_padding(orc):
+    """Zero columns appended to Q and K (same scale) change nothing: a (192, 128)
+    problem whose last 64 q/k columns are zero equals the (128, 128) one."""
+    q, k, v = make_qkv(1, 2, 2, 8, 11, 128, 128, seed=51)
+    z = torch.zeros((1, 2, 8, 64), dtype=torch.bfloat16)
+    zk = torch.zeros((1, 2, 11, 64), dtype=torch.bfloat16)
+    qp = torch.cat([q, z], dim=-1).contiguous()
+    kp = torch.cat([k, zk], dim=-1).contiguous()
+    s = 1.0 / math.sqrt(128.0)
+    for causal in (False, True):
+        o1, l1 = orc.attn_rows(q, k, v, causal=causal, scale=s)
+        o2, l2 = orc.attn_rows(qp, kp, v, causal=causal, scale=s)
+        _close(o1, o2, 0.0, f"zero padding O (causal={causal})")
+        _close(l1, l2, 0.0, f"zero padding lse (causal={causal})")
+
+
+def pin_constant_shift(orc):
+    """Adding the same constant to every score of a row leaves O unchanged and
+    shifts lse by that constant.  Realised by an extra column: q' = [q, c],
+    k' = [k, 1], so each score gains scale * c."""
+    q, k, v = make_qkv(1, 2, 1, 7, 9, 8, 4, seed=61)
+    c = 6.0
+    qs = torch.cat([q, torch.full((1, 2, 7, 1), c, dtype=torch.bfloat16)], -1).contiguous()
+    ks = torch.cat([k, torch.ones((1, 1, 9, 1), dtype=torch.bfloat16)], -1).contiguous()
+    s = 0.5
+    for causal in (False, True):
+        o1, l1 = orc.attn_rows(q, k, v, causal=causal, scale=s)
+        o2, l2 = orc.attn_rows(qs, ks, v, causal=causal, scale=s)
+        _close(o1, o2, 1e-13, f"score shift O (causal={causal})")
+        _close(l2 - l1, np.full_like(l1, s * c), 1e-12, f"score shift lse (causal={causal})")
+
+
+# --------------------------------------------------------------------------
+# The tiled method against the definition
+# --------------------------------------------------------------------------
+
+ONLINE_SHAPES = [
+    # B, Hq, Hkv, Lq, Lk, dqk, dv, causal, q_mult
+    (1, 1, 1, 37, 37, 16, 16, False, 1.0),
+    (1, 2, 1, 40, 53, 8, 12, True, 6.0),
+    (2, 4, 2, 33, 33, 16, 8, True, 6.0),
+    (1, 2, 2, 25, 12, 8, 8, True, 1.0),   # Lq > Lk
+    (1, 1, 1, 64, 200, 32, 32, False, 6.0),
+]
+
+
+def pin_online_matches_definition(orc):
+    for idx, (B, Hq, Hkv, Lq, Lk, dqk, dv, causal, qm) in enumerate(ONLINE_SHAPES):
+        q, k, v = make_qkv(B, Hq, Hkv, Lq, Lk, dqk, dv, seed=200 + idx, q_mult=qm)
+        o_ref, l_ref = orc.attn_rows(q, k, v, causal=causal)
+        for mode in (0, 1, 2):
+            for bn in (1, 7, 16, 64):
+                for tau in ((8.0,) if mode == 0 else (0.0, 8.0)):
+                    o, l, _, _ = orc.online_rows(q, k, v, causal=causal, bn=bn, mode=mode,
+                                                 tau=tau, group=8)
+                    tag = f"shape {idx} mode {mode} bn {bn} tau {tau}"
+                    _close(o, o_ref, 1e-12, f"{tag}: O")
+                    _close(l, l_ref, 1e-12, f"{tag}: lse")
+
+
+def pin_rescale_events(orc):
+    """Scores with a wide spread (Q scaled by 6) move the reference past the
+    threshold; an unreachable threshold never rescales; threshold 0 rescales at
+    every increase of the running max; a shared decision rescales at least as
+    often as the per-row one."""
+    q, k, v = make_qkv(1, 1, 1, 64, 256, 64, 64, seed=1, q_mult=6.0)
+    _, _, _, ev8 = orc.online_rows(q, k, v, causal=False, bn=64, mode=1, tau=8.0)
+    _, _, _, evbig = orc.online_rows(q, k, v, causal=False, bn=64, mode=1, tau=1e9)
+    _, _, _, ev0 = orc.online_rows(q, k, v, causal=False, bn=64, mode=1, tau=0.0)
+    _, _, _, evg = orc.online_rows(q, k, v, causal=False, bn=64, mode=2, tau=8.0, group=32)
+    assert ev8 > 0, "Q x 6 should fire at least one rescale at threshold 8"
+    assert evbig == 0, "an unreachable threshold must never rescale"
+    assert ev0 >= ev8, "threshold 0 must rescale at least as often as threshold 8"
+    assert evg >= ev8, "a shared decision must rescale at least as often as per row"
+    # count at threshold 0 equals the number of blocks after the first whose
+    # block max exceeds the running max (independent count from the scores)
+    s = torch.matmul(q.double(), k.double().transpose(-1, -2))[0, 0]
+    want = 0
+    for i in range(64):
+        run = s[i, :64].max().item()
+        for j0 in range(64, 256, 64):
+            bm = s[i, j0:j0 + 64].max().item()
+            if bm > run:
+                want += 1
+                run = bm
+    assert ev0 == want, f"threshold-0 events {ev0} != increases of the running max {want}"
+
+
+ALL_PINS = [
+    pin_worked_example,
+    pin_conditional_cases,
+    pin_zero_query,
+    pin_causal_first_row,
+    pin_powers_of_two,
+    pin_library_sdpa,
+    pin_value_ones,
+    pin_permutation,
+    pin_gqa_repeat,
+    pin_zero_padding,
+    pin_constant_shift,
+    pin_online_matches_definition,
+    pin_rescale_events,
+]

@@ -1,0 +1,55 @@
+"""Planted mistakes in copies of the oracle must each trip at least one pin.
+
+Each mutation rewrites one line of oracle/attn_oracle.c (the committed source
+is never touched), builds the copy into a temporary library and runs every pin
+against it.  A mutation that no pin notices would mean the pins leave that
+part of the oracle unchecked.  CPU only.
+"""
+import os
+import tempfile
+
+import pytest
+
+import oracle
+import oracle_pins
+
+MUTATIONS = {
+    "gqa_head_mapping": ("int64_t hk = h / group;", "int64_t hk = h % group;"),
+    "causal_top_left": ("int64_t last = i + d->Lk - d->Lq;", "int64_t last = i;"),
+    "dropped_scale": ("s[j] = d->scale * dot;", "s[j] = dot;"),
+    "exp_sign": ("s[j] = exp(s[j] - m);", "s[j] = exp(m - s[j]);"),
+    "lse_dropped_max": ("*lse_out = m + log(l);", "*lse_out = log(l);"),
+    "transposed_k": ("            dot += qd[c] * bf16_bits_to_double(kj[c]);\n        s[j]",
+                     "            dot += qd[c] * bf16_bits_to_double(rr.kh[c * d->Lk + j]);\n        s[j]"),
+    "value_index": ("o_row[c] += p * bf16_bits_to_double(vj[c]);",
+                    "o_row[c] += p * bf16_bits_to_double(vj[d->dv - 1 - c]);"),
+    "bf16_widening": ("uint32_t word = ((uint32_t)bits) << 16;",
+                      "uint32_t word = ((uint32_t)bits) << 15;"),
+    "threshold_not_strict": ("if (delta < -tau)", "if (delta <= -tau)"),
+    "rescale_dropped": ("acc_scale = exp2((s->ref - cand) * scale_log2);", "acc_scale = 1.0;"),
+    "online_lse_units": ("lse[t] = (mode == 0) ? s->ref + log(s->l)\n                                         : scale * s->ref + log(s->l);",
+                         "lse[t] = s->ref + log(s->l);"),
+    "first_block_not_adopted": ("s->ref = bmax[a];\n                acc_scale = 1.0;",
+                                "s->ref = 0.0;\n                acc_scale = 1.0;"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_mutation_is_caught(name):
+    old, new = MUTATIONS[name]
+    with open(oracle.SOURCE, encoding="utf-8") as f:
+        src = f.read()
+    assert src.count(old) == 1, f"mutation site for {name} not found exactly once"
+    with tempfile.TemporaryDirectory() as tmp:
+        path_c = os.path.join(tmp, "mutant.c")
+        with open(path_c, "w", encoding="utf-8") as f:
+            f.write(src.replace(old, new))
+        lib = oracle.build(path_c, os.path.join(tmp, "libmutant.so"))
+        mutant = oracle.Oracle(lib)
+        tripped = []
+        for pin in oracle_pins.ALL_PINS:
+            try:
+                pin(mutant)
+            except (AssertionError, ValueError):
+                tripped.append(pin.__name__)
+        assert tripped, f"no pin notices the planted mistake {name!r}"
