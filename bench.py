@@ -1,0 +1,195 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused attention forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one call of the whole hot path (one fused forward kernel) over the
+workload's seeded synthetic inputs, already resident in HBM.  Prints ONE JSON
+line: throughput in TFLOP/s (FLOPs = 2*B*Hq*Lq*Lk*(d_qk+d_v), halved when
+causal), the roofline object of the kernel (per-launch duration from HIP
+events on the launch stream), and the CPU oracle timed on a bounded sample of
+the same workload on this host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd TFLOP/s (bf16, 1 GPU) and % of MI355X dense bf16 MFMA peak"
+PEAK_BF16_TFLOPS = 2500.0  # MI355X published dense bf16 MFMA peak
+KERNEL_SOURCE = os.path.join(ROOT, "exact_attention_forward_02_amd", "csrc",
+                             "attn_fwd_kernel.hip")
+
+
+def kernel_source_digest() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel source; otherwise None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_attn_fwd_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path, encoding="utf-8") as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_sha256") != kernel_source_digest():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def host_threads() -> int:
+    env = os.environ.get("OMP_NUM_THREADS")
+    if env and env.isdigit() and int(env) > 0:
+        return int(env)
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:
+        return os.cpu_count() or 1
+
+
+def cpu_baseline(w, q, k, v, target_s: float = 12.0):
+    """Oracle (fp64, as it stands) on a bounded random sample of query rows."""
+    import oracle
+    from exact_attention_forward_02_amd.inputs import sample_rows
+
+    orc = oracle.load()
+    threads = host_threads()
+    per_row_flops = 2.0 * w.Lk * (w.dqk + w.dv)  # non-causal rows see every key
+    if w.causal:
+        per_row_flops /= 2.0  # average visible keys under the causal mask
+    total_rows = w.B * w.Hq * w.Lq
+    probe = sample_rows(w.B, w.Hq, w.Lq, 8 * threads, seed=12345).numpy()
+    t0 = time.perf_counter()
+    orc.attn_rows(q, k, v, causal=w.causal, rows=probe, threads=threads)
+    t_probe = time.perf_counter() - t0
+    n = int(min(total_rows, max(len(probe), len(probe) * target_s / max(t_probe, 1e-6))))
+    rows = sample_rows(w.B, w.Hq, w.Lq, n, seed=54321).numpy()
+    t0 = time.perf_counter()
+    orc.attn_rows(q, k, v, causal=w.causal, rows=rows, threads=threads)
+    dt = time.perf_counter() - t0
+    # exact FLOPs of the sampled rows
+    if w.causal:
+        off = w.Lk - w.Lq
+        i = rows % w.Lq
+        keys = (i + off + 1).clip(0, w.Lk)
+        flops = float((2.0 * keys * (w.dqk + w.dv)).sum())
+    else:
+        flops = per_row_flops * len(rows)
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{len(rows)} of {total_rows} query rows of {w.name} drawn at random "
+                  f"(seeded), fp64 materialised softmax, {dt:.1f} s",
+        "seconds": dt,
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="mha_l2k")
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip the oracle timing (for profiler runs)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this kernel runs on a single MI355X and "
+              "the multi-GPU path is not built; run with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import torch
+
+    from exact_attention_forward_02_amd import attn_fwd
+    from exact_attention_forward_02_amd.inputs import WORKLOADS, workload_qkv
+
+    if args.workload not in WORKLOADS:
+        print(f"unknown workload {args.workload}; choose from {sorted(WORKLOADS)}",
+              file=sys.stderr)
+        return 2
+    w = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    q, k, v = workload_qkv(w)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    o = torch.empty((w.B, w.Hq, w.Lq, w.dv), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((w.B, w.Hq, w.Lq), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    for _ in range(args.warmup):
+        attn_fwd(qd, kd, vd, causal=w.causal, out=o, lse=lse, stream=stream)
+    torch.cuda.synchronize()
+
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        attn_fwd(qd, kd, vd, causal=w.causal, out=o, lse=lse, stream=stream)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    ms_launch = sum(launch_ms) / len(launch_ms)
+    ms_step = wall * 1e3 / args.steps
+
+    flops = w.flops()
+    value = flops * args.steps / wall / 1e12
+    achieved = flops / (ms_launch * 1e-3) / 1e12
+    traffic = measured_traffic(w.name)
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Lq": w.Lq,
+                   "Lk": w.Lk, "d_qk": w.dqk, "d_v": w.dv, "causal": w.causal,
+                   "flops_per_step": flops},
+        "pct_of_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic,
+            "kernel": "attn_fwd_kernel",
+            "ms_per_launch": round(ms_launch, 4),
+            "ms_per_launch_min": round(min(launch_ms), 4),
+            "ms_per_launch_max": round(max(launch_ms), 4),
+        },
+    }
+    if not args.no_cpu_baseline:
+        cb = cpu_baseline(w, q, k, v)
+        cb.pop("seconds", None)
+        cb["value"] = float(f"{cb['value']:.4g}")
+        result["cpu_baseline"] = cb
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,136 @@
+"""ctypes binding of libattn_fwd.so (include/attn_fwd.h).
+
+Argument marshalling only: every step of the attention computation runs in
+the library's gfx950 kernels.  PyTorch supplies device memory and the current
+stream.  If the library cannot be loaded the calls raise; there is no other
+code path.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import threading
+
+import torch
+
+from . import build as _build
+
+_lock = threading.Lock()
+_lib = None
+
+ATTN_OK = 0
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(_build.LIBRARY):
+            _build.build()
+        try:
+            lib = ctypes.CDLL(_build.LIBRARY)
+        except OSError as exc:  # pragma: no cover - exercised only when broken
+            raise RuntimeError(f"cannot load the HIP attention library {_build.LIBRARY}: {exc}")
+        vp, i = ctypes.c_void_p, ctypes.c_int
+        lib.attn_fwd.restype = i
+        lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, ctypes.c_float, vp]
+        lib.attn_fwd_dbg.restype = i
+        lib.attn_fwd_dbg.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i,
+                                     ctypes.c_float, vp, ctypes.c_float, vp]
+        lib.attn_status_string.restype = ctypes.c_char_p
+        lib.attn_status_string.argtypes = [i]
+        lib.attn_abi_version.restype = i
+        lib.attn_abi_version.argtypes = []
+        _lib = lib
+        return lib
+
+
+def library():
+    """The loaded ctypes library (loads it on first use)."""
+    return _load()
+
+
+def status_string(rc: int) -> str:
+    return _load().attn_status_string(int(rc)).decode()
+
+
+def _check_inputs(q, k, v):
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch.Tensor")
+        if t.dtype != torch.bfloat16:
+            raise TypeError(f"{name} must be bfloat16, got {t.dtype}")
+        if t.device.type != "cuda":
+            raise ValueError(f"{name} must be on a GPU device, got {t.device}")
+        if t.dim() != 4 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous [B, H, L, d] tensor")
+    if not (q.device == k.device == v.device):
+        raise ValueError("q, k and v must be on the same device")
+    B, Hq, Lq, dqk = q.shape
+    Bk, Hkv, Lk, dk = k.shape
+    if Bk != B or dk != dqk or tuple(v.shape[:3]) != (B, Hkv, Lk):
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    return B, Hq, Hkv, Lq, Lk, dqk, v.shape[3]
+
+
+def _outputs(q, dv, out, lse):
+    B, Hq, Lq, _ = q.shape
+    if out is None:
+        out = torch.empty((B, Hq, Lq, dv), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, Hq, Lq), dtype=torch.float32, device=q.device)
+    if out.shape != (B, Hq, Lq, dv) or out.dtype != torch.bfloat16 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous bf16 [B, Hq, Lq, d_v] tensor")
+    if lse.shape != (B, Hq, Lq) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous fp32 [B, Hq, Lq] tensor")
+    return out, lse
+
+
+def attn_fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse=None,
+             stream=None):
+    """O, lse = attention forward on the GPU (see include/attn_fwd.h).
+
+    q [B,Hq,Lq,d_qk], k [B,Hkv,Lk,d_qk], v [B,Hkv,Lk,d_v]: contiguous bf16 on
+    one GPU.  scale defaults to 1/sqrt(d_qk).  Enqueued on `stream` (default:
+    torch's current stream on q's device)."""
+    lib = _load()
+    B, Hq, Hkv, Lq, Lk, dqk, dv = _check_inputs(q, k, v)
+    if scale is None:
+        scale = 1.0 / math.sqrt(dqk)
+    out, lse = _outputs(q, dv, out, lse)
+    with torch.cuda.device(q.device):
+        s = stream if stream is not None else torch.cuda.current_stream(q.device)
+        rc = lib.attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                          lse.data_ptr(), B, Hq, Hkv, Lq, Lk, dqk, dv, int(bool(causal)),
+                          float(scale), s.cuda_stream)
+    if rc != ATTN_OK:
+        raise RuntimeError(f"attn_fwd failed: {status_string(rc)} (code {rc})")
+    return out, lse
+
+
+def attn_fwd_dbg(q, k, v, causal: bool = False, scale: float | None = None,
+                 rescale_threshold: float = 8.0, rescale_count=None, out=None, lse=None,
+                 stream=None):
+    """attn_fwd with the rescale threshold exposed; rescale_count, if given, is a
+    zeroed int64 GPU tensor of one element that receives the event count."""
+    lib = _load()
+    B, Hq, Hkv, Lq, Lk, dqk, dv = _check_inputs(q, k, v)
+    if scale is None:
+        scale = 1.0 / math.sqrt(dqk)
+    out, lse = _outputs(q, dv, out, lse)
+    cnt = 0
+    if rescale_count is not None:
+        if (rescale_count.dtype != torch.int64 or rescale_count.numel() != 1
+                or rescale_count.device != q.device):
+            raise ValueError("rescale_count must be a one-element int64 tensor on q's device")
+        cnt = rescale_count.data_ptr()
+    with torch.cuda.device(q.device):
+        s = stream if stream is not None else torch.cuda.current_stream(q.device)
+        rc = lib.attn_fwd_dbg(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                              lse.data_ptr(), B, Hq, Hkv, Lq, Lk, dqk, dv, int(bool(causal)),
+                              float(scale), s.cuda_stream, float(rescale_threshold), cnt)
+    if rc != ATTN_OK:
+        raise RuntimeError(f"attn_fwd_dbg failed: {status_string(rc)} (code {rc})")
+    return out, lse

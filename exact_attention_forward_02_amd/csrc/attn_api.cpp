@@ -1,0 +1,176 @@
+// attn_api.cpp -- C ABI of the gfx950 fused attention forward (declared in
+// include/attn_fwd.h): argument validation, device checks, the tile schedule
+// parameters, and the launch on the caller's stream.
+
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <atomic>
+
+#include <hip/hip_runtime_api.h>
+
+#include "attn_fwd.h"
+#include "attn_params.h"
+
+namespace {
+
+constexpr int kAbiVersion = 1;
+constexpr int kMaxDevices = 64;
+constexpr int kXcds = 8;                 // MI355X: 8 accelerator complex dies
+constexpr int kTilesPerXcdWave = 64;     // ~ concurrent workgroups per XCD (32 CUs x 2)
+constexpr float kDefaultThreshold = 8.0f;  // log2 units: a factor of 256
+
+// -1 unknown, 0 not gfx950, 1 gfx950
+std::atomic<int> g_arch_ok[kMaxDevices];
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int check_args(const void* q, const void* k, const void* v, const void* o, const float* lse,
+               int B, int Hq, int Hkv, int Lq, int Lk, int d_qk, int d_v, float scale) {
+    if (!q || !k || !v || !o || !lse) return ATTN_ERR_NULL_PTR;
+    if (B < 1 || Hq < 1 || Hkv < 1 || Lq < 1 || Lk < 1) return ATTN_ERR_BAD_SHAPE;
+    if (Hq % Hkv != 0) return ATTN_ERR_GQA_RATIO;
+    const bool dims_ok = (d_qk == 64 && d_v == 64) || (d_qk == 128 && d_v == 128) ||
+                         (d_qk == 192 && d_v == 128);
+    if (!dims_ok) return ATTN_ERR_UNSUPPORTED_HEAD_DIM;
+    if (!(scale > 0.0f) || !isfinite(scale)) return ATTN_ERR_BAD_SCALE;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+        !aligned(lse, 4))
+        return ATTN_ERR_MISALIGNED;
+    // row counts must fit 32-bit row indices in the kernel
+    const long long q_rows = (long long)B * Hq * Lq;
+    const long long kv_rows = (long long)B * Hkv * Lk;
+    if (q_rows > INT32_MAX || kv_rows > INT32_MAX) return ATTN_ERR_TOO_LARGE;
+    return ATTN_OK;
+}
+
+int check_device() {
+    int count = 0;
+    if (hipGetDeviceCount(&count) != hipSuccess || count < 1) {
+        (void)hipGetLastError();
+        return ATTN_ERR_NO_DEVICE;
+    }
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return ATTN_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return ATTN_ERR_UNSUPPORTED_ARCH;
+    int ok = g_arch_ok[dev].load(std::memory_order_relaxed);
+    if (ok < 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return ATTN_ERR_HIP;
+        ok = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 0;
+        g_arch_ok[dev].store(ok, std::memory_order_relaxed);
+    }
+    return ok ? ATTN_OK : ATTN_ERR_UNSUPPORTED_ARCH;
+}
+
+// Largest divisor of n that is <= cap (at least 1).
+int largest_divisor_at_most(int n, int cap) {
+    for (int d = cap < n ? cap : n; d > 1; --d)
+        if (n % d == 0) return d;
+    return 1;
+}
+
+int fill_schedule(attn::FwdParams& p) {
+    p.G = p.Hq / p.Hkv;
+    // query heads that share a K/V head are packed into one workgroup, one
+    // head per wave group, so the K/V block is loaded once for all of them
+    p.Gp = (p.G % 4 == 0) ? 4 : (p.G % 2 == 0) ? 2 : 1;
+    p.n_hg = p.G / p.Gp;
+    p.bm_pos = attn::kRowsPerWave * attn::kWaves / p.Gp;
+    p.n_m = (p.Lq + p.bm_pos - 1) / p.bm_pos;
+    const long long units = (long long)p.B * p.Hkv * p.n_hg;
+    const long long tiles = units * p.n_m;
+    if (tiles > INT32_MAX) return ATTN_ERR_TOO_LARGE;
+    p.units = (int)units;
+    // XCD-aware order: workgroup i is dispatched to XCD i % 8; give each XCD
+    // a contiguous range of units so the K/V blocks it streams stay in its L2.
+    p.xcd_mode = (p.units % kXcds == 0) ? 1 : 0;
+    p.upx = p.xcd_mode ? p.units / kXcds : p.units;
+    // units per cache section: enough tiles to occupy one XCD at a time
+    int cap = kTilesPerXcdWave / p.n_m;
+    if (cap < 1) cap = 1;
+    p.sec_units = largest_divisor_at_most(p.upx, cap);
+    return ATTN_OK;
+}
+
+int run(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
+        int Hkv, int Lq, int Lk, int d_qk, int d_v, int causal, float scale, void* stream,
+        float threshold, unsigned long long* counter, bool debug) {
+    int rc = check_args(q, k, v, o, lse, B, Hq, Hkv, Lq, Lk, d_qk, d_v, scale);
+    if (rc != ATTN_OK) return rc;
+    attn::FwdParams p;
+    memset(&p, 0, sizeof p);
+    p.q = static_cast<const uint16_t*>(q);
+    p.k = static_cast<const uint16_t*>(k);
+    p.v = static_cast<const uint16_t*>(v);
+    p.o = static_cast<uint16_t*>(o);
+    p.lse = lse;
+    p.rescale_count = counter;
+    p.B = B;
+    p.Hq = Hq;
+    p.Hkv = Hkv;
+    p.Lq = Lq;
+    p.Lk = Lk;
+    p.scale = scale;
+    p.scale_log2 = (float)((double)scale * 1.4426950408889634);  // log2(e)
+    p.threshold = threshold;
+    rc = fill_schedule(p);
+    if (rc != ATTN_OK) return rc;
+    rc = check_device();
+    if (rc != ATTN_OK) return rc;
+    hipError_t err = attn::launch_fwd(p, d_qk, d_v, causal != 0, debug,
+                                      static_cast<hipStream_t>(stream));
+    if (err != hipSuccess) return ATTN_ERR_HIP;
+    return ATTN_OK;
+}
+
+struct ArchCacheInit {
+    ArchCacheInit() {
+        for (auto& a : g_arch_ok) a.store(-1, std::memory_order_relaxed);
+    }
+} g_arch_cache_init;
+
+}  // namespace
+
+extern "C" {
+
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
+             int Hkv, int Lq, int Lk, int d_qk, int d_v, int causal, float scale,
+             void* stream) {
+    return run(q, k, v, o, lse, B, Hq, Hkv, Lq, Lk, d_qk, d_v, causal, scale, stream,
+               kDefaultThreshold, nullptr, false);
+}
+
+int attn_fwd_dbg(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                 int Hq, int Hkv, int Lq, int Lk, int d_qk, int d_v, int causal, float scale,
+                 void* stream, float rescale_threshold, unsigned long long* rescale_count) {
+    if (!(rescale_threshold >= 0.0f) || !isfinite(rescale_threshold))
+        return ATTN_ERR_BAD_ARGUMENT;
+    return run(q, k, v, o, lse, B, Hq, Hkv, Lq, Lk, d_qk, d_v, causal, scale, stream,
+               rescale_threshold, rescale_count, true);
+}
+
+const char* attn_status_string(int status) {
+    switch (status) {
+        case ATTN_OK: return "success";
+        case ATTN_ERR_NULL_PTR: return "a required pointer is NULL";
+        case ATTN_ERR_BAD_SHAPE: return "B, Hq, Hkv, Lq and Lk must all be >= 1";
+        case ATTN_ERR_GQA_RATIO: return "Hq must be a multiple of Hkv";
+        case ATTN_ERR_UNSUPPORTED_HEAD_DIM:
+            return "unsupported (d_qk, d_v): use (64,64), (128,128) or (192,128)";
+        case ATTN_ERR_BAD_SCALE: return "scale must be finite and > 0";
+        case ATTN_ERR_MISALIGNED:
+            return "q, k, v and o must be 16-byte aligned and lse 4-byte aligned";
+        case ATTN_ERR_TOO_LARGE: return "problem too large for the kernel's index types";
+        case ATTN_ERR_NO_DEVICE: return "no HIP device is visible";
+        case ATTN_ERR_UNSUPPORTED_ARCH: return "the current device is not gfx950 (MI355X)";
+        case ATTN_ERR_HIP: return "the HIP runtime reported an error";
+        case ATTN_ERR_BAD_ARGUMENT: return "rescale threshold must be finite and >= 0";
+        default: return "unknown attn status";
+    }
+}
+
+int attn_abi_version(void) { return kAbiVersion; }
+
+}  // extern "C"

@@ -1,0 +1,46 @@
+// attn_params.h -- launch parameters shared by the C ABI layer and the
+// gfx950 kernels.  Internal to the library; not part of the public ABI.
+#pragma once
+
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+namespace attn {
+
+// Work decomposition constants of the forward kernel.
+constexpr int kWaves = 4;            // waves per workgroup
+constexpr int kThreads = 64 * kWaves;
+constexpr int kRowsPerWave = 32;     // query rows owned by one wave (MFMA N)
+constexpr int kBlockN = 64;          // keys per K/V block
+
+struct FwdParams {
+    const uint16_t* q;   // [B, Hq, Lq, dqk] bf16
+    const uint16_t* k;   // [B, Hkv, Lk, dqk] bf16
+    const uint16_t* v;   // [B, Hkv, Lk, dv] bf16
+    uint16_t* o;         // [B, Hq, Lq, dv] bf16
+    float* lse;          // [B, Hq, Lq] fp32
+    unsigned long long* rescale_count;  // optional event counter
+
+    int B, Hq, Hkv, Lq, Lk;
+    int G;          // Hq / Hkv: query heads per K/V head
+    int Gp;         // query heads packed into one workgroup (divides G and kWaves)
+    int n_hg;       // G / Gp: head groups per K/V head
+    int bm_pos;     // query positions per tile = kRowsPerWave * kWaves / Gp
+    int n_m;        // position tiles per head group = ceil(Lq / bm_pos)
+    int units;      // B * Hkv * n_hg: groups of query heads sharing one K/V head
+    int xcd_mode;   // 1: workgroup i runs on XCD i % 8, which owns a contiguous
+                    //    range of units (upx of them)
+    int upx;        // units per XCD when xcd_mode
+    int sec_units;  // units per cache section (divides upx, or units)
+
+    float scale;        // softmax scale (natural units), used for lse
+    float scale_log2;   // scale * log2(e): base-2 exponent multiplier
+    float threshold;    // conditional rescale threshold, log2 units
+};
+
+// Launches the forward kernel instantiation matching (dqk, dv, causal, debug).
+hipError_t launch_fwd(const FwdParams& p, int dqk, int dv, bool causal, bool debug,
+                      hipStream_t stream);
+
+}  // namespace attn

@@ -1,0 +1,112 @@
+/*
+ * attn_fwd.h -- C ABI of the fused exact-attention forward pass for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * What it computes (per batch b and query head h):
+ *     O   = softmax(scale * Q K^T) V                 softmax along the keys
+ *     lse = log sum_j exp(scale * q_i . k_j)         natural log, per query row
+ * with the key/value head h / (Hq / Hkv) serving query head h (grouped-query
+ * attention), and, when causal != 0, the mask aligned to the bottom-right
+ * corner: query i attends keys j <= i + Lk - Lq.
+ * Definitions: "Infra: Flash Attention" (pufanyi.com), opening section and
+ * Algorithm 1 (O and L = m + log l); "Flash Attention 4: 在 Blackwell 上把
+ * Softmax 接进 Tensor Core 流水线" (fangpin gpu-hpc-book ch. 13), sections on
+ * online softmax with conditional rescaling and on causal attention and GQA.
+ * The score matrix is never written to memory: keys are visited block by
+ * block with an online softmax whose base-2 reference moves only when the
+ * block maximum exceeds it by more than 8 (log2 units).
+ *
+ * Tensor layouts (all contiguous, row-major, device memory):
+ *     q    [B, Hq,  Lq, d_qk]   bfloat16
+ *     k    [B, Hkv, Lk, d_qk]   bfloat16
+ *     v    [B, Hkv, Lk, d_v ]   bfloat16
+ *     o    [B, Hq,  Lq, d_v ]   bfloat16 (output, rounded to nearest even)
+ *     lse  [B, Hq,  Lq]         float32  (output)
+ * A query row with no visible key (causal with Lq > Lk) gets O = 0 and
+ * lse = -inf.
+ *
+ * Ownership: every pointer is a device pointer owned by the caller; the
+ * library allocates no memory.  o and lse must not overlap the inputs or each
+ * other.  q, k, v and o must be 16-byte aligned, lse 4-byte aligned.
+ *
+ * Asynchrony: the call enqueues one kernel on `stream` (a hipStream_t; NULL
+ * means the null stream) and returns.  The return value reports argument
+ * errors (checked before any HIP call) and launch errors; faults during
+ * execution surface at the caller's next synchronisation.  The library keeps
+ * no mutable state between calls except a per-device cache of the
+ * architecture check, and may be called from several host threads.
+ */
+#ifndef ATTN_FWD_H
+#define ATTN_FWD_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes returned by every entry point. */
+enum attn_status {
+    ATTN_OK = 0,
+    ATTN_ERR_NULL_PTR = 1,              /* a required pointer is NULL */
+    ATTN_ERR_BAD_SHAPE = 2,             /* B, Hq, Hkv, Lq or Lk < 1 */
+    ATTN_ERR_GQA_RATIO = 3,             /* Hq is not a multiple of Hkv */
+    ATTN_ERR_UNSUPPORTED_HEAD_DIM = 4,  /* (d_qk, d_v) not one of (64,64), (128,128), (192,128) */
+    ATTN_ERR_BAD_SCALE = 5,             /* scale not finite or not > 0 */
+    ATTN_ERR_MISALIGNED = 6,            /* q/k/v/o not 16-byte or lse not 4-byte aligned */
+    ATTN_ERR_TOO_LARGE = 7,             /* a row or tile count does not fit the index types */
+    ATTN_ERR_NO_DEVICE = 8,             /* no HIP device is visible */
+    ATTN_ERR_UNSUPPORTED_ARCH = 9,      /* the current device is not gfx950 */
+    ATTN_ERR_HIP = 10,                  /* the HIP runtime reported an error at launch */
+    ATTN_ERR_BAD_ARGUMENT = 11          /* a debug-only argument is out of range */
+};
+
+/*
+ * attn_fwd -- fused attention forward.
+ *   q, k, v     inputs as laid out above
+ *   o, lse      outputs as laid out above
+ *   B, Hq, Hkv  batch, query heads, key/value heads (Hq % Hkv == 0)
+ *   Lq, Lk      query and key sequence lengths (any values >= 1)
+ *   d_qk, d_v   head dims: (64,64), (128,128) or (192,128)
+ *   causal      0: full attention; nonzero: bottom-right causal mask
+ *   scale       softmax scale applied to q.k (callers usually pass
+ *               1/sqrt(d_qk)); must be finite and > 0
+ *   stream      hipStream_t to enqueue on (NULL: the null stream)
+ * Returns ATTN_OK or one of the codes above.
+ */
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+             int B, int Hq, int Hkv, int Lq, int Lk, int d_qk, int d_v,
+             int causal, float scale, void* stream);
+
+/*
+ * attn_fwd_dbg -- attn_fwd with the conditional-rescale threshold exposed and
+ * an event counter, for checking the rescale rule of "Flash Attention 4 ..."
+ * ch. 13 (section on online softmax and conditional rescaling).
+ *   rescale_threshold  log2-units threshold tau >= 0 (finite): the reference
+ *                      moves when (ref - cand) * scale * log2(e) < -tau.
+ *                      0 rescales at every increase of the running max; the
+ *                      production entry point uses 8.
+ *   rescale_count      device pointer to one unsigned 64-bit counter, or NULL.
+ *                      When given, the kernel atomically adds the number of
+ *                      (query row, key block) pairs, after the row's first
+ *                      visible block, at which the row's reference moved.  The
+ *                      caller zeroes it beforehand.
+ * Other arguments and returns as attn_fwd; ATTN_ERR_BAD_ARGUMENT for a bad
+ * threshold.
+ */
+int attn_fwd_dbg(const void* q, const void* k, const void* v, void* o, float* lse,
+                 int B, int Hq, int Hkv, int Lq, int Lk, int d_qk, int d_v,
+                 int causal, float scale, void* stream,
+                 float rescale_threshold, unsigned long long* rescale_count);
+
+/* attn_status_string -- static, NUL-terminated description of a status code
+ * (never NULL; unknown codes give "unknown attn status"). */
+const char* attn_status_string(int status);
+
+/* attn_abi_version -- version of this ABI (incremented on any change to the
+ * signatures or semantics above). */
+int attn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_FWD_H */

@@ -1,0 +1,139 @@
+"""The C ABI without a GPU: the library loads, exports every function that
+include/*.h declares, and rejects every bad argument with its status code
+before touching the HIP runtime.  CPU only (no compute calls)."""
+import ctypes
+import glob
+import os
+import re
+import subprocess
+
+import pytest
+
+from exact_attention_forward_02_amd import _binding, build
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+CODES = {
+    "ATTN_OK": 0, "ATTN_ERR_NULL_PTR": 1, "ATTN_ERR_BAD_SHAPE": 2, "ATTN_ERR_GQA_RATIO": 3,
+    "ATTN_ERR_UNSUPPORTED_HEAD_DIM": 4, "ATTN_ERR_BAD_SCALE": 5, "ATTN_ERR_MISALIGNED": 6,
+    "ATTN_ERR_TOO_LARGE": 7, "ATTN_ERR_NO_DEVICE": 8, "ATTN_ERR_UNSUPPORTED_ARCH": 9,
+    "ATTN_ERR_HIP": 10, "ATTN_ERR_BAD_ARGUMENT": 11,
+}
+
+
+def _declared_functions():
+    names = set()
+    for path in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(path, encoding="utf-8").read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        for m in re.finditer(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b([a-z_][a-z0-9_]*)\s*\(",
+                             text, flags=re.M):
+            names.add(m.group(1))
+    return names
+
+
+def _exported_symbols(path):
+    out = subprocess.run(["nm", "-D", "--defined-only", path], check=True,
+                         capture_output=True, text=True).stdout
+    return {line.split()[-1] for line in out.splitlines() if line.strip()}
+
+
+def test_header_declares_the_entry_points():
+    assert {"attn_fwd", "attn_fwd_dbg", "attn_status_string",
+            "attn_abi_version"} <= _declared_functions()
+
+
+def test_status_codes_match_header():
+    text = open(os.path.join(ROOT, "include", "attn_fwd.h"), encoding="utf-8").read()
+    for name, value in CODES.items():
+        assert re.search(rf"\b{name}\s*=\s*{value}\b", text), name
+
+
+def test_library_exports_every_declared_function():
+    lib = _binding.library()
+    assert lib is not None
+    exported = _exported_symbols(build.LIBRARY)
+    missing = _declared_functions() - exported
+    assert not missing, f"declared but not exported: {sorted(missing)}"
+
+
+def test_abi_version_and_status_strings():
+    lib = _binding.library()
+    assert lib.attn_abi_version() == 1
+    for code in CODES.values():
+        s = _binding.status_string(code)
+        assert s and s != "unknown attn status"
+    assert _binding.status_string(999) == "unknown attn status"
+
+
+# fake device addresses: never dereferenced, validation happens first
+A = 0x10000
+GOOD = dict(q=A, k=A * 2, v=A * 3, o=A * 4, lse=A * 5, B=1, Hq=4, Hkv=2, Lq=64, Lk=64,
+            d_qk=128, d_v=128, causal=0, scale=0.088, stream=None)
+ORDER = ["q", "k", "v", "o", "lse", "B", "Hq", "Hkv", "Lq", "Lk", "d_qk", "d_v", "causal",
+         "scale", "stream"]
+
+
+def _call(**over):
+    args = dict(GOOD)
+    args.update(over)
+    return _binding.library().attn_fwd(*[args[n] for n in ORDER])
+
+
+def _call_dbg(threshold, **over):
+    args = dict(GOOD)
+    args.update(over)
+    return _binding.library().attn_fwd_dbg(*[args[n] for n in ORDER], threshold, None)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(q=None), "ATTN_ERR_NULL_PTR"),
+    (dict(k=None), "ATTN_ERR_NULL_PTR"),
+    (dict(v=None), "ATTN_ERR_NULL_PTR"),
+    (dict(o=None), "ATTN_ERR_NULL_PTR"),
+    (dict(lse=None), "ATTN_ERR_NULL_PTR"),
+    (dict(B=0), "ATTN_ERR_BAD_SHAPE"),
+    (dict(Hq=0), "ATTN_ERR_BAD_SHAPE"),
+    (dict(Hkv=-1), "ATTN_ERR_BAD_SHAPE"),
+    (dict(Lq=0), "ATTN_ERR_BAD_SHAPE"),
+    (dict(Lk=0), "ATTN_ERR_BAD_SHAPE"),
+    (dict(Hq=6, Hkv=4), "ATTN_ERR_GQA_RATIO"),
+    (dict(d_qk=96, d_v=96), "ATTN_ERR_UNSUPPORTED_HEAD_DIM"),
+    (dict(d_qk=128, d_v=64), "ATTN_ERR_UNSUPPORTED_HEAD_DIM"),
+    (dict(d_qk=192, d_v=192), "ATTN_ERR_UNSUPPORTED_HEAD_DIM"),
+    (dict(scale=0.0), "ATTN_ERR_BAD_SCALE"),
+    (dict(scale=-1.0), "ATTN_ERR_BAD_SCALE"),
+    (dict(scale=float("inf")), "ATTN_ERR_BAD_SCALE"),
+    (dict(scale=float("nan")), "ATTN_ERR_BAD_SCALE"),
+    (dict(q=A + 8), "ATTN_ERR_MISALIGNED"),
+    (dict(o=A * 4 + 2), "ATTN_ERR_MISALIGNED"),
+    (dict(lse=A * 5 + 2), "ATTN_ERR_MISALIGNED"),
+    (dict(B=2 ** 16, Hq=2 ** 8, Hkv=2 ** 8, Lq=2 ** 8), "ATTN_ERR_TOO_LARGE"),
+])
+def test_argument_errors_come_before_any_device_call(over, code):
+    assert _call(**over) == CODES[code]
+
+
+def test_debug_threshold_is_validated():
+    assert _call_dbg(-1.0) == CODES["ATTN_ERR_BAD_ARGUMENT"]
+    assert _call_dbg(float("nan")) == CODES["ATTN_ERR_BAD_ARGUMENT"]
+    assert _call_dbg(float("inf")) == CODES["ATTN_ERR_BAD_ARGUMENT"]
+
+
+def test_valid_call_without_a_gpu_reports_no_device():
+    import torch
+
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert _call() == CODES["ATTN_ERR_NO_DEVICE"]
+    assert _call_dbg(8.0) == CODES["ATTN_ERR_NO_DEVICE"]
+
+
+def test_python_binding_rejects_bad_tensors():
+    import torch
+
+    q = torch.zeros((1, 1, 8, 64), dtype=torch.bfloat16)
+    with pytest.raises((ValueError, TypeError)):
+        _binding.attn_fwd(q, q, q)  # CPU tensors are refused before any call
+    with pytest.raises(TypeError):
+        _binding.attn_fwd(q.float(), q, q)
