@@ -96,6 +96,26 @@ def cpu_baseline(w, q, k, v, target_s: float = 12.0):
     }
 
 
+COPY_BYTES = 1 << 30  # bytes read (and written) per calibration launch
+
+
+def copy_calibration() -> int:
+    """torch.neg over 1 GiB of bf16: one elementwise kernel reading COPY_BYTES
+    and writing COPY_BYTES, launched three times."""
+    import torch
+
+    dev = torch.device("cuda:0")
+    x = torch.ones(COPY_BYTES // 2, dtype=torch.bfloat16, device=dev)
+    y = torch.empty_like(x)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        torch.neg(x, out=y)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration": {"bytes_read": COPY_BYTES,
+                                           "bytes_written": COPY_BYTES, "launches": 3}}))
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -104,6 +124,9 @@ def main() -> int:
     ap.add_argument("--workload", default="mha_l2k")
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle timing (for profiler runs)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain copy kernel of known size (3 launches) to "
+                         "calibrate the FETCH_SIZE / WRITE_SIZE counters")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -116,6 +139,8 @@ def main() -> int:
     from exact_attention_forward_02_amd import attn_fwd
     from exact_attention_forward_02_amd.inputs import WORKLOADS, workload_qkv
 
+    if args.copy_calibration:
+        return copy_calibration()
     if args.workload not in WORKLOADS:
         print(f"unknown workload {args.workload}; choose from {sorted(WORKLOADS)}",
               file=sys.stderr)

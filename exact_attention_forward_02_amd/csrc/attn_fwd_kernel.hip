@@ -37,6 +37,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "attn_params.h"
 
 namespace attn {
@@ -53,36 +55,42 @@ constexpr float kNegInf = -__builtin_inff();
 template <int DQK, int DV>
 struct Shape {
     static constexpr int kChunksK = DQK / 8;               // 16-byte chunks per K row
+    static constexpr int kChunksV = DV / 8;                // 16-byte chunks per V row
     static constexpr int kKBytes = kBlockN * DQK * 2;      // one K block in LDS
-    static constexpr int kVBytes = kBlockN * DV * 2;       // one V^T block in LDS
-    static constexpr int kBufBytes = kKBytes + kVBytes;
-    static constexpr int kLdsBytes = 2 * kBufBytes;        // double buffered
-    static constexpr int kKLoads = kBlockN * kChunksK / kThreads;  // 16 B loads / thread
-    static constexpr int kVItems = (kBlockN / 4) * (DV / 8);      // (4 keys x 8 dv) items
-    static constexpr int kVIters = (kVItems + kThreads - 1) / kThreads;
+    static constexpr int kVBytes = kBlockN * DV * 2;       // one V block in LDS
+    static constexpr int kKCopies = kChunksK / kWaves;     // 1 KiB direct copies / wave
+    static constexpr int kVCopies = kChunksV / kWaves;
     static constexpr int kKSteps = DQK / 16;               // MFMA k-steps for S
     static constexpr int kDvBlocks = DV / 32;              // 32-wide output blocks
-    static_assert(kBlockN * kChunksK % kThreads == 0, "K block must split evenly");
+    static_assert(kChunksK % kWaves == 0 && kChunksV % kWaves == 0, "blocks split evenly");
     static_assert(DQK % 16 == 0 && DV % 32 == 0, "head dims must fit the MFMA tiles");
 };
 
-// Byte offset of 16-byte chunk c of key row r in a K block.  The chunk index
-// is XOR-swizzled with the row so that the 16 lanes reading one chunk column
-// of 16 consecutive rows hit 16 distinct bank groups.
+// K block in LDS: 64 key rows of DQK bf16, 16-byte chunk c of row r stored at
+// slot c ^ kswz(r).  The 16 lanes that read one chunk column of 16
+// consecutive rows (S^T operand, ds_read_b128) then hit 16 distinct bank
+// groups.  The XOR only touches the low bits, so the slot stays in the row.
 template <int DQK>
-__device__ __forceinline__ int k_offset(int r, int c) {
-    const int swz = (DQK == 128) ? (r & 15) : ((r >> 1) & 7);
-    return r * (DQK * 2) + ((c ^ swz) << 4);
+__device__ __forceinline__ int kswz(int r) {
+    return (DQK == 128) ? (r & 15) : ((r >> 1) & 7);
 }
 
-// V^T block: row = output dim (DV rows), 64 keys per row (128 bytes).  Within
-// each group of 16 keys the keys are permuted so that one 16-byte chunk holds
-// the 8 keys a lane feeds to one PV MFMA: lane half h takes keys
-// {4h..4h+3, 8+4h..8+4h+3}.  Key kk sits in chunk 2*(kk/16) + ((kk>>2)&1) at
-// element ((kk>>3)&1)*4 + (kk&3).  Chunks are XOR-swizzled by row pair.
-__device__ __forceinline__ int vt_offset(int row, int chunk) {
-    return row * (kBlockN * 2) + ((chunk ^ ((row >> 1) & 7)) << 4);
+// V block in LDS: 64 key rows of DV bf16 (row-major, as in HBM), chunk c of
+// row r stored at slot c ^ vswz(r).  The PV operand is read with
+// ds_read_b64_tr_b16: a 16-lane group reads 8 bytes from each of 4
+// consecutive rows (r = 0..3) at 2 adjacent chunks; the two groups of a
+// half-wave read the next 2 chunks.  The swizzle gives the 4 rows distinct
+// chunk bits so that neither a 16-lane (128-byte) nor a 32-lane (256-byte)
+// access window repeats a bank.
+template <int DV>
+__device__ __forceinline__ int vswz(int r) {
+    const int q = r & 3;
+    return (DV == 128) ? (4 * q + 2 * (q >> 1)) : (4 * (q & 1) + 2 * (q >> 1));
 }
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 __device__ __forceinline__ float pair_max(float x) {
     // lanes l and l ^ 32 hold the two halves of one query's keys
@@ -101,10 +109,28 @@ __device__ __forceinline__ u32x4 load16(const uint16_t* p) {
     return *reinterpret_cast<const u32x4*>(p);
 }
 
+// Copy 16 bytes per lane from global memory straight into LDS: lane l's data
+// lands at lds_dst + 16 * l (the destination is one contiguous KiB per wave).
+__device__ __forceinline__ void copy_to_lds(const unsigned char* src, void* lds_dst) {
+    __builtin_amdgcn_global_load_lds(src, lds_dst, 16, 0, 0);
+}
+
+// Heads up to 128 wide keep two score tiles in registers and overlap the next
+// block's QK^T with the current block's softmax; wider heads would spill.
+template <int DQK>
+constexpr bool kPipelined = DQK <= 128;
+
 template <int DQK, int DV, bool CAUSAL, bool DEBUG>
 __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const FwdParams p) {
     using S = Shape<DQK, DV>;
-    __shared__ __attribute__((aligned(16))) unsigned char lds[S::kLdsBytes];
+    constexpr int kRowK = DQK * 2;  // bytes per K row
+    constexpr int kRowV = DV * 2;   // bytes per V row
+    // two buffers each for K and V, distinct objects so that reads of one
+    // buffer are never ordered behind copies into the other
+    __shared__ __attribute__((aligned(1024))) unsigned char lds_k0[S::kKBytes];
+    __shared__ __attribute__((aligned(1024))) unsigned char lds_k1[S::kKBytes];
+    __shared__ __attribute__((aligned(1024))) unsigned char lds_v0[S::kVBytes];
+    __shared__ __attribute__((aligned(1024))) unsigned char lds_v1[S::kVBytes];
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
@@ -137,8 +163,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const FwdParams p
     const int qw = pos0 + (wave / p.Gp) * kRowsPerWave;  // first row of this wave
     const int off = p.Lk - p.Lq;                          // causal diagonal offset
 
-    const uint16_t* kbase = p.k + (size_t)bk * p.Lk * DQK;
-    const uint16_t* vbase = p.v + (size_t)bk * p.Lk * DV;
+    const unsigned char* kbase =
+        reinterpret_cast<const unsigned char*>(p.k + (size_t)bk * p.Lk * DQK);
+    const unsigned char* vbase =
+        reinterpret_cast<const unsigned char*>(p.v + (size_t)bk * p.Lk * DV);
     const size_t qrow0 = (size_t)(b * p.Hq + hq) * p.Lq;
 
     // key range of the tile and of this wave
@@ -167,70 +195,85 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const FwdParams p
         }
     }
 
-    // ---- K/V block staging: global -> registers -> LDS --------------------
-    u32x4 kst[S::kKLoads];
-    u32x4 vst[S::kVIters][4];
+    // ---- direct global -> LDS copies of one K or V block -------------------
+    // Copy n of the workgroup fills LDS slots [64 n, 64 n + 64); lane l takes
+    // slot 64 n + l = (row r, stored chunk c') and fetches source chunk
+    // c' ^ swizzle(r) of key row key0 + r.  The per-lane byte offsets within
+    // a block are fixed, so they are computed once.  In a block that runs
+    // past the last key, rows are clamped to the last key: those rows are
+    // masked to -inf (K) or weighted by exactly 0 (V).
+    uint32_t koff[S::kKCopies], voff_copy[S::kVCopies];
+#pragma unroll
+    for (int i = 0; i < S::kKCopies; ++i) {
+        const int slot = 64 * (wave * S::kKCopies + i) + lane;
+        const int r = slot / S::kChunksK;
+        const int c = (slot - r * S::kChunksK) ^ kswz<DQK>(r);
+        koff[i] = r * kRowK + 16 * c;
+    }
+#pragma unroll
+    for (int i = 0; i < S::kVCopies; ++i) {
+        const int slot = 64 * (wave * S::kVCopies + i) + lane;
+        const int r = slot / S::kChunksV;
+        const int c = (slot - r * S::kChunksV) ^ vswz<DV>(r);
+        voff_copy[i] = r * kRowV + 16 * c;
+    }
 
-    auto load_block = [&](int jb) {
+    auto copy_k = [&](int jb, unsigned char* dst) {
         const int key0 = jb * kBlockN;
+        const unsigned char* src = kbase + (size_t)key0 * kRowK;
+        if (key0 + kBlockN <= p.Lk) {
 #pragma unroll
-        for (int it = 0; it < S::kKLoads; ++it) {
-            const int item = tid + it * kThreads;
-            const int r = item / S::kChunksK;
-            const int c = item - r * S::kChunksK;
-            const int key = key0 + r;
-            kst[it] = key < p.Lk ? load16(kbase + (size_t)key * DQK + 8 * c)
-                                 : u32x4{0u, 0u, 0u, 0u};
+            for (int i = 0; i < S::kKCopies; ++i)
+                copy_to_lds(src + koff[i], dst + 1024 * (wave * S::kKCopies + i));
+        } else {
+            const int last = p.Lk - 1 - key0;
+#pragma unroll
+            for (int i = 0; i < S::kKCopies; ++i) {
+                const int r = (int)koff[i] / kRowK;
+                const int rr = min(r, last);
+                copy_to_lds(src + (koff[i] - (uint32_t)((r - rr) * kRowK)),
+                            dst + 1024 * (wave * S::kKCopies + i));
+            }
         }
+    };
+    auto copy_v = [&](int jb, unsigned char* dst) {
+        const int key0 = jb * kBlockN;
+        const unsigned char* src = vbase + (size_t)key0 * kRowV;
+        if (key0 + kBlockN <= p.Lk) {
 #pragma unroll
-        for (int it = 0; it < S::kVIters; ++it) {
-            const int item = tid + it * kThreads;
-            if (item < S::kVItems) {
-                const int kg = item & 15;  // group of 4 keys
-                const int c8 = item >> 4;  // 8-wide chunk of the value dim
+            for (int i = 0; i < S::kVCopies; ++i)
+                copy_to_lds(src + voff_copy[i], dst + 1024 * (wave * S::kVCopies + i));
+        } else {
+            const int last = p.Lk - 1 - key0;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int key = key0 + 4 * kg + e;
-                    vst[it][e] = key < p.Lk ? load16(vbase + (size_t)key * DV + 8 * c8)
-                                            : u32x4{0u, 0u, 0u, 0u};
-                }
+            for (int i = 0; i < S::kVCopies; ++i) {
+                const int r = (int)voff_copy[i] / kRowV;
+                const int rr = min(r, last);
+                copy_to_lds(src + (voff_copy[i] - (uint32_t)((r - rr) * kRowV)),
+                            dst + 1024 * (wave * S::kVCopies + i));
             }
         }
     };
 
-    auto store_block = [&](int buf) {
-        unsigned char* kl = lds + buf * S::kBufBytes;
-        unsigned char* vl = kl + S::kKBytes;
+    // ---- LDS read offsets (bytes within a block buffer) -----------------------
+    // S^T operand: row 32 mb + l32, chunk 2 ks + hi (mb adds 32 rows)
+    int kread[S::kKSteps];
 #pragma unroll
-        for (int it = 0; it < S::kKLoads; ++it) {
-            const int item = tid + it * kThreads;
-            const int r = item / S::kChunksK;
-            const int c = item - r * S::kChunksK;
-            *reinterpret_cast<u32x4*>(kl + k_offset<DQK>(r, c)) = kst[it];
-        }
+    for (int ks = 0; ks < S::kKSteps; ++ks)
+        kread[ks] = (l32 * S::kChunksK + ((2 * ks + hi) ^ kswz<DQK>(l32))) * 16;
+    // PV operand (transposed V reads): 16-lane group g = lane / 16 with index
+    // 4 r + j reads row 16 G + 8 t + 4 (g / 2) + r, dims 32 i + 16 (g & 1) +
+    // 4 j .. +3, so lane l receives V[keys][32 i + (l & 31)] for the keys
+    // whose P values its accumulator registers hold.  G and t add whole rows.
+    int vread[S::kDvBlocks];
+    {
+        const int tg = lane >> 4, ti = lane & 15, tr = ti >> 2, tj = ti & 3;
+        const int row = 4 * (tg >> 1) + tr;
+        const int cl = 2 * (tg & 1) + (tj >> 1);
 #pragma unroll
-        for (int it = 0; it < S::kVIters; ++it) {
-            const int item = tid + it * kThreads;
-            if (item < S::kVItems) {
-                const int kg = item & 15;
-                const int c8 = item >> 4;
-                // 4 keys x 8 dims -> 8 rows of V^T, 4 consecutive slots each
-                const int chunk = 2 * (kg >> 2) + (kg & 1);
-                const int elem_byte = ((kg >> 1) & 1) * 8;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const uint32_t a0 = vst[it][0][e], a1 = vst[it][1][e];
-                    const uint32_t a2 = vst[it][2][e], a3 = vst[it][3][e];
-                    const u32x2 even = {(a0 & 0xffffu) | (a1 << 16), (a2 & 0xffffu) | (a3 << 16)};
-                    const u32x2 odd = {(a0 >> 16) | (a1 & 0xffff0000u),
-                                       (a2 >> 16) | (a3 & 0xffff0000u)};
-                    const int row = 8 * c8 + 2 * e;
-                    *reinterpret_cast<u32x2*>(vl + vt_offset(row, chunk) + elem_byte) = even;
-                    *reinterpret_cast<u32x2*>(vl + vt_offset(row + 1, chunk) + elem_byte) = odd;
-                }
-            }
-        }
-    };
+        for (int i = 0; i < S::kDvBlocks; ++i)
+            vread[i] = row * kRowV + 16 * ((4 * i + cl) ^ vswz<DV>(row)) + 8 * (tj & 1);
+    }
 
     // ---- running state -------------------------------------------------------
     f32x16 oacc[S::kDvBlocks];
@@ -239,129 +282,222 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const FwdParams p
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[i][r] = 0.0f;
     float ref = kNegInf;  // exponent reference, raw q.k units
-    float ell = 0.0f;     // this lane's share of the denominator
+    float ell = 0.0f;     // this lane's share of sum P (fp32 P), for lse
+    float ell_o = 0.0f;   // this lane's share of sum P (bf16 P), normalises O
     const float c2 = p.scale_log2;
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-    if (nblk > 0) {
-        load_block(0);
-        store_block(0);
-        __syncthreads();
-    }
+    auto active = [&](int jb) { return wave_rows && jb * kBlockN < wend; };
 
-    for (int jb = 0; jb < nblk; ++jb) {
-        const int buf = jb & 1;
-        if (jb + 1 < nblk) load_block(jb + 1);
-        const int key0 = jb * kBlockN;
-
-        if (wave_rows && key0 < wend) {
-            const unsigned char* kl = lds + buf * S::kBufBytes;
-            const unsigned char* vl = kl + S::kKBytes;
-
-            // S^T = K Q^T for 64 keys x 32 queries: two 32x32 tiles
-            f32x16 s[kBlockN / 32];
+    // S^T = K Q^T for 64 keys x 32 queries: two 32x32 tiles
+    auto compute_s = [&](const unsigned char* kl, f32x16 (&s)[kBlockN / 32]) {
 #pragma unroll
-            for (int mb = 0; mb < kBlockN / 32; ++mb)
+        for (int mb = 0; mb < kBlockN / 32; ++mb)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) s[mb][r] = 0.0f;
+            for (int r = 0; r < 16; ++r) s[mb][r] = 0.0f;
 #pragma unroll
-            for (int ks = 0; ks < S::kKSteps; ++ks) {
-#pragma unroll
-                for (int mb = 0; mb < kBlockN / 32; ++mb) {
-                    const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-                        kl + k_offset<DQK>(mb * 32 + l32, 2 * ks + hi));
-                    s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[mb], 0, 0, 0);
-                }
-            }
-
-            // mask keys past the end or past the causal diagonal
-            const bool need_mask =
-                (key0 + kBlockN > p.Lk) || (CAUSAL && key0 + kBlockN - 1 > qw + off);
-            if (need_mask) {
-                const int qi = qw + l32;
-                const int klim = CAUSAL ? min(p.Lk, qi + off + 1) : p.Lk;
-#pragma unroll
-                for (int mb = 0; mb < kBlockN / 32; ++mb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int key = key0 + mb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-                        if (key >= klim) s[mb][r] = kNegInf;
-                    }
-            }
-
-            // block max of this row (raw units)
-            float bmax = kNegInf;
-#pragma unroll
-            for (int mb = 0; mb < kBlockN / 32; ++mb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) bmax = fmaxf(bmax, s[mb][r]);
-            bmax = pair_max(bmax);
-
-            // conditional rescale decision
-            const float cand = fmaxf(ref, bmax);
-            bool moved = false;
-            float acc_scale = 1.0f;
-            if (ref == kNegInf) {
-                ref = cand;  // first visible block: adopt its max, state is empty
-            } else {
-                const float delta = (ref - cand) * c2;
-                if (delta < -p.threshold) {
-                    moved = true;
-                    acc_scale = __builtin_amdgcn_exp2f(delta);
-                    ref = cand;
-                }
-            }
-            const unsigned long long vote = __ballot(moved);
-            if (vote) {  // wave-uniform: some row of this wave moved its reference
-#pragma unroll
-                for (int i = 0; i < S::kDvBlocks; ++i)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) oacc[i][r] *= acc_scale;
-                ell *= acc_scale;
-                if (DEBUG && p.rescale_count != nullptr && lane == 0)
-                    atomicAdd(p.rescale_count,
-                              (unsigned long long)__builtin_popcountll(vote & 0xffffffffull));
-            }
-
-            // P = 2^(x * c2 - ref * c2), kept in registers as bf16
-            const float refc = (ref == kNegInf) ? 0.0f : ref * c2;
-            float rs = 0.0f;
-            bf16x8 pb[kBlockN / 16];
+        for (int ks = 0; ks < S::kKSteps; ++ks) {
 #pragma unroll
             for (int mb = 0; mb < kBlockN / 32; ++mb) {
-#pragma unroll
-                for (int t = 0; t < 2; ++t) {
-                    f32x8 e;
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) {
-                        e[i] = __builtin_amdgcn_exp2f(fmaf(s[mb][8 * t + i], c2, -refc));
-                        rs += e[i];
-                    }
-                    pb[2 * mb + t] = __builtin_convertvector(e, bf16x8);
-                }
+                const bf16x8 a = *reinterpret_cast<const bf16x8*>(
+                    kl + kread[ks] + mb * 32 * kRowK);
+                s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[mb], 0, 0, 0);
             }
-            ell += rs;
+        }
+    };
 
-            // O^T += V^T P^T, 16 keys per MFMA
+    // Online softmax of one block's scores, then O^T += V^T P^T.  With
+    // next_tag = true, the scores of the next block (K from next_kl, into
+    // s_next) are computed in the same straight-line stretch as the
+    // exponentials and the PV product, so that the MFMA work of both can
+    // interleave with the VALU work.
+    auto softmax_pv = [&](auto next_tag, int jb, f32x16 (&s)[kBlockN / 32],
+                          const unsigned char* vl, const unsigned char* next_kl,
+                          f32x16 (&s_next)[kBlockN / 32]) {
+        const int key0 = jb * kBlockN;
+        // mask keys past the end or past the causal diagonal
+        const bool need_mask =
+            (key0 + kBlockN > p.Lk) || (CAUSAL && key0 + kBlockN - 1 > qw + off);
+        if (need_mask) {
+            const int qi = qw + l32;
+            const int klim = CAUSAL ? min(p.Lk, qi + off + 1) : p.Lk;
 #pragma unroll
-            for (int g = 0; g < kBlockN / 16; ++g) {
+            for (int mb = 0; mb < kBlockN / 32; ++mb)
 #pragma unroll
-                for (int i = 0; i < S::kDvBlocks; ++i) {
-                    const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-                        vl + vt_offset(32 * i + l32, 2 * g + hi));
-                    oacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[g], oacc[i], 0, 0, 0);
+                for (int r = 0; r < 16; ++r) {
+                    const int key = key0 + mb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+                    if (key >= klim) s[mb][r] = kNegInf;
+                }
+        }
+
+        // block max of this row (raw units)
+        float bmax = kNegInf;
+#pragma unroll
+        for (int mb = 0; mb < kBlockN / 32; ++mb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) bmax = fmaxf(bmax, s[mb][r]);
+        bmax = pair_max(bmax);
+
+        // conditional rescale decision
+        const float cand = fmaxf(ref, bmax);
+        bool moved = false;
+        float acc_scale = 1.0f;
+        if (ref == kNegInf) {
+            ref = cand;  // first visible block: adopt its max, state is empty
+        } else {
+            const float delta = (ref - cand) * c2;
+            if (delta < -p.threshold) {
+                moved = true;
+                acc_scale = __builtin_amdgcn_exp2f(delta);
+                ref = cand;
+            }
+        }
+        const unsigned long long vote = __ballot(moved);
+        if (vote) {  // wave-uniform: some row of this wave moved its reference
+#pragma unroll
+            for (int i = 0; i < S::kDvBlocks; ++i)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) oacc[i][r] *= acc_scale;
+            ell *= acc_scale;
+            ell_o *= acc_scale;
+            if (DEBUG && p.rescale_count != nullptr && lane == 0)
+                atomicAdd(p.rescale_count,
+                          (unsigned long long)__builtin_popcountll(vote & 0xffffffffull));
+        }
+
+        // P = 2^(x * c2 - ref * c2), rounded to bf16 in registers.  Two row
+        // sums: the fp32 P for lse, and the bf16 P that feed the PV product,
+        // which normalises O with exactly the weights it was built from.
+        const float refc = (ref == kNegInf) ? 0.0f : ref * c2;
+        float rs[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        float rb[2] = {0.0f, 0.0f};
+        bf16x8 pb[kBlockN / 16];
+#pragma unroll
+        for (int mb = 0; mb < kBlockN / 32; ++mb) {
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                f32x8 e;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    e[i] = __builtin_amdgcn_exp2f(fmaf(s[mb][8 * t + i], c2, -refc));
+                    rs[i & 3] += e[i];
+                }
+                const bf16x8 pk = __builtin_convertvector(e, bf16x8);
+                pb[2 * mb + t] = pk;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const bf16x2 pr = {pk[2 * i], pk[2 * i + 1]};
+                    rb[i & 1] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, rb[i & 1], false);
                 }
             }
         }
+        ell += (rs[0] + rs[1]) + (rs[2] + rs[3]);
+        ell_o += rb[0] + rb[1];
 
-        if (jb + 1 < nblk) store_block(buf ^ 1);
-        __syncthreads();
+        if constexpr (decltype(next_tag)::value) compute_s(next_kl, s_next);
+
+        // O^T += V^T P^T, 16 keys per MFMA; the V^T operand comes from two
+        // transposed LDS reads of row-major V
+#pragma unroll
+        for (int g = 0; g < kBlockN / 16; ++g) {
+#pragma unroll
+            for (int i = 0; i < S::kDvBlocks; ++i) {
+                i16x4 part[2];
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+                    part[t] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (lds_i16x4*)(vl + vread[i] + (16 * g + 8 * t) * kRowV));
+                const bf16x8 a = __builtin_bit_cast(
+                    bf16x8, __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
+                oacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[g], oacc[i], 0, 0, 0);
+            }
+        }
+    };
+
+    // ---- sweep over key blocks --------------------------------------------
+    f32x16 sa[kBlockN / 32], sb[kBlockN / 32];
+    if constexpr (kPipelined<DQK>) {
+        // Software pipelined.  Step j: copy K(j+2) and V(j+1) into the free
+        // buffers, compute the scores of block j+1 (MFMA work independent of
+        // the rest of the step), then the softmax and PV product of block j,
+        // whose scores were computed in step j-1.  K runs one block ahead of
+        // V, so K(j+1) and V(j) are resident during step j.  Even steps read K
+        // from lds_k1 and V from lds_v0; odd steps the other buffers.
+        if (nblk > 0) {
+            copy_k(0, lds_k0);
+            copy_v(0, lds_v0);
+            if (nblk > 1) copy_k(1, lds_k1);
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+            if (active(0)) compute_s(lds_k0, sa);
+        }
+        // a wave's active blocks are a prefix [0, nact) of the tile's blocks
+        const int nact =
+            wave_rows ? min(nblk, (wend + kBlockN - 1) / kBlockN) : 0;
+        const std::true_type with_next{};
+        const std::false_type last{};
+        for (int jb = 0; jb < nblk; jb += 2) {
+            // even step j = jb
+            if (jb + 2 < nblk) copy_k(jb + 2, lds_k0);
+            if (jb + 1 < nblk) copy_v(jb + 1, lds_v1);
+            if (jb + 1 < nact)
+                softmax_pv(with_next, jb, sa, lds_v0, lds_k1, sb);
+            else if (jb < nact)
+                softmax_pv(last, jb, sa, lds_v0, lds_k1, sb);
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+            if (jb + 1 >= nblk) break;
+            // odd step j = jb + 1
+            if (jb + 3 < nblk) copy_k(jb + 3, lds_k1);
+            if (jb + 2 < nblk) copy_v(jb + 2, lds_v0);
+            if (jb + 2 < nact)
+                softmax_pv(with_next, jb + 1, sb, lds_v1, lds_k0, sa);
+            else if (jb + 1 < nact)
+                softmax_pv(last, jb + 1, sb, lds_v1, lds_k0, sa);
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+        }
+    } else {
+        // One score tile live (wide heads): step j copies block j+1 into the
+        // free buffers, then computes scores, softmax and PV of block j.
+        if (nblk > 0) {
+            copy_k(0, lds_k0);
+            copy_v(0, lds_v0);
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+        }
+        for (int jb = 0; jb < nblk; jb += 2) {
+            if (jb + 1 < nblk) {
+                copy_k(jb + 1, lds_k1);
+                copy_v(jb + 1, lds_v1);
+            }
+            if (active(jb)) {
+                compute_s(lds_k0, sa);
+                softmax_pv(std::false_type{}, jb, sa, lds_v0, lds_k1, sb);
+            }
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+            if (jb + 1 >= nblk) break;
+            if (jb + 2 < nblk) {
+                copy_k(jb + 2, lds_k0);
+                copy_v(jb + 2, lds_v0);
+            }
+            if (active(jb + 1)) {
+                compute_s(lds_k1, sa);
+                softmax_pv(std::false_type{}, jb + 1, sa, lds_v1, lds_k0, sb);
+            }
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+        }
+        (void)sb;
     }
 
     // ---- epilogue: O = U / l (bf16), lse = scale * ref + ln l ----------------
     const int qi = qw + l32;
     const float ell_row = pair_sum(ell);
+    const float ell_o_row = pair_sum(ell_o);
     if (qi < p.Lq) {
-        const float inv = ell_row > 0.0f ? 1.0f / ell_row : 0.0f;
+        const float inv = ell_o_row > 0.0f ? 1.0f / ell_o_row : 0.0f;
         uint16_t* orow = p.o + (qrow0 + qi) * DV;
 #pragma unroll
         for (int i = 0; i < S::kDvBlocks; ++i) {

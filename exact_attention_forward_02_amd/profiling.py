@@ -1,0 +1,144 @@
+"""Summaries of rocprofv3 output for the attention kernel.
+
+    python -m exact_attention_forward_02_amd.profiling stats  RUN_kernel_stats.csv
+    python -m exact_attention_forward_02_amd.profiling pmc    RUN_counter_collection.csv [--kernel NAME]
+    python -m exact_attention_forward_02_amd.profiling traffic --fetch F.csv --write W.csv \\
+        --copy-fetch CF.csv --copy-write CW.csv --copy-bytes N --workload NAME [--out PATH]
+
+`stats` prints per-kernel call counts and durations from a --kernel-trace
+--stats run (CSV output).  `pmc` averages every counter per dispatch of the
+kernels whose name contains NAME.  `traffic` turns FETCH_SIZE / WRITE_SIZE
+(KiB per dispatch) of the attention kernel into HBM bytes per launch, each
+scaled by what the same counter reads for a plain copy kernel that moves a
+known number of bytes, and writes the JSON record bench.py reports while the
+kernel source is unchanged.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import hashlib
+import json
+import os
+import sys
+from collections import defaultdict
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+KERNEL_SOURCE = os.path.join(ROOT, "exact_attention_forward_02_amd", "csrc",
+                             "attn_fwd_kernel.hip")
+
+
+def kernel_source_digest() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def read_kernel_stats(path):
+    rows = []
+    with open(path, newline="") as f:
+        for r in csv.DictReader(f):
+            rows.append({
+                "name": r.get("Name") or r.get("KERNEL_NAME") or r.get("Kernel_Name"),
+                "calls": int(r.get("Calls", 0)),
+                "total_ns": float(r.get("TotalDurationNs", 0)),
+                "avg_ns": float(r.get("AverageNs", 0)),
+                "min_ns": float(r.get("MinNs", 0)),
+                "max_ns": float(r.get("MaxNs", 0)),
+                "pct": float(r.get("Percentage", 0)),
+            })
+    return rows
+
+
+def read_counters(path, kernel="attn_fwd_kernel"):
+    """Mean value of each counter per dispatch of the matching kernels."""
+    per = defaultdict(lambda: defaultdict(float))
+    names = {}
+    with open(path, newline="") as f:
+        for r in csv.DictReader(f):
+            kname = r.get("Kernel_Name", "")
+            if kernel and kernel not in kname:
+                continue
+            d = r.get("Dispatch_Id") or r.get("Correlation_Id")
+            per[d][r["Counter_Name"]] += float(r["Counter_Value"])
+            names[d] = kname
+    if not per:
+        return {}, 0, ""
+    keys = sorted({k for v in per.values() for k in v})
+    mean = {k: sum(v.get(k, 0.0) for v in per.values()) / len(per) for k in keys}
+    return mean, len(per), next(iter(names.values()))
+
+
+def cmd_stats(args):
+    for r in read_kernel_stats(args.csv):
+        print(f"{r['name'][:100]:100s} calls={r['calls']:4d} avg={r['avg_ns'] / 1e3:9.2f} us "
+              f"min={r['min_ns'] / 1e3:9.2f} max={r['max_ns'] / 1e3:9.2f} ({r['pct']:.1f}%)")
+
+
+def cmd_pmc(args):
+    mean, n, name = read_counters(args.csv, args.kernel)
+    print(f"kernel: {name}\ndispatches: {n}")
+    for k, v in mean.items():
+        print(f"{k:32s} {v:,.0f}")
+
+
+def cmd_traffic(args):
+    fetch, nf, _ = read_counters(args.fetch, args.kernel)
+    write, nw, _ = read_counters(args.write, args.kernel)
+    cfetch, _, _ = read_counters(args.copy_fetch, args.copy_kernel)
+    cwrite, _, _ = read_counters(args.copy_write, args.copy_kernel)
+    f_scale = args.copy_bytes / (cfetch["FETCH_SIZE"] * 1024.0)
+    w_scale = args.copy_bytes / (cwrite["WRITE_SIZE"] * 1024.0)
+    fetch_b = fetch["FETCH_SIZE"] * 1024.0 * f_scale
+    write_b = write["WRITE_SIZE"] * 1024.0 * w_scale
+    rec = {
+        "kernel": args.kernel,
+        "workload": args.workload,
+        "kernel_source_sha256": kernel_source_digest(),
+        "fetch_kib_per_dispatch": fetch["FETCH_SIZE"],
+        "write_kib_per_dispatch": write["WRITE_SIZE"],
+        "dispatches": [nf, nw],
+        "copy_bytes": args.copy_bytes,
+        "copy_fetch_kib": cfetch["FETCH_SIZE"],
+        "copy_write_kib": cwrite["WRITE_SIZE"],
+        "fetch_scale": f_scale,
+        "write_scale": w_scale,
+        "hbm_bytes_per_launch": fetch_b + write_b,
+        "hbm_read_bytes_per_launch": fetch_b,
+        "hbm_write_bytes_per_launch": write_b,
+    }
+    text = json.dumps(rec, indent=2)
+    print(text)
+    if args.out:
+        with open(args.out, "w", encoding="utf-8") as f:
+            f.write(text + "\n")
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__,
+                                 formatter_class=argparse.RawDescriptionHelpFormatter)
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    a = sub.add_parser("stats")
+    a.add_argument("csv")
+    a.set_defaults(fn=cmd_stats)
+    b = sub.add_parser("pmc")
+    b.add_argument("csv")
+    b.add_argument("--kernel", default="attn_fwd_kernel")
+    b.set_defaults(fn=cmd_pmc)
+    c = sub.add_parser("traffic")
+    c.add_argument("--fetch", required=True)
+    c.add_argument("--write", required=True)
+    c.add_argument("--copy-fetch", required=True)
+    c.add_argument("--copy-write", required=True)
+    c.add_argument("--copy-bytes", type=float, required=True)
+    c.add_argument("--copy-kernel", default="")
+    c.add_argument("--kernel", default="attn_fwd_kernel")
+    c.add_argument("--workload", required=True)
+    c.add_argument("--out")
+    c.set_defaults(fn=cmd_traffic)
+    args = ap.parse_args(argv)
+    args.fn(args)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -5,6 +5,14 @@ mean |dO| <= 1e-3 of the fp64 oracle, lse within 1e-3 (fp32 output).  Rows
 with no visible key must come back exactly as O = 0, lse = -inf.  The floor
 printed beside the error, mean |bf16(O_oracle) - O_oracle|, is what rounding
 the exact result to bf16 alone costs.
+
+Stress inputs (Q scaled by 6 at more rows than the tiny workload) make rows
+nearly one-hot with |O| up to ~4, where one bf16 ulp is 1.6e-2: rounding P to
+bf16 before the PV product (the method's design) can then move an output by
+one ulp.  For those cases the max bound is the one the FA4 chapter validates
+its kernel with (assert_close with rtol = atol = 1e-2, section on compile and
+validation constraints): |dO| <= 1e-2 + 1e-2 |O_ref| per element; the mean
+and lse bars are unchanged.
 """
 from __future__ import annotations
 
@@ -27,7 +35,9 @@ def parity_stats(o_gpu, lse_gpu, o_ref, lse_ref):
     floor = np.abs(torch.from_numpy(o_ref[full]).to(torch.bfloat16).double().numpy()
                    - o_ref[full])
     dl = np.abs(lg[full] - lse_ref[full])
+    rel_excess = err - TOL_O_MAX * np.abs(o_ref[full])
     return {
+        "o_max_minus_rtol": float(rel_excess.max()) if rel_excess.size else 0.0,
         "rows": int(o_ref.shape[0]),
         "empty_rows": int(empty.sum()),
         "o_max": float(err.max()) if err.size else 0.0,
@@ -39,14 +49,18 @@ def parity_stats(o_gpu, lse_gpu, o_ref, lse_ref):
     }
 
 
-def assert_parity(tag, o_gpu, lse_gpu, o_ref, lse_ref):
+def assert_parity(tag, o_gpu, lse_gpu, o_ref, lse_ref, stress=False):
     st = parity_stats(o_gpu, lse_gpu, o_ref, lse_ref)
     print(f"[parity] {tag}: " + ", ".join(
         f"{k}={v:.3e}" if isinstance(v, float) else f"{k}={v}" for k, v in st.items()),
         flush=True)
     assert st["finite"], f"{tag}: non-finite output"
     assert st["empty_ok"], f"{tag}: rows without keys must give O = 0 and lse = -inf"
-    assert st["o_max"] <= TOL_O_MAX, f"{tag}: max |dO| {st['o_max']:.3e} > {TOL_O_MAX}"
+    if stress:
+        assert st["o_max_minus_rtol"] <= TOL_O_MAX, (
+            f"{tag}: max |dO| - 1e-2 |O| = {st['o_max_minus_rtol']:.3e} > {TOL_O_MAX}")
+    else:
+        assert st["o_max"] <= TOL_O_MAX, f"{tag}: max |dO| {st['o_max']:.3e} > {TOL_O_MAX}"
     assert st["o_mean"] <= TOL_O_MEAN, f"{tag}: mean |dO| {st['o_mean']:.3e} > {TOL_O_MEAN}"
     assert st["lse_max"] <= TOL_LSE_MAX, f"{tag}: max |dlse| {st['lse_max']:.3e} > {TOL_LSE_MAX}"
     return st

@@ -26,12 +26,13 @@ def _run(q, k, v, causal, scale=None):
     return o.cpu(), lse.cpu()
 
 
-def _full_check(tag, q, k, v, causal, orc, scale=None):
+def _full_check(tag, q, k, v, causal, orc, scale=None, stress=False):
     print(f"[case] {tag} q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)} "
           f"causal={causal}", flush=True)
     o, lse = _run(q, k, v, causal, scale)
     o_ref, l_ref = orc.attn_rows(q, k, v, causal=causal, scale=scale)
-    return assert_parity(tag, o.reshape(-1, o.shape[-1]), lse.reshape(-1), o_ref, l_ref)
+    return assert_parity(tag, o.reshape(-1, o.shape[-1]), lse.reshape(-1), o_ref, l_ref,
+                         stress=stress)
 
 
 def test_tiny_workload(orc):
@@ -67,7 +68,7 @@ SMALL = [
 def test_small_shapes(orc, shape):
     B, Hq, Hkv, Lq, Lk, dqk, dv, causal, qm = shape
     q, k, v = make_qkv(B, Hq, Hkv, Lq, Lk, dqk, dv, seed=hash(shape) % 10007, q_mult=qm)
-    _full_check(f"small {shape}", q, k, v, causal, orc)
+    _full_check(f"small {shape}", q, k, v, causal, orc, stress=qm != 1.0)
 
 
 @pytest.mark.parametrize("name", ["mha_l2k", "causal_l8k", "gqa_l16k", "dsv3_l32k"])
