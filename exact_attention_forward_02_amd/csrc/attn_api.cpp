@@ -18,7 +18,7 @@ namespace {
 constexpr int kAbiVersion = 1;
 constexpr int kMaxDevices = 64;
 constexpr int kXcds = 8;                 // MI355X: 8 accelerator complex dies
-constexpr int kTilesPerXcdWave = 64;     // ~ concurrent workgroups per XCD (32 CUs x 2)
+constexpr int kTilesPerXcdWave = 32;     // concurrent workgroups per XCD (32 CUs x 1)
 constexpr float kDefaultThreshold = 8.0f;  // log2 units: a factor of 256
 
 // -1 unknown, 0 not gfx950, 1 gfx950
@@ -42,6 +42,9 @@ int check_args(const void* q, const void* k, const void* v, const void* o, const
     const long long q_rows = (long long)B * Hq * Lq;
     const long long kv_rows = (long long)B * Hkv * Lk;
     if (q_rows > INT32_MAX || kv_rows > INT32_MAX) return ATTN_ERR_TOO_LARGE;
+    // one K or V head is addressed with 32-bit byte offsets in the kernel
+    const int dmax = d_qk > d_v ? d_qk : d_v;
+    if ((long long)Lk * dmax * 2 > INT32_MAX) return ATTN_ERR_TOO_LARGE;
     return ATTN_OK;
 }
 
@@ -75,7 +78,7 @@ int fill_schedule(attn::FwdParams& p) {
     p.G = p.Hq / p.Hkv;
     // query heads that share a K/V head are packed into one workgroup, one
     // head per wave group, so the K/V block is loaded once for all of them
-    p.Gp = (p.G % 4 == 0) ? 4 : (p.G % 2 == 0) ? 2 : 1;
+    p.Gp = (p.G % 8 == 0) ? 8 : (p.G % 4 == 0) ? 4 : (p.G % 2 == 0) ? 2 : 1;
     p.n_hg = p.G / p.Gp;
     p.bm_pos = attn::kRowsPerWave * attn::kWaves / p.Gp;
     p.n_m = (p.Lq + p.bm_pos - 1) / p.bm_pos;

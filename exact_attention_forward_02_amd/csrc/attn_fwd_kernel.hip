@@ -109,34 +109,54 @@ __device__ __forceinline__ u32x4 load16(const uint16_t* p) {
     return *reinterpret_cast<const u32x4*>(p);
 }
 
-// Copy 16 bytes per lane from global memory straight into LDS: lane l's data
-// lands at lds_dst + 16 * l (the destination is one contiguous KiB per wave).
-__device__ __forceinline__ void copy_to_lds(const unsigned char* src, void* lds_dst) {
-    __builtin_amdgcn_global_load_lds(src, lds_dst, 16, 0, 0);
+// Copy 16 bytes per lane from global memory straight into LDS through a
+// buffer descriptor: lane l's data lands at lds_dst + 16 * l (one contiguous
+// KiB per wave).  The buffer form (rather than the global-address form) lets
+// LDS reads issued after it wait for just the reads they need.  Offsets at or
+// past the descriptor's record count read as zero instead of faulting.
+typedef __attribute__((address_space(3))) void lds_void;
+__device__ __forceinline__ void copy_to_lds(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff,
+                                            void* lds_dst) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)lds_dst, 16, voff, 0, 0, 0);
 }
 
-// Heads up to 128 wide keep two score tiles in registers and overlap the next
-// block's QK^T with the current block's softmax; wider heads would spill.
-template <int DQK>
-constexpr bool kPipelined = DQK <= 128;
+// Raw buffer descriptor over [base, base + bytes): 32-bit data format, no stride.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
 
 template <int DQK, int DV, bool CAUSAL, bool DEBUG>
-__global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const FwdParams p) {
+__global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
     using S = Shape<DQK, DV>;
     constexpr int kRowK = DQK * 2;  // bytes per K row
     constexpr int kRowV = DV * 2;   // bytes per V row
-    // two buffers each for K and V, distinct objects so that reads of one
-    // buffer are never ordered behind copies into the other
+    // two stage buffers each for K and V, distinct objects so that reads of
+    // one buffer are never ordered behind copies into the other
     __shared__ __attribute__((aligned(1024))) unsigned char lds_k0[S::kKBytes];
     __shared__ __attribute__((aligned(1024))) unsigned char lds_k1[S::kKBytes];
     __shared__ __attribute__((aligned(1024))) unsigned char lds_v0[S::kVBytes];
     __shared__ __attribute__((aligned(1024))) unsigned char lds_v1[S::kVBytes];
+
+    // Bring every kernel argument the sweep uses into SGPRs now: a scalar
+    // load still in flight inside the loop would force each LDS wait there to
+    // drain all outstanding LDS reads instead of only the oldest ones.
+    const float c2 = p.scale_log2;
+    const float threshold = p.threshold;
+    const float scale = p.scale;
+    float* const lse_out = p.lse;
+    uint16_t* const o_out = p.o;
+    unsigned long long* const rescale_count = p.rescale_count;
+    asm volatile("" ::"s"(c2), "s"(threshold), "s"(scale), "s"(lse_out), "s"(o_out),
+                 "s"(rescale_count));
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
     const int lane = tid & 63;
     const int l32 = lane & 31;
     const int hi = lane >> 5;
+    // waves are spread round-robin over the 4 SIMDs: waves w and w + 4 share
+    // one; the two wave groups alternate between MFMA and VALU phases
+    const int grp = wave / kGroupWaves;
 
     // ---- tile of this workgroup: (unit, position tile m) ------------------
     int unit, mo;
@@ -179,7 +199,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const FwdParams p
         wend = min(p.Lk, wave_last + off + 1);
     }
     const int nblk = kend > 0 ? (kend + kBlockN - 1) / kBlockN : 0;
-    const bool wave_rows = qw < p.Lq;
+    // this wave's blocks are a prefix [0, nact) of the tile's blocks
+    const int nact =
+        (qw < p.Lq && wend > 0) ? min(nblk, (wend + kBlockN - 1) / kBlockN) : 0;
 
     // ---- Q fragment, resident in registers for the whole sweep -----------
     // lane holds Q[qw + l32][16 ks + 8 hi .. +7] for every k-step ks
@@ -218,48 +240,61 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const FwdParams p
         voff_copy[i] = r * kRowV + 16 * c;
     }
 
+    // one descriptor per K/V head; a head is at most 2^31 bytes (checked on
+    // the host), so 32-bit byte offsets address all of it
+    const __amdgpu_buffer_rsrc_t krsrc = make_rsrc(kbase, (uint32_t)p.Lk * kRowK);
+    const __amdgpu_buffer_rsrc_t vrsrc = make_rsrc(vbase, (uint32_t)p.Lk * kRowV);
     auto copy_k = [&](int jb, unsigned char* dst) {
         const int key0 = jb * kBlockN;
-        const unsigned char* src = kbase + (size_t)key0 * kRowK;
+        const uint32_t blk = (uint32_t)key0 * kRowK;
         if (key0 + kBlockN <= p.Lk) {
 #pragma unroll
             for (int i = 0; i < S::kKCopies; ++i)
-                copy_to_lds(src + koff[i], dst + 1024 * (wave * S::kKCopies + i));
+                copy_to_lds(krsrc, blk + koff[i], dst + 1024 * (wave * S::kKCopies + i));
         } else {
             const int last = p.Lk - 1 - key0;
 #pragma unroll
             for (int i = 0; i < S::kKCopies; ++i) {
                 const int r = (int)koff[i] / kRowK;
                 const int rr = min(r, last);
-                copy_to_lds(src + (koff[i] - (uint32_t)((r - rr) * kRowK)),
+                copy_to_lds(krsrc, blk + koff[i] - (uint32_t)((r - rr) * kRowK),
                             dst + 1024 * (wave * S::kKCopies + i));
             }
         }
     };
     auto copy_v = [&](int jb, unsigned char* dst) {
         const int key0 = jb * kBlockN;
-        const unsigned char* src = vbase + (size_t)key0 * kRowV;
+        const uint32_t blk = (uint32_t)key0 * kRowV;
         if (key0 + kBlockN <= p.Lk) {
 #pragma unroll
             for (int i = 0; i < S::kVCopies; ++i)
-                copy_to_lds(src + voff_copy[i], dst + 1024 * (wave * S::kVCopies + i));
+                copy_to_lds(vrsrc, blk + voff_copy[i], dst + 1024 * (wave * S::kVCopies + i));
         } else {
             const int last = p.Lk - 1 - key0;
 #pragma unroll
             for (int i = 0; i < S::kVCopies; ++i) {
                 const int r = (int)voff_copy[i] / kRowV;
                 const int rr = min(r, last);
-                copy_to_lds(src + (voff_copy[i] - (uint32_t)((r - rr) * kRowV)),
+                copy_to_lds(vrsrc, blk + voff_copy[i] - (uint32_t)((r - rr) * kRowV),
                             dst + 1024 * (wave * S::kVCopies + i));
             }
         }
     };
+    // stage t holds K(t) and V(t - 1) (whichever exist)
+    auto copy_stage = [&](int t, unsigned char* kdst, unsigned char* vdst) {
+        if (t < nblk) copy_k(t, kdst);
+        if (t >= 1 && t - 1 < nblk) copy_v(t - 1, vdst);
+    };
 
     // ---- LDS read offsets (bytes within a block buffer) -----------------------
-    // S^T operand: row 32 mb + l32, chunk 2 ks + hi (mb adds 32 rows)
-    int kread[S::kKSteps];
+    // S^T operand: row 32 mb + l32, chunk 2 ks + hi (mb adds 32 rows).  The
+    // swizzle XORs the low 4 (d = 128) or 3 (other widths) bits of the chunk
+    // index, so the lane-dependent part of the offset repeats every
+    // kReadTable k-steps and the rest is a constant.
+    constexpr int kReadTable = (DQK == 128) ? 8 : 4;
+    int kread[kReadTable];
 #pragma unroll
-    for (int ks = 0; ks < S::kKSteps; ++ks)
+    for (int ks = 0; ks < kReadTable; ++ks)
         kread[ks] = (l32 * S::kChunksK + ((2 * ks + hi) ^ kswz<DQK>(l32))) * 16;
     // PV operand (transposed V reads): 16-lane group g = lane / 16 with index
     // 4 r + j reads row 16 G + 8 t + 4 (g / 2) + r, dims 32 i + 16 (g & 1) +
@@ -284,37 +319,97 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const FwdParams p
     float ref = kNegInf;  // exponent reference, raw q.k units
     float ell = 0.0f;     // this lane's share of sum P (fp32 P), for lse
     float ell_o = 0.0f;   // this lane's share of sum P (bf16 P), normalises O
-    const float c2 = p.scale_log2;
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+    f32x16 s[kBlockN / 32];  // scores of the block between its M and V phases
+    bf16x8 pb[kBlockN / 16];  // its bf16 weights between its V and M phases
 
-    auto active = [&](int jb) { return wave_rows && jb * kBlockN < wend; };
-
-    // S^T = K Q^T for 64 keys x 32 queries: two 32x32 tiles
-    auto compute_s = [&](const unsigned char* kl, f32x16 (&s)[kBlockN / 32]) {
+    // ---- MFMA phase M(j): O^T += V^T P^T for block j, then S^T = K Q^T for
+    // block j + 1 (j = -1: scores of block 0 only) --------------------------
+    // The phase is a sequence of MFMA units, each with one LDS operand: 16 PV
+    // units (g, i) and 16 score units (ks, mb).  Operands are loaded kAhead
+    // units before their MFMA into a small register ring, and scheduling
+    // barriers keep that order, so LDS latency overlaps earlier MFMAs instead
+    // of stalling each one.
+    constexpr int kPvUnits = (kBlockN / 16) * S::kDvBlocks;
+    constexpr int kSUnits = S::kKSteps * (kBlockN / 32);
+    constexpr int kAhead = DQK > 128 ? 3 : 4;  // wide heads have fewer spare VGPRs
+    auto load_pv = [&](int u, const unsigned char* vl) {
+        const int g = u / S::kDvBlocks, i = u % S::kDvBlocks;
+        i16x4 part[2];
 #pragma unroll
-        for (int mb = 0; mb < kBlockN / 32; ++mb)
+        for (int t = 0; t < 2; ++t)
+            part[t] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_i16x4*)(vl + vread[i] + (16 * g + 8 * t) * kRowV));
+        return __builtin_bit_cast(
+            bf16x8, __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    auto load_s = [&](int u, const unsigned char* kl) {
+        const int ks = u / (kBlockN / 32), mb = u % (kBlockN / 32);
+        return *reinterpret_cast<const bf16x8*>(kl + kread[ks % kReadTable] +
+                                                (ks / kReadTable) * kReadTable * 32 +
+                                                mb * 32 * kRowK);
+    };
+    auto m_phase = [&](int j, const unsigned char* kl, const unsigned char* vl) {
+        const bool do_pv = j >= 0 && j < nact;
+        const bool do_s = j + 1 < nact;
+        if (do_s) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) s[mb][r] = 0.0f;
+            for (int mb = 0; mb < kBlockN / 32; ++mb)
 #pragma unroll
-        for (int ks = 0; ks < S::kKSteps; ++ks) {
+                for (int r = 0; r < 16; ++r) s[mb][r] = 0.0f;
+        }
+        if (do_pv && do_s) {
+            constexpr int kUnits = kPvUnits + kSUnits;
+            bf16x8 ring[kAhead];
 #pragma unroll
-            for (int mb = 0; mb < kBlockN / 32; ++mb) {
-                const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-                    kl + kread[ks] + mb * 32 * kRowK);
+            for (int u = 0; u < kAhead; ++u) ring[u] = load_pv(u, vl);
+#pragma unroll
+            for (int u = 0; u < kUnits; ++u) {
+                const bf16x8 a = ring[u % kAhead];
+                const int n = u + kAhead;
+                if (n < kUnits) ring[u % kAhead] = n < kPvUnits ? load_pv(n, vl)
+                                                                : load_s(n - kPvUnits, kl);
+                if (u < kPvUnits) {
+                    const int g = u / S::kDvBlocks, i = u % S::kDvBlocks;
+                    oacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[g], oacc[i], 0, 0, 0);
+                } else {
+                    const int v = u - kPvUnits;
+                    const int ks = v / (kBlockN / 32), mb = v % (kBlockN / 32);
+                    s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[mb], 0, 0, 0);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        } else if (do_pv) {
+            bf16x8 ring[kAhead];
+#pragma unroll
+            for (int u = 0; u < kAhead; ++u) ring[u] = load_pv(u, vl);
+#pragma unroll
+            for (int u = 0; u < kPvUnits; ++u) {
+                const bf16x8 a = ring[u % kAhead];
+                if (u + kAhead < kPvUnits) ring[u % kAhead] = load_pv(u + kAhead, vl);
+                const int g = u / S::kDvBlocks, i = u % S::kDvBlocks;
+                oacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[g], oacc[i], 0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        } else if (do_s) {
+            bf16x8 ring[kAhead];
+#pragma unroll
+            for (int u = 0; u < kAhead; ++u) ring[u] = load_s(u, kl);
+#pragma unroll
+            for (int u = 0; u < kSUnits; ++u) {
+                const bf16x8 a = ring[u % kAhead];
+                if (u + kAhead < kSUnits) ring[u % kAhead] = load_s(u + kAhead, kl);
+                const int ks = u / (kBlockN / 32), mb = u % (kBlockN / 32);
                 s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[mb], 0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
     };
 
-    // Online softmax of one block's scores, then O^T += V^T P^T.  With
-    // next_tag = true, the scores of the next block (K from next_kl, into
-    // s_next) are computed in the same straight-line stretch as the
-    // exponentials and the PV product, so that the MFMA work of both can
-    // interleave with the VALU work.
-    auto softmax_pv = [&](auto next_tag, int jb, f32x16 (&s)[kBlockN / 32],
-                          const unsigned char* vl, const unsigned char* next_kl,
-                          f32x16 (&s_next)[kBlockN / 32]) {
-        const int key0 = jb * kBlockN;
+    // ---- VALU phase V(j): online softmax of block j's scores -----------------
+    auto v_phase = [&](int j) {
+        if (j >= nact) return;
+        const int key0 = j * kBlockN;
         // mask keys past the end or past the causal diagonal
         const bool need_mask =
             (key0 + kBlockN > p.Lk) || (CAUSAL && key0 + kBlockN - 1 > qw + off);
@@ -346,7 +441,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const FwdParams p
             ref = cand;  // first visible block: adopt its max, state is empty
         } else {
             const float delta = (ref - cand) * c2;
-            if (delta < -p.threshold) {
+            if (delta < -threshold) {
                 moved = true;
                 acc_scale = __builtin_amdgcn_exp2f(delta);
                 ref = cand;
@@ -360,8 +455,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const FwdParams p
                 for (int r = 0; r < 16; ++r) oacc[i][r] *= acc_scale;
             ell *= acc_scale;
             ell_o *= acc_scale;
-            if (DEBUG && p.rescale_count != nullptr && lane == 0)
-                atomicAdd(p.rescale_count,
+            if (DEBUG && rescale_count != nullptr && lane == 0)
+                atomicAdd(rescale_count,
                           (unsigned long long)__builtin_popcountll(vote & 0xffffffffull));
         }
 
@@ -371,7 +466,6 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const FwdParams p
         const float refc = (ref == kNegInf) ? 0.0f : ref * c2;
         float rs[4] = {0.0f, 0.0f, 0.0f, 0.0f};
         float rb[2] = {0.0f, 0.0f};
-        bf16x8 pb[kBlockN / 16];
 #pragma unroll
         for (int mb = 0; mb < kBlockN / 32; ++mb) {
 #pragma unroll
@@ -393,103 +487,49 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const FwdParams p
         }
         ell += (rs[0] + rs[1]) + (rs[2] + rs[3]);
         ell_o += rb[0] + rb[1];
-
-        if constexpr (decltype(next_tag)::value) compute_s(next_kl, s_next);
-
-        // O^T += V^T P^T, 16 keys per MFMA; the V^T operand comes from two
-        // transposed LDS reads of row-major V
-#pragma unroll
-        for (int g = 0; g < kBlockN / 16; ++g) {
-#pragma unroll
-            for (int i = 0; i < S::kDvBlocks; ++i) {
-                i16x4 part[2];
-#pragma unroll
-                for (int t = 0; t < 2; ++t)
-                    part[t] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (lds_i16x4*)(vl + vread[i] + (16 * g + 8 * t) * kRowV));
-                const bf16x8 a = __builtin_bit_cast(
-                    bf16x8, __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
-                oacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[g], oacc[i], 0, 0, 0);
-            }
-        }
     };
 
-    // ---- sweep over key blocks --------------------------------------------
-    f32x16 sa[kBlockN / 32], sb[kBlockN / 32];
-    if constexpr (kPipelined<DQK>) {
-        // Software pipelined.  Step j: copy K(j+2) and V(j+1) into the free
-        // buffers, compute the scores of block j+1 (MFMA work independent of
-        // the rest of the step), then the softmax and PV product of block j,
-        // whose scores were computed in step j-1.  K runs one block ahead of
-        // V, so K(j+1) and V(j) are resident during step j.  Even steps read K
-        // from lds_k1 and V from lds_v0; odd steps the other buffers.
-        if (nblk > 0) {
-            copy_k(0, lds_k0);
-            copy_v(0, lds_v0);
-            if (nblk > 1) copy_k(1, lds_k1);
+    // ---- ping-pong sweep over key blocks ---------------------------------------
+    // A wave's work is the sequence M(-1), V(0), M(0), V(1), M(1), ... with
+    // local phase lambda: lambda = 0 is M(-1), odd lambda = 2 j + 1 is V(j),
+    // even lambda = 2 j + 2 is M(j).  Group 0 runs local phase lambda in global
+    // phase phi = lambda, group 1 one phase later, and every phase ends with a
+    // workgroup barrier: on each SIMD one wave issues MFMA work while the
+    // other issues softmax VALU work.  M(j) reads stage j + 1 (K(j+1), V(j))
+    // in global phases 2 j + 2 and 2 j + 3; stage t + 1 is copied at the start
+    // of phase 2 t into the buffers stage t - 1 used, and waited for at the
+    // end of phase 2 t + 1.  Stages alternate between buffers 0 and 1, so the
+    // phase loop is unrolled by four to make every buffer a compile-time choice.
+    auto work = [&](int phi, const unsigned char* kl, const unsigned char* vl) {
+        const int lam = phi - grp;
+        if (lam < 0) return;
+        if (lam & 1)
+            v_phase(lam >> 1);
+        else
+            m_phase((lam >> 1) - 1, kl, vl);
+    };
+
+    if (nblk > 0) {
+        copy_stage(0, lds_k0, lds_v0);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        const int nphase = 2 * nblk + 2;
+        for (int phi = 0; phi < nphase; phi += 4) {
+            const int t = phi >> 1;  // stage read in phases phi, phi + 1 (buffers 0)
+            if (t + 1 <= nblk) copy_stage(t + 1, lds_k1, lds_v1);
+            work(phi, lds_k0, lds_v0);
+            __builtin_amdgcn_s_barrier();
+            work(phi + 1, lds_k0, lds_v0);
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
-            if (active(0)) compute_s(lds_k0, sa);
-        }
-        // a wave's active blocks are a prefix [0, nact) of the tile's blocks
-        const int nact =
-            wave_rows ? min(nblk, (wend + kBlockN - 1) / kBlockN) : 0;
-        const std::true_type with_next{};
-        const std::false_type last{};
-        for (int jb = 0; jb < nblk; jb += 2) {
-            // even step j = jb
-            if (jb + 2 < nblk) copy_k(jb + 2, lds_k0);
-            if (jb + 1 < nblk) copy_v(jb + 1, lds_v1);
-            if (jb + 1 < nact)
-                softmax_pv(with_next, jb, sa, lds_v0, lds_k1, sb);
-            else if (jb < nact)
-                softmax_pv(last, jb, sa, lds_v0, lds_k1, sb);
-            __builtin_amdgcn_s_waitcnt(0);
-            __syncthreads();
-            if (jb + 1 >= nblk) break;
-            // odd step j = jb + 1
-            if (jb + 3 < nblk) copy_k(jb + 3, lds_k1);
-            if (jb + 2 < nblk) copy_v(jb + 2, lds_v0);
-            if (jb + 2 < nact)
-                softmax_pv(with_next, jb + 1, sb, lds_v1, lds_k0, sa);
-            else if (jb + 1 < nact)
-                softmax_pv(last, jb + 1, sb, lds_v1, lds_k0, sa);
-            __builtin_amdgcn_s_waitcnt(0);
-            __syncthreads();
-        }
-    } else {
-        // One score tile live (wide heads): step j copies block j+1 into the
-        // free buffers, then computes scores, softmax and PV of block j.
-        if (nblk > 0) {
-            copy_k(0, lds_k0);
-            copy_v(0, lds_v0);
+            if (phi + 2 >= nphase) break;
+            if (t + 2 <= nblk) copy_stage(t + 2, lds_k0, lds_v0);
+            work(phi + 2, lds_k1, lds_v1);
+            __builtin_amdgcn_s_barrier();
+            work(phi + 3, lds_k1, lds_v1);
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
         }
-        for (int jb = 0; jb < nblk; jb += 2) {
-            if (jb + 1 < nblk) {
-                copy_k(jb + 1, lds_k1);
-                copy_v(jb + 1, lds_v1);
-            }
-            if (active(jb)) {
-                compute_s(lds_k0, sa);
-                softmax_pv(std::false_type{}, jb, sa, lds_v0, lds_k1, sb);
-            }
-            __builtin_amdgcn_s_waitcnt(0);
-            __syncthreads();
-            if (jb + 1 >= nblk) break;
-            if (jb + 2 < nblk) {
-                copy_k(jb + 2, lds_k0);
-                copy_v(jb + 2, lds_v0);
-            }
-            if (active(jb + 1)) {
-                compute_s(lds_k1, sa);
-                softmax_pv(std::false_type{}, jb + 1, sa, lds_v1, lds_k0, sb);
-            }
-            __builtin_amdgcn_s_waitcnt(0);
-            __syncthreads();
-        }
-        (void)sb;
     }
 
     // ---- epilogue: O = U / l (bf16), lse = scale * ref + ln l ----------------
@@ -498,7 +538,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const FwdParams p
     const float ell_o_row = pair_sum(ell_o);
     if (qi < p.Lq) {
         const float inv = ell_o_row > 0.0f ? 1.0f / ell_o_row : 0.0f;
-        uint16_t* orow = p.o + (qrow0 + qi) * DV;
+        uint16_t* orow = o_out + (qrow0 + qi) * DV;
 #pragma unroll
         for (int i = 0; i < S::kDvBlocks; ++i) {
 #pragma unroll
@@ -512,7 +552,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const FwdParams p
             }
         }
         if (hi == 0)
-            p.lse[qrow0 + qi] = ell_row > 0.0f ? ref * p.scale + logf(ell_row) : kNegInf;
+            lse_out[qrow0 + qi] = ell_row > 0.0f ? ref * scale + logf(ell_row) : kNegInf;
     }
 }
 

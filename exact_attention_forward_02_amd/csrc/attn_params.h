@@ -9,7 +9,9 @@
 namespace attn {
 
 // Work decomposition constants of the forward kernel.
-constexpr int kWaves = 4;            // waves per workgroup
+constexpr int kWaves = 8;            // waves per workgroup: two groups of 4, one wave
+                                     // of each group per SIMD
+constexpr int kGroupWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kRowsPerWave = 32;     // query rows owned by one wave (MFMA N)
 constexpr int kBlockN = 64;          // keys per K/V block

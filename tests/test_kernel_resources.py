@@ -1,0 +1,33 @@
+"""The gfx950 kernels keep every per-lane array in registers: no scratch
+memory and no VGPR spills (either would put global-memory traffic on the hot
+loop).  Compiles the kernel source with hipcc's resource-usage remarks; CPU only."""
+import re
+import shutil
+import subprocess
+
+import pytest
+
+from exact_attention_forward_02_amd import build
+
+
+def _remarks():
+    cmd = [build.hipcc(), *[f for f in build.HIPCC_FLAGS if f not in ("-shared", "-fPIC")],
+           "-c", build.SOURCES[0], "-o", "/dev/null",
+           "-Rpass-analysis=kernel-resource-usage"]
+    out = subprocess.run(cmd, capture_output=True, text=True, check=True)
+    return out.stderr
+
+
+@pytest.mark.skipif(shutil.which(build.hipcc()) is None and not build.hipcc().startswith("/"),
+                    reason="hipcc not available")
+def test_no_scratch_and_no_vgpr_spills():
+    text = _remarks()
+    kernels = re.findall(r"Function Name: (\S+)", text)
+    assert len(kernels) == 12, f"expected 12 kernel instantiations, found {len(kernels)}"
+    scratch = [int(x) for x in re.findall(r"ScratchSize \[bytes/lane\]: (\d+)", text)]
+    spills = [int(x) for x in re.findall(r"VGPRs Spill: (\d+)", text)]
+    occupancy = [int(x) for x in re.findall(r"Occupancy \[waves/SIMD\]: (\d+)", text)]
+    assert len(scratch) == len(kernels) and all(s == 0 for s in scratch), scratch
+    assert all(s == 0 for s in spills), spills
+    # one 8-wave workgroup per CU needs two waves per SIMD
+    assert all(o >= 2 for o in occupancy), occupancy
