@@ -47,6 +47,7 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
@@ -89,7 +90,6 @@ __device__ __forceinline__ int vswz(int r) {
 }
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 __device__ __forceinline__ float pair_max(float x) {
@@ -110,14 +110,14 @@ __device__ __forceinline__ u32x4 load16(const uint16_t* p) {
 }
 
 // Copy 16 bytes per lane from global memory straight into LDS through a
-// buffer descriptor: lane l's data lands at lds_dst + 16 * l (one contiguous
-// KiB per wave).  The buffer form (rather than the global-address form) lets
+// buffer descriptor: lane l reads at byte soff + voff (soff wave-uniform) and
+// its data lands at lds_dst + 16 * l (one contiguous KiB per wave).  The buffer form (rather than the global-address form) lets
 // LDS reads issued after it wait for just the reads they need.  Offsets at or
 // past the descriptor's record count read as zero instead of faulting.
 typedef __attribute__((address_space(3))) void lds_void;
 __device__ __forceinline__ void copy_to_lds(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff,
-                                            void* lds_dst) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)lds_dst, 16, voff, 0, 0, 0);
+                                            uint32_t soff, void* lds_dst) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)lds_dst, 16, voff, soff, 0, 0);
 }
 
 // Raw buffer descriptor over [base, base + bytes): 32-bit data format, no stride.
@@ -241,24 +241,28 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
     }
 
     // one descriptor per K/V head; a head is at most 2^31 bytes (checked on
-    // the host), so 32-bit byte offsets address all of it
+    // the host), so 32-bit byte offsets address all of it.  The block offset
+    // goes in the scalar offset operand and this wave's LDS destination is a
+    // scalar too, so a copy needs no vector arithmetic.
     const __amdgpu_buffer_rsrc_t krsrc = make_rsrc(kbase, (uint32_t)p.Lk * kRowK);
     const __amdgpu_buffer_rsrc_t vrsrc = make_rsrc(vbase, (uint32_t)p.Lk * kRowV);
+    const int kdst = __builtin_amdgcn_readfirstlane(1024 * S::kKCopies * wave);
+    const int vdst = __builtin_amdgcn_readfirstlane(1024 * S::kVCopies * wave);
     auto copy_k = [&](int jb, unsigned char* dst) {
         const int key0 = jb * kBlockN;
         const uint32_t blk = (uint32_t)key0 * kRowK;
         if (key0 + kBlockN <= p.Lk) {
 #pragma unroll
             for (int i = 0; i < S::kKCopies; ++i)
-                copy_to_lds(krsrc, blk + koff[i], dst + 1024 * (wave * S::kKCopies + i));
+                copy_to_lds(krsrc, koff[i], blk, dst + kdst + 1024 * i);
         } else {
             const int last = p.Lk - 1 - key0;
 #pragma unroll
             for (int i = 0; i < S::kKCopies; ++i) {
                 const int r = (int)koff[i] / kRowK;
                 const int rr = min(r, last);
-                copy_to_lds(krsrc, blk + koff[i] - (uint32_t)((r - rr) * kRowK),
-                            dst + 1024 * (wave * S::kKCopies + i));
+                copy_to_lds(krsrc, koff[i] - (uint32_t)((r - rr) * kRowK), blk,
+                            dst + kdst + 1024 * i);
             }
         }
     };
@@ -268,22 +272,17 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
         if (key0 + kBlockN <= p.Lk) {
 #pragma unroll
             for (int i = 0; i < S::kVCopies; ++i)
-                copy_to_lds(vrsrc, blk + voff_copy[i], dst + 1024 * (wave * S::kVCopies + i));
+                copy_to_lds(vrsrc, voff_copy[i], blk, dst + vdst + 1024 * i);
         } else {
             const int last = p.Lk - 1 - key0;
 #pragma unroll
             for (int i = 0; i < S::kVCopies; ++i) {
                 const int r = (int)voff_copy[i] / kRowV;
                 const int rr = min(r, last);
-                copy_to_lds(vrsrc, blk + voff_copy[i] - (uint32_t)((r - rr) * kRowV),
-                            dst + 1024 * (wave * S::kVCopies + i));
+                copy_to_lds(vrsrc, voff_copy[i] - (uint32_t)((r - rr) * kRowV), blk,
+                            dst + vdst + 1024 * i);
             }
         }
-    };
-    // stage t holds K(t) and V(t - 1) (whichever exist)
-    auto copy_stage = [&](int t, unsigned char* kdst, unsigned char* vdst) {
-        if (t < nblk) copy_k(t, kdst);
-        if (t >= 1 && t - 1 < nblk) copy_v(t - 1, vdst);
     };
 
     // ---- LDS read offsets (bytes within a block buffer) -----------------------
@@ -318,8 +317,20 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
         for (int r = 0; r < 16; ++r) oacc[i][r] = 0.0f;
     float ref = kNegInf;  // exponent reference, raw q.k units
     float ell = 0.0f;     // this lane's share of sum P (fp32 P), for lse
-    float ell_o = 0.0f;   // this lane's share of sum P (bf16 P), normalises O
-    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+    // Row sums of the bf16 P that feed the PV product (they normalise O with
+    // exactly the weights it was built from), accumulated by a 16x16x32 MFMA
+    // with a 0/1 selector as A: in that shape lane l supplies B column l % 16
+    // from k-group l / 16, so with A[m][k] = 1 iff m and k's group have equal
+    // parity, even rows of D sum the P of query l % 16 (groups 0, 2) and odd
+    // rows those of query l % 16 + 16 (groups 1, 3).  Lane l then finds its
+    // own query's sum in register (l / 16) & 1 of the accumulator.
+    f32x4 ell_o = {0.0f, 0.0f, 0.0f, 0.0f};
+    bf16x8 sel;
+    {
+        const __bf16 v = (((lane & 15) ^ (lane >> 4)) & 1) ? (__bf16)0.0f : (__bf16)1.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) sel[i] = v;
+    }
     f32x16 s[kBlockN / 32];  // scores of the block between its M and V phases
     bf16x8 pb[kBlockN / 16];  // its bf16 weights between its V and M phases
 
@@ -352,56 +363,68 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
     auto m_phase = [&](int j, const unsigned char* kl, const unsigned char* vl) {
         const bool do_pv = j >= 0 && j < nact;
         const bool do_s = j + 1 < nact;
-        if (do_s) {
-#pragma unroll
-            for (int mb = 0; mb < kBlockN / 32; ++mb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) s[mb][r] = 0.0f;
-        }
-        if (do_pv && do_s) {
-            constexpr int kUnits = kPvUnits + kSUnits;
-            bf16x8 ring[kAhead];
-#pragma unroll
-            for (int u = 0; u < kAhead; ++u) ring[u] = load_pv(u, vl);
-#pragma unroll
-            for (int u = 0; u < kUnits; ++u) {
-                const bf16x8 a = ring[u % kAhead];
-                const int n = u + kAhead;
-                if (n < kUnits) ring[u % kAhead] = n < kPvUnits ? load_pv(n, vl)
-                                                                : load_s(n - kPvUnits, kl);
-                if (u < kPvUnits) {
-                    const int g = u / S::kDvBlocks, i = u % S::kDvBlocks;
-                    oacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[g], oacc[i], 0, 0, 0);
-                } else {
-                    const int v = u - kPvUnits;
-                    const int ks = v / (kBlockN / 32), mb = v % (kBlockN / 32);
-                    s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[mb], 0, 0, 0);
-                }
-                __builtin_amdgcn_sched_barrier(0);
-            }
-        } else if (do_pv) {
-            bf16x8 ring[kAhead];
-#pragma unroll
-            for (int u = 0; u < kAhead; ++u) ring[u] = load_pv(u, vl);
-#pragma unroll
-            for (int u = 0; u < kPvUnits; ++u) {
-                const bf16x8 a = ring[u % kAhead];
-                if (u + kAhead < kPvUnits) ring[u % kAhead] = load_pv(u + kAhead, vl);
+        const f32x16 zero = {};
+        // one MFMA unit: PV unit u < kPvUnits, else score unit u - kPvUnits; the
+        // first k-step of a score block starts from an inline zero accumulator
+        auto mfma_unit = [&](int u, bf16x8 a) {
+            if (u < kPvUnits) {
                 const int g = u / S::kDvBlocks, i = u % S::kDvBlocks;
                 oacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[g], oacc[i], 0, 0, 0);
-                __builtin_amdgcn_sched_barrier(0);
+                if (i == S::kDvBlocks - 1)
+                    ell_o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sel, pb[g], ell_o, 0, 0, 0);
+            } else {
+                const int v = u - kPvUnits;
+                const int ks = v / (kBlockN / 32), mb = v % (kBlockN / 32);
+                s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], ks == 0 ? zero : s[mb],
+                                                                0, 0, 0);
             }
-        } else if (do_s) {
-            bf16x8 ring[kAhead];
+        };
+        if (do_pv || do_s) {
+            auto load = [&](int u) {
+                return u < kPvUnits ? load_pv(u, vl) : load_s(u - kPvUnits, kl);
+            };
+            if (do_pv && do_s) {
+                // PV units (two transposed 8-byte LDS reads each) and score units
+                // (one 16-byte read) alternate, which spreads the LDS demand
+                // evenly over the phase instead of saturating it in one half
+                constexpr int kUnits = kPvUnits + kSUnits;
+                static_assert(kSUnits >= kPvUnits, "every PV unit has a score partner");
+                auto order = [](int n) {
+                    return n < 2 * kPvUnits ? ((n & 1) ? kPvUnits + (n >> 1) : (n >> 1))
+                                            : kPvUnits + n - kPvUnits;
+                };
+                bf16x8 ring[kAhead];
 #pragma unroll
-            for (int u = 0; u < kAhead; ++u) ring[u] = load_s(u, kl);
+                for (int n = 0; n < kAhead; ++n) ring[n] = load(order(n));
 #pragma unroll
-            for (int u = 0; u < kSUnits; ++u) {
-                const bf16x8 a = ring[u % kAhead];
-                if (u + kAhead < kSUnits) ring[u % kAhead] = load_s(u + kAhead, kl);
-                const int ks = u / (kBlockN / 32), mb = u % (kBlockN / 32);
-                s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[mb], 0, 0, 0);
-                __builtin_amdgcn_sched_barrier(0);
+                for (int n = 0; n < kUnits; ++n) {
+                    const bf16x8 a = ring[n % kAhead];
+                    if (n + kAhead < kUnits) ring[n % kAhead] = load(order(n + kAhead));
+                    mfma_unit(order(n), a);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            } else if (do_pv) {
+                bf16x8 ring[kAhead];
+#pragma unroll
+                for (int u = 0; u < kAhead; ++u) ring[u] = load(u);
+#pragma unroll
+                for (int u = 0; u < kPvUnits; ++u) {
+                    const bf16x8 a = ring[u % kAhead];
+                    if (u + kAhead < kPvUnits) ring[u % kAhead] = load(u + kAhead);
+                    mfma_unit(u, a);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            } else {
+                bf16x8 ring[kAhead];
+#pragma unroll
+                for (int u = 0; u < kAhead; ++u) ring[u] = load(kPvUnits + u);
+#pragma unroll
+                for (int u = 0; u < kSUnits; ++u) {
+                    const bf16x8 a = ring[u % kAhead];
+                    if (u + kAhead < kSUnits) ring[u % kAhead] = load(kPvUnits + u + kAhead);
+                    mfma_unit(kPvUnits + u, a);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
             }
         }
     };
@@ -425,81 +448,88 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
                 }
         }
 
-        // block max of this row (raw units)
-        float bmax = kNegInf;
+        // block max of this row (raw units), two independent chains
+        float bm0 = kNegInf, bm1 = kNegInf;
 #pragma unroll
-        for (int mb = 0; mb < kBlockN / 32; ++mb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) bmax = fmaxf(bmax, s[mb][r]);
-        bmax = pair_max(bmax);
-
-        // conditional rescale decision
-        const float cand = fmaxf(ref, bmax);
-        bool moved = false;
-        float acc_scale = 1.0f;
-        if (ref == kNegInf) {
-            ref = cand;  // first visible block: adopt its max, state is empty
-        } else {
-            const float delta = (ref - cand) * c2;
-            if (delta < -threshold) {
-                moved = true;
-                acc_scale = __builtin_amdgcn_exp2f(delta);
-                ref = cand;
-            }
+        for (int r = 0; r < 16; r += 2) {
+            bm0 = fmaxf(fmaxf(bm0, s[0][r]), s[0][r + 1]);
+            bm1 = fmaxf(fmaxf(bm1, s[kBlockN / 32 - 1][r]), s[kBlockN / 32 - 1][r + 1]);
         }
-        const unsigned long long vote = __ballot(moved);
-        if (vote) {  // wave-uniform: some row of this wave moved its reference
+        static_assert(kBlockN / 32 == 2, "two 32-key score blocks per key block");
+        const float bmax = pair_max(fmaxf(bm0, bm1));
+
+        // Conditional rescale decision, branch-free.  delta is -inf when the
+        // row had no reference yet (the first block with a visible key adopts
+        // its own max: scale 0 applied to an empty state) and NaN while the
+        // row has seen no visible key at all (nothing moves).
+        const float cand = fmaxf(ref, bmax);
+        const float delta = (ref - cand) * c2;
+        const bool moved = delta < -threshold;
+        const float acc_scale = moved ? __builtin_amdgcn_exp2f(delta) : 1.0f;
+        if (DEBUG && rescale_count != nullptr) {
+            // events count reference moves after the first one of a row
+            const unsigned long long ev = __ballot(moved && ref != kNegInf);
+            if (lane == 0 && ev)
+                atomicAdd(rescale_count, (unsigned long long)__builtin_popcountll(ev & 0xffffffffull));
+        }
+        ref = moved ? cand : ref;
+        if (__ballot(moved)) {  // wave-uniform: some row of this wave moved its reference
 #pragma unroll
             for (int i = 0; i < S::kDvBlocks; ++i)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) oacc[i][r] *= acc_scale;
             ell *= acc_scale;
+            // only the register holding this lane's own query matters
             ell_o *= acc_scale;
-            if (DEBUG && rescale_count != nullptr && lane == 0)
-                atomicAdd(rescale_count,
-                          (unsigned long long)__builtin_popcountll(vote & 0xffffffffull));
         }
 
-        // P = 2^(x * c2 - ref * c2), rounded to bf16 in registers.  Two row
-        // sums: the fp32 P for lse, and the bf16 P that feed the PV product,
-        // which normalises O with exactly the weights it was built from.
+        // P = 2^(x * c2 - ref * c2), rounded to bf16 in registers; the fp32
+        // P are summed here for lse, the bf16 P by the MFMA phase.  Computed in
+        // place, all exponent arguments first, then all exponentials, then the
+        // sums: independent instructions back to back, since this wave is the
+        // only VALU issuer on its SIMD while the other wave runs MFMAs.
         const float refc = (ref == kNegInf) ? 0.0f : ref * c2;
-        float rs[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-        float rb[2] = {0.0f, 0.0f};
 #pragma unroll
-        for (int mb = 0; mb < kBlockN / 32; ++mb) {
+        for (int mb = 0; mb < kBlockN / 32; ++mb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) s[mb][r] = fmaf(s[mb][r], c2, -refc);
+#pragma unroll
+        for (int mb = 0; mb < kBlockN / 32; ++mb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) s[mb][r] = __builtin_amdgcn_exp2f(s[mb][r]);
+        float rs[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) rs[i] = s[0][i] + s[0][i + 8];
+#pragma unroll
+        for (int mb = 1; mb < kBlockN / 32; ++mb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) rs[r & 7] += s[mb][r];
+#pragma unroll
+        for (int mb = 0; mb < kBlockN / 32; ++mb)
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
                 f32x8 e;
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    e[i] = __builtin_amdgcn_exp2f(fmaf(s[mb][8 * t + i], c2, -refc));
-                    rs[i & 3] += e[i];
-                }
-                const bf16x8 pk = __builtin_convertvector(e, bf16x8);
-                pb[2 * mb + t] = pk;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const bf16x2 pr = {pk[2 * i], pk[2 * i + 1]};
-                    rb[i & 1] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, rb[i & 1], false);
-                }
+                for (int i = 0; i < 8; ++i) e[i] = s[mb][8 * t + i];
+                pb[2 * mb + t] = __builtin_convertvector(e, bf16x8);
             }
-        }
-        ell += (rs[0] + rs[1]) + (rs[2] + rs[3]);
-        ell_o += rb[0] + rb[1];
+        ell += ((rs[0] + rs[1]) + (rs[2] + rs[3])) + ((rs[4] + rs[5]) + (rs[6] + rs[7]));
     };
 
     // ---- ping-pong sweep over key blocks ---------------------------------------
     // A wave's work is the sequence M(-1), V(0), M(0), V(1), M(1), ... with
     // local phase lambda: lambda = 0 is M(-1), odd lambda = 2 j + 1 is V(j),
     // even lambda = 2 j + 2 is M(j).  Group 0 runs local phase lambda in global
-    // phase phi = lambda, group 1 one phase later, and every phase ends with a
-    // workgroup barrier: on each SIMD one wave issues MFMA work while the
-    // other issues softmax VALU work.  M(j) reads stage j + 1 (K(j+1), V(j))
-    // in global phases 2 j + 2 and 2 j + 3; stage t + 1 is copied at the start
-    // of phase 2 t into the buffers stage t - 1 used, and waited for at the
-    // end of phase 2 t + 1.  Stages alternate between buffers 0 and 1, so the
-    // phase loop is unrolled by four to make every buffer a compile-time choice.
+    // phase phi = lambda and group 1 one phase later, so on each SIMD one wave
+    // issues MFMA work while the other issues softmax VALU work.  M(j) reads
+    // stage j + 1 = {K(j + 1), V(j)} in global phases 2 j + 2 and 2 j + 3.
+    // Stage t + 1 is copied during phases 2 t (K) and 2 t + 1 (V) into the
+    // buffers stage t - 1 used, and a workgroup barrier after phase 2 t + 1
+    // both publishes it and retires every read of stage t - 1.  Nothing else
+    // synchronises the waves: the two groups start each two-phase window on
+    // opposite phase kinds and keep that pairing by themselves.  Stages
+    // alternate between buffers 0 and 1, so the phase loop is unrolled by four
+    // to make every buffer a compile-time choice.
     auto work = [&](int phi, const unsigned char* kl, const unsigned char* vl) {
         const int lam = phi - grp;
         if (lam < 0) return;
@@ -510,22 +540,22 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
     };
 
     if (nblk > 0) {
-        copy_stage(0, lds_k0, lds_v0);
+        copy_k(0, lds_k0);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         const int nphase = 2 * nblk + 2;
         for (int phi = 0; phi < nphase; phi += 4) {
             const int t = phi >> 1;  // stage read in phases phi, phi + 1 (buffers 0)
-            if (t + 1 <= nblk) copy_stage(t + 1, lds_k1, lds_v1);
+            if (t + 1 < nblk) copy_k(t + 1, lds_k1);
             work(phi, lds_k0, lds_v0);
-            __builtin_amdgcn_s_barrier();
+            if (t < nblk) copy_v(t, lds_v1);
             work(phi + 1, lds_k0, lds_v0);
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
             if (phi + 2 >= nphase) break;
-            if (t + 2 <= nblk) copy_stage(t + 2, lds_k0, lds_v0);
+            if (t + 2 < nblk) copy_k(t + 2, lds_k0);
             work(phi + 2, lds_k1, lds_v1);
-            __builtin_amdgcn_s_barrier();
+            if (t + 1 < nblk) copy_v(t + 1, lds_v0);
             work(phi + 3, lds_k1, lds_v1);
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
@@ -535,7 +565,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
     // ---- epilogue: O = U / l (bf16), lse = scale * ref + ln l ----------------
     const int qi = qw + l32;
     const float ell_row = pair_sum(ell);
-    const float ell_o_row = pair_sum(ell_o);
+    const float ell_o_row = ((lane >> 4) & 1) ? ell_o[1] : ell_o[0];
     if (qi < p.Lq) {
         const float inv = ell_o_row > 0.0f ? 1.0f / ell_o_row : 0.0f;
         uint16_t* orow = o_out + (qrow0 + qi) * DV;
@@ -543,7 +573,6 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
         for (int i = 0; i < S::kDvBlocks; ++i) {
 #pragma unroll
             for (int r4 = 0; r4 < 4; ++r4) {
-                typedef float f32x4 __attribute__((ext_vector_type(4)));
                 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
                 f32x4 x = {oacc[i][4 * r4 + 0] * inv, oacc[i][4 * r4 + 1] * inv,
                            oacc[i][4 * r4 + 2] * inv, oacc[i][4 * r4 + 3] * inv};
