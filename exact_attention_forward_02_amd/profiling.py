@@ -130,7 +130,7 @@ def main(argv=None):
     c.add_argument("--copy-fetch", required=True)
     c.add_argument("--copy-write", required=True)
     c.add_argument("--copy-bytes", type=float, required=True)
-    c.add_argument("--copy-kernel", default="")
+    c.add_argument("--copy-kernel", default="neg")  # the calibration copy is torch.neg
     c.add_argument("--kernel", default="attn_fwd_kernel")
     c.add_argument("--workload", required=True)
     c.add_argument("--out")
