@@ -10,7 +10,10 @@ present and marshals arguments through ctypes.
 
 Functions
 ---------
-attn_rows      the definition, materialised one score row at a time
+attn_rows      the definition, materialised one score row at a time; with
+               k_range=(k0, k1) the partial state of one key segment
+merge          the two-block merge rule folded over the partial states of
+               several key segments
 online_rows    the tiled method (always-rescale Algorithm 1, or conditional
                base-2 rescaling per row or per row group), for checking the
                algorithm against the definition
@@ -64,6 +67,12 @@ class Oracle:
         lib.oracle_attn_rows.argtypes = [
             _ptr, _ptr, _ptr, _i64, _i64, _i64, _i64, _i64, _i64, _i64,
             ctypes.c_int, ctypes.c_double, _ptr, _i64, _ptr, _ptr, ctypes.c_int]
+        lib.oracle_attn_rows_range.restype = ctypes.c_int
+        lib.oracle_attn_rows_range.argtypes = [
+            _ptr, _ptr, _ptr, _i64, _i64, _i64, _i64, _i64, _i64, _i64,
+            ctypes.c_int, ctypes.c_double, _i64, _i64, _ptr, _i64, _ptr, _ptr, ctypes.c_int]
+        lib.oracle_merge_states.restype = ctypes.c_int
+        lib.oracle_merge_states.argtypes = [_ptr, _ptr, _i64, _i64, _i64, _ptr, _ptr]
         lib.oracle_online_rows.restype = ctypes.c_int
         lib.oracle_online_rows.argtypes = [
             _ptr, _ptr, _ptr, _i64, _i64, _i64, _i64, _i64, _i64, _i64,
@@ -91,25 +100,45 @@ class Oracle:
         return r, r.size
 
     def attn_rows(self, q, k, v, causal: bool, scale: float | None = None,
-                  rows=None, threads: int = 0):
+                  rows=None, threads: int = 0, k_range=None):
         """Exact O [n, dv] and lse [n] (float64) for the requested query rows.
 
         A row index is (b*Hq + h)*Lq + i; rows=None means every row in order.
+        k_range=(k0, k1) restricts the softmax to the visible keys in [k0, k1):
+        the partial state of that key segment (O = 0, lse = -inf where the
+        segment holds no visible key).
         """
         qb, kb, vb = _as_bits(q), _as_bits(k), _as_bits(v)
         B, Hq, Hkv, Lq, Lk, dqk, dv = self._shapes(qb, kb, vb)
         if scale is None:
             scale = 1.0 / math.sqrt(dqk)
+        k0, k1 = (0, Lk) if k_range is None else (int(k_range[0]), int(k_range[1]))
         r, n = self._rows(rows, B * Hq * Lq)
         o = np.empty((n, dv), dtype=np.float64)
         lse = np.empty((n,), dtype=np.float64)
-        rc = self._lib.oracle_attn_rows(
+        rc = self._lib.oracle_attn_rows_range(
             qb.ctypes.data, kb.ctypes.data, vb.ctypes.data,
-            B, Hq, Hkv, Lq, Lk, dqk, dv, int(bool(causal)), float(scale),
+            B, Hq, Hkv, Lq, Lk, dqk, dv, int(bool(causal)), float(scale), k0, k1,
             None if r is None else r.ctypes.data, n,
             o.ctypes.data, lse.ctypes.data, int(threads))
         if rc != 0:
             raise ValueError(f"oracle_attn_rows rejected its arguments (code {rc})")
+        return o, lse
+
+    def merge(self, o_parts, lse_parts):
+        """Merge segment states: o_parts [n, rows, dv], lse_parts [n, rows]
+        (float64) -> (O [rows, dv], lse [rows])."""
+        op = np.ascontiguousarray(np.asarray(o_parts, dtype=np.float64))
+        lp = np.ascontiguousarray(np.asarray(lse_parts, dtype=np.float64))
+        if op.ndim != 3 or lp.shape != op.shape[:2]:
+            raise ValueError(f"o_parts {op.shape} and lse_parts {lp.shape} do not match")
+        n, rows, dv = op.shape
+        o = np.empty((rows, dv), dtype=np.float64)
+        lse = np.empty((rows,), dtype=np.float64)
+        rc = self._lib.oracle_merge_states(op.ctypes.data, lp.ctypes.data, n, rows, dv,
+                                           o.ctypes.data, lse.ctypes.data)
+        if rc != 0:
+            raise ValueError(f"oracle_merge_states rejected its arguments (code {rc})")
         return o, lse
 
     def online_rows(self, q, k, v, causal: bool, scale: float | None = None,
@@ -161,3 +190,7 @@ def attn_rows(*args, **kwargs):
 
 def online_rows(*args, **kwargs):
     return load().online_rows(*args, **kwargs)
+
+
+def merge(*args, **kwargs):
+    return load().merge(*args, **kwargs)

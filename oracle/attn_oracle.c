@@ -33,7 +33,8 @@
  *
  * The online (tiled) variants in the second half follow the algorithms the
  * pages describe step by step; they exist to check that the tiled method
- * reaches the same result as the definition.
+ * reaches the same result as the definition.  The key-segment form of the
+ * definition and the merge of segment states check the split-key path.
  */
 #include <math.h>
 #include <stdint.h>
@@ -112,22 +113,28 @@ static row_ref_t locate_row(const dims_t* d, const uint16_t* q, const uint16_t* 
 /* 1. The definition, materialised: one full score row at a time.           */
 /* ------------------------------------------------------------------------ */
 
-static void exact_row(const dims_t* d, row_ref_t rr, double* qd, double* s,
-                      double* o_row, double* lse_out)
+/* Softmax attention of one query row over the visible keys j with
+ * j0 <= j < j1 (the whole row when [j0, j1) = [0, Lk)). */
+static void exact_row(const dims_t* d, row_ref_t rr, int64_t j0, int64_t j1, double* qd,
+                      double* s, double* o_row, double* lse_out)
 {
     int64_t n = valid_keys(d, rr.i);
+    if (j1 > n)
+        j1 = n;
+    if (j0 < 0)
+        j0 = 0;
     for (int64_t c = 0; c < d->dv; ++c)
         o_row[c] = 0.0;
-    if (n == 0) {
+    if (j1 <= j0) {
         *lse_out = -INFINITY;
         return;
     }
     for (int64_t c = 0; c < d->dqk; ++c)
         qd[c] = bf16_bits_to_double(rr.qrow[c]);
 
-    /* S_i,j = scale * q_i . k_j for every visible key j */
+    /* S_i,j = scale * q_i . k_j for every key j in range */
     double m = -INFINITY;
-    for (int64_t j = 0; j < n; ++j) {
+    for (int64_t j = j0; j < j1; ++j) {
         const uint16_t* kj = rr.kh + j * d->dqk;
         double dot = 0.0;
         for (int64_t c = 0; c < d->dqk; ++c)
@@ -138,12 +145,12 @@ static void exact_row(const dims_t* d, row_ref_t rr, double* qd, double* s,
     }
     /* P_i,j = e^{S_i,j - m} / l with l = sum_j e^{S_i,j - m} */
     double l = 0.0;
-    for (int64_t j = 0; j < n; ++j) {
+    for (int64_t j = j0; j < j1; ++j) {
         s[j] = exp(s[j] - m);
         l += s[j];
     }
     /* O_i = sum_j P_i,j V_j */
-    for (int64_t j = 0; j < n; ++j) {
+    for (int64_t j = j0; j < j1; ++j) {
         const uint16_t* vj = rr.vh + j * d->dv;
         double p = s[j] / l;
         for (int64_t c = 0; c < d->dv; ++c)
@@ -153,15 +160,21 @@ static void exact_row(const dims_t* d, row_ref_t rr, double* qd, double* s,
 }
 
 /*
- * oracle_attn_rows: exact attention for a list of query rows (or all rows
- * when rows == NULL, in which case n_rows must equal B*Hq*Lq).
+ * oracle_attn_rows_range: exact attention for a list of query rows (or all
+ * rows when rows == NULL, in which case n_rows must equal B*Hq*Lq), with the
+ * softmax taken over the visible keys in [k_begin, k_end) only.  That is the
+ * partial state of one key segment: its normalised output and its
+ * log-sum-exp, lse = -inf (and O = 0) where the segment holds no visible key.
+ * ("Infra: Flash Attention", section on prefill versus decode: the key
+ * sequence may be cut into segments computed separately and merged.)
  * Returns 0 on success, nonzero on bad arguments.
  */
-int oracle_attn_rows(const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                     int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk,
-                     int64_t dqk, int64_t dv, int causal, double scale,
-                     const int64_t* rows, int64_t n_rows,
-                     double* o, double* lse, int n_threads)
+int oracle_attn_rows_range(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                           int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk,
+                           int64_t dqk, int64_t dv, int causal, double scale,
+                           int64_t k_begin, int64_t k_end,
+                           const int64_t* rows, int64_t n_rows,
+                           double* o, double* lse, int n_threads)
 {
     dims_t d = {B, Hq, Hkv, Lq, Lk, dqk, dv, causal, scale};
     int rc = check_dims(&d);
@@ -200,12 +213,72 @@ int oracle_attn_rows(const uint16_t* q, const uint16_t* k, const uint16_t* v,
             }
             int64_t r = rows ? rows[t] : t;
             row_ref_t rr = locate_row(&d, q, k, v, r);
-            exact_row(&d, rr, qd, s, o + t * dv, lse + t);
+            exact_row(&d, rr, k_begin, k_end, qd, s, o + t * dv, lse + t);
         }
         free(qd);
         free(s);
     }
     return failed ? 7 : 0;
+}
+
+/* oracle_attn_rows: the whole definition, every visible key of each row. */
+int oracle_attn_rows(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                     int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk,
+                     int64_t dqk, int64_t dv, int causal, double scale,
+                     const int64_t* rows, int64_t n_rows,
+                     double* o, double* lse, int n_threads)
+{
+    return oracle_attn_rows_range(q, k, v, B, Hq, Hkv, Lq, Lk, dqk, dv, causal, scale, 0, Lk,
+                                  rows, n_rows, o, lse, n_threads);
+}
+
+/*
+ * oracle_merge_states: combine the partial states of n_parts key segments,
+ * row by row, with the two-block merge rule of "Infra: Flash Attention"
+ * (section on computing softmax in segments):
+ *     m = max(m_A, m_B),  alpha = e^{m_A - m},  beta = e^{m_B - m},
+ *     l = alpha l_A + beta l_B,  u = alpha u_A + beta u_B,  O = u / l.
+ * A finished segment with normalised output O_g and log-sum-exp lse_g is the
+ * state (m, l, u) = (lse_g, 1, O_g): with the reference at lse_g the
+ * denominator sum_j e^{x_j - lse_g} is exactly 1.  The segments are folded
+ * left to right into one state; a segment with lse = -inf holds no key and
+ * is passed over.  The result is O = u / l and lse = m + ln l, or O = 0 and
+ * lse = -inf when no segment holds a key.
+ * Layouts: o_parts [n_parts, n_rows, dv], lse_parts [n_parts, n_rows],
+ * o [n_rows, dv], lse [n_rows].
+ */
+int oracle_merge_states(const double* o_parts, const double* lse_parts, int64_t n_parts,
+                        int64_t n_rows, int64_t dv, double* o, double* lse)
+{
+    if (!o_parts || !lse_parts || !o || !lse || n_parts < 1 || n_rows < 0 || dv < 1)
+        return 1;
+    for (int64_t r = 0; r < n_rows; ++r) {
+        double m = -INFINITY, l = 0.0;
+        double* u = o + r * dv;
+        for (int64_t c = 0; c < dv; ++c)
+            u[c] = 0.0;
+        for (int64_t g = 0; g < n_parts; ++g) {
+            double mb = lse_parts[g * n_rows + r];
+            if (mb == -INFINITY)
+                continue;
+            const double* ob = o_parts + (g * n_rows + r) * dv;
+            double mm = m > mb ? m : mb;
+            double alpha = (m == -INFINITY) ? 0.0 : exp(m - mm);
+            double beta = exp(mb - mm);
+            l = alpha * l + beta * 1.0;
+            for (int64_t c = 0; c < dv; ++c)
+                u[c] = alpha * u[c] + beta * ob[c];
+            m = mm;
+        }
+        if (m == -INFINITY) {
+            lse[r] = -INFINITY;
+            continue;
+        }
+        for (int64_t c = 0; c < dv; ++c)
+            u[c] /= l;
+        lse[r] = m + log(l);
+    }
+    return 0;
 }
 
 /* ------------------------------------------------------------------------ */

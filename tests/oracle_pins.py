@@ -11,7 +11,10 @@ AssertionError when the oracle disagrees with:
     score shift, value rows of ones),
   * the tiled method's own algebra (always-rescale and conditional variants
     agree with the definition; the rescale-event count behaves as the pages
-    describe).
+    describe),
+  * the split-key path: the partial states of key segments and their merge
+    reproduce the pages' worked example block by block and the whole
+    definition for any cut of the keys.
 They run unchanged against deliberately broken copies of the oracle in
 test_oracle_mutations.py, which checks that each planted mistake trips at
 least one pin.
@@ -379,6 +382,93 @@ def pin_rescale_events(orc):
     assert ev0 == want, f"threshold-0 events {ev0} != increases of the running max {want}"
 
 
+# --------------------------------------------------------------------------
+# Key segments and their merge (the split-key path)
+# --------------------------------------------------------------------------
+
+def pin_segment_worked_example(orc):
+    """The pages' two blocks as two key segments: each segment's state is the
+    printed (m, l, u) expressed at its own log-sum-exp, and merging the two
+    gives the printed merged state and 49/15."""
+    with open(os.path.join(GOLDEN, "online_merge_example.json"), encoding="utf-8") as f:
+        fx = json.load(f)
+    exps = fx["exp_scores"]
+    keys = [round(math.log2(e)) for e in exps]
+    q, k, v = _example_tensors(keys, fx["values"])
+    parts_o, parts_l = [], []
+    for name, ref_m in (("block_a", math.log(2.0)), ("block_b", math.log(8.0))):
+        sel = fx[name]["keys"]
+        o, lse = orc.attn_rows(q, k, v, causal=False, scale=LN2,
+                               k_range=(sel[0], sel[-1] + 1))
+        # O = u / l and lse = m + ln l for the printed block state
+        _close(o[0, 0], fx[name]["u"] / fx[name]["l"], 1e-14, f"{name} segment O")
+        _close(lse[0], ref_m + math.log(fx[name]["l"]), 1e-14, f"{name} segment lse")
+        parts_o.append(o)
+        parts_l.append(lse)
+    o, lse = orc.merge(np.stack(parts_o), np.stack(parts_l))
+    m = math.log(8.0)
+    _close(lse[0] - m, math.log(fx["merge"]["l"]), 1e-14, "merged l")
+    _close(o[0, 0] * fx["merge"]["l"], fx["merge"]["u"], 1e-14, "merged u")
+    _close(o[0, 0], fx["output"]["num"] / fx["output"]["den"], 1e-14, "merged O")
+    # the scale factor applied to block A: its share of the merged denominator
+    _close(math.exp(parts_l[0][0] - lse[0]) * fx["merge"]["l"],
+           fx["merge"]["scale_a"] * fx["block_a"]["l"], 1e-14, "scale of block A")
+
+
+SEGMENT_SHAPES = [
+    # B, Hq, Hkv, Lq, Lk, dqk, dv, causal, q_mult, cuts of [0, Lk]
+    (1, 2, 1, 20, 37, 8, 8, False, 1.0, (10, 16, 37)),
+    (1, 2, 1, 20, 37, 8, 8, True, 6.0, (3, 19, 30)),
+    (2, 4, 2, 33, 64, 16, 8, True, 1.0, (32,)),
+    (1, 2, 2, 25, 12, 8, 8, True, 1.0, (5, 6, 7)),     # Lq > Lk: rows with no key
+    (1, 1, 1, 9, 50, 4, 4, False, 6.0, (1, 2, 49)),
+]
+
+
+def pin_segments_merge_to_definition(orc):
+    """Any cut of the keys into segments, merged, is the whole definition
+    (real-arithmetic identity of the merge rule); a segment past the visible
+    keys holds nothing (O = 0, lse = -inf) and changes nothing."""
+    for idx, (B, Hq, Hkv, Lq, Lk, dqk, dv, causal, qm, cuts) in enumerate(SEGMENT_SHAPES):
+        q, k, v = make_qkv(B, Hq, Hkv, Lq, Lk, dqk, dv, seed=300 + idx, q_mult=qm)
+        o_ref, l_ref = orc.attn_rows(q, k, v, causal=causal)
+        bounds = (0,) + tuple(cuts) + (Lk, Lk + 64)   # last segment is empty
+        parts = [orc.attn_rows(q, k, v, causal=causal, k_range=(a, b))
+                 for a, b in zip(bounds[:-1], bounds[1:])]
+        assert np.all(parts[-1][0] == 0.0) and np.all(np.isneginf(parts[-1][1]))
+        o, l = orc.merge(np.stack([x[0] for x in parts]), np.stack([x[1] for x in parts]))
+        _close(o, o_ref, 1e-12, f"segments {idx}: merged O")
+        _close(l, l_ref, 1e-12, f"segments {idx}: merged lse")
+        # merge order does not matter
+        perm = list(reversed(range(len(parts))))
+        o2, l2 = orc.merge(np.stack([parts[i][0] for i in perm]),
+                           np.stack([parts[i][1] for i in perm]))
+        _close(o2, o_ref, 1e-12, f"segments {idx}: reversed merge O")
+        _close(l2, l_ref, 1e-12, f"segments {idx}: reversed merge lse")
+
+
+def pin_segment_closed_form(orc):
+    """Q = 0 over a key segment: O is the mean of the visible V rows inside
+    the segment and lse = ln(their count); one segment merges to itself."""
+    _, k, v = make_qkv(1, 1, 1, 30, 40, 8, 8, seed=11)
+    q = torch.zeros((1, 1, 30, 8), dtype=torch.bfloat16)
+    vd = v.double()[0, 0]
+    for causal in (False, True):
+        vis = _visible(30, 40, causal)
+        for a, b in ((0, 40), (5, 17), (25, 40)):
+            o, lse = orc.attn_rows(q, k, v, causal=causal, k_range=(a, b))
+            for i in range(30):
+                sel = [j for j in range(a, b) if vis[i, j]]
+                if not sel:
+                    assert np.all(o[i] == 0.0) and lse[i] == -math.inf
+                    continue
+                _close(o[i], vd[sel].mean(dim=0).numpy(), 1e-14, f"segment ({a},{b}) row {i} O")
+                _close(lse[i], math.log(len(sel)), 1e-14, f"segment ({a},{b}) row {i} lse")
+            o1, l1 = orc.merge(o[None], lse[None])
+            _close(o1, o, 1e-15, "single-segment merge O")
+            _close(l1, lse, 1e-15, "single-segment merge lse")
+
+
 ALL_PINS = [
     pin_worked_example,
     pin_conditional_cases,
@@ -393,4 +483,7 @@ ALL_PINS = [
     pin_constant_shift,
     pin_online_matches_definition,
     pin_rescale_events,
+    pin_segment_worked_example,
+    pin_segments_merge_to_definition,
+    pin_segment_closed_form,
 ]

@@ -31,6 +31,11 @@ MUTATIONS = {
                          "lse[t] = s->ref + log(s->l);"),
     "first_block_not_adopted": ("s->ref = bmax[a];\n                acc_scale = 1.0;",
                                 "s->ref = 0.0;\n                acc_scale = 1.0;"),
+    "segment_start_ignored": ("    if (j0 < 0)\n        j0 = 0;", "    j0 = 0;"),
+    "merge_unweighted": ("double beta = exp(mb - mm);", "double beta = 1.0;"),
+    "merge_old_state_not_rescaled": ("u[c] = alpha * u[c] + beta * ob[c];",
+                                     "u[c] = u[c] + beta * ob[c];"),
+    "merge_lse_without_max": ("lse[r] = m + log(l);", "lse[r] = log(l);"),
 }
 
 
