@@ -39,6 +39,13 @@ def _load():
         lib.attn_fwd_dbg.restype = i
         lib.attn_fwd_dbg.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i,
                                      ctypes.c_float, vp, ctypes.c_float, vp]
+        lib.attn_split_keys.restype = i
+        lib.attn_split_keys.argtypes = [i, i]
+        lib.attn_fwd_split.restype = i
+        lib.attn_fwd_split.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i,
+                                       ctypes.c_float, i, vp]
+        lib.attn_merge.restype = i
+        lib.attn_merge.argtypes = [vp, vp, vp, vp, i, ctypes.c_longlong, i, vp]
         lib.attn_status_string.restype = ctypes.c_char_p
         lib.attn_status_string.argtypes = [i]
         lib.attn_abi_version.restype = i
@@ -134,3 +141,81 @@ def attn_fwd_dbg(q, k, v, causal: bool = False, scale: float | None = None,
     if rc != ATTN_OK:
         raise RuntimeError(f"attn_fwd_dbg failed: {status_string(rc)} (code {rc})")
     return out, lse
+
+
+def split_keys(Lk: int, n_split: int) -> int:
+    """Keys per split: split s covers keys [s*W, min(Lk, (s+1)*W))."""
+    w = _load().attn_split_keys(int(Lk), int(n_split))
+    if w < 0:
+        raise ValueError(f"attn_split_keys: {status_string(-w)}")
+    return w
+
+
+def attn_fwd_split(q, k, v, n_split: int, causal: bool = False, scale: float | None = None,
+                   o_part=None, lse_part=None, stream=None):
+    """Per-split states (o_part fp32 [n_split,B,Hq,Lq,d_v], lse_part fp32
+    [n_split,B,Hq,Lq]): the forward pass over each key split alone."""
+    lib = _load()
+    B, Hq, Hkv, Lq, Lk, dqk, dv = _check_inputs(q, k, v)
+    if scale is None:
+        scale = 1.0 / math.sqrt(dqk)
+    n = int(n_split)
+    if o_part is None:
+        o_part = torch.empty((n, B, Hq, Lq, dv), dtype=torch.float32, device=q.device)
+    if lse_part is None:
+        lse_part = torch.empty((n, B, Hq, Lq), dtype=torch.float32, device=q.device)
+    if (o_part.shape != (n, B, Hq, Lq, dv) or o_part.dtype != torch.float32
+            or not o_part.is_contiguous()):
+        raise ValueError("o_part must be a contiguous fp32 [n_split, B, Hq, Lq, d_v] tensor")
+    if (lse_part.shape != (n, B, Hq, Lq) or lse_part.dtype != torch.float32
+            or not lse_part.is_contiguous()):
+        raise ValueError("lse_part must be a contiguous fp32 [n_split, B, Hq, Lq] tensor")
+    with torch.cuda.device(q.device):
+        s = stream if stream is not None else torch.cuda.current_stream(q.device)
+        rc = lib.attn_fwd_split(q.data_ptr(), k.data_ptr(), v.data_ptr(), o_part.data_ptr(),
+                                lse_part.data_ptr(), B, Hq, Hkv, Lq, Lk, dqk, dv,
+                                int(bool(causal)), float(scale), n, s.cuda_stream)
+    if rc != ATTN_OK:
+        raise RuntimeError(f"attn_fwd_split failed: {status_string(rc)} (code {rc})")
+    return o_part, lse_part
+
+
+def attn_merge(o_part, lse_part, out=None, lse=None, stream=None):
+    """Merge per-split states [n_split, ..., d_v] / [n_split, ...] into the bf16
+    output [..., d_v] and lse [...] (leading dims as in the per-split tensors)."""
+    lib = _load()
+    if o_part.dtype != torch.float32 or lse_part.dtype != torch.float32:
+        raise TypeError("o_part and lse_part must be float32")
+    if not (o_part.is_contiguous() and lse_part.is_contiguous()):
+        raise ValueError("o_part and lse_part must be contiguous")
+    if o_part.dim() < 2 or tuple(o_part.shape[:-1]) != tuple(lse_part.shape):
+        raise ValueError(f"o_part {tuple(o_part.shape)} and lse_part {tuple(lse_part.shape)} "
+                         "do not match")
+    n, dv = o_part.shape[0], o_part.shape[-1]
+    lead = tuple(o_part.shape[1:-1])
+    rows = 1
+    for x in lead:
+        rows *= x
+    if out is None:
+        out = torch.empty(lead + (dv,), dtype=torch.bfloat16, device=o_part.device)
+    if lse is None:
+        lse = torch.empty(lead, dtype=torch.float32, device=o_part.device)
+    if tuple(out.shape) != lead + (dv,) or out.dtype != torch.bfloat16 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous bf16 tensor of the merged shape")
+    if tuple(lse.shape) != lead or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous fp32 tensor of the merged shape")
+    with torch.cuda.device(o_part.device):
+        s = stream if stream is not None else torch.cuda.current_stream(o_part.device)
+        rc = lib.attn_merge(o_part.data_ptr(), lse_part.data_ptr(), out.data_ptr(),
+                            lse.data_ptr(), int(n), int(rows), int(dv), s.cuda_stream)
+    if rc != ATTN_OK:
+        raise RuntimeError(f"attn_merge failed: {status_string(rc)} (code {rc})")
+    return out, lse
+
+
+def attn_fwd_splitkv(q, k, v, n_split: int, causal: bool = False, scale: float | None = None,
+                     stream=None):
+    """O, lse by the split-key path: attn_fwd_split, then attn_merge."""
+    o_part, lse_part = attn_fwd_split(q, k, v, n_split, causal=causal, scale=scale,
+                                      stream=stream)
+    return attn_merge(o_part, lse_part, stream=stream)

@@ -9,7 +9,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIBRARY = os.path.join(PKG, "libattn_fwd.so")
-SOURCES = [os.path.join(CSRC, "attn_fwd_kernel.hip"), os.path.join(CSRC, "attn_api.cpp")]
+SOURCES = [os.path.join(CSRC, "attn_fwd_kernel.hip"), os.path.join(CSRC, "attn_merge_kernel.hip"),
+           os.path.join(CSRC, "attn_api.cpp")]
 ARCH = "gfx950"
 
 # Packed fp32 VALU forms are kept out of the generated code.

@@ -1,6 +1,7 @@
-// attn_api.cpp -- C ABI of the gfx950 fused attention forward (declared in
-// include/attn_fwd.h): argument validation, device checks, the tile schedule
-// parameters, and the launch on the caller's stream.
+// attn_api.cpp -- C ABI of the gfx950 fused attention forward and of its
+// split-key variant and merge (declared in include/attn_fwd.h): argument
+// validation, device checks, the tile schedule parameters, and the launches
+// on the caller's stream.
 
 #include <math.h>
 #include <stdint.h>
@@ -15,7 +16,8 @@
 
 namespace {
 
-constexpr int kAbiVersion = 1;
+constexpr int kAbiVersion = 2;
+constexpr int kMaxSplits = 4096;
 constexpr int kMaxDevices = 64;
 constexpr int kXcds = 8;                 // MI355X: 8 accelerator complex dies
 constexpr int kTilesPerXcdWave = 32;     // concurrent workgroups per XCD (32 CUs x 1)
@@ -74,6 +76,12 @@ int largest_divisor_at_most(int n, int cap) {
     return 1;
 }
 
+// 64 * ceil(ceil(Lk / 64) / n_split): keys per split
+int split_keys(int Lk, int n_split) {
+    const int nb = (Lk + attn::kBlockN - 1) / attn::kBlockN;
+    return attn::kBlockN * ((nb + n_split - 1) / n_split);
+}
+
 int fill_schedule(attn::FwdParams& p) {
     p.G = p.Hq / p.Hkv;
     // query heads that share a K/V head are packed into one workgroup, one
@@ -82,9 +90,11 @@ int fill_schedule(attn::FwdParams& p) {
     p.n_hg = p.G / p.Gp;
     p.bm_pos = attn::kRowsPerWave * attn::kWaves / p.Gp;
     p.n_m = (p.Lq + p.bm_pos - 1) / p.bm_pos;
-    const long long units = (long long)p.B * p.Hkv * p.n_hg;
+    const long long units_kv = (long long)p.B * p.Hkv * p.n_hg;
+    const long long units = units_kv * p.n_split;
     const long long tiles = units * p.n_m;
     if (tiles > INT32_MAX) return ATTN_ERR_TOO_LARGE;
+    p.units_kv = (int)units_kv;
     p.units = (int)units;
     // XCD-aware order: workgroup i is dispatched to XCD i % 8; give each XCD
     // a contiguous range of units so the K/V blocks it streams stay in its L2.
@@ -97,17 +107,32 @@ int fill_schedule(attn::FwdParams& p) {
     return ATTN_OK;
 }
 
+// o is the bf16 output when n_split == 0 (whole key range), else the fp32
+// per-split output [n_split, B, Hq, Lq, d_v]
 int run(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
         int Hkv, int Lq, int Lk, int d_qk, int d_v, int causal, float scale, void* stream,
-        float threshold, unsigned long long* counter, bool debug) {
+        float threshold, unsigned long long* counter, bool debug, int n_split) {
     int rc = check_args(q, k, v, o, lse, B, Hq, Hkv, Lq, Lk, d_qk, d_v, scale);
     if (rc != ATTN_OK) return rc;
+    if (n_split < 0 || n_split > kMaxSplits) return ATTN_ERR_BAD_ARGUMENT;
+    // per-split rows are addressed with 64-bit offsets; the split count times
+    // the rows must still fit the 32-bit row range of one launch's tiles
+    if ((long long)(n_split > 0 ? n_split : 1) * B * Hq * Lq > INT32_MAX)
+        return ATTN_ERR_TOO_LARGE;
     attn::FwdParams p;
     memset(&p, 0, sizeof p);
     p.q = static_cast<const uint16_t*>(q);
     p.k = static_cast<const uint16_t*>(k);
     p.v = static_cast<const uint16_t*>(v);
-    p.o = static_cast<uint16_t*>(o);
+    if (n_split == 0) {
+        p.o = static_cast<uint16_t*>(o);
+        p.n_split = 1;
+        p.split_blocks = (Lk + attn::kBlockN - 1) / attn::kBlockN;
+    } else {
+        p.o_part = static_cast<float*>(o);
+        p.n_split = n_split;
+        p.split_blocks = split_keys(Lk, n_split) / attn::kBlockN;
+    }
     p.lse = lse;
     p.rescale_count = counter;
     p.B = B;
@@ -142,7 +167,7 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
              int Hkv, int Lq, int Lk, int d_qk, int d_v, int causal, float scale,
              void* stream) {
     return run(q, k, v, o, lse, B, Hq, Hkv, Lq, Lk, d_qk, d_v, causal, scale, stream,
-               kDefaultThreshold, nullptr, false);
+               kDefaultThreshold, nullptr, false, 0);
 }
 
 int attn_fwd_dbg(const void* q, const void* k, const void* v, void* o, float* lse, int B,
@@ -151,7 +176,36 @@ int attn_fwd_dbg(const void* q, const void* k, const void* v, void* o, float* ls
     if (!(rescale_threshold >= 0.0f) || !isfinite(rescale_threshold))
         return ATTN_ERR_BAD_ARGUMENT;
     return run(q, k, v, o, lse, B, Hq, Hkv, Lq, Lk, d_qk, d_v, causal, scale, stream,
-               rescale_threshold, rescale_count, true);
+               rescale_threshold, rescale_count, true, 0);
+}
+
+int attn_split_keys(int Lk, int n_split) {
+    if (Lk < 1) return -ATTN_ERR_BAD_SHAPE;
+    if (n_split < 1 || n_split > kMaxSplits) return -ATTN_ERR_BAD_ARGUMENT;
+    return split_keys(Lk, n_split);
+}
+
+int attn_fwd_split(const void* q, const void* k, const void* v, float* o_part, float* lse_part,
+                   int B, int Hq, int Hkv, int Lq, int Lk, int d_qk, int d_v, int causal,
+                   float scale, int n_split, void* stream) {
+    if (n_split < 1 || n_split > kMaxSplits) return ATTN_ERR_BAD_ARGUMENT;
+    return run(q, k, v, o_part, lse_part, B, Hq, Hkv, Lq, Lk, d_qk, d_v, causal, scale, stream,
+               kDefaultThreshold, nullptr, false, n_split);
+}
+
+int attn_merge(const float* o_part, const float* lse_part, void* o, float* lse, int n_split,
+               long long rows, int d_v, void* stream) {
+    if (!o_part || !lse_part || !o || !lse) return ATTN_ERR_NULL_PTR;
+    if (n_split < 1 || n_split > kMaxSplits || rows < 0) return ATTN_ERR_BAD_ARGUMENT;
+    if (d_v != 64 && d_v != 128) return ATTN_ERR_UNSUPPORTED_HEAD_DIM;
+    if (!aligned(o_part, 16) || !aligned(o, 16) || !aligned(lse_part, 4) || !aligned(lse, 4))
+        return ATTN_ERR_MISALIGNED;
+    int rc = check_device();
+    if (rc != ATTN_OK) return rc;
+    hipError_t err = attn::launch_merge(o_part, lse_part, static_cast<uint16_t*>(o), lse,
+                                        n_split, rows, d_v, static_cast<hipStream_t>(stream));
+    if (err != hipSuccess) return ATTN_ERR_HIP;
+    return ATTN_OK;
 }
 
 const char* attn_status_string(int status) {
@@ -169,7 +223,9 @@ const char* attn_status_string(int status) {
         case ATTN_ERR_NO_DEVICE: return "no HIP device is visible";
         case ATTN_ERR_UNSUPPORTED_ARCH: return "the current device is not gfx950 (MI355X)";
         case ATTN_ERR_HIP: return "the HIP runtime reported an error";
-        case ATTN_ERR_BAD_ARGUMENT: return "rescale threshold must be finite and >= 0";
+        case ATTN_ERR_BAD_ARGUMENT:
+            return "argument out of range (rescale threshold finite and >= 0, split count in "
+                   "[1, 4096], merge rows >= 0)";
         default: return "unknown attn status";
     }
 }

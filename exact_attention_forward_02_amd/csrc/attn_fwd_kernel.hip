@@ -145,9 +145,10 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
     const float scale = p.scale;
     float* const lse_out = p.lse;
     uint16_t* const o_out = p.o;
+    float* const o_part = p.o_part;
     unsigned long long* const rescale_count = p.rescale_count;
     asm volatile("" ::"s"(c2), "s"(threshold), "s"(scale), "s"(lse_out), "s"(o_out),
-                 "s"(rescale_count));
+                 "s"(o_part), "s"(rescale_count));
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
@@ -174,8 +175,10 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
     }
     // causal tiles are ordered heaviest first (longest processing time first)
     const int m = CAUSAL ? (p.n_m - 1 - mo) : mo;
-    const int hg = unit % p.n_hg;
-    const int bk = unit / p.n_hg;  // b * Hkv + kv head
+    const int split = unit / p.units_kv;  // key split of this tile (0 without splits)
+    const int ukv = unit - split * p.units_kv;
+    const int hg = ukv % p.n_hg;
+    const int bk = ukv / p.n_hg;  // b * Hkv + kv head
     const int kvh = bk % p.Hkv;
     const int b = bk / p.Hkv;
     const int hq = kvh * p.G + hg * p.Gp + (wave % p.Gp);
@@ -189,19 +192,25 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
         reinterpret_cast<const unsigned char*>(p.v + (size_t)bk * p.Lk * DV);
     const size_t qrow0 = (size_t)(b * p.Hq + hq) * p.Lq;
 
-    // key range of the tile and of this wave
-    int kend = p.Lk;
-    int wend = p.Lk;
+    // key range of the tile and of this wave: the split's blocks
+    // [jb0, jb0 + split_blocks), cut at the end of the keys and, with the
+    // causal mask, after the last key the tile's (the wave's) rows can see.
+    // Block indices below are relative to jb0.
+    const int jb0 = split * p.split_blocks;
+    const int kbeg = jb0 * kBlockN;
+    const int ksplit = min(p.Lk, kbeg + p.split_blocks * kBlockN);
+    int kend = ksplit;
+    int wend = ksplit;
     if (CAUSAL) {
         const int tile_last = min(p.Lq, pos0 + p.bm_pos) - 1;
-        kend = min(p.Lk, tile_last + off + 1);
+        kend = min(ksplit, tile_last + off + 1);
         const int wave_last = min(p.Lq, qw + kRowsPerWave) - 1;
-        wend = min(p.Lk, wave_last + off + 1);
+        wend = min(ksplit, wave_last + off + 1);
     }
-    const int nblk = kend > 0 ? (kend + kBlockN - 1) / kBlockN : 0;
+    const int nblk = kend > kbeg ? (kend - kbeg + kBlockN - 1) / kBlockN : 0;
     // this wave's blocks are a prefix [0, nact) of the tile's blocks
     const int nact =
-        (qw < p.Lq && wend > 0) ? min(nblk, (wend + kBlockN - 1) / kBlockN) : 0;
+        (qw < p.Lq && wend > kbeg) ? min(nblk, (wend - kbeg + kBlockN - 1) / kBlockN) : 0;
 
     // ---- Q fragment, resident in registers for the whole sweep -----------
     // lane holds Q[qw + l32][16 ks + 8 hi .. +7] for every k-step ks
@@ -248,8 +257,8 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
     const __amdgpu_buffer_rsrc_t vrsrc = make_rsrc(vbase, (uint32_t)p.Lk * kRowV);
     const int kdst = __builtin_amdgcn_readfirstlane(1024 * S::kKCopies * wave);
     const int vdst = __builtin_amdgcn_readfirstlane(1024 * S::kVCopies * wave);
-    auto copy_k = [&](int jb, unsigned char* dst) {
-        const int key0 = jb * kBlockN;
+    auto copy_k = [&](int jl, unsigned char* dst) {
+        const int key0 = (jb0 + jl) * kBlockN;
         const uint32_t blk = (uint32_t)key0 * kRowK;
         if (key0 + kBlockN <= p.Lk) {
 #pragma unroll
@@ -266,8 +275,8 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
             }
         }
     };
-    auto copy_v = [&](int jb, unsigned char* dst) {
-        const int key0 = jb * kBlockN;
+    auto copy_v = [&](int jl, unsigned char* dst) {
+        const int key0 = (jb0 + jl) * kBlockN;
         const uint32_t blk = (uint32_t)key0 * kRowV;
         if (key0 + kBlockN <= p.Lk) {
 #pragma unroll
@@ -432,7 +441,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
     // ---- VALU phase V(j): online softmax of block j's scores -----------------
     auto v_phase = [&](int j) {
         if (j >= nact) return;
-        const int key0 = j * kBlockN;
+        const int key0 = (jb0 + j) * kBlockN;
         // mask keys past the end or past the causal diagonal
         const bool need_mask =
             (key0 + kBlockN > p.Lk) || (CAUSAL && key0 + kBlockN - 1 > qw + off);
@@ -568,20 +577,36 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
     const float ell_o_row = ((lane >> 4) & 1) ? ell_o[1] : ell_o[0];
     if (qi < p.Lq) {
         const float inv = ell_o_row > 0.0f ? 1.0f / ell_o_row : 0.0f;
-        uint16_t* orow = o_out + (qrow0 + qi) * DV;
+        const float lse_row = ell_row > 0.0f ? ref * scale + logf(ell_row) : kNegInf;
+        if (o_part == nullptr) {
+            uint16_t* orow = o_out + (qrow0 + qi) * DV;
 #pragma unroll
-        for (int i = 0; i < S::kDvBlocks; ++i) {
+            for (int i = 0; i < S::kDvBlocks; ++i) {
 #pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4) {
-                typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-                f32x4 x = {oacc[i][4 * r4 + 0] * inv, oacc[i][4 * r4 + 1] * inv,
-                           oacc[i][4 * r4 + 2] * inv, oacc[i][4 * r4 + 3] * inv};
-                const bf16x4 y = __builtin_convertvector(x, bf16x4);
-                *reinterpret_cast<bf16x4*>(orow + 32 * i + 8 * r4 + 4 * hi) = y;
+                for (int r4 = 0; r4 < 4; ++r4) {
+                    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+                    f32x4 x = {oacc[i][4 * r4 + 0] * inv, oacc[i][4 * r4 + 1] * inv,
+                               oacc[i][4 * r4 + 2] * inv, oacc[i][4 * r4 + 3] * inv};
+                    const bf16x4 y = __builtin_convertvector(x, bf16x4);
+                    *reinterpret_cast<bf16x4*>(orow + 32 * i + 8 * r4 + 4 * hi) = y;
+                }
             }
+            if (hi == 0) lse_out[qrow0 + qi] = lse_row;
+        } else {
+            // one split's state in fp32: its normalised output and lse
+            const size_t prow = (size_t)split * p.B * p.Hq * p.Lq + qrow0 + qi;
+            float* orow = o_part + prow * DV;
+#pragma unroll
+            for (int i = 0; i < S::kDvBlocks; ++i) {
+#pragma unroll
+                for (int r4 = 0; r4 < 4; ++r4) {
+                    f32x4 x = {oacc[i][4 * r4 + 0] * inv, oacc[i][4 * r4 + 1] * inv,
+                               oacc[i][4 * r4 + 2] * inv, oacc[i][4 * r4 + 3] * inv};
+                    *reinterpret_cast<f32x4*>(orow + 32 * i + 8 * r4 + 4 * hi) = x;
+                }
+            }
+            if (hi == 0) lse_out[prow] = lse_row;
         }
-        if (hi == 0)
-            lse_out[qrow0 + qi] = ell_row > 0.0f ? ref * scale + logf(ell_row) : kNegInf;
     }
 }
 

@@ -20,8 +20,9 @@ struct FwdParams {
     const uint16_t* q;   // [B, Hq, Lq, dqk] bf16
     const uint16_t* k;   // [B, Hkv, Lk, dqk] bf16
     const uint16_t* v;   // [B, Hkv, Lk, dv] bf16
-    uint16_t* o;         // [B, Hq, Lq, dv] bf16
-    float* lse;          // [B, Hq, Lq] fp32
+    uint16_t* o;         // [B, Hq, Lq, dv] bf16 (whole-key output), or
+    float* o_part;       // [n_split, B, Hq, Lq, dv] fp32 (per-split output) when set
+    float* lse;          // [B, Hq, Lq] fp32, or [n_split, B, Hq, Lq] with o_part
     unsigned long long* rescale_count;  // optional event counter
 
     int B, Hq, Hkv, Lq, Lk;
@@ -30,7 +31,10 @@ struct FwdParams {
     int n_hg;       // G / Gp: head groups per K/V head
     int bm_pos;     // query positions per tile = kRowsPerWave * kWaves / Gp
     int n_m;        // position tiles per head group = ceil(Lq / bm_pos)
-    int units;      // B * Hkv * n_hg: groups of query heads sharing one K/V head
+    int n_split;      // key splits (1: the whole key range)
+    int split_blocks; // key blocks per split
+    int units_kv;   // B * Hkv * n_hg: groups of query heads sharing one K/V head
+    int units;      // units_kv * n_split
     int xcd_mode;   // 1: workgroup i runs on XCD i % 8, which owns a contiguous
                     //    range of units (upx of them)
     int upx;        // units per XCD when xcd_mode
@@ -44,5 +48,10 @@ struct FwdParams {
 // Launches the forward kernel instantiation matching (dqk, dv, causal, debug).
 hipError_t launch_fwd(const FwdParams& p, int dqk, int dv, bool causal, bool debug,
                       hipStream_t stream);
+
+// Merges n_split partial states per row: o_part [n_split, rows, dv] fp32,
+// lse_part [n_split, rows] -> o [rows, dv] bf16, lse [rows].
+hipError_t launch_merge(const float* o_part, const float* lse_part, uint16_t* o, float* lse,
+                        int n_split, long long rows, int dv, hipStream_t stream);
 
 }  // namespace attn

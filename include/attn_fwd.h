@@ -56,7 +56,8 @@ enum attn_status {
     ATTN_ERR_NO_DEVICE = 8,             /* no HIP device is visible */
     ATTN_ERR_UNSUPPORTED_ARCH = 9,      /* the current device is not gfx950 */
     ATTN_ERR_HIP = 10,                  /* the HIP runtime reported an error at launch */
-    ATTN_ERR_BAD_ARGUMENT = 11          /* a debug-only argument is out of range */
+    ATTN_ERR_BAD_ARGUMENT = 11          /* a debug-only argument, a split count or a
+                                           merge row count is out of range */
 };
 
 /*
@@ -96,6 +97,58 @@ int attn_fwd_dbg(const void* q, const void* k, const void* v, void* o, float* ls
                  int B, int Hq, int Hkv, int Lq, int Lk, int d_qk, int d_v,
                  int causal, float scale, void* stream,
                  float rescale_threshold, unsigned long long* rescale_count);
+
+/*
+ * Split-key path.  "Infra: Flash Attention" (section on prefill versus
+ * decode) notes that the merge rule of its section on computing softmax in
+ * segments does not fix the order of the keys: the key sequence may be cut
+ * into segments that are computed separately and whose states are merged
+ * afterwards.  That gives work to many CUs when there are few query rows
+ * (decode), and it is the combine step when different devices hold
+ * different key ranges.
+ *
+ * attn_split_keys -- keys per split for Lk keys in n_split splits: the key
+ * blocks of 64 are dealt out in contiguous runs, so split s covers keys
+ * [s * W, min(Lk, (s + 1) * W)) with W = 64 * ceil(ceil(Lk / 64) / n_split).
+ * Trailing splits may be empty.  Returns W, or -ATTN_ERR_BAD_SHAPE /
+ * -ATTN_ERR_BAD_ARGUMENT for Lk < 1 or n_split outside [1, 4096].
+ */
+int attn_split_keys(int Lk, int n_split);
+
+/*
+ * attn_fwd_split -- the forward pass restricted to each key split.
+ *   o_part    float32 [n_split, B, Hq, Lq, d_v]: split s's softmax-normalised
+ *             output over the visible keys of split s (16-byte aligned)
+ *   lse_part  float32 [n_split, B, Hq, Lq]: split s's log-sum-exp (4-byte
+ *             aligned); a row with no visible key in split s gets O = 0 and
+ *             lse = -inf
+ *   n_split   1 .. 4096
+ * Other arguments, layouts, ownership, asynchrony and errors as attn_fwd (the
+ * causal mask and GQA mapping are the same; the rescale threshold is 8).
+ * attn_merge turns the per-split states into attn_fwd's o and lse.
+ */
+int attn_fwd_split(const void* q, const void* k, const void* v, float* o_part, float* lse_part,
+                   int B, int Hq, int Hkv, int Lq, int Lk, int d_qk, int d_v,
+                   int causal, float scale, int n_split, void* stream);
+
+/*
+ * attn_merge -- merge n_split per-split states row by row:
+ *     m = max_g lse_g,  w_g = exp(lse_g - m),  l = sum_g w_g,
+ *     O = sum_g w_g O_g / l  (rounded to bfloat16),  lse = m + ln l,
+ * the two-block merge rule of "Infra: Flash Attention" applied to states
+ * (m, l, u) = (lse_g, 1, O_g).  Rows that no split reaches get O = 0 and
+ * lse = -inf.
+ *   o_part    float32 [n_split, rows, d_v] (16-byte aligned)
+ *   lse_part  float32 [n_split, rows]
+ *   o         bfloat16 [rows, d_v] output (16-byte aligned); lse float32 [rows]
+ *   rows      number of query rows, >= 0 (B * Hq * Lq for attn_fwd_split's
+ *             output); d_v 64 or 128
+ * One kernel on `stream`; errors as attn_fwd (ATTN_ERR_BAD_ARGUMENT for
+ * rows < 0 or n_split outside [1, 4096], ATTN_ERR_UNSUPPORTED_HEAD_DIM for
+ * another d_v).
+ */
+int attn_merge(const float* o_part, const float* lse_part, void* o, float* lse,
+               int n_split, long long rows, int d_v, void* stream);
 
 /* attn_status_string -- static, NUL-terminated description of a status code
  * (never NULL; unknown codes give "unknown attn status"). */

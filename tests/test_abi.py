@@ -39,8 +39,8 @@ def _exported_symbols(path):
 
 
 def test_header_declares_the_entry_points():
-    assert {"attn_fwd", "attn_fwd_dbg", "attn_status_string",
-            "attn_abi_version"} <= _declared_functions()
+    assert {"attn_fwd", "attn_fwd_dbg", "attn_split_keys", "attn_fwd_split", "attn_merge",
+            "attn_status_string", "attn_abi_version"} <= _declared_functions()
 
 
 def test_status_codes_match_header():
@@ -59,7 +59,7 @@ def test_library_exports_every_declared_function():
 
 def test_abi_version_and_status_strings():
     lib = _binding.library()
-    assert lib.attn_abi_version() == 1
+    assert lib.attn_abi_version() == 2
     for code in CODES.values():
         s = _binding.status_string(code)
         assert s and s != "unknown attn status"
@@ -137,3 +137,52 @@ def test_python_binding_rejects_bad_tensors():
         _binding.attn_fwd(q, q, q)  # CPU tensors are refused before any call
     with pytest.raises(TypeError):
         _binding.attn_fwd(q.float(), q, q)
+
+
+def test_split_keys_arithmetic():
+    """W = 64 * ceil(ceil(Lk / 64) / n_split) (host arithmetic, no GPU)."""
+    for Lk, n, want in ((2048, 1, 2048), (2048, 4, 512), (2048, 3, 704), (100, 2, 64),
+                        (100, 8, 64), (1, 1, 64), (32768, 32, 1024), (5000, 7, 768)):
+        assert _binding.split_keys(Lk, n) == want, (Lk, n)
+        # the splits cover every key exactly once
+        assert n * want >= Lk and (n - 1) * want < Lk or want == 64
+    lib = _binding.library()
+    assert lib.attn_split_keys(0, 4) == -CODES["ATTN_ERR_BAD_SHAPE"]
+    assert lib.attn_split_keys(100, 0) == -CODES["ATTN_ERR_BAD_ARGUMENT"]
+    assert lib.attn_split_keys(100, 4097) == -CODES["ATTN_ERR_BAD_ARGUMENT"]
+
+
+def _call_split(n_split, **over):
+    args = dict(GOOD)
+    args.update(over)
+    a = [args[n] for n in ORDER]
+    return _binding.library().attn_fwd_split(*a[:14], n_split, a[14])
+
+
+def _call_merge(o_part=A, lse_part=A * 2, o=A * 3, lse=A * 4, n_split=4, rows=100, d_v=128):
+    return _binding.library().attn_merge(o_part, lse_part, o, lse, n_split, rows, d_v, None)
+
+
+def test_split_and_merge_arguments_are_validated_first():
+    assert _call_split(0) == CODES["ATTN_ERR_BAD_ARGUMENT"]
+    assert _call_split(4097) == CODES["ATTN_ERR_BAD_ARGUMENT"]
+    assert _call_split(4, q=None) == CODES["ATTN_ERR_NULL_PTR"]
+    assert _call_split(4, o=A * 4 + 4) == CODES["ATTN_ERR_MISALIGNED"]
+    assert _call_split(4, Hq=6, Hkv=4) == CODES["ATTN_ERR_GQA_RATIO"]
+    # split count times rows beyond the 32-bit row range
+    assert _call_split(4096, B=2 ** 10, Hq=2 ** 8, Hkv=2 ** 8, Lq=2) == CODES["ATTN_ERR_TOO_LARGE"]
+    assert _call_merge(o_part=None) == CODES["ATTN_ERR_NULL_PTR"]
+    assert _call_merge(lse=None) == CODES["ATTN_ERR_NULL_PTR"]
+    assert _call_merge(n_split=0) == CODES["ATTN_ERR_BAD_ARGUMENT"]
+    assert _call_merge(rows=-1) == CODES["ATTN_ERR_BAD_ARGUMENT"]
+    assert _call_merge(d_v=96) == CODES["ATTN_ERR_UNSUPPORTED_HEAD_DIM"]
+    assert _call_merge(o=A * 3 + 8) == CODES["ATTN_ERR_MISALIGNED"]
+
+
+def test_valid_split_and_merge_without_a_gpu_report_no_device():
+    import torch
+
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert _call_split(4) == CODES["ATTN_ERR_NO_DEVICE"]
+    assert _call_merge() == CODES["ATTN_ERR_NO_DEVICE"]

@@ -10,9 +10,9 @@ import pytest
 from exact_attention_forward_02_amd import build
 
 
-def _remarks():
+def _remarks(source):
     cmd = [build.hipcc(), *[f for f in build.HIPCC_FLAGS if f not in ("-shared", "-fPIC")],
-           "-c", build.SOURCES[0], "-o", "/dev/null",
+           "-c", source, "-o", "/dev/null",
            "-Rpass-analysis=kernel-resource-usage"]
     out = subprocess.run(cmd, capture_output=True, text=True, check=True)
     return out.stderr
@@ -21,7 +21,7 @@ def _remarks():
 @pytest.mark.skipif(shutil.which(build.hipcc()) is None and not build.hipcc().startswith("/"),
                     reason="hipcc not available")
 def test_no_scratch_and_no_vgpr_spills():
-    text = _remarks()
+    text = _remarks(build.SOURCES[0])
     kernels = re.findall(r"Function Name: (\S+)", text)
     assert len(kernels) == 12, f"expected 12 kernel instantiations, found {len(kernels)}"
     scratch = [int(x) for x in re.findall(r"ScratchSize \[bytes/lane\]: (\d+)", text)]
@@ -31,3 +31,13 @@ def test_no_scratch_and_no_vgpr_spills():
     assert all(s == 0 for s in spills), spills
     # one 8-wave workgroup per CU needs two waves per SIMD
     assert all(o >= 2 for o in occupancy), occupancy
+
+
+@pytest.mark.skipif(shutil.which(build.hipcc()) is None and not build.hipcc().startswith("/"),
+                    reason="hipcc not available")
+def test_merge_kernel_resources():
+    text = _remarks(build.SOURCES[1])
+    kernels = re.findall(r"Function Name: (\S+)", text)
+    assert len(kernels) == 2, kernels
+    scratch = [int(x) for x in re.findall(r"ScratchSize \[bytes/lane\]: (\d+)", text)]
+    assert scratch == [0, 0], scratch
