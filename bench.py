@@ -15,6 +15,7 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
+import math
 import os
 import sys
 import time
@@ -25,6 +26,7 @@ if ROOT not in sys.path:
 
 METRIC = "attention fwd TFLOP/s (bf16, 1 GPU) and % of MI355X dense bf16 MFMA peak"
 PEAK_BF16_TFLOPS = 2500.0  # MI355X published dense bf16 MFMA peak
+PEAK_HBM_GBS = 8000.0      # MI355X published HBM3E bandwidth
 KERNEL_SOURCE = os.path.join(ROOT, "exact_attention_forward_02_amd", "csrc",
                              "attn_fwd_kernel.hip")
 
@@ -124,6 +126,108 @@ def copy_calibration() -> int:
     return 0
 
 
+def bench_split(args, w, qd, kd, vd) -> int:
+    """The split-key path: per step one attn_fwd_split launch (the dominant
+    kernel, timed alone with HIP events on its stream) and one attn_merge.
+    Few query rows make it bound by reading K and V: its roofline is HBM."""
+    import torch
+
+    from exact_attention_forward_02_amd import attn_fwd_split, attn_merge, library
+
+    n = args.splits
+    dev = qd.device
+    stream = torch.cuda.current_stream(dev)
+    o_part = torch.empty((n, w.B, w.Hq, w.Lq, w.dv), dtype=torch.float32, device=dev)
+    lse_part = torch.empty((n, w.B, w.Hq, w.Lq), dtype=torch.float32, device=dev)
+    o = torch.empty((w.B, w.Hq, w.Lq, w.dv), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((w.B, w.Hq, w.Lq), dtype=torch.float32, device=dev)
+
+    # one checked call through the binding, then the same C-ABI entry points
+    # called directly with the prepared arguments, so that the host enqueues
+    # faster than these short kernels run and no host time falls between a
+    # launch and its events
+    attn_fwd_split(qd, kd, vd, n, causal=w.causal, o_part=o_part, lse_part=lse_part,
+                   stream=stream)
+    attn_merge(o_part, lse_part, out=o, lse=lse, stream=stream)
+    lib = library()
+    scale = 1.0 / math.sqrt(w.dqk)
+    a_split = (qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), o_part.data_ptr(), lse_part.data_ptr(),
+               w.B, w.Hq, w.Hkv, w.Lq, w.Lk, w.dqk, w.dv, int(w.causal), scale, n,
+               stream.cuda_stream)
+    a_merge = (o_part.data_ptr(), lse_part.data_ptr(), o.data_ptr(), lse.data_ptr(), n,
+               w.B * w.Hq * w.Lq, w.dv, stream.cuda_stream)
+    codes = []
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        codes.append(lib.attn_fwd_split(*a_split))
+        if ev is not None:
+            ev[1].record(stream)
+        codes.append(lib.attn_merge(*a_merge))
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    if any(c != 0 for c in codes):
+        raise RuntimeError(f"split path returned status {sorted(set(codes))}")
+    split_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    merge_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    ms_split = sum(split_ms) / len(split_ms)
+    ms_merge = sum(merge_ms) / len(merge_ms)
+    flops = w.flops()
+    # algorithmic bytes of the split kernel: Q, K, V read once, every split's
+    # fp32 state written once
+    rows = w.B * w.Hq * w.Lq
+    split_bytes = (2 * (w.B * w.Hq * w.Lq * w.dqk + w.B * w.Hkv * w.Lk * (w.dqk + w.dv))
+                   + n * rows * (4 * w.dv + 4))
+    merge_bytes = n * rows * (4 * w.dv + 4) + rows * (2 * w.dv + 4)
+    gbs = split_bytes / (ms_split * 1e-3) / 1e9
+    result = {
+        "metric": METRIC,
+        "value": round(flops * args.steps / wall / 1e12, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Lq": w.Lq,
+                   "Lk": w.Lk, "d_qk": w.dqk, "d_v": w.dv, "causal": w.causal,
+                   "splits": n, "flops_per_step": flops},
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(gbs, 1),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(gbs / PEAK_HBM_GBS, 4),
+            "traffic": None,
+            "kernel": "attn_fwd_kernel (split)",
+            "bytes_per_launch": split_bytes,
+            "ms_per_launch": round(ms_split, 4),
+            "ms_per_launch_min": round(min(split_ms), 4),
+            "ms_per_launch_max": round(max(split_ms), 4),
+            "merge_ms_per_launch": round(ms_merge, 4),
+            "merge_gbs": round(merge_bytes / (ms_merge * 1e-3) / 1e9, 1),
+        },
+    }
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -135,6 +239,9 @@ def main() -> int:
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain copy kernel of known size (3 launches) to "
                          "calibrate the FETCH_SIZE / WRITE_SIZE counters")
+    ap.add_argument("--splits", type=int, default=0,  # decode_l32k is timed with 4
+                    help="time the split-key path instead (attn_fwd_split with this many "
+                         "key splits, then attn_merge); reported against the HBM roofline")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -158,6 +265,8 @@ def main() -> int:
     torch.cuda.set_device(dev)
     q, k, v = workload_qkv(w)
     qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    if args.splits > 0:
+        return bench_split(args, w, qd, kd, vd)
     o = torch.empty((w.B, w.Hq, w.Lq, w.dv), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((w.B, w.Hq, w.Lq), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)

@@ -68,6 +68,9 @@ WORKLOADS = {
     "causal_l8k": Workload("causal_l8k", 4, 16, 16, 8192, 8192, 128, 128, True, seed=3),
     "gqa_l16k": Workload("gqa_l16k", 2, 32, 8, 16384, 16384, 128, 128, True, seed=4),
     "dsv3_l32k": Workload("dsv3_l32k", 1, 16, 16, 32768, 32768, 192, 128, True, seed=5),
+    # one decode step over a long key cache (split-key path): B8 Hq32 Hkv8,
+    # one new query per sequence, 32k cached keys
+    "decode_l32k": Workload("decode_l32k", 8, 32, 8, 1, 32768, 128, 128, False, seed=6),
 }
 
 

@@ -104,3 +104,20 @@ def test_decode_shape_sampled(orc, causal):
     o_ref, l_ref = orc.attn_rows(q, k, v, causal=causal, rows=rows.numpy())
     assert_parity(f"decode causal={causal}", og, lg, o_ref, l_ref)
     assert torch.isfinite(o).all().item() and torch.isfinite(lse).all().item()
+
+
+def test_decode_workload_in_bench_configuration(orc):
+    """decode_l32k with the 4 key splits bench.py times: sampled rows against
+    the oracle."""
+    from exact_attention_forward_02_amd.inputs import WORKLOADS, workload_qkv
+
+    w = WORKLOADS["decode_l32k"]
+    print(f"[case] {w.name} {w.as_dict()} splits 4", flush=True)
+    q, k, v = workload_qkv(w)
+    o, lse = attn_fwd_splitkv(q.to(DEV), k.to(DEV), v.to(DEV), 4, causal=w.causal)
+    torch.cuda.synchronize()
+    rows = sample_rows(w.B, w.Hq, w.Lq, 96, seed=w.seed)
+    og, lg = gather_rows(o, lse, rows)
+    o_ref, l_ref = orc.attn_rows(q, k, v, causal=w.causal, rows=rows.numpy())
+    assert_parity(w.name, og, lg, o_ref, l_ref)
+    assert torch.isfinite(o).all().item() and torch.isfinite(lse).all().item()
