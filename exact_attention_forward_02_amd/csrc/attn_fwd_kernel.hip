@@ -539,13 +539,21 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
     // opposite phase kinds and keep that pairing by themselves.  Stages
     // alternate between buffers 0 and 1, so the phase loop is unrolled by four
     // to make every buffer a compile-time choice.
+    // The wave in its MFMA phase runs at a raised issue priority: its MFMAs
+    // (one every 32 cycles) then issue as soon as their operands are in,
+    // instead of waiting behind the partner wave's stream of softmax VALU
+    // instructions, which otherwise wins arbitration whenever its wave is the
+    // older one.
     auto work = [&](int phi, const unsigned char* kl, const unsigned char* vl) {
         const int lam = phi - grp;
         if (lam < 0) return;
-        if (lam & 1)
+        if (lam & 1) {
+            __builtin_amdgcn_s_setprio(0);
             v_phase(lam >> 1);
-        else
+        } else {
+            __builtin_amdgcn_s_setprio(2);
             m_phase((lam >> 1) - 1, kl, vl);
+        }
     };
 
     if (nblk > 0) {
