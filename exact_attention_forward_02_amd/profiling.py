@@ -1,12 +1,16 @@
 """Summaries of rocprofv3 output for the attention kernel.
 
     python -m exact_attention_forward_02_amd.profiling stats  RUN_kernel_stats.csv
+    python -m exact_attention_forward_02_amd.profiling trace  RUN_kernel_trace.csv [--last K]
     python -m exact_attention_forward_02_amd.profiling pmc    RUN_counter_collection.csv [--kernel NAME]
     python -m exact_attention_forward_02_amd.profiling traffic --fetch F.csv --write W.csv \\
         --copy-fetch CF.csv --copy-write CW.csv --copy-bytes N --workload NAME [--out PATH]
 
 `stats` prints per-kernel call counts and durations from a --kernel-trace
---stats run (CSV output).  `pmc` averages every counter per dispatch of the
+--stats run (CSV output).  `trace` reads the per-dispatch records of the same
+run and prints the durations of the attention kernel over all its dispatches
+and over the last K (the timed steps, after the warmup launches that bring
+the clocks up).  `pmc` averages every counter per dispatch of the
 kernels whose name contains NAME.  `traffic` turns FETCH_SIZE / WRITE_SIZE
 (KiB per dispatch) of the attention kernel into HBM bytes per launch, each
 scaled by what the same counter reads for a plain copy kernel that moves a
@@ -74,6 +78,36 @@ def cmd_stats(args):
               f"min={r['min_ns'] / 1e3:9.2f} max={r['max_ns'] / 1e3:9.2f} ({r['pct']:.1f}%)")
 
 
+def read_dispatch_durations(path, kernel="attn_fwd_kernel"):
+    """Durations (ns) of the matching kernel's dispatches, in dispatch order."""
+    recs = []
+    with open(path, newline="") as f:
+        for r in csv.DictReader(f):
+            if kernel and kernel not in r.get("Kernel_Name", ""):
+                continue
+            recs.append((int(r["Dispatch_Id"]),
+                         float(r["End_Timestamp"]) - float(r["Start_Timestamp"])))
+    recs.sort()
+    return [d for _, d in recs]
+
+
+def _summary(label, durs):
+    n = len(durs)
+    avg = sum(durs) / n
+    print(f"{label:28s} dispatches={n:4d} avg={avg / 1e3:9.2f} us "
+          f"min={min(durs) / 1e3:9.2f} max={max(durs) / 1e3:9.2f}")
+
+
+def cmd_trace(args):
+    durs = read_dispatch_durations(args.csv, args.kernel)
+    if not durs:
+        print(f"no dispatch of a kernel matching {args.kernel!r}")
+        return
+    _summary("all dispatches", durs)
+    if args.last and args.last < len(durs):
+        _summary(f"last {args.last} dispatches", durs[-args.last:])
+
+
 def cmd_pmc(args):
     mean, n, name = read_counters(args.csv, args.kernel)
     print(f"kernel: {name}\ndispatches: {n}")
@@ -120,6 +154,11 @@ def main(argv=None):
     a = sub.add_parser("stats")
     a.add_argument("csv")
     a.set_defaults(fn=cmd_stats)
+    t = sub.add_parser("trace")
+    t.add_argument("csv")
+    t.add_argument("--kernel", default="attn_fwd_kernel")
+    t.add_argument("--last", type=int, default=0)
+    t.set_defaults(fn=cmd_trace)
     b = sub.add_parser("pmc")
     b.add_argument("csv")
     b.add_argument("--kernel", default="attn_fwd_kernel")
