@@ -25,6 +25,8 @@ constexpr float kDefaultThreshold = 8.0f;  // log2 units: a factor of 256
 
 // -1 unknown, 0 not gfx950, 1 gfx950
 std::atomic<int> g_arch_ok[kMaxDevices];
+// compute units of each device (0 unknown)
+std::atomic<int> g_cu_count[kMaxDevices];
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -50,7 +52,8 @@ int check_args(const void* q, const void* k, const void* v, const void* o, const
     return ATTN_OK;
 }
 
-int check_device() {
+// Checks that the current device is a gfx950 and reports its compute units.
+int check_device(int* n_cu = nullptr) {
     int count = 0;
     if (hipGetDeviceCount(&count) != hipSuccess || count < 1) {
         (void)hipGetLastError();
@@ -64,8 +67,11 @@ int check_device() {
         hipDeviceProp_t prop;
         if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return ATTN_ERR_HIP;
         ok = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 0;
+        g_cu_count[dev].store(prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 0,
+                              std::memory_order_relaxed);
         g_arch_ok[dev].store(ok, std::memory_order_relaxed);
     }
+    if (n_cu) *n_cu = g_cu_count[dev].load(std::memory_order_relaxed);
     return ok ? ATTN_OK : ATTN_ERR_UNSUPPORTED_ARCH;
 }
 
@@ -145,8 +151,17 @@ int run(const void* q, const void* k, const void* v, void* o, float* lse, int B,
     p.threshold = threshold;
     rc = fill_schedule(p);
     if (rc != ATTN_OK) return rc;
-    rc = check_device();
+    int n_cu = 0;
+    rc = check_device(&n_cu);
     if (rc != ATTN_OK) return rc;
+    // Persistent grid: one workgroup per CU (its registers allow no second
+    // one), each looping over its tiles, as many as a multiple of 8 keeps
+    // every workgroup on the XCD of its tiles.
+    const long long tiles = (long long)p.units * p.n_m;
+    long long grid = tiles;
+    const long long slots = (long long)(n_cu / kXcds) * kXcds;
+    if (slots > 0 && tiles > slots) grid = slots;
+    p.grid = (int)grid;
     hipError_t err = attn::launch_fwd(p, d_qk, d_v, causal != 0, debug,
                                       static_cast<hipStream_t>(stream));
     if (err != hipSuccess) return ATTN_ERR_HIP;
@@ -156,6 +171,7 @@ int run(const void* q, const void* k, const void* v, void* o, float* lse, int B,
 struct ArchCacheInit {
     ArchCacheInit() {
         for (auto& a : g_arch_ok) a.store(-1, std::memory_order_relaxed);
+        for (auto& a : g_cu_count) a.store(0, std::memory_order_relaxed);
     }
 } g_arch_cache_init;
 

@@ -1,10 +1,13 @@
 // attn_fwd_kernel.hip -- fused exact-attention forward for gfx950 (MI355X).
 //
-// One workgroup = 4 waves; each wave owns 32 query rows for the whole key
-// sweep (rows are split across waves, never keys, so no cross-wave output
-// reduction: "Infra: Flash Attention", FA2 split-Q figure).  Keys are visited
-// in blocks of 64; each block of K and V is staged through LDS, double
-// buffered, and consumed by bf16 MFMA with fp32 accumulation.
+// One workgroup = 8 waves, two per SIMD; each wave owns 32 query rows for
+// the whole key sweep (rows are split across waves, never keys, so no
+// cross-wave output reduction: "Infra: Flash Attention", FA2 split-Q
+// figure).  Keys are visited in blocks of 64; each block of K and V is staged
+// through LDS, double buffered, and consumed by bf16 MFMA with fp32
+// accumulation.  The two waves of a SIMD alternate between an MFMA phase and
+// a softmax phase (the ping-pong described at the sweep below).  The grid is
+// persistent, one workgroup per CU looping over tiles of 256 query rows.
 //
 // Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16:
 // keys on the MFMA M axis, the wave's 32 queries on N.  In the 32x32
@@ -125,6 +128,75 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
 }
 
+// Tile t of the launch -> its key split, K/V head, and this wave's query head
+// and first query row.  With xcd_mode, tile t runs on XCD t % 8 (the
+// hardware deals workgroups round-robin over the 8 XCDs, and a persistent
+// grid is a multiple of 8) and each XCD owns a contiguous range of upx
+// units; within it, sections of sec_units units are swept position tile by
+// position tile, so the workgroups an XCD runs at one time share their K/V
+// blocks in its L2.
+struct TileCoord {
+    int split, bk, hq, pos0, qw;
+    size_t qrow0;  // row of (b, hq, position 0) in Q, O and lse
+};
+
+template <bool CAUSAL>
+__device__ __forceinline__ TileCoord tile_coord(const FwdParams& p, int t, int wave) {
+    const int per_sec = p.sec_units * p.n_m;
+    int local = t, base = 0;
+    if (p.xcd_mode) {
+        local = t >> 3;
+        base = (t & 7) * p.upx;
+    }
+    const int sec = local / per_sec;
+    const int r = local - sec * per_sec;
+    const int mo = r / p.sec_units;
+    const int unit = base + sec * p.sec_units + (r - mo * p.sec_units);
+    // causal tiles are ordered heaviest first (longest processing time first)
+    const int m = CAUSAL ? (p.n_m - 1 - mo) : mo;
+    TileCoord c;
+    c.split = unit / p.units_kv;  // key split of this tile (0 without splits)
+    const int ukv = unit - c.split * p.units_kv;
+    const int hg = ukv % p.n_hg;
+    c.bk = ukv / p.n_hg;  // b * Hkv + kv head
+    const int kvh = c.bk % p.Hkv;
+    const int b = c.bk / p.Hkv;
+    c.hq = kvh * p.G + hg * p.Gp + (wave % p.Gp);
+    c.pos0 = m * p.bm_pos;
+    c.qw = c.pos0 + (wave / p.Gp) * kRowsPerWave;  // first row of this wave
+    c.qrow0 = (size_t)(b * p.Hq + c.hq) * p.Lq;
+    return c;
+}
+
+// Key range of a tile and of one wave: the split's blocks [jb0, jb0 +
+// split_blocks), cut at the end of the keys and, with the causal mask, after
+// the last key the tile's (the wave's) rows can see.  The tile visits nblk
+// blocks from jb0; the wave's own blocks are the prefix [0, nact).
+struct KeyRange {
+    int jb0, nblk, nact;
+};
+
+template <bool CAUSAL>
+__device__ __forceinline__ KeyRange key_range(const FwdParams& p, const TileCoord& c) {
+    KeyRange r;
+    r.jb0 = c.split * p.split_blocks;
+    const int kbeg = r.jb0 * kBlockN;
+    const int ksplit = min(p.Lk, kbeg + p.split_blocks * kBlockN);
+    int kend = ksplit;
+    int wend = ksplit;
+    if (CAUSAL) {
+        const int off = p.Lk - p.Lq;
+        const int tile_last = min(p.Lq, c.pos0 + p.bm_pos) - 1;
+        kend = min(ksplit, tile_last + off + 1);
+        const int wave_last = min(p.Lq, c.qw + kRowsPerWave) - 1;
+        wend = min(ksplit, wave_last + off + 1);
+    }
+    r.nblk = kend > kbeg ? (kend - kbeg + kBlockN - 1) / kBlockN : 0;
+    r.nact = (c.qw < p.Lq && wend > kbeg) ? min(r.nblk, (wend - kbeg + kBlockN - 1) / kBlockN)
+                                          : 0;
+    return r;
+}
+
 template <int DQK, int DV, bool CAUSAL, bool DEBUG>
 __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
     using S = Shape<DQK, DV>;
@@ -136,6 +208,16 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
     __shared__ __attribute__((aligned(1024))) unsigned char lds_k1[S::kKBytes];
     __shared__ __attribute__((aligned(1024))) unsigned char lds_v0[S::kVBytes];
     __shared__ __attribute__((aligned(1024))) unsigned char lds_v1[S::kVBytes];
+    // Per-wave slices that carry the next tile's Q in and the last tile's O
+    // out (equal head dims only: a slice row then fits both).  Slice rows use
+    // the K block's row layout and swizzle.
+    constexpr bool kStage = DQK == DV;
+    constexpr int kRowQ = DQK * 2;                          // bytes per Q (and O) row
+    constexpr int kSlice = kRowsPerWave * kRowQ;            // bytes per wave
+    constexpr int kSliceChunks = kSlice / 1024;             // 1 KiB wave copies per slice
+    // (16-byte alignment places it after the K/V buffers, which then keep LDS
+    // addresses below 64 KiB that fit the read instructions' offset field)
+    __shared__ __attribute__((aligned(16))) unsigned char lds_s[kStage ? kWaves * kSlice : 16];
 
     // Bring every kernel argument the sweep uses into SGPRs now: a scalar
     // load still in flight inside the loop would force each LDS wait there to
@@ -159,63 +241,59 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
     // one; the two wave groups alternate between MFMA and VALU phases
     const int grp = wave / kGroupWaves;
 
-    // ---- tile of this workgroup: (unit, position tile m) ------------------
-    int unit, mo;
-    {
-        const int per_sec = p.sec_units * p.n_m;
-        int local = blockIdx.x, base = 0;
-        if (p.xcd_mode) {
-            local = blockIdx.x >> 3;
-            base = (blockIdx.x & 7) * p.upx;
-        }
-        const int sec = local / per_sec;
-        const int r = local - sec * per_sec;
-        mo = r / p.sec_units;
-        unit = base + sec * p.sec_units + (r - mo * p.sec_units);
-    }
-    // causal tiles are ordered heaviest first (longest processing time first)
-    const int m = CAUSAL ? (p.n_m - 1 - mo) : mo;
-    const int split = unit / p.units_kv;  // key split of this tile (0 without splits)
-    const int ukv = unit - split * p.units_kv;
-    const int hg = ukv % p.n_hg;
-    const int bk = ukv / p.n_hg;  // b * Hkv + kv head
-    const int kvh = bk % p.Hkv;
-    const int b = bk / p.Hkv;
-    const int hq = kvh * p.G + hg * p.Gp + (wave % p.Gp);
-    const int pos0 = m * p.bm_pos;
-    const int qw = pos0 + (wave / p.Gp) * kRowsPerWave;  // first row of this wave
-    const int off = p.Lk - p.Lq;                          // causal diagonal offset
+    // ---- tiles of this workgroup ---------------------------------------------
+    // With one workgroup per CU the grid is persistent: each workgroup runs
+    // one tile per round.  While a tile's key sweep runs, each wave prefetches
+    // its rows of the next tile's Q into its own LDS slice and drains the
+    // previous tile's output from that slice, a chunk per key-block pair, and
+    // the last pair copies the next tile's first K block, so tiles follow each
+    // other without a load burst between them.  Round r takes the workgroups'
+    // next cnt tiles in the order of the tile index (per XCD with xcd_mode,
+    // which keeps every tile on its XCD), reversed in odd rounds: causal tiles
+    // come heaviest first, so a workgroup that gets a heavy tile in one round
+    // gets a light one in the next.
+    const int n_tiles = p.units * p.n_m;
+    const int xcd = p.xcd_mode ? (int)(blockIdx.x & 7) : 0;
+    const int slot = p.xcd_mode ? (int)(blockIdx.x >> 3) : (int)blockIdx.x;
+    const int per_round = p.xcd_mode ? (int)(gridDim.x >> 3) : (int)gridDim.x;
+    const int n_local = p.xcd_mode ? (n_tiles >> 3) : n_tiles;
+    // tile of round r, or -1 when the workgroup has none
+    auto tile_of_round = [&](int r) __attribute__((always_inline)) {
+        const int first = r * per_round;
+        const int cnt = min(per_round, n_local - first);
+        if (slot >= cnt) return -1;
+        const int local = first + ((r & 1) ? cnt - 1 - slot : slot);
+        return p.xcd_mode ? (local << 3) | xcd : local;
+    };
+    int round = 0;
+    int tile = tile_of_round(0);
+    if (tile < 0) return;  // only if the grid exceeds the tiles (workgroup-uniform)
 
-    const unsigned char* kbase =
-        reinterpret_cast<const unsigned char*>(p.k + (size_t)bk * p.Lk * DQK);
-    const unsigned char* vbase =
-        reinterpret_cast<const unsigned char*>(p.v + (size_t)bk * p.Lk * DV);
-    const size_t qrow0 = (size_t)(b * p.Hq + hq) * p.Lq;
-
-    // key range of the tile and of this wave: the split's blocks
-    // [jb0, jb0 + split_blocks), cut at the end of the keys and, with the
-    // causal mask, after the last key the tile's (the wave's) rows can see.
-    // Block indices below are relative to jb0.
-    const int jb0 = split * p.split_blocks;
-    const int kbeg = jb0 * kBlockN;
-    const int ksplit = min(p.Lk, kbeg + p.split_blocks * kBlockN);
-    int kend = ksplit;
-    int wend = ksplit;
-    if (CAUSAL) {
-        const int tile_last = min(p.Lq, pos0 + p.bm_pos) - 1;
-        kend = min(ksplit, tile_last + off + 1);
-        const int wave_last = min(p.Lq, qw + kRowsPerWave) - 1;
-        wend = min(ksplit, wave_last + off + 1);
-    }
-    const int nblk = kend > kbeg ? (kend - kbeg + kBlockN - 1) / kBlockN : 0;
-    // this wave's blocks are a prefix [0, nact) of the tile's blocks
-    const int nact =
-        (qw < p.Lq && wend > kbeg) ? min(nblk, (wend - kbeg + kBlockN - 1) / kBlockN) : 0;
+    // per-tile values of this wave (set_tile)
+    int split, qw, jb0, nblk, nact;
+    size_t qrow0;  // row index of (b, hq, position 0) in Q, O and lse
+    __amdgpu_buffer_rsrc_t krsrc, vrsrc;
+    const int off = p.Lk - p.Lq;  // causal diagonal offset
+    auto set_tile = [&](int t) __attribute__((always_inline)) {
+        const TileCoord c = tile_coord<CAUSAL>(p, t, wave);
+        split = c.split;
+        qw = c.qw;
+        qrow0 = c.qrow0;
+        const KeyRange r = key_range<CAUSAL>(p, c);
+        jb0 = r.jb0;
+        nblk = r.nblk;
+        nact = r.nact;
+        // one descriptor per K/V head; a head is at most 2^31 bytes (checked
+        // on the host), so 32-bit byte offsets address all of it
+        krsrc = make_rsrc(p.k + (size_t)c.bk * p.Lk * DQK, (uint32_t)p.Lk * kRowK);
+        vrsrc = make_rsrc(p.v + (size_t)c.bk * p.Lk * DV, (uint32_t)p.Lk * kRowV);
+    };
+    set_tile(tile);
 
     // ---- Q fragment, resident in registers for the whole sweep -----------
     // lane holds Q[qw + l32][16 ks + 8 hi .. +7] for every k-step ks
     bf16x8 qf[S::kKSteps];
-    {
+    auto load_q_global = [&]() __attribute__((always_inline)) {
         const int qi = qw + l32;
         const bool ok = qi < p.Lq;
         const uint16_t* src = p.q + (qrow0 + (ok ? qi : 0)) * DQK + 8 * hi;
@@ -224,7 +302,8 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
             u32x4 w = ok ? load16(src + 16 * ks) : u32x4{0u, 0u, 0u, 0u};
             qf[ks] = __builtin_bit_cast(bf16x8, w);
         }
-    }
+    };
+    load_q_global();
 
     // ---- direct global -> LDS copies of one K or V block -------------------
     // Copy n of the workgroup fills LDS slots [64 n, 64 n + 64); lane l takes
@@ -249,33 +328,32 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
         voff_copy[i] = r * kRowV + 16 * c;
     }
 
-    // one descriptor per K/V head; a head is at most 2^31 bytes (checked on
-    // the host), so 32-bit byte offsets address all of it.  The block offset
-    // goes in the scalar offset operand and this wave's LDS destination is a
-    // scalar too, so a copy needs no vector arithmetic.
-    const __amdgpu_buffer_rsrc_t krsrc = make_rsrc(kbase, (uint32_t)p.Lk * kRowK);
-    const __amdgpu_buffer_rsrc_t vrsrc = make_rsrc(vbase, (uint32_t)p.Lk * kRowV);
+    // The block offset goes in the scalar offset operand and this wave's LDS
+    // destination is a scalar too, so a copy needs no vector arithmetic.
     const int kdst = __builtin_amdgcn_readfirstlane(1024 * S::kKCopies * wave);
     const int vdst = __builtin_amdgcn_readfirstlane(1024 * S::kVCopies * wave);
-    auto copy_k = [&](int jl, unsigned char* dst) {
-        const int key0 = (jb0 + jl) * kBlockN;
+    auto copy_kblock = [&](__amdgpu_buffer_rsrc_t rs, int key0, unsigned char* dst)
+                           __attribute__((always_inline)) {
         const uint32_t blk = (uint32_t)key0 * kRowK;
         if (key0 + kBlockN <= p.Lk) {
 #pragma unroll
             for (int i = 0; i < S::kKCopies; ++i)
-                copy_to_lds(krsrc, koff[i], blk, dst + kdst + 1024 * i);
+                copy_to_lds(rs, koff[i], blk, dst + kdst + 1024 * i);
         } else {
             const int last = p.Lk - 1 - key0;
 #pragma unroll
             for (int i = 0; i < S::kKCopies; ++i) {
                 const int r = (int)koff[i] / kRowK;
                 const int rr = min(r, last);
-                copy_to_lds(krsrc, koff[i] - (uint32_t)((r - rr) * kRowK), blk,
+                copy_to_lds(rs, koff[i] - (uint32_t)((r - rr) * kRowK), blk,
                             dst + kdst + 1024 * i);
             }
         }
     };
-    auto copy_v = [&](int jl, unsigned char* dst) {
+    auto copy_k = [&](int jl, unsigned char* dst) __attribute__((always_inline)) {
+        copy_kblock(krsrc, (jb0 + jl) * kBlockN, dst);
+    };
+    auto copy_v = [&](int jl, unsigned char* dst) __attribute__((always_inline)) {
         const int key0 = (jb0 + jl) * kBlockN;
         const uint32_t blk = (uint32_t)key0 * kRowV;
         if (key0 + kBlockN <= p.Lk) {
@@ -318,14 +396,10 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
             vread[i] = row * kRowV + 16 * ((4 * i + cl) ^ vswz<DV>(row)) + 8 * (tj & 1);
     }
 
-    // ---- running state -------------------------------------------------------
+    // ---- running state (reset at each tile) -----------------------------------
     f32x16 oacc[S::kDvBlocks];
-#pragma unroll
-    for (int i = 0; i < S::kDvBlocks; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[i][r] = 0.0f;
-    float ref = kNegInf;  // exponent reference, raw q.k units
-    float ell = 0.0f;     // this lane's share of sum P (fp32 P), for lse
+    float ref;  // exponent reference, raw q.k units
+    float ell;  // this lane's share of sum P (fp32 P), for lse
     // Row sums of the bf16 P that feed the PV product (they normalise O with
     // exactly the weights it was built from), accumulated by a 16x16x32 MFMA
     // with a 0/1 selector as A: in that shape lane l supplies B column l % 16
@@ -333,7 +407,16 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
     // parity, even rows of D sum the P of query l % 16 (groups 0, 2) and odd
     // rows those of query l % 16 + 16 (groups 1, 3).  Lane l then finds its
     // own query's sum in register (l / 16) & 1 of the accumulator.
-    f32x4 ell_o = {0.0f, 0.0f, 0.0f, 0.0f};
+    f32x4 ell_o;
+    auto reset_state = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < S::kDvBlocks; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) oacc[i][r] = 0.0f;
+        ref = kNegInf;
+        ell = 0.0f;
+        ell_o = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    };
     bf16x8 sel;
     {
         const __bf16 v = (((lane & 15) ^ (lane >> 4)) & 1) ? (__bf16)0.0f : (__bf16)1.0f;
@@ -477,7 +560,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
         const float acc_scale = moved ? __builtin_amdgcn_exp2f(delta) : 1.0f;
         if (DEBUG && rescale_count != nullptr) {
             // events count reference moves after the first one of a row
-            const unsigned long long ev = __ballot(moved && ref != kNegInf);
+            const unsigned long long ev = __ballot(moved && ref != kNegInf && qw + l32 < p.Lq);
             if (lane == 0 && ev)
                 atomicAdd(rescale_count, (unsigned long long)__builtin_popcountll(ev & 0xffffffffull));
         }
@@ -544,7 +627,8 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
     // instead of waiting behind the partner wave's stream of softmax VALU
     // instructions, which otherwise wins arbitration whenever its wave is the
     // older one.
-    auto work = [&](int phi, const unsigned char* kl, const unsigned char* vl) {
+    auto work = [&](int phi, const unsigned char* kl, const unsigned char* vl)
+                    __attribute__((always_inline)) {
         const int lam = phi - grp;
         if (lam < 0) return;
         if (lam & 1) {
@@ -556,51 +640,184 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
         }
     };
 
-    if (nblk > 0) {
-        copy_k(0, lds_k0);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        const int nphase = 2 * nblk + 2;
-        for (int phi = 0; phi < nphase; phi += 4) {
-            const int t = phi >> 1;  // stage read in phases phi, phi + 1 (buffers 0)
-            if (t + 1 < nblk) copy_k(t + 1, lds_k1);
-            work(phi, lds_k0, lds_v0);
-            if (t < nblk) copy_v(t, lds_v1);
-            work(phi + 1, lds_k0, lds_v0);
-            __builtin_amdgcn_s_waitcnt(0);
-            __syncthreads();
-            if (phi + 2 >= nphase) break;
-            if (t + 2 < nblk) copy_k(t + 2, lds_k0);
-            work(phi + 2, lds_k1, lds_v1);
-            if (t + 1 < nblk) copy_v(t + 1, lds_v0);
-            work(phi + 3, lds_k1, lds_v1);
+    // ---- this wave's LDS slice: next tile's Q in, previous tile's O out -------
+    // Chunk k of a slice is its k-th KiB, rows [k R, (k + 1) R) with R = 1024 /
+    // row bytes; a chunk moves with one 16-byte-per-lane instruction.  Each
+    // wave owns its slice, so the hand-offs below need no workgroup barrier:
+    // LDS accesses of one wave execute in order, and the copies of the next
+    // tile's Q are complete at the barrier that closes the pair issuing them.
+    unsigned char* const slice = lds_s + __builtin_amdgcn_readfirstlane(kSlice * wave);
+    int pend = 0;                // 1: the slice holds an output tile not yet stored
+    uint16_t* pend_dst = o_out;  // its first row in O
+    int pend_rows = 0;           // its rows inside Lq
+    auto store_o_chunk = [&](int k) __attribute__((always_inline)) {
+        const int sl = 64 * k + lane;
+        const int r = sl / S::kChunksV;
+        const int c = sl % S::kChunksV;
+        const u32x4 x = *reinterpret_cast<const u32x4*>(slice + r * kRowQ + 16 * (c ^ kswz<DV>(r)));
+        if (r < pend_rows) *reinterpret_cast<u32x4*>(pend_dst + (size_t)r * DV + 8 * c) = x;
+    };
+    // next tile: this wave's Q rows and the tile's first K block
+    const uint16_t* nq_src = p.q;
+    int nq_rows = 0;
+    bool nk_copy = false;
+    int nk_key0 = 0;
+    __amdgpu_buffer_rsrc_t nk_rsrc = krsrc;
+    auto prefetch_q_chunk = [&](int k) __attribute__((always_inline)) {
+        const int sl = 64 * k + lane;
+        const int r = sl / S::kChunksK;
+        const int c = (sl % S::kChunksK) ^ kswz<DQK>(r);
+        const int rr = min(r, nq_rows - 1);  // rows past Lq repeat the last row
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(nq_src, (uint32_t)kSlice);
+        copy_to_lds(rs, (uint32_t)(rr * kRowQ + 16 * c), 0, slice + 1024 * k);
+    };
+    auto load_q_slice = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int ks = 0; ks < S::kKSteps; ++ks)
+            qf[ks] = *reinterpret_cast<const bf16x8*>(slice + kread[ks % kReadTable] +
+                                                      (ks / kReadTable) * kReadTable * 32);
+    };
+    // Pair u of the sweep (phases 2u, 2u + 1), 1 <= u <= nblk.  Output chunk
+    // k goes out in pair min(1 + k, nblk).  The next tile's Q chunk k comes in
+    // during pair nblk - C + k (C chunks per slice) when the sweep has more
+    // than C pairs after the first, else together with output chunk k.
+    // Spread over the sweep, neither competes for HBM with the other
+    // workgroups' tile boundaries.  The chunk ranges are computed rather than
+    // tested chunk by chunk, so no per-chunk address stays live across the
+    // sweep.
+    auto pair_io = [&](int u) __attribute__((always_inline)) {
+        if constexpr (kStage) {
+            int klo = u - 1;
+            int khi = (u == nblk) ? kSliceChunks : min(u, kSliceChunks);
+            if (pend) {
+#pragma unroll 1
+                for (int k = max(klo, 0); k < khi; ++k) store_o_chunk(k);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            if (nblk > kSliceChunks) {
+                klo = u - nblk + kSliceChunks;
+                khi = klo + 1;
+            }
+            if (nq_rows > 0) {
+#pragma unroll 1
+                for (int k = max(klo, 0); k < min(khi, kSliceChunks); ++k) prefetch_q_chunk(k);
+            }
+        }
+    };
+
+    // ---- ping-pong sweep over key blocks, tile after tile -----------------------
+    if (nblk > 0) copy_k(0, lds_k0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    for (;;) {
+        const int tile_n = tile_of_round(round + 1);
+        const bool has_next = tile_n >= 0;
+        nq_rows = 0;
+        nk_copy = false;
+        if (has_next) {
+            const TileCoord c = tile_coord<CAUSAL>(p, tile_n, wave);
+            const KeyRange r = key_range<CAUSAL>(p, c);
+            nk_copy = r.nblk > 0;
+            nk_key0 = r.jb0 * kBlockN;
+            nk_rsrc = make_rsrc(p.k + (size_t)c.bk * p.Lk * DQK, (uint32_t)p.Lk * kRowK);
+            if (kStage) {
+                nq_rows = max(0, min(kRowsPerWave, p.Lq - c.qw));
+                nq_src = p.q + (c.qrow0 + (nq_rows > 0 ? c.qw : 0)) * DQK;
+            }
+        }
+        reset_state();
+        if (nblk > 0) {
+            const int nphase = 2 * nblk + 2;
+            for (int phi = 0; phi < nphase; phi += 4) {
+                const int t = phi >> 1;  // pair t reads stage t (buffers 0)
+                pair_io(t);
+                if (t + 1 < nblk)
+                    copy_k(t + 1, lds_k1);
+                else if (t == nblk && nk_copy)
+                    copy_kblock(nk_rsrc, nk_key0, lds_k0);  // next tile's stage 0
+                work(phi, lds_k0, lds_v0);
+                if (t < nblk) copy_v(t, lds_v1);
+                work(phi + 1, lds_k0, lds_v0);
+                __builtin_amdgcn_s_waitcnt(0);
+                __syncthreads();
+                if (phi + 2 >= nphase) break;
+                pair_io(t + 1);
+                if (t + 2 < nblk)
+                    copy_k(t + 2, lds_k0);
+                else if (t + 1 == nblk && nk_copy)
+                    copy_kblock(nk_rsrc, nk_key0, lds_k0);
+                work(phi + 2, lds_k1, lds_v1);
+                if (t + 1 < nblk) copy_v(t + 1, lds_v0);
+                work(phi + 3, lds_k1, lds_v1);
+                __builtin_amdgcn_s_waitcnt(0);
+                __syncthreads();
+            }
+        } else {
+            // a tile without visible keys: only the hand-offs
+            if constexpr (kStage) {
+                if (pend) {
+#pragma unroll 1
+                    for (int k = 0; k < kSliceChunks; ++k) store_o_chunk(k);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                if (nq_rows > 0) {
+#pragma unroll 1
+                    for (int k = 0; k < kSliceChunks; ++k) prefetch_q_chunk(k);
+                }
+            }
+            if (nk_copy) copy_kblock(nk_rsrc, nk_key0, lds_k0);
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
         }
-    }
+        pend = 0;
 
-    // ---- epilogue: O = U / l (bf16), lse = scale * ref + ln l ----------------
-    const int qi = qw + l32;
-    const float ell_row = pair_sum(ell);
-    const float ell_o_row = ((lane >> 4) & 1) ? ell_o[1] : ell_o[0];
-    if (qi < p.Lq) {
+        // ---- epilogue: O = U / l (bf16), lse = scale * ref + ln l ------------
+        // The next tile's Q leaves the slice before this tile's O enters it.
+        if (kStage && nq_rows > 0) load_q_slice();
+        const int qi = qw + l32;
+        const float ell_row = pair_sum(ell);
+        const float ell_o_row = ((lane >> 4) & 1) ? ell_o[1] : ell_o[0];
         const float inv = ell_o_row > 0.0f ? 1.0f / ell_o_row : 0.0f;
         const float lse_row = ell_row > 0.0f ? ref * scale + logf(ell_row) : kNegInf;
+        typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
         if (o_part == nullptr) {
-            uint16_t* orow = o_out + (qrow0 + qi) * DV;
+            if constexpr (kStage) {
+                // row l32 of the slice; this lane's 4 columns 32 i + 8 r4 + 4 hi
+                // are the half hi of 16-byte chunk 4 i + r4.  The row index goes
+                // through an empty asm so that these per-lane addresses are
+                // computed here, not hoisted out of the tile loop and kept in
+                // registers across the sweep.
+                int orow = l32;
+                asm volatile("" : "+v"(orow));
 #pragma unroll
-            for (int i = 0; i < S::kDvBlocks; ++i) {
+                for (int i = 0; i < S::kDvBlocks; ++i) {
 #pragma unroll
-                for (int r4 = 0; r4 < 4; ++r4) {
-                    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-                    f32x4 x = {oacc[i][4 * r4 + 0] * inv, oacc[i][4 * r4 + 1] * inv,
-                               oacc[i][4 * r4 + 2] * inv, oacc[i][4 * r4 + 3] * inv};
-                    const bf16x4 y = __builtin_convertvector(x, bf16x4);
-                    *reinterpret_cast<bf16x4*>(orow + 32 * i + 8 * r4 + 4 * hi) = y;
+                    for (int r4 = 0; r4 < 4; ++r4) {
+                        f32x4 x = {oacc[i][4 * r4 + 0] * inv, oacc[i][4 * r4 + 1] * inv,
+                                   oacc[i][4 * r4 + 2] * inv, oacc[i][4 * r4 + 3] * inv};
+                        const bf16x4 y = __builtin_convertvector(x, bf16x4);
+                        *reinterpret_cast<bf16x4*>(slice + orow * kRowQ +
+                                                   16 * ((4 * i + r4) ^ kswz<DV>(orow)) + 8 * hi) = y;
+                    }
+                }
+                pend = 1;
+                pend_rows = max(0, min(kRowsPerWave, p.Lq - qw));
+                pend_dst = o_out + (qrow0 + (pend_rows > 0 ? qw : 0)) * DV;
+            } else if (qi < p.Lq) {
+                uint16_t* orow = o_out + (qrow0 + qi) * DV;
+#pragma unroll
+                for (int i = 0; i < S::kDvBlocks; ++i) {
+#pragma unroll
+                    for (int r4 = 0; r4 < 4; ++r4) {
+                        f32x4 x = {oacc[i][4 * r4 + 0] * inv, oacc[i][4 * r4 + 1] * inv,
+                                   oacc[i][4 * r4 + 2] * inv, oacc[i][4 * r4 + 3] * inv};
+                        const bf16x4 y = __builtin_convertvector(x, bf16x4);
+                        *reinterpret_cast<bf16x4*>(orow + 32 * i + 8 * r4 + 4 * hi) = y;
+                    }
                 }
             }
-            if (hi == 0) lse_out[qrow0 + qi] = lse_row;
-        } else {
+            if (hi == 0 && qi < p.Lq) lse_out[qrow0 + qi] = lse_row;
+        } else if (qi < p.Lq) {
             // one split's state in fp32: its normalised output and lse
             const size_t prow = (size_t)split * p.B * p.Hq * p.Lq + qrow0 + qi;
             float* orow = o_part + prow * DV;
@@ -615,13 +832,24 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
             }
             if (hi == 0) lse_out[prow] = lse_row;
         }
+        if (!has_next) break;
+        ++round;
+        tile = tile_n;
+        set_tile(tile);
+        if (!kStage) load_q_global();
+    }
+    // the last tile's output
+    if constexpr (kStage) {
+        if (pend) {
+#pragma unroll 1
+            for (int k = 0; k < kSliceChunks; ++k) store_o_chunk(k);
+        }
     }
 }
 
 template <int DQK, int DV, bool CAUSAL, bool DEBUG>
 hipError_t launch_one(const FwdParams& p, hipStream_t stream) {
-    const long long tiles = (long long)p.units * p.n_m;
-    dim3 grid((unsigned)tiles), block(kThreads);
+    dim3 grid((unsigned)p.grid), block(kThreads);
     FwdParams arg = p;
     void* args[] = {&arg};
     return hipLaunchKernel(reinterpret_cast<const void*>(&attn_fwd_kernel<DQK, DV, CAUSAL, DEBUG>),

@@ -39,6 +39,8 @@ struct FwdParams {
                     //    range of units (upx of them)
     int upx;        // units per XCD when xcd_mode
     int sec_units;  // units per cache section (divides upx, or units)
+    int grid;       // workgroups launched; each processes tiles i, i + grid, ...
+                    // (a multiple of 8 when smaller than the tile count)
 
     float scale;        // softmax scale (natural units), used for lse
     float scale_log2;   // scale * log2(e): base-2 exponent multiplier

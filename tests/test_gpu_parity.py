@@ -90,6 +90,50 @@ def test_full_size_workloads_sampled(orc, name):
     assert torch.isfinite(lse).all().item()
 
 
+# More than 256 tiles: one workgroup per CU loops over several tiles,
+# prefetching each next tile's queries and draining each output tile through
+# LDS.  Checked on sampled rows (always including the first and last).
+PERSISTENT = [
+    (2, 16, 16, 2100, 700, 128, 128, False, 1.0),   # 288 tiles, ragged Lq and Lk
+    (4, 8, 8, 2304, 300, 128, 128, True, 1.0),      # Lq > Lk: tiles with 0, 1, 2 blocks
+    (2, 32, 4, 1100, 1500, 64, 64, True, 1.0),      # GQA 8, d = 64: 280 tiles
+    (1, 32, 32, 2304, 512, 128, 128, False, 6.0),   # Q x 6
+    (3, 12, 6, 2000, 2000, 128, 128, True, 1.0),    # causal square, GQA 2
+    (1, 16, 16, 4200, 1000, 192, 128, True, 1.0),   # (192, 128): Q loaded per tile
+]
+
+
+@pytest.mark.parametrize("shape", PERSISTENT, ids=lambda s: "x".join(map(str, s)))
+def test_persistent_shapes_sampled(orc, shape):
+    B, Hq, Hkv, Lq, Lk, dqk, dv, causal, qm = shape
+    print(f"[case] persistent {shape}", flush=True)
+    q, k, v = make_qkv(B, Hq, Hkv, Lq, Lk, dqk, dv, seed=hash(shape) % 10007, q_mult=qm)
+    qd, kd, vd = _gpu(q, k, v)
+    o, lse = attn_fwd(qd, kd, vd, causal=causal)
+    torch.cuda.synchronize()
+    rows = sample_rows(B, Hq, Lq, 512, seed=hash(shape) % 997)
+    og, lg = gather_rows(o, lse, rows)
+    o_ref, l_ref = orc.attn_rows(q, k, v, causal=causal, rows=rows.numpy())
+    assert_parity(f"persistent {shape}", og, lg, o_ref, l_ref, stress=qm != 1.0)
+    if Lq <= Lk:
+        assert torch.isfinite(o).all().item() and torch.isfinite(lse).all().item()
+
+
+def test_persistent_equals_one_tile_per_workgroup():
+    """The same rows computed in a launch of 288 tiles (workgroups loop over
+    tiles) and, batch by batch, in launches of 144 tiles (one tile per
+    workgroup) agree bit for bit."""
+    q, k, v = make_qkv(2, 16, 16, 2100, 700, 128, 128, seed=123)
+    qd, kd, vd = _gpu(q, k, v)
+    for causal in (False, True):
+        o, lse = attn_fwd(qd, kd, vd, causal=causal)
+        for b in range(2):
+            ob, lb = attn_fwd(qd[b:b + 1].contiguous(), kd[b:b + 1].contiguous(),
+                              vd[b:b + 1].contiguous(), causal=causal)
+            torch.cuda.synchronize()
+            assert torch.equal(o[b:b + 1], ob) and torch.equal(lse[b:b + 1], lb)
+
+
 def test_zero_query_closed_form():
     """Q = 0: O is the mean of the visible V rows and lse = ln(#visible)."""
     for causal in (False, True):

@@ -106,6 +106,20 @@ def test_decode_shape_sampled(orc, causal):
     assert torch.isfinite(o).all().item() and torch.isfinite(lse).all().item()
 
 
+def test_split_many_tiles_sampled(orc):
+    """768 tiles of 16 splits: workgroups loop over tiles of different splits."""
+    B, Hq, Hkv, Lq, Lk, d, n = 2, 8, 8, 600, 3000, 128, 16
+    print(f"[case] split B{B} Hq{Hq} Hkv{Hkv} Lq{Lq} Lk{Lk} d{d} splits {n}", flush=True)
+    q, k, v = make_qkv(B, Hq, Hkv, Lq, Lk, d, d, seed=51)
+    for causal in (False, True):
+        o, lse = attn_fwd_splitkv(q.to(DEV), k.to(DEV), v.to(DEV), n, causal=causal)
+        torch.cuda.synchronize()
+        rows = sample_rows(B, Hq, Lq, 128, seed=52)
+        og, lg = gather_rows(o, lse, rows)
+        o_ref, l_ref = orc.attn_rows(q, k, v, causal=causal, rows=rows.numpy())
+        assert_parity(f"split many tiles causal={causal}", og, lg, o_ref, l_ref)
+
+
 def test_decode_workload_in_bench_configuration(orc):
     """decode_l32k with the 4 key splits bench.py times: sampled rows against
     the oracle."""
