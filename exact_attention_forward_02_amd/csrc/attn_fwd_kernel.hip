@@ -436,7 +436,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
     constexpr int kPvUnits = (kBlockN / 16) * S::kDvBlocks;
     constexpr int kSUnits = S::kKSteps * (kBlockN / 32);
     constexpr int kAhead = DQK > 128 ? 3 : 4;  // wide heads have fewer spare VGPRs
-    auto load_pv = [&](int u, const unsigned char* vl) {
+    auto load_pv = [&](int u, const unsigned char* vl) __attribute__((always_inline)) {
         const int g = u / S::kDvBlocks, i = u % S::kDvBlocks;
         i16x4 part[2];
 #pragma unroll
@@ -446,19 +446,19 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
         return __builtin_bit_cast(
             bf16x8, __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
     };
-    auto load_s = [&](int u, const unsigned char* kl) {
+    auto load_s = [&](int u, const unsigned char* kl) __attribute__((always_inline)) {
         const int ks = u / (kBlockN / 32), mb = u % (kBlockN / 32);
         return *reinterpret_cast<const bf16x8*>(kl + kread[ks % kReadTable] +
                                                 (ks / kReadTable) * kReadTable * 32 +
                                                 mb * 32 * kRowK);
     };
-    auto m_phase = [&](int j, const unsigned char* kl, const unsigned char* vl) {
+    auto m_phase = [&](int j, const unsigned char* kl, const unsigned char* vl) __attribute__((always_inline)) {
         const bool do_pv = j >= 0 && j < nact;
         const bool do_s = j + 1 < nact;
         const f32x16 zero = {};
         // one MFMA unit: PV unit u < kPvUnits, else score unit u - kPvUnits; the
         // first k-step of a score block starts from an inline zero accumulator
-        auto mfma_unit = [&](int u, bf16x8 a) {
+        auto mfma_unit = [&](int u, bf16x8 a) __attribute__((always_inline)) {
             if (u < kPvUnits) {
                 const int g = u / S::kDvBlocks, i = u % S::kDvBlocks;
                 oacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[g], oacc[i], 0, 0, 0);
@@ -472,7 +472,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
             }
         };
         if (do_pv || do_s) {
-            auto load = [&](int u) {
+            auto load = [&](int u) __attribute__((always_inline)) {
                 return u < kPvUnits ? load_pv(u, vl) : load_s(u - kPvUnits, kl);
             };
             if (do_pv && do_s) {
@@ -522,7 +522,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
     };
 
     // ---- VALU phase V(j): online softmax of block j's scores -----------------
-    auto v_phase = [&](int j) {
+    auto v_phase = [&](int j) __attribute__((always_inline)) {
         if (j >= nact) return;
         const int key0 = (jb0 + j) * kBlockN;
         // mask keys past the end or past the causal diagonal
@@ -627,11 +627,17 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
     // instead of waiting behind the partner wave's stream of softmax VALU
     // instructions, which otherwise wins arbitration whenever its wave is the
     // older one.
-    auto work = [&](int phi, const unsigned char* kl, const unsigned char* vl)
+    // Phase phi = base + C (base a multiple of 4) of a wave of group G.  The
+    // sweep is compiled once per group, so whether a phase is an MFMA or a
+    // softmax phase is known at compile time and the only branches left in
+    // the loop test wave-uniform scalars.
+    auto work = [&](auto gc, auto cc, int base, const unsigned char* kl, const unsigned char* vl)
                     __attribute__((always_inline)) {
-        const int lam = phi - grp;
+        constexpr int G = decltype(gc)::value;
+        constexpr int C = decltype(cc)::value;
+        const int lam = base + C - G;
         if (lam < 0) return;
-        if (lam & 1) {
+        if constexpr (((C - G) & 1) != 0) {
             __builtin_amdgcn_s_setprio(0);
             v_phase(lam >> 1);
         } else {
@@ -726,7 +732,13 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
             }
         }
         reset_state();
-        if (nblk > 0) {
+        // Both groups run the same pairs, copies and barriers; only the order
+        // of their phase kinds differs.
+        auto sweep = [&](auto gc) __attribute__((always_inline)) {
+            using C0 = std::integral_constant<int, 0>;
+            using C1 = std::integral_constant<int, 1>;
+            using C2 = std::integral_constant<int, 2>;
+            using C3 = std::integral_constant<int, 3>;
             const int nphase = 2 * nblk + 2;
             for (int phi = 0; phi < nphase; phi += 4) {
                 const int t = phi >> 1;  // pair t reads stage t (buffers 0)
@@ -735,9 +747,9 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
                     copy_k(t + 1, lds_k1);
                 else if (t == nblk && nk_copy)
                     copy_kblock(nk_rsrc, nk_key0, lds_k0);  // next tile's stage 0
-                work(phi, lds_k0, lds_v0);
+                work(gc, C0{}, phi, lds_k0, lds_v0);
                 if (t < nblk) copy_v(t, lds_v1);
-                work(phi + 1, lds_k0, lds_v0);
+                work(gc, C1{}, phi, lds_k0, lds_v0);
                 __builtin_amdgcn_s_waitcnt(0);
                 __syncthreads();
                 if (phi + 2 >= nphase) break;
@@ -746,12 +758,18 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
                     copy_k(t + 2, lds_k0);
                 else if (t + 1 == nblk && nk_copy)
                     copy_kblock(nk_rsrc, nk_key0, lds_k0);
-                work(phi + 2, lds_k1, lds_v1);
+                work(gc, C2{}, phi, lds_k1, lds_v1);
                 if (t + 1 < nblk) copy_v(t + 1, lds_v0);
-                work(phi + 3, lds_k1, lds_v1);
+                work(gc, C3{}, phi, lds_k1, lds_v1);
                 __builtin_amdgcn_s_waitcnt(0);
                 __syncthreads();
             }
+        };
+        if (nblk > 0) {
+            if (grp == 0)
+                sweep(std::integral_constant<int, 0>{});
+            else
+                sweep(std::integral_constant<int, 1>{});
         } else {
             // a tile without visible keys: only the hand-offs
             if constexpr (kStage) {
