@@ -62,11 +62,14 @@ struct Shape {
     static constexpr int kChunksV = DV / 8;                // 16-byte chunks per V row
     static constexpr int kKBytes = kBlockN * DQK * 2;      // one K block in LDS
     static constexpr int kVBytes = kBlockN * DV * 2;       // one V block in LDS
-    static constexpr int kKCopies = kChunksK / kWaves;     // 1 KiB direct copies / wave
-    static constexpr int kVCopies = kChunksV / kWaves;
+    // K blocks are copied by the 4 waves of group 1, V blocks by those of
+    // group 0: 1 KiB direct copies per copying wave
+    static constexpr int kKCopies = kChunksK / kGroupWaves;
+    static constexpr int kVCopies = kChunksV / kGroupWaves;
     static constexpr int kKSteps = DQK / 16;               // MFMA k-steps for S
     static constexpr int kDvBlocks = DV / 32;              // 32-wide output blocks
-    static_assert(kChunksK % kWaves == 0 && kChunksV % kWaves == 0, "blocks split evenly");
+    static_assert(kChunksK % kGroupWaves == 0 && kChunksV % kGroupWaves == 0,
+                  "blocks split evenly");
     static_assert(DQK % 16 == 0 && DV % 32 == 0, "head dims must fit the MFMA tiles");
 };
 
@@ -306,23 +309,27 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
     load_q_global();
 
     // ---- direct global -> LDS copies of one K or V block -------------------
-    // Copy n of the workgroup fills LDS slots [64 n, 64 n + 64); lane l takes
+    // The copies are issued by the waves whose phase at that moment is the
+    // softmax one (group 1 copies K, group 0 copies V), so the wave running
+    // MFMAs issues nothing else.  Copy n of the block fills LDS slots
+    // [64 n, 64 n + 64); lane l takes
     // slot 64 n + l = (row r, stored chunk c') and fetches source chunk
     // c' ^ swizzle(r) of key row key0 + r.  The per-lane byte offsets within
     // a block are fixed, so they are computed once.  In a block that runs
     // past the last key, rows are clamped to the last key: those rows are
     // masked to -inf (K) or weighted by exactly 0 (V).
+    const int wq = wave % kGroupWaves;  // index of the wave within its group
     uint32_t koff[S::kKCopies], voff_copy[S::kVCopies];
 #pragma unroll
     for (int i = 0; i < S::kKCopies; ++i) {
-        const int slot = 64 * (wave * S::kKCopies + i) + lane;
+        const int slot = 64 * (wq * S::kKCopies + i) + lane;
         const int r = slot / S::kChunksK;
         const int c = (slot - r * S::kChunksK) ^ kswz<DQK>(r);
         koff[i] = r * kRowK + 16 * c;
     }
 #pragma unroll
     for (int i = 0; i < S::kVCopies; ++i) {
-        const int slot = 64 * (wave * S::kVCopies + i) + lane;
+        const int slot = 64 * (wq * S::kVCopies + i) + lane;
         const int r = slot / S::kChunksV;
         const int c = (slot - r * S::kChunksV) ^ vswz<DV>(r);
         voff_copy[i] = r * kRowV + 16 * c;
@@ -330,8 +337,8 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
 
     // The block offset goes in the scalar offset operand and this wave's LDS
     // destination is a scalar too, so a copy needs no vector arithmetic.
-    const int kdst = __builtin_amdgcn_readfirstlane(1024 * S::kKCopies * wave);
-    const int vdst = __builtin_amdgcn_readfirstlane(1024 * S::kVCopies * wave);
+    const int kdst = __builtin_amdgcn_readfirstlane(1024 * S::kKCopies * wq);
+    const int vdst = __builtin_amdgcn_readfirstlane(1024 * S::kVCopies * wq);
     auto copy_kblock = [&](__amdgpu_buffer_rsrc_t rs, int key0, unsigned char* dst)
                            __attribute__((always_inline)) {
         const uint32_t blk = (uint32_t)key0 * kRowK;
@@ -712,7 +719,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
     };
 
     // ---- ping-pong sweep over key blocks, tile after tile -----------------------
-    if (nblk > 0) copy_k(0, lds_k0);
+    if (nblk > 0 && grp == 1) copy_k(0, lds_k0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     for (;;) {
@@ -732,9 +739,12 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
             }
         }
         reset_state();
-        // Both groups run the same pairs, copies and barriers; only the order
-        // of their phase kinds differs.
+        // Both groups run the same pairs and barriers; only the order of their
+        // phase kinds differs.  In each phase the group in its softmax phase
+        // also issues that phase's copy (group 1: K at even phases, group 0:
+        // V at odd phases) and its own slice hand-offs.
         auto sweep = [&](auto gc) __attribute__((always_inline)) {
+            constexpr int G = decltype(gc)::value;
             using C0 = std::integral_constant<int, 0>;
             using C1 = std::integral_constant<int, 1>;
             using C2 = std::integral_constant<int, 2>;
@@ -742,24 +752,34 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
             const int nphase = 2 * nblk + 2;
             for (int phi = 0; phi < nphase; phi += 4) {
                 const int t = phi >> 1;  // pair t reads stage t (buffers 0)
-                pair_io(t);
-                if (t + 1 < nblk)
-                    copy_k(t + 1, lds_k1);
-                else if (t == nblk && nk_copy)
-                    copy_kblock(nk_rsrc, nk_key0, lds_k0);  // next tile's stage 0
+                if constexpr (G == 1) {
+                    pair_io(t);
+                    if (t + 1 < nblk)
+                        copy_k(t + 1, lds_k1);
+                    else if (t == nblk && nk_copy)
+                        copy_kblock(nk_rsrc, nk_key0, lds_k0);  // next tile's stage 0
+                }
                 work(gc, C0{}, phi, lds_k0, lds_v0);
-                if (t < nblk) copy_v(t, lds_v1);
+                if constexpr (G == 0) {
+                    pair_io(t);
+                    if (t < nblk) copy_v(t, lds_v1);
+                }
                 work(gc, C1{}, phi, lds_k0, lds_v0);
                 __builtin_amdgcn_s_waitcnt(0);
                 __syncthreads();
                 if (phi + 2 >= nphase) break;
-                pair_io(t + 1);
-                if (t + 2 < nblk)
-                    copy_k(t + 2, lds_k0);
-                else if (t + 1 == nblk && nk_copy)
-                    copy_kblock(nk_rsrc, nk_key0, lds_k0);
+                if constexpr (G == 1) {
+                    pair_io(t + 1);
+                    if (t + 2 < nblk)
+                        copy_k(t + 2, lds_k0);
+                    else if (t + 1 == nblk && nk_copy)
+                        copy_kblock(nk_rsrc, nk_key0, lds_k0);
+                }
                 work(gc, C2{}, phi, lds_k1, lds_v1);
-                if (t + 1 < nblk) copy_v(t + 1, lds_v0);
+                if constexpr (G == 0) {
+                    pair_io(t + 1);
+                    if (t + 1 < nblk) copy_v(t + 1, lds_v0);
+                }
                 work(gc, C3{}, phi, lds_k1, lds_v1);
                 __builtin_amdgcn_s_waitcnt(0);
                 __syncthreads();
@@ -783,7 +803,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
                     for (int k = 0; k < kSliceChunks; ++k) prefetch_q_chunk(k);
                 }
             }
-            if (nk_copy) copy_kblock(nk_rsrc, nk_key0, lds_k0);
+            if (nk_copy && grp == 1) copy_kblock(nk_rsrc, nk_key0, lds_k0);
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
         }
