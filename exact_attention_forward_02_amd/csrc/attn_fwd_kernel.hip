@@ -469,14 +469,20 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
             if (u < kPvUnits) {
                 const int g = u / S::kDvBlocks, i = u % S::kDvBlocks;
                 oacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[g], oacc[i], 0, 0, 0);
-                if (i == S::kDvBlocks - 1)
-                    ell_o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sel, pb[g], ell_o, 0, 0, 0);
             } else {
                 const int v = u - kPvUnits;
                 const int ks = v / (kBlockN / 32), mb = v % (kBlockN / 32);
                 s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], ks == 0 ? zero : s[mb],
                                                                 0, 0, 0);
             }
+        };
+        // the bf16 row sums need no LDS operand: they run while the first
+        // operands of the ring are still in flight
+        auto row_sums = [&]() __attribute__((always_inline)) {
+#pragma unroll
+            for (int g = 0; g < kBlockN / 16; ++g)
+                ell_o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sel, pb[g], ell_o, 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
         };
         if (do_pv || do_s) {
             auto load = [&](int u) __attribute__((always_inline)) {
@@ -495,6 +501,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
                 bf16x8 ring[kAhead];
 #pragma unroll
                 for (int n = 0; n < kAhead; ++n) ring[n] = load(order(n));
+                row_sums();
 #pragma unroll
                 for (int n = 0; n < kUnits; ++n) {
                     const bf16x8 a = ring[n % kAhead];
@@ -506,6 +513,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
                 bf16x8 ring[kAhead];
 #pragma unroll
                 for (int u = 0; u < kAhead; ++u) ring[u] = load(u);
+                row_sums();
 #pragma unroll
                 for (int u = 0; u < kPvUnits; ++u) {
                     const bf16x8 a = ring[u % kAhead];
