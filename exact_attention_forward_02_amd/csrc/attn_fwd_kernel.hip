@@ -126,6 +126,16 @@ __device__ __forceinline__ void copy_to_lds(__amdgpu_buffer_rsrc_t rsrc, uint32_
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)lds_dst, 16, voff, soff, 0, 0);
 }
 
+// A wave-uniform pointer held in VGPRs, moved to SGPRs (a buffer descriptor
+// built from it then needs no per-lane loop).
+template <typename T>
+__device__ __forceinline__ const T* uniform(const T* p) {
+    const uint64_t v = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return reinterpret_cast<const T*>(((uint64_t)hi << 32) | lo);
+}
+
 // Raw buffer descriptor over [base, base + bytes): 32-bit data format, no stride.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
@@ -342,10 +352,15 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
     auto copy_kblock = [&](__amdgpu_buffer_rsrc_t rs, int key0, unsigned char* dst)
                            __attribute__((always_inline)) {
         const uint32_t blk = (uint32_t)key0 * kRowK;
+        // an opaque copy of the wave's offset: the destinations are formed
+        // here with one scalar add each, not precomputed for every buffer
+        // and copy and held (or spilled) across the sweep
+        int kd = kdst;
+        asm volatile("" : "+s"(kd));
         if (key0 + kBlockN <= p.Lk) {
 #pragma unroll
             for (int i = 0; i < S::kKCopies; ++i)
-                copy_to_lds(rs, koff[i], blk, dst + kdst + 1024 * i);
+                copy_to_lds(rs, koff[i], blk, dst + kd + 1024 * i);
         } else {
             const int last = p.Lk - 1 - key0;
 #pragma unroll
@@ -353,7 +368,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
                 const int r = (int)koff[i] / kRowK;
                 const int rr = min(r, last);
                 copy_to_lds(rs, koff[i] - (uint32_t)((r - rr) * kRowK), blk,
-                            dst + kdst + 1024 * i);
+                            dst + kd + 1024 * i);
             }
         }
     };
@@ -363,10 +378,12 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
     auto copy_v = [&](int jl, unsigned char* dst) __attribute__((always_inline)) {
         const int key0 = (jb0 + jl) * kBlockN;
         const uint32_t blk = (uint32_t)key0 * kRowV;
+        int vd = vdst;
+        asm volatile("" : "+s"(vd));
         if (key0 + kBlockN <= p.Lk) {
 #pragma unroll
             for (int i = 0; i < S::kVCopies; ++i)
-                copy_to_lds(vrsrc, voff_copy[i], blk, dst + vdst + 1024 * i);
+                copy_to_lds(vrsrc, voff_copy[i], blk, dst + vd + 1024 * i);
         } else {
             const int last = p.Lk - 1 - key0;
 #pragma unroll
@@ -374,7 +391,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
                 const int r = (int)voff_copy[i] / kRowV;
                 const int rr = min(r, last);
                 copy_to_lds(vrsrc, voff_copy[i] - (uint32_t)((r - rr) * kRowV), blk,
-                            dst + vdst + 1024 * i);
+                            dst + vd + 1024 * i);
             }
         }
     };
@@ -556,9 +573,10 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
         }
 
         // block max of this row (raw units), two independent chains
-        float bm0 = kNegInf, bm1 = kNegInf;
+        float bm0 = fmaxf(s[0][0], s[0][1]);
+        float bm1 = fmaxf(s[kBlockN / 32 - 1][0], s[kBlockN / 32 - 1][1]);
 #pragma unroll
-        for (int r = 0; r < 16; r += 2) {
+        for (int r = 2; r < 16; r += 2) {
             bm0 = fmaxf(fmaxf(bm0, s[0][r]), s[0][r + 1]);
             bm1 = fmaxf(fmaxf(bm1, s[kBlockN / 32 - 1][r]), s[kBlockN / 32 - 1][r + 1]);
         }
@@ -689,7 +707,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
         const int r = sl / S::kChunksK;
         const int c = (sl % S::kChunksK) ^ kswz<DQK>(r);
         const int rr = min(r, nq_rows - 1);  // rows past Lq repeat the last row
-        const __amdgpu_buffer_rsrc_t rs = make_rsrc(nq_src, (uint32_t)kSlice);
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(uniform(nq_src), (uint32_t)kSlice);
         copy_to_lds(rs, (uint32_t)(rr * kRowQ + 16 * c), 0, slice + 1024 * k);
     };
     auto load_q_slice = [&]() __attribute__((always_inline)) {
