@@ -44,17 +44,34 @@ def build(source: str = SOURCE, output: str = LIBRARY, extra_flags=()) -> str:
     return output
 
 
+ELEM_BF16, ELEM_FP16 = 0, 1
+
+
 def _as_bits(t) -> np.ndarray:
     """bf16 tensor (torch, any device) or uint16 array -> contiguous uint16."""
+    bits, elem = _as_bits_elem(t)
+    if elem != ELEM_BF16:
+        raise TypeError("expected bfloat16 input")
+    return bits
+
+
+def _as_bits_elem(t):
+    """16-bit tensor (torch bf16 or fp16, any device and strides) or uint16 array of
+    bf16 patterns -> (contiguous uint16 bit patterns, element type)."""
     if isinstance(t, np.ndarray):
         if t.dtype != np.uint16:
             raise TypeError("numpy inputs must hold bf16 bit patterns as uint16")
-        return np.ascontiguousarray(t)
+        return np.ascontiguousarray(t), ELEM_BF16
     import torch
 
-    if t.dtype != torch.bfloat16:
-        raise TypeError(f"expected a bfloat16 tensor, got {t.dtype}")
-    return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+    if t.dtype == torch.bfloat16:
+        elem = ELEM_BF16
+    elif t.dtype == torch.float16:
+        elem = ELEM_FP16
+    else:
+        raise TypeError(f"expected a bfloat16 or float16 tensor, got {t.dtype}")
+    bits = t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+    return bits, elem
 
 
 class Oracle:
@@ -71,6 +88,13 @@ class Oracle:
         lib.oracle_attn_rows_range.argtypes = [
             _ptr, _ptr, _ptr, _i64, _i64, _i64, _i64, _i64, _i64, _i64,
             ctypes.c_int, ctypes.c_double, _i64, _i64, _ptr, _i64, _ptr, _ptr, ctypes.c_int]
+        lib.oracle_attn_rows_elem.restype = ctypes.c_int
+        lib.oracle_attn_rows_elem.argtypes = [
+            _ptr, _ptr, _ptr, _i64, _i64, _i64, _i64, _i64, _i64, _i64,
+            ctypes.c_int, ctypes.c_double, _i64, _i64, _ptr, _i64, _ptr, _ptr, ctypes.c_int,
+            ctypes.c_int]
+        lib.oracle_widen.restype = ctypes.c_double
+        lib.oracle_widen.argtypes = [ctypes.c_uint16, ctypes.c_int]
         lib.oracle_merge_states.restype = ctypes.c_int
         lib.oracle_merge_states.argtypes = [_ptr, _ptr, _i64, _i64, _i64, _ptr, _ptr]
         lib.oracle_online_rows.restype = ctypes.c_int
@@ -101,14 +125,17 @@ class Oracle:
 
     def attn_rows(self, q, k, v, causal: bool, scale: float | None = None,
                   rows=None, threads: int = 0, k_range=None):
-        """Exact O [n, dv] and lse [n] (float64) for the requested query rows.
+        """Exact O [n, dv] and lse [n] (float64) for the requested query rows of
+        bf16 or fp16 inputs (any strides; q, k, v of one element type).
 
         A row index is (b*Hq + h)*Lq + i; rows=None means every row in order.
         k_range=(k0, k1) restricts the softmax to the visible keys in [k0, k1):
         the partial state of that key segment (O = 0, lse = -inf where the
         segment holds no visible key).
         """
-        qb, kb, vb = _as_bits(q), _as_bits(k), _as_bits(v)
+        (qb, eq), (kb, ek), (vb, ev) = _as_bits_elem(q), _as_bits_elem(k), _as_bits_elem(v)
+        if not eq == ek == ev:
+            raise TypeError("q, k and v must have one element type")
         B, Hq, Hkv, Lq, Lk, dqk, dv = self._shapes(qb, kb, vb)
         if scale is None:
             scale = 1.0 / math.sqrt(dqk)
@@ -116,14 +143,18 @@ class Oracle:
         r, n = self._rows(rows, B * Hq * Lq)
         o = np.empty((n, dv), dtype=np.float64)
         lse = np.empty((n,), dtype=np.float64)
-        rc = self._lib.oracle_attn_rows_range(
+        rc = self._lib.oracle_attn_rows_elem(
             qb.ctypes.data, kb.ctypes.data, vb.ctypes.data,
             B, Hq, Hkv, Lq, Lk, dqk, dv, int(bool(causal)), float(scale), k0, k1,
             None if r is None else r.ctypes.data, n,
-            o.ctypes.data, lse.ctypes.data, int(threads))
+            o.ctypes.data, lse.ctypes.data, int(threads), eq)
         if rc != 0:
             raise ValueError(f"oracle_attn_rows rejected its arguments (code {rc})")
         return o, lse
+
+    def widen(self, bits: int, elem: int) -> float:
+        """The oracle's exact widening of one 16-bit pattern (ELEM_BF16 / ELEM_FP16)."""
+        return self._lib.oracle_widen(int(bits), int(elem))
 
     def merge(self, o_parts, lse_parts):
         """Merge segment states: o_parts [n, rows, dv], lse_parts [n, rows]

@@ -7,9 +7,9 @@
  * CPU-baseline leg do.  It shares no code, header, table or helper with the
  * GPU library.
  *
- * Inputs are bf16 bit patterns (uint16).  Each is widened exactly to double
- * (a bf16 value is the top half of an IEEE binary32), so the oracle works on
- * the exact values the GPU receives.
+ * Inputs are 16-bit bit patterns (uint16): bf16, or IEEE binary16 (fp16)
+ * through oracle_attn_rows_elem.  Each is widened exactly to double, so the
+ * oracle works on the exact values the GPU receives.
  *
  * Layouts (all contiguous, row-major):
  *   q   [B, Hq,  Lq, dqk]      k [B, Hkv, Lk, dqk]      v [B, Hkv, Lk, dv]
@@ -55,11 +55,47 @@ static double bf16_bits_to_double(uint16_t bits)
     return (double)f;
 }
 
+/* Exact widening of an IEEE binary16 (fp16) bit pattern: 1 sign bit, 5
+ * exponent bits (bias 15), 10 fraction bits.  Exponent 0 holds zero and the
+ * subnormals f * 2^-24; exponent 31 holds infinities and NaNs; otherwise the
+ * value is (1024 + f) * 2^(e - 25).  Every such value is a double. */
+static double fp16_bits_to_double(uint16_t bits)
+{
+    int e = (bits >> 10) & 31;
+    int f = bits & 1023;
+    double v;
+    if (e == 0)
+        v = ldexp((double)f, -24);
+    else if (e == 31)
+        v = f ? NAN : INFINITY;
+    else
+        v = ldexp((double)(1024 + f), e - 25);
+    return (bits & 0x8000) ? -v : v;
+}
+
+/* Element types of the 16-bit inputs. */
+enum { ELEM_BF16 = 0, ELEM_FP16 = 1 };
+
 typedef struct {
     int64_t B, Hq, Hkv, Lq, Lk, dqk, dv;
     int causal;
     double scale;
+    int elem; /* ELEM_BF16 or ELEM_FP16 */
 } dims_t;
+
+static double widen(const dims_t* d, uint16_t bits)
+{
+    return d->elem == ELEM_FP16 ? fp16_bits_to_double(bits) : bf16_bits_to_double(bits);
+}
+
+/* Test hook: the widening of one 16-bit pattern (elem 0 bf16, 1 fp16). */
+double oracle_widen(uint16_t bits, int elem)
+{
+    dims_t d;
+    memset(&d, 0, sizeof d);
+    d.elem = elem;
+    return widen(&d, bits);
+}
 
 static int check_dims(const dims_t* d)
 {
@@ -130,7 +166,7 @@ static void exact_row(const dims_t* d, row_ref_t rr, int64_t j0, int64_t j1, dou
         return;
     }
     for (int64_t c = 0; c < d->dqk; ++c)
-        qd[c] = bf16_bits_to_double(rr.qrow[c]);
+        qd[c] = widen(d, rr.qrow[c]);
 
     /* S_i,j = scale * q_i . k_j for every key j in range */
     double m = -INFINITY;
@@ -138,7 +174,7 @@ static void exact_row(const dims_t* d, row_ref_t rr, int64_t j0, int64_t j1, dou
         const uint16_t* kj = rr.kh + j * d->dqk;
         double dot = 0.0;
         for (int64_t c = 0; c < d->dqk; ++c)
-            dot += qd[c] * bf16_bits_to_double(kj[c]);
+            dot += qd[c] * widen(d, kj[c]);
         s[j] = d->scale * dot;
         if (s[j] > m)
             m = s[j];
@@ -154,7 +190,7 @@ static void exact_row(const dims_t* d, row_ref_t rr, int64_t j0, int64_t j1, dou
         const uint16_t* vj = rr.vh + j * d->dv;
         double p = s[j] / l;
         for (int64_t c = 0; c < d->dv; ++c)
-            o_row[c] += p * bf16_bits_to_double(vj[c]);
+            o_row[c] += p * widen(d, vj[c]);
     }
     *lse_out = m + log(l);
 }
@@ -169,14 +205,16 @@ static void exact_row(const dims_t* d, row_ref_t rr, int64_t j0, int64_t j1, dou
  * sequence may be cut into segments computed separately and merged.)
  * Returns 0 on success, nonzero on bad arguments.
  */
-int oracle_attn_rows_range(const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                           int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk,
-                           int64_t dqk, int64_t dv, int causal, double scale,
-                           int64_t k_begin, int64_t k_end,
-                           const int64_t* rows, int64_t n_rows,
-                           double* o, double* lse, int n_threads)
+int oracle_attn_rows_elem(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                          int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk,
+                          int64_t dqk, int64_t dv, int causal, double scale,
+                          int64_t k_begin, int64_t k_end,
+                          const int64_t* rows, int64_t n_rows,
+                          double* o, double* lse, int n_threads, int elem)
 {
-    dims_t d = {B, Hq, Hkv, Lq, Lk, dqk, dv, causal, scale};
+    dims_t d = {B, Hq, Hkv, Lq, Lk, dqk, dv, causal, scale, elem};
+    if (elem != ELEM_BF16 && elem != ELEM_FP16)
+        return 8;
     int rc = check_dims(&d);
     if (rc)
         return rc;
@@ -219,6 +257,18 @@ int oracle_attn_rows_range(const uint16_t* q, const uint16_t* k, const uint16_t*
         free(s);
     }
     return failed ? 7 : 0;
+}
+
+/* oracle_attn_rows_range: oracle_attn_rows_elem on bf16 inputs. */
+int oracle_attn_rows_range(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                           int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk,
+                           int64_t dqk, int64_t dv, int causal, double scale,
+                           int64_t k_begin, int64_t k_end,
+                           const int64_t* rows, int64_t n_rows,
+                           double* o, double* lse, int n_threads)
+{
+    return oracle_attn_rows_elem(q, k, v, B, Hq, Hkv, Lq, Lk, dqk, dv, causal, scale, k_begin,
+                                 k_end, rows, n_rows, o, lse, n_threads, ELEM_BF16);
 }
 
 /* oracle_attn_rows: the whole definition, every visible key of each row. */
@@ -353,7 +403,7 @@ static void online_rows_group(const dims_t* d, int mode, int64_t bn, double tau,
                 const uint16_t* kj = s->rr.kh + j * d->dqk;
                 double dot = 0.0;
                 for (int64_t c = 0; c < d->dqk; ++c)
-                    dot += s->qd[c] * bf16_bits_to_double(kj[c]);
+                    dot += s->qd[c] * widen(d, kj[c]);
                 *xj = (mode == 0) ? d->scale * dot : dot;
                 if (*xj > bmax[a])
                     bmax[a] = *xj;
@@ -387,7 +437,7 @@ static void online_rows_group(const dims_t* d, int mode, int64_t bn, double tau,
                     s->l += w;
                     const uint16_t* vj = s->rr.vh + j * d->dv;
                     for (int64_t c = 0; c < d->dv; ++c)
-                        s->u[c] += w * bf16_bits_to_double(vj[c]);
+                        s->u[c] += w * widen(d, vj[c]);
                 }
                 continue;
             }
@@ -417,7 +467,7 @@ static void online_rows_group(const dims_t* d, int mode, int64_t bn, double tau,
                 s->l += w;
                 const uint16_t* vj = s->rr.vh + j * d->dv;
                 for (int64_t c = 0; c < d->dv; ++c)
-                    s->u[c] += w * bf16_bits_to_double(vj[c]);
+                    s->u[c] += w * widen(d, vj[c]);
             }
         }
     }
@@ -431,7 +481,7 @@ int oracle_online_rows(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                        double* o, double* lse, double* state,
                        int64_t* n_rescale, int n_threads)
 {
-    dims_t d = {B, Hq, Hkv, Lq, Lk, dqk, dv, causal, scale};
+    dims_t d = {B, Hq, Hkv, Lq, Lk, dqk, dv, causal, scale, ELEM_BF16};
     int rc = check_dims(&d);
     if (rc)
         return rc;
@@ -496,7 +546,7 @@ int oracle_online_rows(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                     for (int64_t c = 0; c < dv; ++c)
                         st[a].u[c] = 0.0;
                     for (int64_t c = 0; c < dqk; ++c)
-                        st[a].qd[c] = bf16_bits_to_double(st[a].rr.qrow[c]);
+                        st[a].qd[c] = widen(&d, st[a].rr.qrow[c]);
                 }
                 online_rows_group(&d, mode, bn, tau, st, g, x, bmax, wants);
                 online_state_t* s = &st[mine];

@@ -14,7 +14,10 @@ AssertionError when the oracle disagrees with:
     describe),
   * the split-key path: the partial states of key segments and their merge
     reproduce the pages' worked example block by block and the whole
-    definition for any cut of the keys.
+    definition for any cut of the keys,
+  * the 16-bit input formats: the widening of every bf16 and fp16 bit pattern
+    (numpy's own conversions), fp16 inputs against torch's float64 SDPA, and
+    values exact in both formats giving identical results.
 They run unchanged against deliberately broken copies of the oracle in
 test_oracle_mutations.py, which checks that each planted mistake trips at
 least one pin.
@@ -469,6 +472,56 @@ def pin_segment_closed_form(orc):
             _close(l1, lse, 1e-15, "single-segment merge lse")
 
 
+# --------------------------------------------------------------------------
+# 16-bit input formats
+# --------------------------------------------------------------------------
+
+def pin_widening_exhaustive(orc):
+    """Every bf16 and fp16 bit pattern widens to the value numpy's conversions
+    give (bf16 as the top half of a binary32; fp16 via numpy.float16)."""
+    import oracle
+
+    bits = np.arange(65536, dtype=np.uint32)
+    want_bf = (bits << 16).view(np.float32).astype(np.float64)
+    want_fp = bits.astype(np.uint16).view(np.float16).astype(np.float64)
+    for elem, want, name in ((oracle.ELEM_BF16, want_bf, "bf16"),
+                             (oracle.ELEM_FP16, want_fp, "fp16")):
+        got = np.array([orc.widen(int(b), elem) for b in bits], dtype=np.float64)
+        both_nan = np.isnan(got) & np.isnan(want)
+        bad = ~both_nan & (got != want)
+        assert not bad.any(), f"{name} widening differs at pattern {int(np.argmax(bad)):#06x}"
+
+
+def pin_fp16_library_sdpa(orc):
+    """fp16 inputs (more mantissa than bf16, so values bf16 cannot hold) against
+    torch's float64 SDPA on the same values."""
+    for idx, (B, Hq, Hkv, Lq, Lk, dqk, dv, causal) in enumerate(SDPA_SHAPES[:4]):
+        g = torch.Generator().manual_seed(300 + idx)
+        q = torch.randn((B, Hq, Lq, dqk), generator=g).to(torch.float16)
+        k = torch.randn((B, Hkv, Lk, dqk), generator=g).to(torch.float16)
+        v = torch.randn((B, Hkv, Lk, dv), generator=g).to(torch.float16)
+        scale = 1.0 / math.sqrt(dqk)
+        o, lse = orc.attn_rows(q, k, v, causal=causal, scale=scale)
+        want_o, want_lse = _library_reference(q, k, v, causal, scale)
+        tag = f"fp16 shape {idx}"
+        _close(o, want_o, 1e-12, f"{tag} O vs torch SDPA")
+        _close(lse, want_lse, 1e-12, f"{tag} lse vs torch logsumexp")
+
+
+def pin_fp16_equals_bf16_on_shared_values(orc):
+    """Inputs exact in both formats (multiples of 1/8 in [-4, 4]) give the same
+    result whichever format carries them."""
+    g = torch.Generator().manual_seed(7)
+    B, Hq, Hkv, Lq, Lk, d = 1, 4, 2, 40, 70, 16
+    vals = [(torch.randint(-32, 33, shape, generator=g).to(torch.float32) / 8.0)
+            for shape in ((B, Hq, Lq, d), (B, Hkv, Lk, d), (B, Hkv, Lk, d))]
+    for causal in (False, True):
+        o16, l16 = orc.attn_rows(*(t.to(torch.float16) for t in vals), causal=causal)
+        obf, lbf = orc.attn_rows(*(t.to(torch.bfloat16) for t in vals), causal=causal)
+        assert np.array_equal(o16, obf) and np.array_equal(l16, lbf), \
+            f"fp16 and bf16 carriers of the same values differ (causal={causal})"
+
+
 ALL_PINS = [
     pin_worked_example,
     pin_conditional_cases,
@@ -486,4 +539,7 @@ ALL_PINS = [
     pin_segment_worked_example,
     pin_segments_merge_to_definition,
     pin_segment_closed_form,
+    pin_widening_exhaustive,
+    pin_fp16_library_sdpa,
+    pin_fp16_equals_bf16_on_shared_values,
 ]

@@ -19,10 +19,10 @@ MUTATIONS = {
     "dropped_scale": ("s[j] = d->scale * dot;", "s[j] = dot;"),
     "exp_sign": ("s[j] = exp(s[j] - m);", "s[j] = exp(m - s[j]);"),
     "lse_dropped_max": ("*lse_out = m + log(l);", "*lse_out = log(l);"),
-    "transposed_k": ("            dot += qd[c] * bf16_bits_to_double(kj[c]);\n        s[j]",
-                     "            dot += qd[c] * bf16_bits_to_double(rr.kh[c * d->Lk + j]);\n        s[j]"),
-    "value_index": ("o_row[c] += p * bf16_bits_to_double(vj[c]);",
-                    "o_row[c] += p * bf16_bits_to_double(vj[d->dv - 1 - c]);"),
+    "transposed_k": ("            dot += qd[c] * widen(d, kj[c]);\n        s[j]",
+                     "            dot += qd[c] * widen(d, rr.kh[c * d->Lk + j]);\n        s[j]"),
+    "value_index": ("o_row[c] += p * widen(d, vj[c]);",
+                    "o_row[c] += p * widen(d, vj[d->dv - 1 - c]);"),
     "bf16_widening": ("uint32_t word = ((uint32_t)bits) << 16;",
                       "uint32_t word = ((uint32_t)bits) << 15;"),
     "threshold_not_strict": ("if (delta < -tau)", "if (delta <= -tau)"),
@@ -36,6 +36,12 @@ MUTATIONS = {
     "merge_old_state_not_rescaled": ("u[c] = alpha * u[c] + beta * ob[c];",
                                      "u[c] = u[c] + beta * ob[c];"),
     "merge_lse_without_max": ("lse[r] = m + log(l);", "lse[r] = log(l);"),
+    "fp16_exponent_bias": ("v = ldexp((double)(1024 + f), e - 25);",
+                           "v = ldexp((double)(1024 + f), e - 24);"),
+    "fp16_subnormal_scale": ("v = ldexp((double)f, -24);", "v = ldexp((double)f, -25);"),
+    "fp16_sign_dropped": ("return (bits & 0x8000) ? -v : v;", "return v;"),
+    "fp16_read_as_bf16": ("return d->elem == ELEM_FP16 ? fp16_bits_to_double(bits) : "
+                          "bf16_bits_to_double(bits);", "return bf16_bits_to_double(bits);"),
 }
 
 
