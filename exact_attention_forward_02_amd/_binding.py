@@ -20,6 +20,13 @@ _lock = threading.Lock()
 _lib = None
 
 ATTN_OK = 0
+ATTN_DTYPE_BF16, ATTN_DTYPE_FP16 = 0, 1
+
+
+class Strides(ctypes.Structure):
+    """attn_strides: element strides (batch, head, row) of a [B, H, L, d] tensor."""
+    _fields_ = [("batch", ctypes.c_longlong), ("head", ctypes.c_longlong),
+                ("row", ctypes.c_longlong)]
 
 
 def _load():
@@ -39,6 +46,9 @@ def _load():
         lib.attn_fwd_dbg.restype = i
         lib.attn_fwd_dbg.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i,
                                      ctypes.c_float, vp, ctypes.c_float, vp]
+        lib.attn_fwd_ex.restype = i
+        lib.attn_fwd_ex.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i,
+                                    Strides, Strides, Strides, Strides, i, i, ctypes.c_float, vp]
         lib.attn_split_keys.restype = i
         lib.attn_split_keys.argtypes = [i, i]
         lib.attn_fwd_split.restype = i
@@ -140,6 +150,64 @@ def attn_fwd_dbg(q, k, v, causal: bool = False, scale: float | None = None,
                               float(scale), s.cuda_stream, float(rescale_threshold), cnt)
     if rc != ATTN_OK:
         raise RuntimeError(f"attn_fwd_dbg failed: {status_string(rc)} (code {rc})")
+    return out, lse
+
+
+def _strides(t) -> Strides:
+    sb, sh, sr, sc = t.stride()
+    if sc != 1:
+        raise ValueError("the head dim must be contiguous (stride 1)")
+    return Strides(sb, sh, sr)
+
+
+def attn_fwd_ex(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse=None,
+                stream=None):
+    """O, lse for [B, H, L, d]-shaped views of any strides with a contiguous head
+    dim (e.g. [B, S, H, d] tensors passed as .transpose(1, 2)), bf16 or fp16.
+
+    out defaults to the layout of q (row-major [B, Lq, Hq, d_v] viewed as
+    [B, Hq, Lq, d_v] when q's rows are further apart than its heads, else
+    contiguous [B, Hq, Lq, d_v]); lse is always contiguous fp32 [B, Hq, Lq]."""
+    lib = _load()
+    ts = (q, k, v)
+    for name, t in zip("qkv", ts):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch.Tensor")
+        if t.dtype not in (torch.bfloat16, torch.float16):
+            raise TypeError(f"{name} must be bfloat16 or float16, got {t.dtype}")
+        if t.device.type != "cuda" or t.dim() != 4:
+            raise ValueError(f"{name} must be a 4-D tensor on a GPU device")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k and v must have one dtype")
+    if not (q.device == k.device == v.device):
+        raise ValueError("q, k and v must be on the same device")
+    B, Hq, Lq, dqk = q.shape
+    Bk, Hkv, Lk, dk = k.shape
+    if Bk != B or dk != dqk or tuple(v.shape[:3]) != (B, Hkv, Lk):
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    dv = v.shape[3]
+    if scale is None:
+        scale = 1.0 / math.sqrt(dqk)
+    if out is None:
+        if q.stride(2) > q.stride(1):
+            out = torch.empty((B, Lq, Hq, dv), dtype=q.dtype, device=q.device).transpose(1, 2)
+        else:
+            out = torch.empty((B, Hq, Lq, dv), dtype=q.dtype, device=q.device)
+    if tuple(out.shape) != (B, Hq, Lq, dv) or out.dtype != q.dtype or out.device != q.device:
+        raise ValueError("out must be a [B, Hq, Lq, d_v] view of q's dtype on q's device")
+    if lse is None:
+        lse = torch.empty((B, Hq, Lq), dtype=torch.float32, device=q.device)
+    if lse.shape != (B, Hq, Lq) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous fp32 [B, Hq, Lq] tensor")
+    dtype = ATTN_DTYPE_FP16 if q.dtype == torch.float16 else ATTN_DTYPE_BF16
+    with torch.cuda.device(q.device):
+        s = stream if stream is not None else torch.cuda.current_stream(q.device)
+        rc = lib.attn_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                             lse.data_ptr(), B, Hq, Hkv, Lq, Lk, dqk, dv, _strides(q),
+                             _strides(k), _strides(v), _strides(out), dtype, int(bool(causal)),
+                             float(scale), s.cuda_stream)
+    if rc != ATTN_OK:
+        raise RuntimeError(f"attn_fwd_ex failed: {status_string(rc)} (code {rc})")
     return out, lse
 
 

@@ -16,7 +16,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 2;
+constexpr int kAbiVersion = 3;
 constexpr int kMaxSplits = 4096;
 constexpr int kMaxDevices = 64;
 constexpr int kXcds = 8;                 // MI355X: 8 accelerator complex dies
@@ -29,6 +29,47 @@ std::atomic<int> g_arch_ok[kMaxDevices];
 std::atomic<int> g_cu_count[kMaxDevices];
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Element strides of the four 16-bit tensors: (batch, head, row), head dim contiguous.
+struct Strides {
+    attn_strides q, k, v, o;
+};
+
+Strides contiguous_strides(int Hq, int Hkv, int Lq, int Lk, int d_qk, int d_v) {
+    Strides st;
+    st.q = {(long long)Hq * Lq * d_qk, (long long)Lq * d_qk, d_qk};
+    st.k = {(long long)Hkv * Lk * d_qk, (long long)Lk * d_qk, d_qk};
+    st.v = {(long long)Hkv * Lk * d_v, (long long)Lk * d_v, d_v};
+    st.o = {(long long)Hq * Lq * d_v, (long long)Lq * d_v, d_v};
+    return st;
+}
+
+// Strides are non-negative multiples of 8 elements (16 bytes, so every row
+// starts 16-byte aligned), rows at least a head-dim apart, and every element
+// offset and the byte extent of the rows the kernel addresses with 32-bit
+// offsets (one K or V head, 32 rows of Q) fits.
+int check_strides(const Strides& st, int B, int Hq, int Hkv, int Lq, int Lk, int d_qk, int d_v) {
+    const attn_strides* all[4] = {&st.q, &st.k, &st.v, &st.o};
+    const int dims[4] = {d_qk, d_qk, d_v, d_v};
+    const long long heads[4] = {Hq, Hkv, Hkv, Hq};
+    const long long rows[4] = {Lq, Lk, Lk, Lq};
+    for (int t = 0; t < 4; ++t) {
+        const attn_strides& a = *all[t];
+        if (a.batch < 0 || a.head < 0 || a.row < dims[t]) return ATTN_ERR_BAD_STRIDE;
+        if (a.batch % 8 || a.head % 8 || a.row % 8) return ATTN_ERR_BAD_STRIDE;
+        if (a.row > INT32_MAX) return ATTN_ERR_TOO_LARGE;
+        // largest element offset, in 64-bit arithmetic without overflow
+        const double last = (double)(B - 1) * a.batch + (double)(heads[t] - 1) * a.head +
+                            (double)(rows[t] - 1) * a.row + dims[t];
+        if (last > 9.0e18) return ATTN_ERR_TOO_LARGE;
+    }
+    const long long k_extent = (long long)(Lk - 1) * st.k.row * 2 + d_qk * 2;
+    const long long v_extent = (long long)(Lk - 1) * st.v.row * 2 + d_v * 2;
+    const long long q_extent = 31LL * st.q.row * 2 + d_qk * 2;
+    if (k_extent > INT32_MAX || v_extent > INT32_MAX || q_extent > INT32_MAX)
+        return ATTN_ERR_TOO_LARGE;
+    return ATTN_OK;
+}
 
 int check_args(const void* q, const void* k, const void* v, const void* o, const float* lse,
                int B, int Hq, int Hkv, int Lq, int Lk, int d_qk, int d_v, float scale) {
@@ -46,9 +87,6 @@ int check_args(const void* q, const void* k, const void* v, const void* o, const
     const long long q_rows = (long long)B * Hq * Lq;
     const long long kv_rows = (long long)B * Hkv * Lk;
     if (q_rows > INT32_MAX || kv_rows > INT32_MAX) return ATTN_ERR_TOO_LARGE;
-    // one K or V head is addressed with 32-bit byte offsets in the kernel
-    const int dmax = d_qk > d_v ? d_qk : d_v;
-    if ((long long)Lk * dmax * 2 > INT32_MAX) return ATTN_ERR_TOO_LARGE;
     return ATTN_OK;
 }
 
@@ -113,12 +151,18 @@ int fill_schedule(attn::FwdParams& p) {
     return ATTN_OK;
 }
 
-// o is the bf16 output when n_split == 0 (whole key range), else the fp32
-// per-split output [n_split, B, Hq, Lq, d_v]
+// o is the 16-bit output when n_split == 0 (whole key range), else the fp32
+// per-split output [n_split, B, Hq, Lq, d_v]; strides default to contiguous
+// [B, H, L, d] tensors
 int run(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
         int Hkv, int Lq, int Lk, int d_qk, int d_v, int causal, float scale, void* stream,
-        float threshold, unsigned long long* counter, bool debug, int n_split) {
+        float threshold, unsigned long long* counter, bool debug, int n_split,
+        const Strides* strides = nullptr, bool fp16 = false) {
     int rc = check_args(q, k, v, o, lse, B, Hq, Hkv, Lq, Lk, d_qk, d_v, scale);
+    if (rc != ATTN_OK) return rc;
+    const Strides st =
+        strides ? *strides : contiguous_strides(Hq, Hkv, Lq, Lk, d_qk, d_v);
+    rc = check_strides(st, B, Hq, Hkv, Lq, Lk, d_qk, d_v);
     if (rc != ATTN_OK) return rc;
     if (n_split < 0 || n_split > kMaxSplits) return ATTN_ERR_BAD_ARGUMENT;
     // per-split rows are addressed with 64-bit offsets; the split count times
@@ -141,6 +185,18 @@ int run(const void* q, const void* k, const void* v, void* o, float* lse, int B,
     }
     p.lse = lse;
     p.rescale_count = counter;
+    p.q_sb = st.q.batch;
+    p.q_sh = st.q.head;
+    p.q_sr = (int)st.q.row;
+    p.k_sb = st.k.batch;
+    p.k_sh = st.k.head;
+    p.k_sr = (int)st.k.row;
+    p.v_sb = st.v.batch;
+    p.v_sh = st.v.head;
+    p.v_sr = (int)st.v.row;
+    p.o_sb = st.o.batch;
+    p.o_sh = st.o.head;
+    p.o_sr = (int)st.o.row;
     p.B = B;
     p.Hq = Hq;
     p.Hkv = Hkv;
@@ -162,7 +218,7 @@ int run(const void* q, const void* k, const void* v, void* o, float* lse, int B,
     const long long slots = (long long)(n_cu / kXcds) * kXcds;
     if (slots > 0 && tiles > slots) grid = slots;
     p.grid = (int)grid;
-    hipError_t err = attn::launch_fwd(p, d_qk, d_v, causal != 0, debug,
+    hipError_t err = attn::launch_fwd(p, d_qk, d_v, causal != 0, debug, fp16,
                                       static_cast<hipStream_t>(stream));
     if (err != hipSuccess) return ATTN_ERR_HIP;
     return ATTN_OK;
@@ -193,6 +249,16 @@ int attn_fwd_dbg(const void* q, const void* k, const void* v, void* o, float* ls
         return ATTN_ERR_BAD_ARGUMENT;
     return run(q, k, v, o, lse, B, Hq, Hkv, Lq, Lk, d_qk, d_v, causal, scale, stream,
                rescale_threshold, rescale_count, true, 0);
+}
+
+int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
+                int Hkv, int Lq, int Lk, int d_qk, int d_v, attn_strides q_strides,
+                attn_strides k_strides, attn_strides v_strides, attn_strides o_strides,
+                int dtype, int causal, float scale, void* stream) {
+    if (dtype != ATTN_DTYPE_BF16 && dtype != ATTN_DTYPE_FP16) return ATTN_ERR_BAD_ARGUMENT;
+    const Strides st = {q_strides, k_strides, v_strides, o_strides};
+    return run(q, k, v, o, lse, B, Hq, Hkv, Lq, Lk, d_qk, d_v, causal, scale, stream,
+               kDefaultThreshold, nullptr, false, 0, &st, dtype == ATTN_DTYPE_FP16);
 }
 
 int attn_split_keys(int Lk, int n_split) {
@@ -241,7 +307,10 @@ const char* attn_status_string(int status) {
         case ATTN_ERR_HIP: return "the HIP runtime reported an error";
         case ATTN_ERR_BAD_ARGUMENT:
             return "argument out of range (rescale threshold finite and >= 0, split count in "
-                   "[1, 4096], merge rows >= 0)";
+                   "[1, 4096], merge rows >= 0, dtype bf16 or fp16)";
+        case ATTN_ERR_BAD_STRIDE:
+            return "strides must be >= 0 and multiples of 8 elements, with row strides of at "
+                   "least the head dim";
         default: return "unknown attn status";
     }
 }

@@ -48,6 +48,9 @@ namespace attn {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -55,6 +58,36 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kNegInf = -__builtin_inff();
+
+// The 16-bit element type of Q, K, V, O and of P in the PV product: bf16 or
+// fp16, with the MFMA forms of that type and fp32 accumulation.  Conversions
+// from fp32 round to nearest even.
+template <bool FP16>
+struct Elem;
+template <>
+struct Elem<false> {
+    using x8 = bf16x8;
+    using x4 = bf16x4;
+    using scalar = __bf16;
+    static __device__ __forceinline__ f32x16 mfma32(x8 a, x8 b, f32x16 c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ f32x4 mfma16(x8 a, x8 b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+    }
+};
+template <>
+struct Elem<true> {
+    using x8 = f16x8;
+    using x4 = f16x4;
+    using scalar = _Float16;
+    static __device__ __forceinline__ f32x16 mfma32(x8 a, x8 b, f32x16 c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ f32x4 mfma16(x8 a, x8 b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+    }
+};
 
 template <int DQK, int DV>
 struct Shape {
@@ -150,7 +183,8 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 // blocks in its L2.
 struct TileCoord {
     int split, bk, hq, pos0, qw;
-    size_t qrow0;  // row of (b, hq, position 0) in Q, O and lse
+    size_t qrow0;  // row of (b, hq, position 0) in lse
+    size_t qbase, obase, kbase, vbase;  // element offsets of (b, head, row 0)
 };
 
 template <bool CAUSAL>
@@ -178,6 +212,10 @@ __device__ __forceinline__ TileCoord tile_coord(const FwdParams& p, int t, int w
     c.pos0 = m * p.bm_pos;
     c.qw = c.pos0 + (wave / p.Gp) * kRowsPerWave;  // first row of this wave
     c.qrow0 = (size_t)(b * p.Hq + c.hq) * p.Lq;
+    c.qbase = (size_t)(b * p.q_sb + c.hq * p.q_sh);
+    c.obase = (size_t)(b * p.o_sb + c.hq * p.o_sh);
+    c.kbase = (size_t)(b * p.k_sb + kvh * p.k_sh);
+    c.vbase = (size_t)(b * p.v_sb + kvh * p.v_sh);
     return c;
 }
 
@@ -210,11 +248,18 @@ __device__ __forceinline__ KeyRange key_range(const FwdParams& p, const TileCoor
     return r;
 }
 
-template <int DQK, int DV, bool CAUSAL, bool DEBUG>
+template <int DQK, int DV, bool CAUSAL, bool DEBUG, bool FP16>
 __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
     using S = Shape<DQK, DV>;
-    constexpr int kRowK = DQK * 2;  // bytes per K row
-    constexpr int kRowV = DV * 2;   // bytes per V row
+    using E = Elem<FP16>;
+    using ex8 = typename E::x8;
+    using ex4 = typename E::x4;
+    constexpr int kRowK = DQK * 2;  // bytes per K row in LDS
+    constexpr int kRowV = DV * 2;   // bytes per V row in LDS
+    // row strides in HBM, bytes (equal to the LDS rows when contiguous)
+    const int k_rb = p.k_sr * 2;
+    const int v_rb = p.v_sr * 2;
+    const int q_rb = p.q_sr * 2;
     // two stage buffers each for K and V, distinct objects so that reads of
     // one buffer are never ordered behind copies into the other
     __shared__ __attribute__((aligned(1024))) unsigned char lds_k0[S::kKBytes];
@@ -284,7 +329,8 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
 
     // per-tile values of this wave (set_tile)
     int split, qw, jb0, nblk, nact;
-    size_t qrow0;  // row index of (b, hq, position 0) in Q, O and lse
+    size_t qrow0;  // row index of (b, hq, position 0) in lse
+    size_t qrow_w, orow_w;  // element offsets of this wave's first Q and O rows
     __amdgpu_buffer_rsrc_t krsrc, vrsrc;
     const int off = p.Lk - p.Lq;  // causal diagonal offset
     auto set_tile = [&](int t) __attribute__((always_inline)) {
@@ -292,28 +338,32 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
         split = c.split;
         qw = c.qw;
         qrow0 = c.qrow0;
+        qrow_w = c.qbase + (size_t)c.qw * p.q_sr;
+        orow_w = c.obase + (size_t)c.qw * p.o_sr;
         const KeyRange r = key_range<CAUSAL>(p, c);
         jb0 = r.jb0;
         nblk = r.nblk;
         nact = r.nact;
-        // one descriptor per K/V head; a head is at most 2^31 bytes (checked
-        // on the host), so 32-bit byte offsets address all of it
-        krsrc = make_rsrc(p.k + (size_t)c.bk * p.Lk * DQK, (uint32_t)p.Lk * kRowK);
-        vrsrc = make_rsrc(p.v + (size_t)c.bk * p.Lk * DV, (uint32_t)p.Lk * kRowV);
+        // one descriptor per K/V head; a head spans less than 2^31 bytes
+        // (checked on the host), so 32-bit byte offsets address all of it
+        krsrc = make_rsrc(p.k + c.kbase, (uint32_t)(p.Lk - 1) * k_rb + kRowK);
+        vrsrc = make_rsrc(p.v + c.vbase, (uint32_t)(p.Lk - 1) * v_rb + kRowV);
     };
     set_tile(tile);
 
     // ---- Q fragment, resident in registers for the whole sweep -----------
     // lane holds Q[qw + l32][16 ks + 8 hi .. +7] for every k-step ks
-    bf16x8 qf[S::kKSteps];
+    ex8 qf[S::kKSteps];
     auto load_q_global = [&]() __attribute__((always_inline)) {
         const int qi = qw + l32;
         const bool ok = qi < p.Lq;
-        const uint16_t* src = p.q + (qrow0 + (ok ? qi : 0)) * DQK + 8 * hi;
+        // lanes past Lq point at row 0 of the head (never read past the tensor)
+        const uint16_t* src =
+            p.q + (ok ? qrow_w + (size_t)l32 * p.q_sr : qrow_w - (size_t)qw * p.q_sr) + 8 * hi;
 #pragma unroll
         for (int ks = 0; ks < S::kKSteps; ++ks) {
             u32x4 w = ok ? load16(src + 16 * ks) : u32x4{0u, 0u, 0u, 0u};
-            qf[ks] = __builtin_bit_cast(bf16x8, w);
+            qf[ks] = __builtin_bit_cast(ex8, w);
         }
     };
     load_q_global();
@@ -324,8 +374,9 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
     // MFMAs issues nothing else.  Copy n of the block fills LDS slots
     // [64 n, 64 n + 64); lane l takes
     // slot 64 n + l = (row r, stored chunk c') and fetches source chunk
-    // c' ^ swizzle(r) of key row key0 + r.  The per-lane byte offsets within
-    // a block are fixed, so they are computed once.  In a block that runs
+    // c' ^ swizzle(r) of key row key0 + r (rows are row-stride bytes apart in
+    // HBM and DQK * 2 apart in LDS).  The per-lane byte offsets within a
+    // block are fixed, so they are computed once.  In a block that runs
     // past the last key, rows are clamped to the last key: those rows are
     // masked to -inf (K) or weighted by exactly 0 (V).
     const int wq = wave % kGroupWaves;  // index of the wave within its group
@@ -335,14 +386,14 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
         const int slot = 64 * (wq * S::kKCopies + i) + lane;
         const int r = slot / S::kChunksK;
         const int c = (slot - r * S::kChunksK) ^ kswz<DQK>(r);
-        koff[i] = r * kRowK + 16 * c;
+        koff[i] = r * k_rb + 16 * c;
     }
 #pragma unroll
     for (int i = 0; i < S::kVCopies; ++i) {
         const int slot = 64 * (wq * S::kVCopies + i) + lane;
         const int r = slot / S::kChunksV;
         const int c = (slot - r * S::kChunksV) ^ vswz<DV>(r);
-        voff_copy[i] = r * kRowV + 16 * c;
+        voff_copy[i] = r * v_rb + 16 * c;
     }
 
     // The block offset goes in the scalar offset operand and this wave's LDS
@@ -351,7 +402,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
     const int vdst = __builtin_amdgcn_readfirstlane(1024 * S::kVCopies * wq);
     auto copy_kblock = [&](__amdgpu_buffer_rsrc_t rs, int key0, unsigned char* dst)
                            __attribute__((always_inline)) {
-        const uint32_t blk = (uint32_t)key0 * kRowK;
+        const uint32_t blk = (uint32_t)key0 * k_rb;
         // an opaque copy of the wave's offset: the destinations are formed
         // here with one scalar add each, not precomputed for every buffer
         // and copy and held (or spilled) across the sweep
@@ -365,9 +416,9 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
             const int last = p.Lk - 1 - key0;
 #pragma unroll
             for (int i = 0; i < S::kKCopies; ++i) {
-                const int r = (int)koff[i] / kRowK;
+                const int r = (64 * (wq * S::kKCopies + i) + lane) / S::kChunksK;
                 const int rr = min(r, last);
-                copy_to_lds(rs, koff[i] - (uint32_t)((r - rr) * kRowK), blk,
+                copy_to_lds(rs, koff[i] - (uint32_t)((r - rr) * k_rb), blk,
                             dst + kd + 1024 * i);
             }
         }
@@ -377,7 +428,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
     };
     auto copy_v = [&](int jl, unsigned char* dst) __attribute__((always_inline)) {
         const int key0 = (jb0 + jl) * kBlockN;
-        const uint32_t blk = (uint32_t)key0 * kRowV;
+        const uint32_t blk = (uint32_t)key0 * v_rb;
         int vd = vdst;
         asm volatile("" : "+s"(vd));
         if (key0 + kBlockN <= p.Lk) {
@@ -388,9 +439,9 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
             const int last = p.Lk - 1 - key0;
 #pragma unroll
             for (int i = 0; i < S::kVCopies; ++i) {
-                const int r = (int)voff_copy[i] / kRowV;
+                const int r = (64 * (wq * S::kVCopies + i) + lane) / S::kChunksV;
                 const int rr = min(r, last);
-                copy_to_lds(vrsrc, voff_copy[i] - (uint32_t)((r - rr) * kRowV), blk,
+                copy_to_lds(vrsrc, voff_copy[i] - (uint32_t)((r - rr) * v_rb), blk,
                             dst + vd + 1024 * i);
             }
         }
@@ -441,14 +492,15 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
         ell = 0.0f;
         ell_o = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     };
-    bf16x8 sel;
+    ex8 sel;
     {
-        const __bf16 v = (((lane & 15) ^ (lane >> 4)) & 1) ? (__bf16)0.0f : (__bf16)1.0f;
+        using es = typename E::scalar;
+        const es v = (((lane & 15) ^ (lane >> 4)) & 1) ? (es)0.0f : (es)1.0f;
 #pragma unroll
         for (int i = 0; i < 8; ++i) sel[i] = v;
     }
     f32x16 s[kBlockN / 32];  // scores of the block between its M and V phases
-    bf16x8 pb[kBlockN / 16];  // its bf16 weights between its V and M phases
+    ex8 pb[kBlockN / 16];  // its 16-bit weights between its V and M phases
 
     // ---- MFMA phase M(j): O^T += V^T P^T for block j, then S^T = K Q^T for
     // block j + 1 (j = -1: scores of block 0 only) --------------------------
@@ -468,11 +520,11 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
             part[t] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                 (lds_i16x4*)(vl + vread[i] + (16 * g + 8 * t) * kRowV));
         return __builtin_bit_cast(
-            bf16x8, __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
+            ex8, __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
     };
     auto load_s = [&](int u, const unsigned char* kl) __attribute__((always_inline)) {
         const int ks = u / (kBlockN / 32), mb = u % (kBlockN / 32);
-        return *reinterpret_cast<const bf16x8*>(kl + kread[ks % kReadTable] +
+        return *reinterpret_cast<const ex8*>(kl + kread[ks % kReadTable] +
                                                 (ks / kReadTable) * kReadTable * 32 +
                                                 mb * 32 * kRowK);
     };
@@ -482,15 +534,14 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
         const f32x16 zero = {};
         // one MFMA unit: PV unit u < kPvUnits, else score unit u - kPvUnits; the
         // first k-step of a score block starts from an inline zero accumulator
-        auto mfma_unit = [&](int u, bf16x8 a) __attribute__((always_inline)) {
+        auto mfma_unit = [&](int u, ex8 a) __attribute__((always_inline)) {
             if (u < kPvUnits) {
                 const int g = u / S::kDvBlocks, i = u % S::kDvBlocks;
-                oacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[g], oacc[i], 0, 0, 0);
+                oacc[i] = E::mfma32(a, pb[g], oacc[i]);
             } else {
                 const int v = u - kPvUnits;
                 const int ks = v / (kBlockN / 32), mb = v % (kBlockN / 32);
-                s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], ks == 0 ? zero : s[mb],
-                                                                0, 0, 0);
+                s[mb] = E::mfma32(a, qf[ks], ks == 0 ? zero : s[mb]);
             }
         };
         // the bf16 row sums need no LDS operand: they run while the first
@@ -498,7 +549,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
         auto row_sums = [&]() __attribute__((always_inline)) {
 #pragma unroll
             for (int g = 0; g < kBlockN / 16; ++g)
-                ell_o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sel, pb[g], ell_o, 0, 0, 0);
+                ell_o = E::mfma16(sel, pb[g], ell_o);
             __builtin_amdgcn_sched_barrier(0);
         };
         if (do_pv || do_s) {
@@ -515,36 +566,36 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
                     return n < 2 * kPvUnits ? ((n & 1) ? kPvUnits + (n >> 1) : (n >> 1))
                                             : kPvUnits + n - kPvUnits;
                 };
-                bf16x8 ring[kAhead];
+                ex8 ring[kAhead];
 #pragma unroll
                 for (int n = 0; n < kAhead; ++n) ring[n] = load(order(n));
                 row_sums();
 #pragma unroll
                 for (int n = 0; n < kUnits; ++n) {
-                    const bf16x8 a = ring[n % kAhead];
+                    const ex8 a = ring[n % kAhead];
                     if (n + kAhead < kUnits) ring[n % kAhead] = load(order(n + kAhead));
                     mfma_unit(order(n), a);
                     __builtin_amdgcn_sched_barrier(0);
                 }
             } else if (do_pv) {
-                bf16x8 ring[kAhead];
+                ex8 ring[kAhead];
 #pragma unroll
                 for (int u = 0; u < kAhead; ++u) ring[u] = load(u);
                 row_sums();
 #pragma unroll
                 for (int u = 0; u < kPvUnits; ++u) {
-                    const bf16x8 a = ring[u % kAhead];
+                    const ex8 a = ring[u % kAhead];
                     if (u + kAhead < kPvUnits) ring[u % kAhead] = load(u + kAhead);
                     mfma_unit(u, a);
                     __builtin_amdgcn_sched_barrier(0);
                 }
             } else {
-                bf16x8 ring[kAhead];
+                ex8 ring[kAhead];
 #pragma unroll
                 for (int u = 0; u < kAhead; ++u) ring[u] = load(kPvUnits + u);
 #pragma unroll
                 for (int u = 0; u < kSUnits; ++u) {
-                    const bf16x8 a = ring[u % kAhead];
+                    const ex8 a = ring[u % kAhead];
                     if (u + kAhead < kSUnits) ring[u % kAhead] = load(kPvUnits + u + kAhead);
                     mfma_unit(kPvUnits + u, a);
                     __builtin_amdgcn_sched_barrier(0);
@@ -636,7 +687,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
                 f32x8 e;
 #pragma unroll
                 for (int i = 0; i < 8; ++i) e[i] = s[mb][8 * t + i];
-                pb[2 * mb + t] = __builtin_convertvector(e, bf16x8);
+                pb[2 * mb + t] = __builtin_convertvector(e, ex8);
             }
         ell += ((rs[0] + rs[1]) + (rs[2] + rs[3])) + ((rs[4] + rs[5]) + (rs[6] + rs[7]));
     };
@@ -694,7 +745,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
         const int r = sl / S::kChunksV;
         const int c = sl % S::kChunksV;
         const u32x4 x = *reinterpret_cast<const u32x4*>(slice + r * kRowQ + 16 * (c ^ kswz<DV>(r)));
-        if (r < pend_rows) *reinterpret_cast<u32x4*>(pend_dst + (size_t)r * DV + 8 * c) = x;
+        if (r < pend_rows) *reinterpret_cast<u32x4*>(pend_dst + (size_t)r * p.o_sr + 8 * c) = x;
     };
     // next tile: this wave's Q rows and the tile's first K block
     const uint16_t* nq_src = p.q;
@@ -707,13 +758,14 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
         const int r = sl / S::kChunksK;
         const int c = (sl % S::kChunksK) ^ kswz<DQK>(r);
         const int rr = min(r, nq_rows - 1);  // rows past Lq repeat the last row
-        const __amdgpu_buffer_rsrc_t rs = make_rsrc(uniform(nq_src), (uint32_t)kSlice);
-        copy_to_lds(rs, (uint32_t)(rr * kRowQ + 16 * c), 0, slice + 1024 * k);
+        const __amdgpu_buffer_rsrc_t rs =
+            make_rsrc(uniform(nq_src), (uint32_t)((kRowsPerWave - 1) * q_rb + kRowQ));
+        copy_to_lds(rs, (uint32_t)(rr * q_rb + 16 * c), 0, slice + 1024 * k);
     };
     auto load_q_slice = [&]() __attribute__((always_inline)) {
 #pragma unroll
         for (int ks = 0; ks < S::kKSteps; ++ks)
-            qf[ks] = *reinterpret_cast<const bf16x8*>(slice + kread[ks % kReadTable] +
+            qf[ks] = *reinterpret_cast<const ex8*>(slice + kread[ks % kReadTable] +
                                                       (ks / kReadTable) * kReadTable * 32);
     };
     // Pair u of the sweep (phases 2u, 2u + 1), 1 <= u <= nblk.  Output chunk
@@ -758,10 +810,10 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
             const KeyRange r = key_range<CAUSAL>(p, c);
             nk_copy = r.nblk > 0;
             nk_key0 = r.jb0 * kBlockN;
-            nk_rsrc = make_rsrc(p.k + (size_t)c.bk * p.Lk * DQK, (uint32_t)p.Lk * kRowK);
+            nk_rsrc = make_rsrc(p.k + c.kbase, (uint32_t)(p.Lk - 1) * k_rb + kRowK);
             if (kStage) {
                 nq_rows = max(0, min(kRowsPerWave, p.Lq - c.qw));
-                nq_src = p.q + (c.qrow0 + (nq_rows > 0 ? c.qw : 0)) * DQK;
+                nq_src = p.q + c.qbase + (size_t)(nq_rows > 0 ? c.qw : 0) * p.q_sr;
             }
         }
         reset_state();
@@ -843,7 +895,6 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
         const float ell_o_row = ((lane >> 4) & 1) ? ell_o[1] : ell_o[0];
         const float inv = ell_o_row > 0.0f ? 1.0f / ell_o_row : 0.0f;
         const float lse_row = ell_row > 0.0f ? ref * scale + logf(ell_row) : kNegInf;
-        typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
         if (o_part == nullptr) {
             if constexpr (kStage) {
                 // row l32 of the slice; this lane's 4 columns 32 i + 8 r4 + 4 hi
@@ -859,24 +910,24 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
                     for (int r4 = 0; r4 < 4; ++r4) {
                         f32x4 x = {oacc[i][4 * r4 + 0] * inv, oacc[i][4 * r4 + 1] * inv,
                                    oacc[i][4 * r4 + 2] * inv, oacc[i][4 * r4 + 3] * inv};
-                        const bf16x4 y = __builtin_convertvector(x, bf16x4);
-                        *reinterpret_cast<bf16x4*>(slice + orow * kRowQ +
+                        const ex4 y = __builtin_convertvector(x, ex4);
+                        *reinterpret_cast<ex4*>(slice + orow * kRowQ +
                                                    16 * ((4 * i + r4) ^ kswz<DV>(orow)) + 8 * hi) = y;
                     }
                 }
                 pend = 1;
                 pend_rows = max(0, min(kRowsPerWave, p.Lq - qw));
-                pend_dst = o_out + (qrow0 + (pend_rows > 0 ? qw : 0)) * DV;
+                pend_dst = o_out + orow_w;
             } else if (qi < p.Lq) {
-                uint16_t* orow = o_out + (qrow0 + qi) * DV;
+                uint16_t* orow = o_out + orow_w + (size_t)l32 * p.o_sr;
 #pragma unroll
                 for (int i = 0; i < S::kDvBlocks; ++i) {
 #pragma unroll
                     for (int r4 = 0; r4 < 4; ++r4) {
                         f32x4 x = {oacc[i][4 * r4 + 0] * inv, oacc[i][4 * r4 + 1] * inv,
                                    oacc[i][4 * r4 + 2] * inv, oacc[i][4 * r4 + 3] * inv};
-                        const bf16x4 y = __builtin_convertvector(x, bf16x4);
-                        *reinterpret_cast<bf16x4*>(orow + 32 * i + 8 * r4 + 4 * hi) = y;
+                        const ex4 y = __builtin_convertvector(x, ex4);
+                        *reinterpret_cast<ex4*>(orow + 32 * i + 8 * r4 + 4 * hi) = y;
                     }
                 }
             }
@@ -911,31 +962,38 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
     }
 }
 
-template <int DQK, int DV, bool CAUSAL, bool DEBUG>
+template <int DQK, int DV, bool CAUSAL, bool DEBUG, bool FP16>
 hipError_t launch_one(const FwdParams& p, hipStream_t stream) {
     dim3 grid((unsigned)p.grid), block(kThreads);
     FwdParams arg = p;
     void* args[] = {&arg};
-    return hipLaunchKernel(reinterpret_cast<const void*>(&attn_fwd_kernel<DQK, DV, CAUSAL, DEBUG>),
-                           grid, block, args, 0, stream);
+    return hipLaunchKernel(
+        reinterpret_cast<const void*>(&attn_fwd_kernel<DQK, DV, CAUSAL, DEBUG, FP16>), grid, block,
+        args, 0, stream);
 }
 
 template <int DQK, int DV>
-hipError_t launch_dims(const FwdParams& p, bool causal, bool debug, hipStream_t stream) {
+hipError_t launch_dims(const FwdParams& p, bool causal, bool debug, bool fp16,
+                       hipStream_t stream) {
+    if (fp16) {
+        if (debug) return hipErrorInvalidValue;  // the debug variant is bf16 only
+        return causal ? launch_one<DQK, DV, true, false, true>(p, stream)
+                      : launch_one<DQK, DV, false, false, true>(p, stream);
+    }
     if (causal)
-        return debug ? launch_one<DQK, DV, true, true>(p, stream)
-                     : launch_one<DQK, DV, true, false>(p, stream);
-    return debug ? launch_one<DQK, DV, false, true>(p, stream)
-                 : launch_one<DQK, DV, false, false>(p, stream);
+        return debug ? launch_one<DQK, DV, true, true, false>(p, stream)
+                     : launch_one<DQK, DV, true, false, false>(p, stream);
+    return debug ? launch_one<DQK, DV, false, true, false>(p, stream)
+                 : launch_one<DQK, DV, false, false, false>(p, stream);
 }
 
 }  // namespace
 
-hipError_t launch_fwd(const FwdParams& p, int dqk, int dv, bool causal, bool debug,
+hipError_t launch_fwd(const FwdParams& p, int dqk, int dv, bool causal, bool debug, bool fp16,
                       hipStream_t stream) {
-    if (dqk == 64 && dv == 64) return launch_dims<64, 64>(p, causal, debug, stream);
-    if (dqk == 128 && dv == 128) return launch_dims<128, 128>(p, causal, debug, stream);
-    if (dqk == 192 && dv == 128) return launch_dims<192, 128>(p, causal, debug, stream);
+    if (dqk == 64 && dv == 64) return launch_dims<64, 64>(p, causal, debug, fp16, stream);
+    if (dqk == 128 && dv == 128) return launch_dims<128, 128>(p, causal, debug, fp16, stream);
+    if (dqk == 192 && dv == 128) return launch_dims<192, 128>(p, causal, debug, fp16, stream);
     return hipErrorInvalidValue;
 }
 

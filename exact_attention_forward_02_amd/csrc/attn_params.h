@@ -17,10 +17,12 @@ constexpr int kRowsPerWave = 32;     // query rows owned by one wave (MFMA N)
 constexpr int kBlockN = 64;          // keys per K/V block
 
 struct FwdParams {
-    const uint16_t* q;   // [B, Hq, Lq, dqk] bf16
-    const uint16_t* k;   // [B, Hkv, Lk, dqk] bf16
-    const uint16_t* v;   // [B, Hkv, Lk, dv] bf16
-    uint16_t* o;         // [B, Hq, Lq, dv] bf16 (whole-key output), or
+    // q, k, v, o: 16-bit elements (bf16 or fp16), element (b, h, i, c) at
+    // b * s_b + h * s_h + i * s_r + c with the strides below
+    const uint16_t* q;   // [B, Hq, Lq, dqk]
+    const uint16_t* k;   // [B, Hkv, Lk, dqk]
+    const uint16_t* v;   // [B, Hkv, Lk, dv]
+    uint16_t* o;         // [B, Hq, Lq, dv] (whole-key output), or
     float* o_part;       // [n_split, B, Hq, Lq, dv] fp32 (per-split output) when set
     float* lse;          // [B, Hq, Lq] fp32, or [n_split, B, Hq, Lq] with o_part
     unsigned long long* rescale_count;  // optional event counter
@@ -42,13 +44,18 @@ struct FwdParams {
     int grid;       // workgroups launched; each processes tiles i, i + grid, ...
                     // (a multiple of 8 when smaller than the tile count)
 
+    long long q_sb, q_sh, k_sb, k_sh, v_sb, v_sh, o_sb, o_sh;  // batch and head strides
+    int q_sr, k_sr, v_sr, o_sr;  // row strides (elements); one K or V head spans
+                                 // less than 2^31 bytes (checked on the host)
+
     float scale;        // softmax scale (natural units), used for lse
     float scale_log2;   // scale * log2(e): base-2 exponent multiplier
     float threshold;    // conditional rescale threshold, log2 units
 };
 
-// Launches the forward kernel instantiation matching (dqk, dv, causal, debug).
-hipError_t launch_fwd(const FwdParams& p, int dqk, int dv, bool causal, bool debug,
+// Launches the forward kernel instantiation matching (dqk, dv, causal, debug,
+// element type); debug is bf16 only.
+hipError_t launch_fwd(const FwdParams& p, int dqk, int dv, bool causal, bool debug, bool fp16,
                       hipStream_t stream);
 
 // Merges n_split partial states per row: o_part [n_split, rows, dv] fp32,

@@ -56,9 +56,26 @@ enum attn_status {
     ATTN_ERR_NO_DEVICE = 8,             /* no HIP device is visible */
     ATTN_ERR_UNSUPPORTED_ARCH = 9,      /* the current device is not gfx950 */
     ATTN_ERR_HIP = 10,                  /* the HIP runtime reported an error at launch */
-    ATTN_ERR_BAD_ARGUMENT = 11          /* a debug-only argument, a split count or a
-                                           merge row count is out of range */
+    ATTN_ERR_BAD_ARGUMENT = 11,         /* a debug-only argument, a split count, a
+                                           merge row count or a dtype is out of range */
+    ATTN_ERR_BAD_STRIDE = 12            /* a stride is negative, not a multiple of 8
+                                           elements, or a row stride is below the
+                                           head dim */
 };
+
+/* Element types of attn_fwd_ex. */
+enum attn_dtype {
+    ATTN_DTYPE_BF16 = 0,
+    ATTN_DTYPE_FP16 = 1
+};
+
+/* Element strides of a [B, H, L, d] tensor whose head dim is contiguous:
+ * element (b, h, i, c) sits at b * batch + h * head + i * row + c. */
+typedef struct attn_strides {
+    long long batch;
+    long long head;
+    long long row;
+} attn_strides;
 
 /*
  * attn_fwd -- fused attention forward.
@@ -97,6 +114,35 @@ int attn_fwd_dbg(const void* q, const void* k, const void* v, void* o, float* ls
                  int B, int Hq, int Hkv, int Lq, int Lk, int d_qk, int d_v,
                  int causal, float scale, void* stream,
                  float rescale_threshold, unsigned long long* rescale_count);
+
+/*
+ * attn_fwd_ex -- attn_fwd for any element strides and for fp16 as well as
+ * bf16 elements.  "Flash Attention 4: 在 Blackwell 上把 Softmax 接进 Tensor
+ * Core 流水线" (fangpin gpu-hpc-book ch. 13), in the section with its usage
+ * example, calls the kernel on fp16 Q, K, V and O laid out [B, S, H, D]; with
+ * strides that layout is (batch, head, row) = (S*H*d, d, H*d), and the
+ * contiguous [B, H, L, d] layout of attn_fwd is (H*L*d, L*d, d).  Views into
+ * a packed QKV tensor work the same way.
+ *   q_strides, k_strides, v_strides, o_strides
+ *               element strides of the four tensors (the head dim is
+ *               contiguous).  Each stride is >= 0 and a multiple of 8
+ *               elements (so rows start 16-byte aligned); row strides are at
+ *               least the head dim.  One K or V head ((Lk - 1) * row + d
+ *               elements) and 32 rows of Q must span less than 2^31 bytes.
+ *               o must not overlap q, k, v or lse.
+ *   dtype       ATTN_DTYPE_BF16 or ATTN_DTYPE_FP16: the element type of q, k,
+ *               v and o.  The weights P enter the PV product in the same type
+ *               (fp16 has 3 more mantissa bits than bf16; P <= 2^8 fits its
+ *               range); accumulation is fp32 either way.
+ *   lse         float32 [B, Hq, Lq], contiguous, as in attn_fwd.
+ * Other arguments, ownership, asynchrony and errors as attn_fwd;
+ * ATTN_ERR_BAD_STRIDE for a stride outside the rules above,
+ * ATTN_ERR_BAD_ARGUMENT for another dtype.
+ */
+int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
+                int B, int Hq, int Hkv, int Lq, int Lk, int d_qk, int d_v,
+                attn_strides q_strides, attn_strides k_strides, attn_strides v_strides,
+                attn_strides o_strides, int dtype, int causal, float scale, void* stream);
 
 /*
  * Split-key path.  "Infra: Flash Attention" (section on prefill versus

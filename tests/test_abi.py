@@ -17,7 +17,7 @@ CODES = {
     "ATTN_OK": 0, "ATTN_ERR_NULL_PTR": 1, "ATTN_ERR_BAD_SHAPE": 2, "ATTN_ERR_GQA_RATIO": 3,
     "ATTN_ERR_UNSUPPORTED_HEAD_DIM": 4, "ATTN_ERR_BAD_SCALE": 5, "ATTN_ERR_MISALIGNED": 6,
     "ATTN_ERR_TOO_LARGE": 7, "ATTN_ERR_NO_DEVICE": 8, "ATTN_ERR_UNSUPPORTED_ARCH": 9,
-    "ATTN_ERR_HIP": 10, "ATTN_ERR_BAD_ARGUMENT": 11,
+    "ATTN_ERR_HIP": 10, "ATTN_ERR_BAD_ARGUMENT": 11, "ATTN_ERR_BAD_STRIDE": 12,
 }
 
 
@@ -39,8 +39,8 @@ def _exported_symbols(path):
 
 
 def test_header_declares_the_entry_points():
-    assert {"attn_fwd", "attn_fwd_dbg", "attn_split_keys", "attn_fwd_split", "attn_merge",
-            "attn_status_string", "attn_abi_version"} <= _declared_functions()
+    assert {"attn_fwd", "attn_fwd_dbg", "attn_fwd_ex", "attn_split_keys", "attn_fwd_split",
+            "attn_merge", "attn_status_string", "attn_abi_version"} <= _declared_functions()
 
 
 def test_status_codes_match_header():
@@ -59,7 +59,7 @@ def test_library_exports_every_declared_function():
 
 def test_abi_version_and_status_strings():
     lib = _binding.library()
-    assert lib.attn_abi_version() == 2
+    assert lib.attn_abi_version() == 3
     for code in CODES.values():
         s = _binding.status_string(code)
         assert s and s != "unknown attn status"
@@ -186,3 +186,52 @@ def test_valid_split_and_merge_without_a_gpu_report_no_device():
         pytest.skip("a GPU is present")
     assert _call_split(4) == CODES["ATTN_ERR_NO_DEVICE"]
     assert _call_merge() == CODES["ATTN_ERR_NO_DEVICE"]
+
+
+# attn_fwd_ex: [B, S, H, d] strides of the GOOD shape (B1 Hq4 Hkv2 L64 d128)
+def _bshd(H, L, d):
+    return _binding.Strides(L * H * d, d, H * d)
+
+
+def _call_ex(dtype=0, qs=None, ks=None, vs=None, os_=None, **over):
+    args = dict(GOOD)
+    args.update(over)
+    a = [args[n] for n in ORDER]
+    qs = qs or _bshd(args["Hq"], args["Lq"], args["d_qk"])
+    ks = ks or _bshd(args["Hkv"], args["Lk"], args["d_qk"])
+    vs = vs or _bshd(args["Hkv"], args["Lk"], args["d_v"])
+    os_ = os_ or _bshd(args["Hq"], args["Lq"], args["d_v"])
+    return _binding.library().attn_fwd_ex(*a[:12], qs, ks, vs, os_, dtype, a[12], a[13], a[14])
+
+
+def test_strided_entry_point_is_validated_first():
+    S = _binding.Strides
+    assert _call_ex(dtype=2) == CODES["ATTN_ERR_BAD_ARGUMENT"]
+    assert _call_ex(dtype=-1) == CODES["ATTN_ERR_BAD_ARGUMENT"]
+    assert _call_ex(q=None) == CODES["ATTN_ERR_NULL_PTR"]
+    assert _call_ex(o=A * 4 + 2) == CODES["ATTN_ERR_MISALIGNED"]
+    # negative, not a multiple of 8 elements, rows closer than the head dim
+    assert _call_ex(qs=S(-4 * 64 * 128, 128, 4 * 128)) == CODES["ATTN_ERR_BAD_STRIDE"]
+    assert _call_ex(ks=S(2 * 64 * 128, 132, 2 * 128)) == CODES["ATTN_ERR_BAD_STRIDE"]
+    assert _call_ex(vs=S(2 * 64 * 128, 128, 120)) == CODES["ATTN_ERR_BAD_STRIDE"]
+    assert _call_ex(os_=S(4 * 64 * 128, 128, 4 * 128 + 4)) == CODES["ATTN_ERR_BAD_STRIDE"]
+    # one K head spanning 2^31 bytes or more
+    assert _call_ex(ks=S(0, 0, 2 ** 25)) == CODES["ATTN_ERR_TOO_LARGE"]
+    # the contiguous [B, H, L, d] strides are accepted like attn_fwd's
+    import torch
+
+    if not torch.cuda.is_available():
+        bhsd = dict(qs=S(4 * 64 * 128, 64 * 128, 128), ks=S(2 * 64 * 128, 64 * 128, 128),
+                    vs=S(2 * 64 * 128, 64 * 128, 128), os_=S(4 * 64 * 128, 64 * 128, 128))
+        assert _call_ex(**bhsd) == CODES["ATTN_ERR_NO_DEVICE"]
+        assert _call_ex(dtype=1) == CODES["ATTN_ERR_NO_DEVICE"]
+
+
+def test_python_strided_binding_rejects_bad_tensors():
+    import torch
+
+    q = torch.zeros((1, 8, 2, 64), dtype=torch.float16).transpose(1, 2)
+    with pytest.raises((ValueError, TypeError)):
+        _binding.attn_fwd_ex(q, q, q)  # CPU tensors are refused before any call
+    with pytest.raises(TypeError):
+        _binding.attn_fwd_ex(q.float(), q, q)
