@@ -239,6 +239,11 @@ def main() -> int:
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain copy kernel of known size (3 launches) to "
                          "calibrate the FETCH_SIZE / WRITE_SIZE counters")
+    ap.add_argument("--dtype", choices=("bf16", "fp16"), default="bf16",
+                    help="element type of q, k, v and o (fp16 runs through attn_fwd_ex)")
+    ap.add_argument("--layout", choices=("bhsd", "bshd"), default="bhsd",
+                    help="storage of q, k, v and o: [B, H, L, d] or [B, S, H, d] (the "
+                         "latter runs through attn_fwd_ex with strides)")
     ap.add_argument("--splits", type=int, default=0,  # decode_l32k is timed with 4
                     help="time the split-key path instead (attn_fwd_split with this many "
                          "key splits, then attn_merge); reported against the HBM roofline")
@@ -251,7 +256,7 @@ def main() -> int:
 
     import torch
 
-    from exact_attention_forward_02_amd import attn_fwd
+    from exact_attention_forward_02_amd import attn_fwd, attn_fwd_ex
     from exact_attention_forward_02_amd.inputs import WORKLOADS, workload_qkv
 
     if args.copy_calibration:
@@ -267,12 +272,26 @@ def main() -> int:
     qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
     if args.splits > 0:
         return bench_split(args, w, qd, kd, vd)
-    o = torch.empty((w.B, w.Hq, w.Lq, w.dv), dtype=torch.bfloat16, device=dev)
+    variant = args.dtype != "bf16" or args.layout != "bhsd"
+    if variant:
+        # the same draws, carried in the requested type and storage
+        et = torch.float16 if args.dtype == "fp16" else torch.bfloat16
+        q, k, v = (t.float().to(et) for t in (q, k, v))
+        qd, kd, vd = (t.to(dev) for t in (q, k, v))
+        if args.layout == "bshd":
+            qd, kd, vd = (t.transpose(1, 2).contiguous().transpose(1, 2) for t in (qd, kd, vd))
+            o = torch.empty((w.B, w.Lq, w.Hq, w.dv), dtype=et, device=dev).transpose(1, 2)
+        else:
+            o = torch.empty((w.B, w.Hq, w.Lq, w.dv), dtype=et, device=dev)
+        fwd = attn_fwd_ex
+    else:
+        o = torch.empty((w.B, w.Hq, w.Lq, w.dv), dtype=torch.bfloat16, device=dev)
+        fwd = attn_fwd
     lse = torch.empty((w.B, w.Hq, w.Lq), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
 
     for _ in range(args.warmup):
-        attn_fwd(qd, kd, vd, causal=w.causal, out=o, lse=lse, stream=stream)
+        fwd(qd, kd, vd, causal=w.causal, out=o, lse=lse, stream=stream)
     torch.cuda.synchronize()
 
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
@@ -281,7 +300,7 @@ def main() -> int:
     t0 = time.perf_counter()
     for i in range(args.steps):
         starts[i].record(stream)
-        attn_fwd(qd, kd, vd, causal=w.causal, out=o, lse=lse, stream=stream)
+        fwd(qd, kd, vd, causal=w.causal, out=o, lse=lse, stream=stream)
         ends[i].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -292,7 +311,8 @@ def main() -> int:
     flops = w.flops()
     value = flops * args.steps / wall / 1e12
     achieved = flops / (ms_launch * 1e-3) / 1e12
-    traffic = measured_traffic(w.name)
+    # the stored counter record covers the default bf16 [B, H, L, d] run
+    traffic = None if variant else measured_traffic(w.name)
 
     result = {
         "metric": METRIC,
@@ -305,11 +325,11 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": args.dtype,
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Lq": w.Lq,
                    "Lk": w.Lk, "d_qk": w.dqk, "d_v": w.dv, "causal": w.causal,
-                   "flops_per_step": flops},
+                   "layout": args.layout, "flops_per_step": flops},
         "pct_of_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "roofline": {
             "bound": "mfma",
