@@ -95,6 +95,10 @@ class Oracle:
             ctypes.c_int]
         lib.oracle_widen.restype = ctypes.c_double
         lib.oracle_widen.argtypes = [ctypes.c_uint16, ctypes.c_int]
+        lib.oracle_attn_bwd.restype = ctypes.c_int
+        lib.oracle_attn_bwd.argtypes = [
+            _ptr, _ptr, _ptr, _ptr, _i64, _i64, _i64, _i64, _i64, _i64, _i64,
+            ctypes.c_int, ctypes.c_double, ctypes.c_int, _ptr, _ptr, _ptr, _ptr, ctypes.c_int]
         lib.oracle_merge_states.restype = ctypes.c_int
         lib.oracle_merge_states.argtypes = [_ptr, _ptr, _i64, _i64, _i64, _ptr, _ptr]
         lib.oracle_online_rows.restype = ctypes.c_int
@@ -151,6 +155,33 @@ class Oracle:
         if rc != 0:
             raise ValueError(f"oracle_attn_rows rejected its arguments (code {rc})")
         return o, lse
+
+    def attn_bwd(self, q, k, v, dout, causal: bool, scale: float | None = None,
+                 threads: int = 0):
+        """Exact gradients (float64) of <dO, O> for the definition:
+        dq [B,Hq,Lq,dqk], dk [B,Hkv,Lk,dqk], dv [B,Hkv,Lk,dv], delta [B,Hq,Lq]
+        (delta_i = sum_j P_ij dP_ij = dO_i . O_i).  Inputs bf16 or fp16 [B,H,L,d]."""
+        ins = [_as_bits_elem(t) for t in (q, k, v, dout)]
+        elems = {e for _, e in ins}
+        if len(elems) != 1:
+            raise TypeError("q, k, v and dout must have one element type")
+        (qb, _), (kb, _), (vb, _), (gb, _) = ins
+        B, Hq, Hkv, Lq, Lk, dqk, dv = self._shapes(qb, kb, vb)
+        if gb.shape != (B, Hq, Lq, dv):
+            raise ValueError(f"dout must be [B, Hq, Lq, d_v], got {gb.shape}")
+        if scale is None:
+            scale = 1.0 / math.sqrt(dqk)
+        dq = np.empty((B, Hq, Lq, dqk), dtype=np.float64)
+        dk = np.empty((B, Hkv, Lk, dqk), dtype=np.float64)
+        dvo = np.empty((B, Hkv, Lk, dv), dtype=np.float64)
+        delta = np.empty((B, Hq, Lq), dtype=np.float64)
+        rc = self._lib.oracle_attn_bwd(
+            qb.ctypes.data, kb.ctypes.data, vb.ctypes.data, gb.ctypes.data,
+            B, Hq, Hkv, Lq, Lk, dqk, dv, int(bool(causal)), float(scale), elems.pop(),
+            dq.ctypes.data, dk.ctypes.data, dvo.ctypes.data, delta.ctypes.data, int(threads))
+        if rc != 0:
+            raise ValueError(f"oracle_attn_bwd rejected its arguments (code {rc})")
+        return dq, dk, dvo, delta
 
     def widen(self, bits: int, elem: int) -> float:
         """The oracle's exact widening of one 16-bit pattern (ELEM_BF16 / ELEM_FP16)."""

@@ -579,3 +579,132 @@ int oracle_online_rows(const uint16_t* q, const uint16_t* k, const uint16_t* v,
         *n_rescale = events;
     return failed ? 7 : 0;
 }
+
+/* ------------------------------------------------------------------------ */
+/* 3. The backward pass: gradients of the definition.                       */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * oracle_attn_bwd: dQ, dK, dV of L(Q, K, V) = <dO, O(Q, K, V)> for the
+ * definition above, following the backward section of "Infra: Flash
+ * Attention" (gradients by recomputation):
+ *     P = softmax(scale * Q K^T)              (rows over the visible keys)
+ *     dV = P^T dO,   dP = dO V^T,
+ *     D_i = sum_j P_ij dP_ij                  (= dO_i . O_i),
+ *     dS_ij = P_ij (dP_ij - D_i),
+ *     dQ = scale * dS K,   dK = scale * dS^T Q.
+ * With grouped-query attention a K/V head's dK and dV sum the contributions
+ * of all query heads it serves.  A row with no visible key contributes
+ * nothing.  Inputs are 16-bit bit patterns (elem as in
+ * oracle_attn_rows_elem): q, k, v, dout contiguous [B, H, L, d]; outputs in
+ * double: dq [B, Hq, Lq, dqk], dk [B, Hkv, Lk, dqk], dv [B, Hkv, Lk, dv], and
+ * delta [B, Hq, Lq] (the D_i above).  Parallel over (b, K/V head).
+ */
+int oracle_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                    const uint16_t* dout, int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq,
+                    int64_t Lk, int64_t dqk, int64_t dv, int causal, double scale, int elem,
+                    double* dq, double* dk, double* dvo, double* delta, int n_threads)
+{
+    dims_t d = {B, Hq, Hkv, Lq, Lk, dqk, dv, causal, scale, elem};
+    if (elem != ELEM_BF16 && elem != ELEM_FP16)
+        return 8;
+    int rc = check_dims(&d);
+    if (rc)
+        return rc;
+    if (!q || !k || !v || !dout || !dq || !dk || !dvo || !delta)
+        return 4;
+#ifdef _OPENMP
+    if (n_threads > 0)
+        omp_set_num_threads(n_threads);
+#else
+    (void)n_threads;
+#endif
+    const int64_t group = Hq / Hkv;
+    int failed = 0;
+#pragma omp parallel
+    {
+        double* qd = (double*)malloc(sizeof(double) * (size_t)dqk);
+        double* gd = (double*)malloc(sizeof(double) * (size_t)dv);
+        double* p = (double*)malloc(sizeof(double) * (size_t)Lk);
+        double* dp = (double*)malloc(sizeof(double) * (size_t)Lk);
+        int ok = qd && gd && p && dp;
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t bk = 0; bk < B * Hkv; ++bk) {
+            if (!ok) {
+#pragma omp atomic write
+                failed = 1;
+                continue;
+            }
+            const int64_t b = bk / Hkv, hk = bk % Hkv;
+            const uint16_t* kh = k + bk * Lk * dqk;
+            const uint16_t* vh = v + bk * Lk * dv;
+            double* dkh = dk + bk * Lk * dqk;
+            double* dvh = dvo + bk * Lk * dv;
+            for (int64_t t = 0; t < Lk * dqk; ++t)
+                dkh[t] = 0.0;
+            for (int64_t t = 0; t < Lk * dv; ++t)
+                dvh[t] = 0.0;
+            for (int64_t h = hk * group; h < (hk + 1) * group; ++h) {
+                for (int64_t i = 0; i < Lq; ++i) {
+                    const int64_t r = (b * Hq + h) * Lq + i;
+                    const uint16_t* qrow = q + r * dqk;
+                    const uint16_t* grow = dout + r * dv;
+                    double* dqrow = dq + r * dqk;
+                    for (int64_t c = 0; c < dqk; ++c)
+                        dqrow[c] = 0.0;
+                    const int64_t n = valid_keys(&d, i);
+                    if (n == 0) {
+                        delta[r] = 0.0;
+                        continue;
+                    }
+                    for (int64_t c = 0; c < dqk; ++c)
+                        qd[c] = widen(&d, qrow[c]);
+                    for (int64_t c = 0; c < dv; ++c)
+                        gd[c] = widen(&d, grow[c]);
+                    /* P_i. over the visible keys (safe softmax) */
+                    double m = -INFINITY;
+                    for (int64_t j = 0; j < n; ++j) {
+                        double dot = 0.0;
+                        for (int64_t c = 0; c < dqk; ++c)
+                            dot += qd[c] * widen(&d, kh[j * dqk + c]);
+                        p[j] = scale * dot;
+                        if (p[j] > m)
+                            m = p[j];
+                    }
+                    double l = 0.0;
+                    for (int64_t j = 0; j < n; ++j) {
+                        p[j] = exp(p[j] - m);
+                        l += p[j];
+                    }
+                    for (int64_t j = 0; j < n; ++j)
+                        p[j] /= l;
+                    /* dP_ij = dO_i . V_j and D_i = sum_j P_ij dP_ij */
+                    double di = 0.0;
+                    for (int64_t j = 0; j < n; ++j) {
+                        double dot = 0.0;
+                        for (int64_t c = 0; c < dv; ++c)
+                            dot += gd[c] * widen(&d, vh[j * dv + c]);
+                        dp[j] = dot;
+                        di += p[j] * dot;
+                    }
+                    delta[r] = di;
+                    for (int64_t j = 0; j < n; ++j) {
+                        const double ds = p[j] * (dp[j] - di);
+                        /* dV_j += P_ij dO_i;  dK_j += scale dS_ij Q_i;  dQ_i += scale dS_ij K_j */
+                        for (int64_t c = 0; c < dv; ++c)
+                            dvh[j * dv + c] += p[j] * gd[c];
+                        for (int64_t c = 0; c < dqk; ++c) {
+                            dkh[j * dqk + c] += scale * ds * qd[c];
+                            dqrow[c] += scale * ds * widen(&d, kh[j * dqk + c]);
+                        }
+                    }
+                }
+            }
+        }
+        free(qd);
+        free(gd);
+        free(p);
+        free(dp);
+    }
+    return failed ? 7 : 0;
+}

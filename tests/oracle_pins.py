@@ -17,7 +17,9 @@ AssertionError when the oracle disagrees with:
     definition for any cut of the keys,
   * the 16-bit input formats: the widening of every bf16 and fp16 bit pattern
     (numpy's own conversions), fp16 inputs against torch's float64 SDPA, and
-    values exact in both formats giving identical results.
+    values exact in both formats giving identical results,
+  * the backward pass: gradients against float64 autograd through torch's
+    SDPA, D_i = dO_i . O_i, rows without keys, and sum_j dK_j = 0.
 They run unchanged against deliberately broken copies of the oracle in
 test_oracle_mutations.py, which checks that each planted mistake trips at
 least one pin.
@@ -522,6 +524,84 @@ def pin_fp16_equals_bf16_on_shared_values(orc):
             f"fp16 and bf16 carriers of the same values differ (causal={causal})"
 
 
+# --------------------------------------------------------------------------
+# Backward pass
+# --------------------------------------------------------------------------
+
+BWD_SHAPES = [
+    # B, Hq, Hkv, Lq, Lk, dqk, dv, causal
+    (1, 2, 2, 17, 23, 8, 8, False),
+    (2, 4, 2, 24, 24, 16, 8, True),     # GQA 2, causal square
+    (1, 3, 1, 9, 30, 8, 16, True),      # MQA, Lq < Lk
+    (1, 2, 2, 5, 40, 64, 64, False),
+]
+
+
+def _bwd_inputs(shape, seed, dtype=torch.bfloat16):
+    B, Hq, Hkv, Lq, Lk, dqk, dv, _ = shape
+    q, k, v = make_qkv(B, Hq, Hkv, Lq, Lk, dqk, dv, seed=seed)
+    g = torch.Generator().manual_seed(seed + 1)
+    dout = torch.randn((B, Hq, Lq, dv), generator=g).to(torch.bfloat16)
+    return [t.float().to(dtype) for t in (q, k, v, dout)]
+
+
+def _autograd_reference(q, k, v, dout, causal, scale):
+    """float64 autograd through torch's SDPA (GQA by repeating K/V heads, whose
+    gradients autograd sums back), bottom-right causal as an explicit mask."""
+    Hq, Lq, Hkv, Lk = q.shape[1], q.shape[2], k.shape[1], k.shape[2]
+    qd, kd, vd = (t.double().requires_grad_(True) for t in (q, k, v))
+    rep = Hq // Hkv
+    kr, vr = kd.repeat_interleave(rep, dim=1), vd.repeat_interleave(rep, dim=1)
+    o = F.scaled_dot_product_attention(qd, kr, vr, attn_mask=_visible(Lq, Lk, causal),
+                                       scale=scale)
+    o.backward(dout.double())
+    return qd.grad.numpy(), kd.grad.numpy(), vd.grad.numpy(), o.detach()
+
+
+def pin_bwd_library_autograd(orc):
+    """dQ, dK, dV against float64 autograd through torch's SDPA."""
+    for idx, shape in enumerate(BWD_SHAPES):
+        causal = shape[7]
+        q, k, v, dout = _bwd_inputs(shape, 400 + idx)
+        scale = 1.0 / math.sqrt(shape[5])
+        dq, dk, dv, delta = orc.attn_bwd(q, k, v, dout, causal=causal, scale=scale)
+        want_dq, want_dk, want_dv, o = _autograd_reference(q, k, v, dout, causal, scale)
+        for name, got, want in (("dq", dq, want_dq), ("dk", dk, want_dk), ("dv", dv, want_dv)):
+            tol = 1e-11 * max(1.0, float(np.abs(want).max()))
+            _close(got, want, tol, f"shape {idx} {name} vs autograd")
+        # D_i = dO_i . O_i, with O from the same autograd forward
+        _close(delta, (dout.double() * o).sum(-1).numpy(), 1e-11, f"shape {idx} delta = dO.O")
+
+
+def pin_bwd_fp16_and_empty_rows(orc):
+    """fp16 inputs, and Lq > Lk causal: rows without keys get dQ = 0 and add
+    nothing to dK, dV, which equal autograd's on the rows that do see keys."""
+    shape = (1, 2, 1, 30, 12, 16, 16, True)
+    for dtype in (torch.bfloat16, torch.float16):
+        q, k, v, dout = _bwd_inputs(shape, 77, dtype)
+        scale = 0.25
+        dq, dk, dv, delta = orc.attn_bwd(q, k, v, dout, causal=True, scale=scale)
+        first = shape[3] - shape[4]  # rows before this one see no key
+        assert np.all(dq[:, :, :first] == 0.0) and np.all(delta[:, :, :first] == 0.0)
+        want_dq, want_dk, want_dv, _ = _autograd_reference(
+            q[:, :, first:], k, v, dout[:, :, first:], True, scale)
+        for name, got, want in (("dq", dq[:, :, first:], want_dq), ("dk", dk, want_dk),
+                                ("dv", dv, want_dv)):
+            _close(got, want, 1e-11 * max(1.0, float(np.abs(want).max())),
+                   f"{dtype} {name} with empty rows")
+
+
+def pin_bwd_dk_sums_to_zero(orc):
+    """Each row of dS sums to zero (softmax gradient), so the dK rows of a K/V
+    head sum to zero under any mask."""
+    for idx, shape in enumerate(BWD_SHAPES):
+        q, k, v, dout = _bwd_inputs(shape, 500 + idx)
+        _, dk, _, _ = orc.attn_bwd(q, k, v, dout, causal=shape[7])
+        col = dk.sum(axis=2)  # sum over keys
+        _close(col, np.zeros_like(col), 1e-11 * max(1.0, float(np.abs(dk).max())),
+               f"shape {idx} sum_j dK_j")
+
+
 ALL_PINS = [
     pin_worked_example,
     pin_conditional_cases,
@@ -542,4 +622,7 @@ ALL_PINS = [
     pin_widening_exhaustive,
     pin_fp16_library_sdpa,
     pin_fp16_equals_bf16_on_shared_values,
+    pin_bwd_library_autograd,
+    pin_bwd_fp16_and_empty_rows,
+    pin_bwd_dk_sums_to_zero,
 ]

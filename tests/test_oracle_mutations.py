@@ -40,6 +40,14 @@ MUTATIONS = {
                            "v = ldexp((double)(1024 + f), e - 24);"),
     "fp16_subnormal_scale": ("v = ldexp((double)f, -24);", "v = ldexp((double)f, -25);"),
     "fp16_sign_dropped": ("return (bits & 0x8000) ? -v : v;", "return v;"),
+    "bwd_delta_dropped": ("const double ds = p[j] * (dp[j] - di);",
+                          "const double ds = p[j] * dp[j];"),
+    "bwd_dv_transposed": ("dvh[j * dv + c] += p[j] * gd[c];",
+                          "dvh[j * dv + c] += p[j] * gd[dv - 1 - c];"),
+    "bwd_dk_unscaled": ("dkh[j * dqk + c] += scale * ds * qd[c];",
+                        "dkh[j * dqk + c] += ds * qd[c];"),
+    "bwd_gqa_first_head_only": ("for (int64_t h = hk * group; h < (hk + 1) * group; ++h) {",
+                                "for (int64_t h = hk * group; h < hk * group + 1; ++h) {"),
     "fp16_read_as_bf16": ("return d->elem == ELEM_FP16 ? fp16_bits_to_double(bits) : "
                           "bf16_bits_to_double(bits);", "return bf16_bits_to_double(bits);"),
 }
