@@ -228,6 +228,83 @@ def bench_split(args, w, qd, kd, vd) -> int:
     return 0
 
 
+def bench_backward(args, w, qd, kd, vd) -> int:
+    """The backward pass: per step one attn_bwd call (three kernels: D, then
+    dK/dV, then dQ) on the forward's o and lse.  Its algorithmic work is the
+    five products of the backward (S recomputed, dP, dV, dK, dQ), each as
+    large as one of the forward's two: 2.5 times the forward's FLOPs."""
+    import torch
+
+    from exact_attention_forward_02_amd import attn_bwd, attn_fwd
+
+    if w.dqk != w.dv or w.dqk not in (64, 128):
+        print(f"the backward supports d_qk == d_v in (64, 128); {w.name} has "
+              f"({w.dqk}, {w.dv})", file=sys.stderr)
+        return 2
+    dev = qd.device
+    stream = torch.cuda.current_stream(dev)
+    g = torch.Generator().manual_seed(w.seed + 1)
+    dout = torch.randn((w.B, w.Hq, w.Lq, w.dv), generator=g).to(torch.bfloat16).to(dev)
+    o, lse = attn_fwd(qd, kd, vd, causal=w.causal, stream=stream)
+    dq, dk, dv = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
+    delta = torch.empty_like(lse)
+
+    def step():
+        attn_bwd(qd, kd, vd, o, lse, dout, causal=w.causal, dq=dq, dk=dk, dv=dv, delta=delta,
+                 stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    ms_launch = sum(launch_ms) / len(launch_ms)
+    flops = 2.5 * w.flops()
+    value = flops * args.steps / wall / 1e12
+    achieved = flops / (ms_launch * 1e-3) / 1e12
+    result = {
+        "metric": "attention bwd TFLOP/s (bf16, 1 GPU) and % of MI355X dense bf16 MFMA peak",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Lq": w.Lq,
+                   "Lk": w.Lk, "d_qk": w.dqk, "d_v": w.dv, "causal": w.causal,
+                   "pass": "backward", "flops_per_step": flops},
+        "pct_of_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": None,
+            "kernel": "attn_bwd (D, dK/dV and dQ kernels)",
+            "ms_per_launch": round(ms_launch, 4),
+            "ms_per_launch_min": round(min(launch_ms), 4),
+            "ms_per_launch_max": round(max(launch_ms), 4),
+        },
+    }
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -247,6 +324,9 @@ def main() -> int:
     ap.add_argument("--splits", type=int, default=0,  # decode_l32k is timed with 4
                     help="time the split-key path instead (attn_fwd_split with this many "
                          "key splits, then attn_merge); reported against the HBM roofline")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the backward pass (attn_bwd on the forward's o and lse) "
+                         "instead of the forward")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -272,6 +352,8 @@ def main() -> int:
     qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
     if args.splits > 0:
         return bench_split(args, w, qd, kd, vd)
+    if args.backward:
+        return bench_backward(args, w, qd, kd, vd)
     variant = args.dtype != "bf16" or args.layout != "bhsd"
     if variant:
         # the same draws, carried in the requested type and storage

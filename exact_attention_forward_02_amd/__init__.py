@@ -3,12 +3,13 @@
 ``attn_fwd(q, k, v, causal=False, scale=None) -> (o, lse)`` runs the
 hand-written HIP kernel through the C ABI in include/attn_fwd.h;
 ``attn_fwd_ex`` takes strided views (e.g. [B, S, H, d] layouts) in bf16 or
-fp16.  The
+fp16; ``attn_bwd`` computes the gradients by recomputation from lse.  The
 split-key path (``attn_fwd_split``, ``attn_merge``, ``attn_fwd_splitkv``)
 computes the same result from per-split states merged afterwards.
 """
-from ._binding import (attn_fwd, attn_fwd_dbg, attn_fwd_ex, attn_fwd_split,  # noqa: F401
-                       attn_fwd_splitkv, attn_merge, library, split_keys, status_string)
+from ._binding import (attn_bwd, attn_fwd, attn_fwd_dbg, attn_fwd_ex,  # noqa: F401
+                       attn_fwd_split, attn_fwd_splitkv, attn_merge, library, split_keys,
+                       status_string)
 
-__all__ = ["attn_fwd", "attn_fwd_dbg", "attn_fwd_ex", "attn_fwd_split", "attn_merge",
-           "attn_fwd_splitkv", "split_keys", "library", "status_string"]
+__all__ = ["attn_fwd", "attn_fwd_dbg", "attn_fwd_ex", "attn_bwd", "attn_fwd_split",
+           "attn_merge", "attn_fwd_splitkv", "split_keys", "library", "status_string"]

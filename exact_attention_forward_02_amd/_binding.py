@@ -49,6 +49,8 @@ def _load():
         lib.attn_fwd_ex.restype = i
         lib.attn_fwd_ex.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i,
                                     Strides, Strides, Strides, Strides, i, i, ctypes.c_float, vp]
+        lib.attn_bwd.restype = i
+        lib.attn_bwd.argtypes = [vp] * 10 + [i] * 8 + [ctypes.c_float, vp]
         lib.attn_split_keys.restype = i
         lib.attn_split_keys.argtypes = [i, i]
         lib.attn_fwd_split.restype = i
@@ -209,6 +211,41 @@ def attn_fwd_ex(q, k, v, causal: bool = False, scale: float | None = None, out=N
     if rc != ATTN_OK:
         raise RuntimeError(f"attn_fwd_ex failed: {status_string(rc)} (code {rc})")
     return out, lse
+
+
+def attn_bwd(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = None,
+             dq=None, dk=None, dv=None, delta=None, stream=None):
+    """dq, dk, dv (and delta = rowsum(dout * o)) of the attention forward pass
+    that produced o and lse from q, k, v: contiguous bf16 [B, H, L, d] tensors,
+    d_qk == d_v in (64, 128)."""
+    lib = _load()
+    B, Hq, Hkv, Lq, Lk, dqk, dvd = _check_inputs(q, k, v)
+    for name, t, shape in (("o", o, (B, Hq, Lq, dvd)), ("dout", dout, (B, Hq, Lq, dvd))):
+        if (not isinstance(t, torch.Tensor) or t.dtype != torch.bfloat16 or t.device != q.device
+                or tuple(t.shape) != shape or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous bf16 {shape} tensor on q's device")
+    if (lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq, Lq) or not lse.is_contiguous()
+            or lse.device != q.device):
+        raise ValueError("lse must be the forward's contiguous fp32 [B, Hq, Lq] tensor")
+    if scale is None:
+        scale = 1.0 / math.sqrt(dqk)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    delta = torch.empty_like(lse) if delta is None else delta
+    for name, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v), ("delta", delta, lse)):
+        if t.shape != ref.shape or t.dtype != ref.dtype or not t.is_contiguous() \
+                or t.device != q.device:
+            raise ValueError(f"{name} must be a contiguous tensor like {tuple(ref.shape)}")
+    with torch.cuda.device(q.device):
+        s = stream if stream is not None else torch.cuda.current_stream(q.device)
+        rc = lib.attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                          dout.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                          dv.data_ptr(), delta.data_ptr(), B, Hq, Hkv, Lq, Lk, dqk, dvd,
+                          int(bool(causal)), float(scale), s.cuda_stream)
+    if rc != ATTN_OK:
+        raise RuntimeError(f"attn_bwd failed: {status_string(rc)} (code {rc})")
+    return dq, dk, dv, delta
 
 
 def split_keys(Lk: int, n_split: int) -> int:

@@ -16,7 +16,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 3;
+constexpr int kAbiVersion = 4;
 constexpr int kMaxSplits = 4096;
 constexpr int kMaxDevices = 64;
 constexpr int kXcds = 8;                 // MI355X: 8 accelerator complex dies
@@ -259,6 +259,49 @@ int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse
     const Strides st = {q_strides, k_strides, v_strides, o_strides};
     return run(q, k, v, o, lse, B, Hq, Hkv, Lq, Lk, d_qk, d_v, causal, scale, stream,
                kDefaultThreshold, nullptr, false, 0, &st, dtype == ATTN_DTYPE_FP16);
+}
+
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+             const float* lse, void* dq, void* dk, void* dv, float* delta, int B, int Hq, int Hkv,
+             int Lq, int Lk, int d_qk, int d_v, int causal, float scale, void* stream) {
+    if (!dout || !dq || !dk || !dv || !delta) return ATTN_ERR_NULL_PTR;
+    // the forward's argument rules, with o and lse as inputs here
+    int rc = check_args(q, k, v, o, lse, B, Hq, Hkv, Lq, Lk, d_qk, d_v, scale);
+    if (rc != ATTN_OK) return rc;
+    if (!(d_qk == d_v && (d_qk == 64 || d_qk == 128))) return ATTN_ERR_UNSUPPORTED_HEAD_DIM;
+    if (!aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) ||
+        !aligned(delta, 4))
+        return ATTN_ERR_MISALIGNED;
+    const Strides st = contiguous_strides(Hq, Hkv, Lq, Lk, d_qk, d_v);
+    rc = check_strides(st, B, Hq, Hkv, Lq, Lk, d_qk, d_v);
+    if (rc != ATTN_OK) return rc;
+    if ((long long)B * Hkv * ((Lk + 127) / 128) > INT32_MAX ||
+        (long long)B * Hq * ((Lq + 127) / 128) > INT32_MAX)
+        return ATTN_ERR_TOO_LARGE;
+    rc = check_device();
+    if (rc != ATTN_OK) return rc;
+    attn::BwdParams p;
+    memset(&p, 0, sizeof p);
+    p.q = static_cast<const uint16_t*>(q);
+    p.k = static_cast<const uint16_t*>(k);
+    p.v = static_cast<const uint16_t*>(v);
+    p.o = static_cast<const uint16_t*>(o);
+    p.dout = static_cast<const uint16_t*>(dout);
+    p.lse = lse;
+    p.delta = delta;
+    p.dq = static_cast<uint16_t*>(dq);
+    p.dk = static_cast<uint16_t*>(dk);
+    p.dv = static_cast<uint16_t*>(dv);
+    p.B = B;
+    p.Hq = Hq;
+    p.Hkv = Hkv;
+    p.Lq = Lq;
+    p.Lk = Lk;
+    p.G = Hq / Hkv;
+    p.scale = scale;
+    p.scale_log2 = (float)((double)scale * 1.4426950408889634);
+    hipError_t err = attn::launch_bwd(p, d_qk, causal != 0, static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
 int attn_split_keys(int Lk, int n_split) {

@@ -58,6 +58,24 @@ struct FwdParams {
 hipError_t launch_fwd(const FwdParams& p, int dqk, int dv, bool causal, bool debug, bool fp16,
                       hipStream_t stream);
 
+// Backward pass (contiguous [B, H, L, d] bf16 tensors, d_qk == d_v).
+struct BwdParams {
+    const uint16_t* q;     // [B, Hq, Lq, d]
+    const uint16_t* k;     // [B, Hkv, Lk, d]
+    const uint16_t* v;     // [B, Hkv, Lk, d]
+    const uint16_t* o;     // [B, Hq, Lq, d]  forward output
+    const uint16_t* dout;  // [B, Hq, Lq, d]  gradient of the loss w.r.t. o
+    const float* lse;      // [B, Hq, Lq]     forward lse
+    float* delta;          // [B, Hq, Lq]     D_i = dO_i . O_i (written)
+    uint16_t* dq;          // [B, Hq, Lq, d]
+    uint16_t* dk;          // [B, Hkv, Lk, d]
+    uint16_t* dv;          // [B, Hkv, Lk, d]
+    int B, Hq, Hkv, Lq, Lk, G;
+    float scale, scale_log2;
+};
+
+hipError_t launch_bwd(const BwdParams& p, int d, bool causal, hipStream_t stream);
+
 // Merges n_split partial states per row: o_part [n_split, rows, dv] fp32,
 // lse_part [n_split, rows] -> o [rows, dv] bf16, lse [rows].
 hipError_t launch_merge(const float* o_part, const float* lse_part, uint16_t* o, float* lse,

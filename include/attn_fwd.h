@@ -196,6 +196,33 @@ int attn_fwd_split(const void* q, const void* k, const void* v, float* o_part, f
 int attn_merge(const float* o_part, const float* lse_part, void* o, float* lse,
                int n_split, long long rows, int d_v, void* stream);
 
+/*
+ * attn_bwd -- gradients of the attention forward pass ("Infra: Flash
+ * Attention", sections on why the backward pass recomputes and on computing
+ * the gradients block by block): for a loss L with dL/dO = dout,
+ *     P = exp(scale * Q K^T - lse)   (recomputed from the forward's lse),
+ *     dV = P^T dout,  dP = dout V^T,  D_i = dout_i . o_i,
+ *     dS = P (dP - D),  dQ = scale * dS K,  dK = scale * dS^T Q,
+ * with the same causal mask and grouped-query head mapping as attn_fwd (a
+ * K/V head's dK and dV sum over the query heads it serves).
+ *   q, k, v, o, lse  as attn_fwd's inputs and outputs (contiguous [B, H, L, d]
+ *                    bf16; lse float32 [B, Hq, Lq]) from the forward call
+ *   dout             bfloat16 [B, Hq, Lq, d_v]
+ *   dq               bfloat16 [B, Hq, Lq, d_qk] (output)
+ *   dk, dv           bfloat16 [B, Hkv, Lk, d_qk] and [B, Hkv, Lk, d_v] (output)
+ *   delta            float32 [B, Hq, Lq] (output, and the kernels' scratch:
+ *                    D_i = dout_i . o_i)
+ *   d_qk == d_v, 64 or 128 (ATTN_ERR_UNSUPPORTED_HEAD_DIM otherwise)
+ * All pointers are caller-owned device pointers; outputs must not overlap
+ * the inputs or each other; every 16-bit tensor is 16-byte aligned, lse and
+ * delta 4-byte aligned.  Three kernels are enqueued on `stream`; errors as
+ * attn_fwd.
+ */
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+             const float* lse, void* dq, void* dk, void* dv, float* delta,
+             int B, int Hq, int Hkv, int Lq, int Lk, int d_qk, int d_v,
+             int causal, float scale, void* stream);
+
 /* attn_status_string -- static, NUL-terminated description of a status code
  * (never NULL; unknown codes give "unknown attn status"). */
 const char* attn_status_string(int status);

@@ -39,7 +39,7 @@ def _exported_symbols(path):
 
 
 def test_header_declares_the_entry_points():
-    assert {"attn_fwd", "attn_fwd_dbg", "attn_fwd_ex", "attn_split_keys", "attn_fwd_split",
+    assert {"attn_fwd", "attn_fwd_dbg", "attn_fwd_ex", "attn_bwd", "attn_split_keys", "attn_fwd_split",
             "attn_merge", "attn_status_string", "attn_abi_version"} <= _declared_functions()
 
 
@@ -59,7 +59,7 @@ def test_library_exports_every_declared_function():
 
 def test_abi_version_and_status_strings():
     lib = _binding.library()
-    assert lib.attn_abi_version() == 3
+    assert lib.attn_abi_version() == 4
     for code in CODES.values():
         s = _binding.status_string(code)
         assert s and s != "unknown attn status"
@@ -235,3 +235,44 @@ def test_python_strided_binding_rejects_bad_tensors():
         _binding.attn_fwd_ex(q, q, q)  # CPU tensors are refused before any call
     with pytest.raises(TypeError):
         _binding.attn_fwd_ex(q.float(), q, q)
+
+
+BWD_ORDER = ["q", "k", "v", "o", "dout", "lse", "dq", "dk", "dv", "delta", "B", "Hq", "Hkv",
+             "Lq", "Lk", "d_qk", "d_v", "causal", "scale", "stream"]
+
+
+def _call_bwd(**over):
+    args = dict(GOOD, dout=A * 6, dq=A * 7, dk=A * 8, dv=A * 9, delta=A * 10)
+    args.update(over)
+    return _binding.library().attn_bwd(*[args[n] for n in BWD_ORDER])
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(dout=None), "ATTN_ERR_NULL_PTR"),
+    (dict(dq=None), "ATTN_ERR_NULL_PTR"),
+    (dict(dk=None), "ATTN_ERR_NULL_PTR"),
+    (dict(dv=None), "ATTN_ERR_NULL_PTR"),
+    (dict(delta=None), "ATTN_ERR_NULL_PTR"),
+    (dict(q=None), "ATTN_ERR_NULL_PTR"),
+    (dict(lse=None), "ATTN_ERR_NULL_PTR"),
+    (dict(Lq=0), "ATTN_ERR_BAD_SHAPE"),
+    (dict(Hq=6, Hkv=4), "ATTN_ERR_GQA_RATIO"),
+    (dict(d_qk=192, d_v=128), "ATTN_ERR_UNSUPPORTED_HEAD_DIM"),  # forward only
+    (dict(d_qk=96, d_v=96), "ATTN_ERR_UNSUPPORTED_HEAD_DIM"),
+    (dict(scale=float("nan")), "ATTN_ERR_BAD_SCALE"),
+    (dict(dout=A * 6 + 2), "ATTN_ERR_MISALIGNED"),
+    (dict(dq=A * 7 + 8), "ATTN_ERR_MISALIGNED"),
+    (dict(delta=A * 10 + 2), "ATTN_ERR_MISALIGNED"),
+    (dict(B=2 ** 16, Hq=2 ** 8, Hkv=2 ** 8, Lq=2 ** 8), "ATTN_ERR_TOO_LARGE"),
+])
+def test_backward_arguments_are_validated_first(over, code):
+    assert _call_bwd(**over) == CODES[code]
+
+
+def test_valid_backward_call_without_a_gpu_reports_no_device():
+    import torch
+
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert _call_bwd() == CODES["ATTN_ERR_NO_DEVICE"]
+    assert _call_bwd(d_qk=64, d_v=64, causal=1) == CODES["ATTN_ERR_NO_DEVICE"]
