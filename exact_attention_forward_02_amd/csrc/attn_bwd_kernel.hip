@@ -17,6 +17,9 @@
 //                          wave owns 32 query rows, holds its Q and dO rows as
 //                          MFMA operands, and streams K/V blocks through LDS,
 //                          like the forward pass.
+// Both main kernels stream their blocks of 64 rows through two LDS stages,
+// filled by direct-to-LDS buffer copies while the other stage is computed on,
+// with one barrier per block.
 // MFMA v_mfma_f32_32x32x16_bf16 with fp32 accumulation.  Operand A is read
 // from LDS (rows with ds_read_b128, transposed with ds_read_b64_tr_b16);
 // operand B is a register fragment: the wave's own K/V or Q/dO rows, or the
@@ -45,34 +48,86 @@ constexpr int kBlk = 64;          // rows of a staged Q/dO (or K/V) block
 constexpr float kLog2e = 1.4426950408889634f;
 
 // LDS block layout: row r of D bf16, 16-byte chunk c stored at c ^ swz(r).
-// The swizzle depends on r mod 4 only, so the transposed reads (4 rows at a
-// time) and the row reads both address any 4-aligned row group the same way.
+// Each block is read two ways: by rows (ds_read_b128, 16 lanes reading one
+// chunk column of 16 consecutive rows) and transposed (ds_read_b64_tr_b16,
+// 32 lanes reading 8 bytes of 4 consecutive rows at 4 adjacent chunks).
+// With 64 banks of 4 bytes, the row read is conflict-free when the 16 rows
+// land on 16 distinct bank groups, and the transposed read when the 4 rows
+// have distinct chunk bits 2-3 (d = 128); for d = 64 two rows share the bank
+// space.  These swizzles satisfy both (swz(r) depends on r mod 16).
 template <int D>
 __device__ __forceinline__ int swz(int r) {
-    const int q = r & 3;
-    return (D == 128) ? (4 * q + 2 * (q >> 1)) : (4 * (q & 1) + 2 * (q >> 1));
+    return (D == 128) ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
 }
 
 __device__ __forceinline__ u32x4 load16(const uint16_t* p) {
     return *reinterpret_cast<const u32x4*>(p);
 }
 
-// Stage rows [row0, row0 + 64) of a [L, D] head (rows past L repeat row
-// L - 1; callers mask them) into an LDS block.
-template <int D>
-__device__ __forceinline__ void stage_rows(const uint16_t* head, int row0, int L,
-                                           unsigned char* dst, int tid) {
-    constexpr int kChunks = D / 8;
-#pragma unroll
-    for (int n = 0; n < kBlk * kChunks / kBwdThreads; ++n) {
-        const int c = tid + n * kBwdThreads;
-        const int r = c / kChunks;
-        const int ch = c % kChunks;
-        const int row = min(row0 + r, L - 1);
-        const u32x4 x = load16(head + (size_t)row * D + 8 * ch);
-        *reinterpret_cast<u32x4*>(dst + r * (D * 2) + 16 * (ch ^ swz<D>(r))) = x;
-    }
+// Copy 16 (or 4) bytes per lane from global memory straight into LDS through
+// a buffer descriptor: lane l reads at byte voff of the buffer and its data
+// lands at lds_dst + 16 l (4 l), one contiguous KiB (256 bytes) per wave.
+typedef __attribute__((address_space(3))) void lds_void;
+__device__ __forceinline__ void copy16_to_lds(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff,
+                                              void* lds_dst) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)lds_dst, 16, voff, 0, 0, 0);
 }
+__device__ __forceinline__ void copy4_to_lds(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff,
+                                             void* lds_dst) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)lds_dst, 4, voff, 0, 0, 0);
+}
+
+// Barrier after which every wave's copies issued so far have landed: each
+// wave first waits for all of its own outstanding memory operations (the
+// compiler's own waits before a barrier do not cover LDS written by a copy).
+__device__ __forceinline__ void wait_copies_and_sync() {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+}
+
+// A wave-uniform pointer held in VGPRs, moved to SGPRs.
+template <typename T>
+__device__ __forceinline__ const T* uniform(const T* p) {
+    const uint64_t v = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return reinterpret_cast<const T*>(((uint64_t)hi << 32) | lo);
+}
+
+// Raw buffer descriptor over [base, base + bytes): 32-bit data format, no stride.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+
+// The copies that fill one LDS block of 64 rows of a [L, D] head: 16-byte
+// slot s of the block (row s / (D / 8), position s % (D / 8)) holds chunk
+// position ^ swz(row) of that row, so the copy that writes slot s reads that
+// chunk.  Each of the 4 waves issues kCopies copies of 64 slots; rows past L
+// read row L - 1 (their products are masked by the caller).
+template <int D>
+struct BlockCopies {
+    static constexpr int kChunks = D / 8;
+    static constexpr int kCopies = kBlk * kChunks / 64 / (kBwdThreads / 64);
+    int slot0;  // this lane's slot in the wave's first copy
+    int dst;    // this wave's first copy, bytes into the block
+
+    __device__ __forceinline__ void init(int wave, int lane) {
+        slot0 = 64 * kCopies * wave + lane;
+        dst = __builtin_amdgcn_readfirstlane(1024 * kCopies * wave);
+    }
+    // rows [row0, row0 + 64) of the head that rs covers (L rows) into blk
+    __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t rs, int row0, int L,
+                                          unsigned char* blk) const {
+#pragma unroll
+        for (int i = 0; i < kCopies; ++i) {
+            const int slot = slot0 + 64 * i;
+            const int r = slot / kChunks;
+            const uint32_t col = 16u * (uint32_t)((slot % kChunks) ^ swz<D>(r));
+            const uint32_t off = (uint32_t)min(row0 + r, L - 1) * (D * 2) + col;
+            copy16_to_lds(rs, off, blk + dst + 1024 * i);
+        }
+    }
+};
 
 // A operand from rows of an LDS block: lane l reads row m0 + (l & 31),
 // elements 16 ks + 8 (l >> 5) .. +7.
@@ -83,30 +138,53 @@ __device__ __forceinline__ bf16x8 row_frag(const unsigned char* blk, int m0, int
     return *reinterpret_cast<const bf16x8*>(blk + m * (D * 2) + 16 * (ch ^ swz<D>(m)));
 }
 
-// Per-lane byte offset of the transposed reads: with 16-lane group g = l / 16
-// and index 4 r + j inside it, the lane reads 8 bytes of row 4 (g / 2) + r at
-// columns 32 i + 16 (g & 1) + 4 j .. + 3 (i added by the caller).
+// Per-lane byte offsets of the transposed reads: with 16-lane group g = l / 16
+// and index 4 r + j inside it, the lane reads 8 bytes of row 4 (g / 2) + r
+// (+ 8 for the second read) at columns 32 i + 16 (g & 1) + 4 j .. + 3.  The
+// swizzle of a row depends on it mod 16, so both reads get their own offset;
+// the block offset 16 g' added later keeps the row mod 16.
 template <int D>
-__device__ __forceinline__ int tr_offset(int lane, int i) {
-    const int tg = lane >> 4, ti = lane & 15, tr = ti >> 2, tj = ti & 3;
-    const int row = 4 * (tg >> 1) + tr;
-    const int cl = 2 * (tg & 1) + (tj >> 1);
-    return row * (D * 2) + 16 * ((4 * i + cl) ^ swz<D>(row)) + 8 * (tj & 1);
-}
+struct TrOffsets {
+    int off[D / 32][2];
+    __device__ __forceinline__ void init(int lane) {
+        const int tg = lane >> 4, ti = lane & 15, tr = ti >> 2, tj = ti & 3;
+        const int cl = 2 * (tg & 1) + (tj >> 1);
+#pragma unroll
+        for (int i = 0; i < D / 32; ++i)
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const int row = 4 * (tg >> 1) + tr + 8 * t;
+                off[i][t] = row * (D * 2) + 16 * ((4 * i + cl) ^ swz<D>(row)) + 8 * (tj & 1);
+            }
+    }
+};
 
 // A operand = (block rows 16 g .. 16 g + 15)^T, columns 32 i .. 32 i + 31:
 // lane l receives column 32 i + (l & 31) at the 8 rows whose values the
 // B fragment g (rows 8 (r >> 2) + 4 (l >> 5) + (r & 3) of an accumulator)
 // carries in the same order.
 template <int D>
-__device__ __forceinline__ bf16x8 tr_frag(const unsigned char* blk, int off, int g) {
+__device__ __forceinline__ bf16x8 tr_frag(const unsigned char* blk, const TrOffsets<D>& tro,
+                                          int i, int g) {
     i16x4 part[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t)
         part[t] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_i16x4*)(blk + off + (16 * g + 8 * t) * (D * 2)));
+            (lds_i16x4*)(blk + tro.off[i][t] + 16 * g * (D * 2)));
     return __builtin_bit_cast(bf16x8,
                               __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// Workgroup order.  The hardware deals workgroups round-robin over the 8
+// XCDs (workgroup x to XCD x % 8), each with its own L2.  Without a causal
+// mask every workgroup does the same work, and the index is remapped so that
+// each XCD runs a contiguous range of logical indices: the workgroups of one
+// head run on one XCD at about the same time and share that head's blocks in
+// its L2.  With the mask, the index is kept, and the caller orders logical
+// indices from the most work to the least (longest first).
+__device__ __forceinline__ int xcd_contiguous(int x, int n) {
+    const int q = n / 8, r = n % 8, k = x % 8;
+    return k * q + min(k, r) + x / 8;
 }
 
 __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
@@ -140,16 +218,27 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kBwdThreads, 1) void attn_bwd_dkdv_kernel(const BwdParams p) {
     constexpr int kKs = D / 16;   // k-steps over the head dim
     constexpr int kDb = D / 32;   // 32-wide output blocks
-    __shared__ __attribute__((aligned(1024))) unsigned char qbuf[kBlk * D * 2];
-    __shared__ __attribute__((aligned(1024))) unsigned char dobuf[kBlk * D * 2];
-    __shared__ __attribute__((aligned(16))) float lsebuf[kBlk];
-    __shared__ __attribute__((aligned(16))) float dbuf[kBlk];
+    // two stages of (Q block, dO block, lse, D), filled by direct-to-LDS copies
+    __shared__ __attribute__((aligned(1024))) unsigned char qbuf0[kBlk * D * 2];
+    __shared__ __attribute__((aligned(1024))) unsigned char dobuf0[kBlk * D * 2];
+    __shared__ __attribute__((aligned(1024))) unsigned char qbuf1[kBlk * D * 2];
+    __shared__ __attribute__((aligned(1024))) unsigned char dobuf1[kBlk * D * 2];
+    __shared__ __attribute__((aligned(256))) float lse0[kBlk], dl0[kBlk], lse1[kBlk], dl1[kBlk];
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int l32 = lane & 31, hi = lane >> 5;
     const int nkb = (p.Lk + 127) / 128;
-    const int bk = blockIdx.x / nkb;  // b * Hkv + kv head
-    const int kb = blockIdx.x % nkb;
+    const int nbk = p.B * p.Hkv;
+    int bk, kb;  // b * Hkv + kv head, and the key block
+    if (CAUSAL) {
+        // the first key blocks see the most query rows
+        kb = blockIdx.x / nbk;
+        bk = blockIdx.x % nbk;
+    } else {
+        const int x = xcd_contiguous(blockIdx.x, nbk * nkb);
+        bk = x / nkb;
+        kb = x % nkb;
+    }
     const int b = bk / p.Hkv, hk = bk % p.Hkv;
     const int key0 = kb * 128 + wave * 32;  // this wave's first key
     const int key = key0 + l32;             // the key of this lane's accumulator column
@@ -171,78 +260,151 @@ __global__ __launch_bounds__(kBwdThreads, 1) void attn_bwd_dkdv_kernel(const Bwd
     for (int i = 0; i < kDb; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r) dkt[i][r] = dvt[i][r] = 0.0f;
-    int tro[kDb];
-#pragma unroll
-    for (int i = 0; i < kDb; ++i) tro[i] = tr_offset<D>(lane, i);
+    TrOffsets<D> tro;
+    tro.init(lane);
+    BlockCopies<D> cp;
+    cp.init(wave, lane);
 
-    // causal: queries before qstart see none of this workgroup's keys
+    // causal: query blocks before qb0 see none of this workgroup's keys
     int qb0 = 0;
     if (CAUSAL) qb0 = max(0, kb * 128 - off) / kBlk;
     const int nqb = (p.Lq + kBlk - 1) / kBlk;
+    const int nq = nqb - qb0;   // query blocks per head, >= 1
+    const int nt = p.G * nq;    // steps: (query head of the group, query block)
+    const size_t head0 = (size_t)(b * p.Hq + hk * p.G) * p.Lq;
+
+    // stage t: Q and dO rows of its block by every wave, lse by wave 0 and
+    // D by wave 1 (one 4-byte copy of 64 rows each)
+    auto issue = [&](int t, unsigned char* qb, unsigned char* dob, float* lb, float* db)
+                     __attribute__((always_inline)) {
+        const int g = t / nq;
+        const int i0 = (qb0 + t % nq) * kBlk;
+        const size_t r0 = head0 + (size_t)g * p.Lq;
+        const uint32_t bytes = (uint32_t)p.Lq * (D * 2);
+        cp.issue(make_rsrc(uniform(p.q + r0 * D), bytes), i0, p.Lq, qb);
+        cp.issue(make_rsrc(uniform(p.dout + r0 * D), bytes), i0, p.Lq, dob);
+        if (wave < 2) {
+            const float* src = wave == 0 ? p.lse : p.delta;
+            float* dst = wave == 0 ? lb : db;
+            copy4_to_lds(make_rsrc(uniform(src + r0), (uint32_t)p.Lq * 4),
+                           (uint32_t)min(i0 + lane, p.Lq - 1) * 4, dst);
+        }
+    };
+    // One step (64 query rows = sub-blocks 0 and 1 of 32 rows) is a sequence
+    // of 64 MFMA units, each with one LDS operand:
+    //   units  0..15  S(0), dP(0)        A = Q / dO rows of sub-block 0
+    //   units 16..31  S(1), dP(1)        (sub-block 1), with P(0), dS(0) formed
+    //                                    one element per unit on the VALU
+    //   units 32..47  dV(0), dK(0)       A = dO^T / Q^T of sub-block 0, B = P(0) /
+    //                                    dS(0), with P(1), dS(1) formed likewise
+    //   units 48..63  dV(1), dK(1)
+    // Operands are loaded kAhead units before their MFMA into a register ring
+    // and scheduling barriers keep that order, so LDS latency and the
+    // softmax arithmetic overlap earlier MFMAs instead of stalling each one.
+    constexpr int kAhead = 4;
+    constexpr int kUnits = 64;
+    // query rows i that see this lane's key: i >= imin (and i < Lq); none
+    // for a key past Lk
+    const int imin = key >= p.Lk ? INT32_MAX : (CAUSAL ? key - off : INT32_MIN);
     const f32x16 zero = {};
-    for (int g = 0; g < p.G; ++g) {
-        const size_t qrow0 = (size_t)(b * p.Hq + hk * p.G + g) * p.Lq;
-        for (int qb = qb0; qb < nqb; ++qb) {
-            const int i0 = qb * kBlk;
-            __syncthreads();  // the previous block's reads are done
-            stage_rows<D>(p.q + qrow0 * D, i0, p.Lq, qbuf, tid);
-            stage_rows<D>(p.dout + qrow0 * D, i0, p.Lq, dobuf, tid);
-            if (tid < kBlk) {
-                const int i = min(i0 + tid, p.Lq - 1);
-                lsebuf[tid] = p.lse[qrow0 + i];
-                dbuf[tid] = p.delta[qrow0 + i];
+    f32x16 sacc[2], dpacc[2], pv, dsv;
+    bf16x8 pb[2][2], db[2][2];
+    f32x4 l4[4], d4[4];
+    auto load = [&](int n, const unsigned char* qbuf, const unsigned char* dobuf)
+                    __attribute__((always_inline)) {
+        const int u = n & 15, sub = (n >> 4) & 1;
+        if (n < 32)  // S / dP unit: k-step u >> 1 of sub-block sub
+            return row_frag<D>((u & 1) ? dobuf : qbuf, 32 * sub, u >> 1, lane);
+        // dV / dK unit: rows 16 (2 sub + t2) .., output block i
+        const int t2 = u >> 3, i = (u >> 1) & 3;
+        return tr_frag<D>((u & 1) ? qbuf : dobuf, tro, i % kDb, 2 * sub + t2);
+    };
+    auto mfma_unit = [&](int n, bf16x8 a) __attribute__((always_inline)) {
+        const int u = n & 15, sub = (n >> 4) & 1;
+        if (n < 32) {
+            const int ks = u >> 1;
+            if (ks < kKs) {
+                if (u & 1)
+                    dpacc[sub] = mfma(a, vf[ks], ks == 0 ? zero : dpacc[sub]);
+                else
+                    sacc[sub] = mfma(a, kf[ks], ks == 0 ? zero : sacc[sub]);
             }
-            __syncthreads();
-#pragma unroll
-            for (int sub = 0; sub < kBlk / 32; ++sub) {
-                const int m0 = 32 * sub;
-                // every key of this wave is past the last query of the sub-block
-                if (CAUSAL && key0 > i0 + m0 + 31 + off) continue;
-                f32x16 s = zero, dp = zero;
-#pragma unroll
-                for (int ks = 0; ks < kKs; ++ks) {
-                    s = mfma(row_frag<D>(qbuf, m0, ks, lane), kf[ks], s);
-                    dp = mfma(row_frag<D>(dobuf, m0, ks, lane), vf[ks], dp);
-                }
-                // P and dS at rows i0 + m0 + acc_row(r), column key
-                f32x16 pv, ds;
-#pragma unroll
-                for (int g4 = 0; g4 < 4; ++g4) {
-                    const f32x4 l4 = *reinterpret_cast<const f32x4*>(lsebuf + m0 + 8 * g4 + 4 * hi);
-                    const f32x4 d4 = *reinterpret_cast<const f32x4*>(dbuf + m0 + 8 * g4 + 4 * hi);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int r = 4 * g4 + e;
-                        const int i = i0 + m0 + acc_row(r, hi);
-                        bool ok = i < p.Lq && key < p.Lk;
-                        if (CAUSAL) ok = ok && key <= i + off;
-                        const float pr =
-                            ok ? __builtin_amdgcn_exp2f(s[r] * c2 - l4[e] * kLog2e) : 0.0f;
-                        pv[r] = pr;
-                        ds[r] = pr * (dp[r] - d4[e]);
-                    }
-                }
-                bf16x8 pb[2], db[2];
-#pragma unroll
-                for (int t = 0; t < 2; ++t) {
-                    f32x8 e1, e2;
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        e1[e] = pv[8 * t + e];
-                        e2[e] = ds[8 * t + e];
-                    }
-                    pb[t] = __builtin_convertvector(e1, bf16x8);
-                    db[t] = __builtin_convertvector(e2, bf16x8);
-                }
-                // dV^T += dO^T P,  dK^T += Q^T dS  (fragment 2 sub + t = rows 16 (2 sub + t) ..)
-#pragma unroll
-                for (int t = 0; t < 2; ++t)
-#pragma unroll
-                    for (int i = 0; i < kDb; ++i) {
-                        dvt[i] = mfma(tr_frag<D>(dobuf, tro[i], 2 * sub + t), pb[t], dvt[i]);
-                        dkt[i] = mfma(tr_frag<D>(qbuf, tro[i], 2 * sub + t), db[t], dkt[i]);
-                    }
+        } else {
+            const int t2 = u >> 3, i = (u >> 1) & 3;
+            if (i < kDb) {
+                if (u & 1)
+                    dkt[i] = mfma(a, db[sub][t2], dkt[i]);
+                else
+                    dvt[i] = mfma(a, pb[sub][t2], dvt[i]);
             }
+        }
+    };
+    // P and dS of sub-block sub at accumulator element r (row i0 + 32 sub +
+    // acc_row(r), column key); after elements 7 and 15, their bf16 fragments
+    auto softmax_elem = [&](int sub, int r, int i0) __attribute__((always_inline)) {
+        const int i = i0 + 32 * sub + acc_row(r, hi);
+        const bool ok = i >= imin && i < p.Lq;
+        const float pr = ok ? __builtin_amdgcn_exp2f(sacc[sub][r] * c2 - l4[r >> 2][r & 3] * kLog2e)
+                            : 0.0f;
+        pv[r] = pr;
+        dsv[r] = pr * (dpacc[sub][r] - d4[r >> 2][r & 3]);
+        if ((r & 7) == 7) {
+            const int t2 = r >> 3;
+            f32x8 e1, e2;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                e1[e] = pv[8 * t2 + e];
+                e2[e] = dsv[8 * t2 + e];
+            }
+            pb[sub][t2] = __builtin_convertvector(e1, bf16x8);
+            db[sub][t2] = __builtin_convertvector(e2, bf16x8);
+        }
+    };
+    auto load_rowstats = [&](int sub, const float* lsebuf, const float* dbuf)
+                             __attribute__((always_inline)) {
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+            l4[g4] = *reinterpret_cast<const f32x4*>(lsebuf + 32 * sub + 8 * g4 + 4 * hi);
+            d4[g4] = *reinterpret_cast<const f32x4*>(dbuf + 32 * sub + 8 * g4 + 4 * hi);
+        }
+    };
+    auto compute = [&](int t, const unsigned char* qbuf, const unsigned char* dobuf,
+                       const float* lsebuf, const float* dbuf) __attribute__((always_inline)) {
+        const int i0 = (qb0 + t % nq) * kBlk;
+        bf16x8 ring[kAhead];
+#pragma unroll
+        for (int n = 0; n < kAhead; ++n) ring[n] = load(n, qbuf, dobuf);
+        auto unit = [&](int n) __attribute__((always_inline)) {
+            const bf16x8 a = ring[n % kAhead];
+            if (n + kAhead < kUnits) ring[n % kAhead] = load(n + kAhead, qbuf, dobuf);
+            mfma_unit(n, a);
+            if (n >= 16 && n < 48) softmax_elem((n >> 4) - 1, n & 15, i0);
+            __builtin_amdgcn_sched_barrier(0);
+        };
+        // four loops of 16 units, each short enough to be unrolled in full
+#pragma unroll
+        for (int n = 0; n < 16; ++n) unit(n);
+        load_rowstats(0, lsebuf, dbuf);
+#pragma unroll
+        for (int n = 16; n < 32; ++n) unit(n);
+        load_rowstats(1, lsebuf, dbuf);
+#pragma unroll
+        for (int n = 32; n < 48; ++n) unit(n);
+#pragma unroll
+        for (int n = 48; n < 64; ++n) unit(n);
+    };
+    // One barrier per step: every wave's copies of stage t have landed (each
+    // wave waits for its own before the barrier) and every wave is done with
+    // stage t - 1, whose buffers the copies of stage t + 1 then refill.
+    issue(0, qbuf0, dobuf0, lse0, dl0);
+    for (int t = 0; t < nt; t += 2) {
+        wait_copies_and_sync();
+        if (t + 1 < nt) issue(t + 1, qbuf1, dobuf1, lse1, dl1);
+        compute(t, qbuf0, dobuf0, lse0, dl0);
+        if (t + 1 < nt) {
+            wait_copies_and_sync();
+            if (t + 2 < nt) issue(t + 2, qbuf0, dobuf0, lse0, dl0);
+            compute(t + 1, qbuf1, dobuf1, lse1, dl1);
         }
     }
     // lane holds key `key`, columns 32 i + 8 (r >> 2) + 4 hi + (r & 3)
@@ -267,17 +429,29 @@ __global__ __launch_bounds__(kBwdThreads, 1) void attn_bwd_dkdv_kernel(const Bwd
 
 // ---- dQ ----------------------------------------------------------------------
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kBwdThreads, 1) void attn_bwd_dq_kernel(const BwdParams p) {
+__global__ __launch_bounds__(kBwdThreads, 2) void attn_bwd_dq_kernel(const BwdParams p) {
     constexpr int kKs = D / 16;
     constexpr int kDb = D / 32;
-    __shared__ __attribute__((aligned(1024))) unsigned char kbuf[kBlk * D * 2];
-    __shared__ __attribute__((aligned(1024))) unsigned char vbuf[kBlk * D * 2];
+    // two stages of (K block, V block), filled by direct-to-LDS copies
+    __shared__ __attribute__((aligned(1024))) unsigned char kbuf0[kBlk * D * 2];
+    __shared__ __attribute__((aligned(1024))) unsigned char vbuf0[kBlk * D * 2];
+    __shared__ __attribute__((aligned(1024))) unsigned char kbuf1[kBlk * D * 2];
+    __shared__ __attribute__((aligned(1024))) unsigned char vbuf1[kBlk * D * 2];
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int l32 = lane & 31, hi = lane >> 5;
     const int nqb = (p.Lq + 127) / 128;
-    const int bh = blockIdx.x / nqb;  // b * Hq + query head
-    const int qb = blockIdx.x % nqb;
+    const int nbh = p.B * p.Hq;
+    int bh, qb;  // b * Hq + query head, and the query block
+    if (CAUSAL) {
+        // the last query blocks see the most keys
+        qb = nqb - 1 - (int)blockIdx.x / nbh;
+        bh = blockIdx.x % nbh;
+    } else {
+        const int x = xcd_contiguous(blockIdx.x, nbh * nqb);
+        bh = x / nqb;
+        qb = x % nqb;
+    }
     const int b = bh / p.Hq, hq = bh % p.Hq;
     const int bk = b * p.Hkv + hq / p.G;
     const int q0 = qb * 128 + wave * 32;  // this wave's first query
@@ -301,9 +475,10 @@ __global__ __launch_bounds__(kBwdThreads, 1) void attn_bwd_dq_kernel(const BwdPa
     for (int i = 0; i < kDb; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r) dqt[i][r] = 0.0f;
-    int tro[kDb];
-#pragma unroll
-    for (int i = 0; i < kDb; ++i) tro[i] = tr_offset<D>(lane, i);
+    TrOffsets<D> tro;
+    tro.init(lane);
+    BlockCopies<D> cp;
+    cp.init(wave, lane);
 
     // keys of the workgroup and of this wave
     int kend = p.Lk, wend = p.Lk;
@@ -312,16 +487,19 @@ __global__ __launch_bounds__(kBwdThreads, 1) void attn_bwd_dq_kernel(const BwdPa
         wend = min(p.Lk, min(p.Lq, q0 + 32) - 1 + off + 1);
     }
     const int nkb = kend > 0 ? (kend + kBlk - 1) / kBlk : 0;
-    const uint16_t* kh = p.k + (size_t)bk * p.Lk * D;
-    const uint16_t* vh = p.v + (size_t)bk * p.Lk * D;
+    const uint32_t bytes = (uint32_t)p.Lk * (D * 2);
+    const __amdgpu_buffer_rsrc_t krs = make_rsrc(uniform(p.k + (size_t)bk * p.Lk * D), bytes);
+    const __amdgpu_buffer_rsrc_t vrs = make_rsrc(uniform(p.v + (size_t)bk * p.Lk * D), bytes);
+    auto issue = [&](int jb, unsigned char* kbuf, unsigned char* vbuf)
+                     __attribute__((always_inline)) {
+        cp.issue(krs, jb * kBlk, p.Lk, kbuf);
+        cp.issue(vrs, jb * kBlk, p.Lk, vbuf);
+    };
     const f32x16 zero = {};
-    for (int jb = 0; jb < nkb; ++jb) {
+    auto compute = [&](int jb, const unsigned char* kbuf, const unsigned char* vbuf)
+                       __attribute__((always_inline)) {
         const int j0 = jb * kBlk;
-        __syncthreads();
-        stage_rows<D>(kh, j0, p.Lk, kbuf, tid);
-        stage_rows<D>(vh, j0, p.Lk, vbuf, tid);
-        __syncthreads();
-        if (q0 >= p.Lq || j0 >= wend) continue;  // no visible key of this block for the wave
+        if (q0 >= p.Lq || j0 >= wend) return;  // no visible key of this block for the wave
         bf16x8 db[4];
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) {
@@ -352,7 +530,19 @@ __global__ __launch_bounds__(kBwdThreads, 1) void attn_bwd_dq_kernel(const BwdPa
 #pragma unroll
         for (int g = 0; g < 4; ++g)
 #pragma unroll
-            for (int i = 0; i < kDb; ++i) dqt[i] = mfma(tr_frag<D>(kbuf, tro[i], g), db[g], dqt[i]);
+            for (int i = 0; i < kDb; ++i) dqt[i] = mfma(tr_frag<D>(kbuf, tro, i, g), db[g], dqt[i]);
+    };
+    // one barrier per block, as in the dK/dV kernel
+    if (nkb > 0) issue(0, kbuf0, vbuf0);
+    for (int jb = 0; jb < nkb; jb += 2) {
+        wait_copies_and_sync();
+        if (jb + 1 < nkb) issue(jb + 1, kbuf1, vbuf1);
+        compute(jb, kbuf0, vbuf0);
+        if (jb + 1 < nkb) {
+            wait_copies_and_sync();
+            if (jb + 2 < nkb) issue(jb + 2, kbuf0, vbuf0);
+            compute(jb + 1, kbuf1, vbuf1);
+        }
     }
     if (qi < p.Lq) {
         uint16_t* row = p.dq + (qrow0 + qi) * D;
