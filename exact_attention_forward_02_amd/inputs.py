@@ -8,6 +8,11 @@ Recipe: a CPU ``torch.Generator`` seeded with the workload's seed draws Q,
 then K, then V as float32 N(0, 1) (Q optionally multiplied by a constant in
 float32), each rounded to bfloat16 with round-to-nearest-even.  Layout is
 [B, H, L, d], contiguous.
+
+Variable-length batches pack their sequences along the token axis ([T, H, d],
+token-major).  Their lengths come from the same kind of seeded generator:
+lengths drawn uniformly from [lo, hi] until the tokens reach the total, the
+last one cut so the total is exact.
 """
 from __future__ import annotations
 
@@ -85,6 +90,84 @@ def make_qkv(B: int, Hq: int, Hkv: int, Lq: int, Lk: int, dqk: int, dv: int,
     k = torch.randn((B, Hkv, Lk, dqk), generator=g, dtype=torch.float32).to(torch.bfloat16)
     v = torch.randn((B, Hkv, Lk, dv), generator=g, dtype=torch.float32).to(torch.bfloat16)
     return q, k, v
+
+
+@dataclass(frozen=True)
+class VarlenWorkload:
+    """A packed batch of sequences of different lengths (self-attention: each
+    sequence's queries attend its own keys, Lq_s = Lk_s)."""
+    name: str
+    total: int      # tokens over all sequences
+    lo: int         # sequence lengths are drawn uniformly from [lo, hi]
+    hi: int
+    Hq: int
+    Hkv: int
+    dqk: int
+    dv: int
+    causal: bool
+    seed: int
+
+    def lengths(self):
+        return seq_lengths(self.total, self.lo, self.hi, self.seed)
+
+    def flops(self) -> float:
+        """Algorithmic FLOPs: sum over sequences of 2*Hq*L_s^2*(dqk+dv), halved
+        under the causal mask."""
+        f = sum(2.0 * self.Hq * L * L * (self.dqk + self.dv) for L in self.lengths())
+        return f / 2.0 if self.causal else f
+
+    def min_hbm_bytes(self) -> int:
+        T = self.total
+        return (T * self.Hq * self.dqk * 2 + T * self.Hkv * (self.dqk + self.dv) * 2
+                + T * self.Hq * self.dv * 2 + T * self.Hq * 4)
+
+    def as_dict(self) -> dict:
+        return asdict(self)
+
+
+# 32k tokens at hidden 2048 (16 heads of 128) as one packed batch of causal
+# sequences of 256 to 8192 tokens
+VARLEN_WORKLOADS = {
+    "varlen_32k": VarlenWorkload("varlen_32k", 32768, 256, 8192, 16, 16, 128, 128, True, seed=7),
+}
+
+
+def seq_lengths(total: int, lo: int, hi: int, seed: int):
+    """Seeded sequence lengths: uniform integers in [lo, hi] drawn until they
+    reach `total` tokens, the last one cut so that they sum to `total`."""
+    g = torch.Generator(device="cpu").manual_seed(int(seed))
+    lens, acc = [], 0
+    while acc < total:
+        n = int(torch.randint(lo, hi + 1, (1,), generator=g).item())
+        n = min(n, total - acc)
+        lens.append(n)
+        acc += n
+    return lens
+
+
+def make_varlen_qkv(lens_q, lens_k, Hq: int, Hkv: int, dqk: int, dv: int, seed: int,
+                    q_mult: float = 1.0):
+    """Seeded bf16 CPU tensors of a packed batch: q [Tq, Hq, dqk], k [Tk, Hkv, dqk],
+    v [Tk, Hkv, dv], and the int64 offsets cu_q, cu_k (n_seq + 1 entries each;
+    sequence s owns tokens [cu[s], cu[s+1]))."""
+    if len(lens_q) != len(lens_k) or not lens_q:
+        raise ValueError("lens_q and lens_k must list the same, nonzero number of sequences")
+    cu_q = torch.tensor([0] + list(lens_q), dtype=torch.int64).cumsum(0)
+    cu_k = torch.tensor([0] + list(lens_k), dtype=torch.int64).cumsum(0)
+    Tq, Tk = int(cu_q[-1]), int(cu_k[-1])
+    g = torch.Generator(device="cpu").manual_seed(int(seed))
+    q = torch.randn((Tq, Hq, dqk), generator=g, dtype=torch.float32)
+    if q_mult != 1.0:
+        q.mul_(float(q_mult))
+    q = q.to(torch.bfloat16)
+    k = torch.randn((Tk, Hkv, dqk), generator=g, dtype=torch.float32).to(torch.bfloat16)
+    v = torch.randn((Tk, Hkv, dv), generator=g, dtype=torch.float32).to(torch.bfloat16)
+    return q, k, v, cu_q, cu_k
+
+
+def varlen_workload_qkv(w: VarlenWorkload):
+    lens = w.lengths()
+    return make_varlen_qkv(lens, lens, w.Hq, w.Hkv, w.dqk, w.dv, w.seed)
 
 
 def workload_qkv(w: Workload):

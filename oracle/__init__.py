@@ -14,6 +14,8 @@ attn_rows      the definition, materialised one score row at a time; with
                k_range=(k0, k1) the partial state of one key segment
 merge          the two-block merge rule folded over the partial states of
                several key segments
+attn_varlen    the definition inside each sequence of a packed
+               variable-length batch (token-major [T, H, d] tensors)
 online_rows    the tiled method (always-rescale Algorithm 1, or conditional
                base-2 rescaling per row or per row group), for checking the
                algorithm against the definition
@@ -93,6 +95,10 @@ class Oracle:
             _ptr, _ptr, _ptr, _i64, _i64, _i64, _i64, _i64, _i64, _i64,
             ctypes.c_int, ctypes.c_double, _i64, _i64, _ptr, _i64, _ptr, _ptr, ctypes.c_int,
             ctypes.c_int]
+        lib.oracle_attn_varlen.restype = ctypes.c_int
+        lib.oracle_attn_varlen.argtypes = [
+            _ptr, _ptr, _ptr, _ptr, _ptr, _i64, _i64, _i64, _i64, _i64, ctypes.c_int,
+            ctypes.c_double, _ptr, _i64, _ptr, _ptr, ctypes.c_int, ctypes.c_int]
         lib.oracle_widen.restype = ctypes.c_double
         lib.oracle_widen.argtypes = [ctypes.c_uint16, ctypes.c_int]
         lib.oracle_attn_bwd.restype = ctypes.c_int
@@ -154,6 +160,40 @@ class Oracle:
             o.ctypes.data, lse.ctypes.data, int(threads), eq)
         if rc != 0:
             raise ValueError(f"oracle_attn_rows rejected its arguments (code {rc})")
+        return o, lse
+
+    def attn_varlen(self, q, k, v, cu_q, cu_k, causal: bool, scale: float | None = None,
+                    rows=None, threads: int = 0):
+        """Exact O [n, dv] and lse [n] (float64) of a packed variable-length
+        batch: q [Tq, Hq, dqk], k [Tk, Hkv, dqk], v [Tk, Hkv, dv] (bf16 or fp16),
+        sequence s owning tokens [cu_q[s], cu_q[s+1]) and keys [cu_k[s], cu_k[s+1]).
+        A row index is h*Tq + t; rows=None means every row in order."""
+        (qb, eq), (kb, ek), (vb, ev) = _as_bits_elem(q), _as_bits_elem(k), _as_bits_elem(v)
+        if not eq == ek == ev:
+            raise TypeError("q, k and v must have one element type")
+        if qb.ndim != 3 or kb.ndim != 3 or vb.ndim != 3:
+            raise ValueError("varlen q, k, v must be [T, H, d]")
+        Tq, Hq, dqk = qb.shape
+        Tk, Hkv, dk = kb.shape
+        if dk != dqk or vb.shape[:2] != (Tk, Hkv):
+            raise ValueError(f"shape mismatch q{qb.shape} k{kb.shape} v{vb.shape}")
+        dv = vb.shape[2]
+        cq = np.ascontiguousarray(np.asarray(cu_q, dtype=np.int64).ravel())
+        ck = np.ascontiguousarray(np.asarray(cu_k, dtype=np.int64).ravel())
+        if cq.size != ck.size or cq.size < 2 or cq[-1] != Tq or ck[-1] != Tk:
+            raise ValueError("cu_q / cu_k must have n_seq + 1 entries ending at Tq / Tk")
+        if scale is None:
+            scale = 1.0 / math.sqrt(dqk)
+        r, n = self._rows(rows, Hq * Tq)
+        o = np.empty((n, dv), dtype=np.float64)
+        lse = np.empty((n,), dtype=np.float64)
+        rc = self._lib.oracle_attn_varlen(
+            qb.ctypes.data, kb.ctypes.data, vb.ctypes.data, cq.ctypes.data, ck.ctypes.data,
+            cq.size - 1, Hq, Hkv, dqk, dv, int(bool(causal)), float(scale),
+            None if r is None else r.ctypes.data, n, o.ctypes.data, lse.ctypes.data,
+            int(threads), eq)
+        if rc != 0:
+            raise ValueError(f"oracle_attn_varlen rejected its arguments (code {rc})")
         return o, lse
 
     def attn_bwd(self, q, k, v, dout, causal: bool, scale: float | None = None,
@@ -248,6 +288,10 @@ def load() -> Oracle:
 
 def attn_rows(*args, **kwargs):
     return load().attn_rows(*args, **kwargs)
+
+
+def attn_varlen(*args, **kwargs):
+    return load().attn_varlen(*args, **kwargs)
 
 
 def online_rows(*args, **kwargs):

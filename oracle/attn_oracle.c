@@ -332,6 +332,142 @@ int oracle_merge_states(const double* o_parts, const double* lse_parts, int64_t 
 }
 
 /* ------------------------------------------------------------------------ */
+/* 1b. Variable-length batches: the definition inside each packed sequence.  */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * oracle_attn_varlen: exact attention over a batch of n_seq sequences of
+ * different lengths packed along the token axis ("Flash Attention 4 ..."
+ * review, method part on scheduling: variable-length batches, ordered by
+ * work-tile execution time).  Sequence s owns query tokens
+ * [cu_q[s], cu_q[s+1]) and key tokens [cu_k[s], cu_k[s+1]); a query sees only
+ * the keys of its own sequence, with the causal mask aligned bottom-right
+ * within the sequence (query i of Lq_s sees keys j <= i + Lk_s - Lq_s).
+ * Layouts (contiguous, token-major):
+ *   q [total_q, Hq, dqk]   k [total_k, Hkv, dqk]   v [total_k, Hkv, dv]
+ *   row index r = h * total_q + t for query head h and token t (the layout
+ *   of lse, [Hq, total_q]); o [n_rows, dv] and lse [n_rows] in double.
+ * cu_q and cu_k hold n_seq + 1 non-decreasing offsets starting at 0.  A
+ * sequence may be empty; a row whose sequence has no visible key gets O = 0
+ * and lse = -inf.  rows == NULL means every row in order (n_rows must then
+ * be Hq * total_q).  elem selects bf16 or fp16 inputs.
+ */
+int oracle_attn_varlen(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                       const int64_t* cu_q, const int64_t* cu_k, int64_t n_seq,
+                       int64_t Hq, int64_t Hkv, int64_t dqk, int64_t dv, int causal,
+                       double scale, const int64_t* rows, int64_t n_rows,
+                       double* o, double* lse, int n_threads, int elem)
+{
+    if (!q || !k || !v || !o || !lse || !cu_q || !cu_k)
+        return 4;
+    if (n_seq < 1 || Hq < 1 || Hkv < 1 || dqk < 1 || dv < 1 || Hq % Hkv != 0)
+        return 1;
+    if (!(scale > 0.0) || !isfinite(scale))
+        return 3;
+    if (elem != ELEM_BF16 && elem != ELEM_FP16)
+        return 8;
+    if (cu_q[0] != 0 || cu_k[0] != 0)
+        return 9;
+    for (int64_t s = 0; s < n_seq; ++s)
+        if (cu_q[s + 1] < cu_q[s] || cu_k[s + 1] < cu_k[s])
+            return 9;
+    const int64_t total_q = cu_q[n_seq], total_k = cu_k[n_seq];
+    const int64_t total = Hq * total_q;
+    if (!rows && n_rows != total)
+        return 5;
+    if (rows)
+        for (int64_t t = 0; t < n_rows; ++t)
+            if (rows[t] < 0 || rows[t] >= total)
+                return 6;
+    int64_t max_lk = 1;
+    for (int64_t s = 0; s < n_seq; ++s)
+        if (cu_k[s + 1] - cu_k[s] > max_lk)
+            max_lk = cu_k[s + 1] - cu_k[s];
+    (void)total_k;
+    dims_t d;
+    memset(&d, 0, sizeof d);
+    d.elem = elem;
+    const int64_t group = Hq / Hkv;
+#ifdef _OPENMP
+    if (n_threads > 0)
+        omp_set_num_threads(n_threads);
+#else
+    (void)n_threads;
+#endif
+
+    int failed = 0;
+#pragma omp parallel
+    {
+        double* qd = (double*)malloc(sizeof(double) * (size_t)dqk);
+        double* s = (double*)malloc(sizeof(double) * (size_t)max_lk);
+        int ok = qd && s;
+#pragma omp for schedule(dynamic, 16)
+        for (int64_t t = 0; t < n_rows; ++t) {
+            if (!ok) {
+#pragma omp atomic write
+                failed = 1;
+                continue;
+            }
+            const int64_t r = rows ? rows[t] : t;
+            const int64_t h = r / total_q;
+            const int64_t tok = r % total_q;
+            const int64_t kvh = h / group;
+            /* the sequence holding this token: cu_q[sq] <= tok < cu_q[sq + 1] */
+            int64_t sq = 0;
+            while (cu_q[sq + 1] <= tok)
+                ++sq;
+            const int64_t Lq = cu_q[sq + 1] - cu_q[sq];
+            const int64_t Lk = cu_k[sq + 1] - cu_k[sq];
+            const int64_t i = tok - cu_q[sq];
+            /* visible keys of query i within its sequence */
+            int64_t n = Lk;
+            if (causal) {
+                const int64_t last = i + Lk - Lq;
+                n = last < 0 ? 0 : (last + 1 < Lk ? last + 1 : Lk);
+            }
+            double* o_row = o + t * dv;
+            for (int64_t c = 0; c < dv; ++c)
+                o_row[c] = 0.0;
+            if (n == 0) {
+                lse[t] = -INFINITY;
+                continue;
+            }
+            const uint16_t* qrow = q + (tok * Hq + h) * dqk;
+            for (int64_t c = 0; c < dqk; ++c)
+                qd[c] = widen(&d, qrow[c]);
+            /* S_j = scale * q . k_j over the sequence's visible keys */
+            double m = -INFINITY;
+            for (int64_t j = 0; j < n; ++j) {
+                const uint16_t* kj = k + ((cu_k[sq] + j) * Hkv + kvh) * dqk;
+                double dot = 0.0;
+                for (int64_t c = 0; c < dqk; ++c)
+                    dot += qd[c] * widen(&d, kj[c]);
+                s[j] = scale * dot;
+                if (s[j] > m)
+                    m = s[j];
+            }
+            /* P_j = e^{S_j - m} / l, O = sum_j P_j V_j, lse = m + ln l */
+            double l = 0.0;
+            for (int64_t j = 0; j < n; ++j) {
+                const double e = exp(s[j] - m);
+                s[j] = e;
+                l += e;
+            }
+            for (int64_t j = 0; j < n; ++j) {
+                const uint16_t* vj = v + ((cu_k[sq] + j) * Hkv + kvh) * dv;
+                const double p = s[j] / l;
+                for (int64_t c = 0; c < dv; ++c)
+                    o_row[c] += p * widen(&d, vj[c]);
+            }
+            lse[t] = m + log(l);
+        }
+        free(qd);
+        free(s);
+    }
+    return failed ? 7 : 0;
+}
+
+/* ------------------------------------------------------------------------ */
 /* 2. The tiled method, block by block over K/V, for checking the algorithm. */
 /* ------------------------------------------------------------------------ */
 /*

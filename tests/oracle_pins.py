@@ -19,7 +19,10 @@ AssertionError when the oracle disagrees with:
     (numpy's own conversions), fp16 inputs against torch's float64 SDPA, and
     values exact in both formats giving identical results,
   * the backward pass: gradients against float64 autograd through torch's
-    SDPA, D_i = dO_i . O_i, rows without keys, and sum_j dK_j = 0.
+    SDPA, D_i = dO_i . O_i, rows without keys, and sum_j dK_j = 0,
+  * variable-length batches: each packed sequence against torch's float64
+    SDPA on that sequence alone, equal lengths against the batched
+    definition, and empty sequences.
 They run unchanged against deliberately broken copies of the oracle in
 test_oracle_mutations.py, which checks that each planted mistake trips at
 least one pin.
@@ -35,7 +38,7 @@ import numpy as np
 import torch
 import torch.nn.functional as F
 
-from exact_attention_forward_02_amd.inputs import make_qkv
+from exact_attention_forward_02_amd.inputs import make_qkv, make_varlen_qkv
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 LN2 = math.log(2.0)
@@ -602,6 +605,94 @@ def pin_bwd_dk_sums_to_zero(orc):
                f"shape {idx} sum_j dK_j")
 
 
+# --------------------------------------------------------------------------
+# Variable-length batches
+# --------------------------------------------------------------------------
+
+# (lens_q, lens_k, Hq, Hkv, dqk, dv, causal): ragged lengths, a sequence with
+# Lq_s != Lk_s (bottom-right mask inside the sequence), one with Lq_s > Lk_s
+# (keyless rows under the mask), empty sequences, GQA and (192, 128)
+VARLEN_SHAPES = [
+    ([5, 17, 1, 33], [5, 17, 1, 33], 2, 2, 8, 8, False),
+    ([5, 17, 1, 33], [5, 17, 1, 33], 2, 1, 8, 8, True),
+    ([7, 0, 12, 3], [9, 4, 12, 0], 4, 2, 16, 16, True),
+    ([7, 0, 12, 3], [9, 4, 12, 5], 4, 2, 16, 8, False),
+    ([20, 6], [11, 30], 3, 3, 24, 16, True),
+]
+
+
+def _varlen_reference(q, k, v, cu_q, cu_k, causal, scale):
+    """torch SDPA (float64) on each sequence alone, rows in the order h*Tq + t."""
+    Tq, Hq, _ = q.shape
+    dv = v.shape[2]
+    o = np.zeros((Hq, Tq, dv))
+    lse = np.full((Hq, Tq), -math.inf)
+    for s in range(len(cu_q) - 1):
+        q0, q1, k0, k1 = int(cu_q[s]), int(cu_q[s + 1]), int(cu_k[s]), int(cu_k[s + 1])
+        if q1 == q0 or k1 == k0:
+            continue  # no query, or no key: rows stay O = 0, lse = -inf
+        qs = q[q0:q1].transpose(0, 1).unsqueeze(0).contiguous()
+        ks = k[k0:k1].transpose(0, 1).unsqueeze(0).contiguous()
+        vs = v[k0:k1].transpose(0, 1).unsqueeze(0).contiguous()
+        os_, ls_ = _library_reference(qs, ks, vs, causal, scale)
+        o[:, q0:q1] = os_.reshape(Hq, q1 - q0, dv)
+        lse[:, q0:q1] = ls_.reshape(Hq, q1 - q0)
+    return o.reshape(Hq * Tq, dv), lse.reshape(-1)
+
+
+def pin_varlen_library_sdpa(orc):
+    """Each packed sequence against torch's float64 SDPA on that sequence alone."""
+    for idx, (lq, lk, Hq, Hkv, dqk, dv, causal) in enumerate(VARLEN_SHAPES):
+        q, k, v, cu_q, cu_k = make_varlen_qkv(lq, lk, Hq, Hkv, dqk, dv, seed=300 + idx)
+        scale = 1.0 / math.sqrt(dqk)
+        o, lse = orc.attn_varlen(q, k, v, cu_q, cu_k, causal=causal, scale=scale)
+        want_o, want_lse = _varlen_reference(q, k, v, cu_q, cu_k, causal, scale)
+        tag = f"varlen shape {idx}"
+        _close(o, want_o, 1e-12, f"{tag} O vs torch SDPA per sequence")
+        _close(lse, want_lse, 1e-12, f"{tag} lse vs torch logsumexp per sequence")
+
+
+def pin_varlen_equal_lengths(orc):
+    """B sequences of one length are the batched problem in token-major layout."""
+    B, L, Hq, Hkv, d = 3, 19, 4, 2, 16
+    for causal in (False, True):
+        q, k, v, cu_q, cu_k = make_varlen_qkv([L] * B, [L] * B, Hq, Hkv, d, d, seed=321)
+        o, lse = orc.attn_varlen(q, k, v, cu_q, cu_k, causal=causal)
+        qb = q.view(B, L, Hq, d).transpose(1, 2).contiguous()
+        kb = k.view(B, L, Hkv, d).transpose(1, 2).contiguous()
+        vb = v.view(B, L, Hkv, d).transpose(1, 2).contiguous()
+        ob, lb = orc.attn_rows(qb, kb, vb, causal=causal)
+        # batched rows (b, h, i) -> varlen rows (h, b*L + i)
+        ob = ob.reshape(B, Hq, L, d).transpose(1, 0, 2, 3).reshape(Hq * B * L, d)
+        lb = lb.reshape(B, Hq, L).transpose(1, 0, 2).reshape(-1)
+        _close(o, ob, 0.0, f"causal={causal} equal-length O")
+        _close(lse, lb, 0.0, f"causal={causal} equal-length lse")
+
+
+def pin_varlen_zero_query(orc):
+    """Q = 0 in a packed batch: O is the mean of the sequence's visible V rows
+    and lse = ln(count), -inf with O = 0 where a row sees no key."""
+    lq, lk = [3, 0, 4, 2], [5, 2, 0, 6]
+    q, k, v, cu_q, cu_k = make_varlen_qkv(lq, lk, 2, 1, 8, 4, seed=77)
+    q = torch.zeros_like(q)
+    for causal in (False, True):
+        o, lse = orc.attn_varlen(q, k, v, cu_q, cu_k, causal=causal)
+        Tq = q.shape[0]
+        vd = v.double()
+        for h in range(2):
+            for s in range(len(lq)):
+                for i in range(lq[s]):
+                    t = int(cu_q[s]) + i
+                    n = lk[s] if not causal else max(0, min(lk[s], i + lk[s] - lq[s] + 1))
+                    r = h * Tq + t
+                    if n == 0:
+                        assert lse[r] == -math.inf and not o[r].any(), f"row {r}"
+                        continue
+                    want = vd[int(cu_k[s]):int(cu_k[s]) + n, 0].mean(dim=0).numpy()
+                    _close(o[r], want, 1e-14, f"causal={causal} row {r} O")
+                    _close(lse[r], math.log(n), 1e-14, f"causal={causal} row {r} lse")
+
+
 ALL_PINS = [
     pin_worked_example,
     pin_conditional_cases,
@@ -625,4 +716,7 @@ ALL_PINS = [
     pin_bwd_library_autograd,
     pin_bwd_fp16_and_empty_rows,
     pin_bwd_dk_sums_to_zero,
+    pin_varlen_library_sdpa,
+    pin_varlen_equal_lengths,
+    pin_varlen_zero_query,
 ]

@@ -50,6 +50,14 @@ MUTATIONS = {
                                 "for (int64_t h = hk * group; h < hk * group + 1; ++h) {"),
     "fp16_read_as_bf16": ("return d->elem == ELEM_FP16 ? fp16_bits_to_double(bits) : "
                           "bf16_bits_to_double(bits);", "return bf16_bits_to_double(bits);"),
+    "varlen_keys_at_query_offset": (
+        "const uint16_t* kj = k + ((cu_k[sq] + j) * Hkv + kvh) * dqk;",
+        "const uint16_t* kj = k + ((cu_q[sq] + j) * Hkv + kvh) * dqk;"),
+    "varlen_causal_top_left": ("const int64_t last = i + Lk - Lq;",
+                               "const int64_t last = i;"),
+    "varlen_sequence_boundary": ("while (cu_q[sq + 1] <= tok)", "while (cu_q[sq + 1] < tok)"),
+    "varlen_value_head": ("const uint16_t* vj = v + ((cu_k[sq] + j) * Hkv + kvh) * dv;",
+                          "const uint16_t* vj = v + ((cu_k[sq] + j) * Hkv + 0) * dv;"),
 }
 
 
