@@ -305,6 +305,110 @@ def bench_backward(args, w, qd, kd, vd) -> int:
     return 0
 
 
+def bench_varlen(args, w) -> int:
+    """A packed variable-length batch: the host planner runs once per batch
+    (its time is reported as plan_ms, outside the steps), then each step is one
+    attn_fwd_varlen launch on the uploaded plan."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from exact_attention_forward_02_amd import attn_fwd_varlen, varlen_plan
+    from exact_attention_forward_02_amd.inputs import varlen_workload_qkv
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    q, k, v, cu_q, cu_k = varlen_workload_qkv(w)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    t0 = time.perf_counter()
+    plan_host = varlen_plan(cu_q, cu_k, w.Hq, w.Hkv, w.causal)
+    plan_ms = (time.perf_counter() - t0) * 1e3
+    plan = torch.from_numpy(plan_host).to(dev)
+    T = q.shape[0]
+    o = torch.empty((T, w.Hq, w.dv), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((w.Hq, T), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        attn_fwd_varlen(qd, kd, vd, cu_q, cu_k, causal=w.causal, plan=plan, out=o, lse=lse,
+                        stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    ms_launch = sum(launch_ms) / len(launch_ms)
+    flops = w.flops()
+    value = flops * args.steps / wall / 1e12
+    achieved = flops / (ms_launch * 1e-3) / 1e12
+    lens = w.lengths()
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "total_tokens": w.total, "n_seq": len(lens),
+                   "seq_lens": lens, "Hq": w.Hq, "Hkv": w.Hkv, "d_qk": w.dqk, "d_v": w.dv,
+                   "causal": w.causal, "layout": "thd", "flops_per_step": flops,
+                   "tile_records": int(plan_host.shape[0]), "plan_ms": round(plan_ms, 3)},
+        "pct_of_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": None,
+            "kernel": "attn_fwd_kernel (varlen)",
+            "ms_per_launch": round(ms_launch, 4),
+            "ms_per_launch_min": round(min(launch_ms), 4),
+            "ms_per_launch_max": round(max(launch_ms), 4),
+        },
+    }
+    if not args.no_cpu_baseline:
+        orc = oracle.load()
+        threads = host_threads()
+        g = torch.Generator().manual_seed(54321)
+        n_rows = min(w.Hq * T, 10000 * threads)  # about 10 s of fp64 work
+        rows = torch.randperm(w.Hq * T, generator=g)[:n_rows].numpy()
+        t0 = time.perf_counter()
+        orc.attn_varlen(q, k, v, cu_q, cu_k, causal=w.causal, rows=rows, threads=threads)
+        dt = time.perf_counter() - t0
+        # exact FLOPs of the sampled rows: each sees its visible keys
+        cq = np.asarray(cu_q)
+        tok = rows % T
+        seq = np.searchsorted(cq, tok, side="right") - 1
+        L = (cq[seq + 1] - cq[seq])
+        i = tok - cq[seq]
+        keys = (i + 1) if w.causal else L
+        rflops = float((2.0 * keys * (w.dqk + w.dv)).sum())
+        result["cpu_baseline"] = {
+            "value": float(f"{rflops / dt / 1e12:.4g}"), "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{len(rows)} of {w.Hq * T} query rows of {w.name} drawn at random "
+                      f"(seeded), fp64 materialised softmax, {dt:.1f} s"}
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -341,8 +445,13 @@ def main() -> int:
 
     if args.copy_calibration:
         return copy_calibration()
+    from exact_attention_forward_02_amd.inputs import VARLEN_WORKLOADS
+
+    if args.workload in VARLEN_WORKLOADS:
+        return bench_varlen(args, VARLEN_WORKLOADS[args.workload])
     if args.workload not in WORKLOADS:
-        print(f"unknown workload {args.workload}; choose from {sorted(WORKLOADS)}",
+        print(f"unknown workload {args.workload}; choose from "
+              f"{sorted(WORKLOADS) + sorted(VARLEN_WORKLOADS)}",
               file=sys.stderr)
         return 2
     w = WORKLOADS[args.workload]

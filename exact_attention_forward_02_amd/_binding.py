@@ -12,6 +12,8 @@ import math
 import os
 import threading
 
+import numpy as np
+
 import torch
 
 from . import build as _build
@@ -21,6 +23,7 @@ _lib = None
 
 ATTN_OK = 0
 ATTN_DTYPE_BF16, ATTN_DTYPE_FP16 = 0, 1
+VARLEN_RECORD_INTS = 8  # ints per tile record of attn_varlen_plan
 
 
 class Strides(ctypes.Structure):
@@ -58,6 +61,12 @@ def _load():
                                        ctypes.c_float, i, vp]
         lib.attn_merge.restype = i
         lib.attn_merge.argtypes = [vp, vp, vp, vp, i, ctypes.c_longlong, i, vp]
+        lib.attn_varlen_plan.restype = i
+        lib.attn_varlen_plan.argtypes = [ctypes.POINTER(i), ctypes.POINTER(i), i, i, i, i,
+                                         ctypes.POINTER(i), i, ctypes.POINTER(i)]
+        lib.attn_fwd_varlen.restype = i
+        lib.attn_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i,
+                                        ctypes.c_float, vp]
         lib.attn_status_string.restype = ctypes.c_char_p
         lib.attn_status_string.argtypes = [i]
         lib.attn_abi_version.restype = i
@@ -324,3 +333,92 @@ def attn_fwd_splitkv(q, k, v, n_split: int, causal: bool = False, scale: float |
     o_part, lse_part = attn_fwd_split(q, k, v, n_split, causal=causal, scale=scale,
                                       stream=stream)
     return attn_merge(o_part, lse_part, stream=stream)
+
+
+def _host_offsets(cu, name):
+    """cu_seqlens (list, numpy array or tensor on any device) -> contiguous int32 numpy."""
+    if isinstance(cu, torch.Tensor):
+        cu = cu.detach().cpu().numpy()
+    a = np.ascontiguousarray(np.asarray(cu, dtype=np.int64).ravel())
+    if a.size < 2 or a.min() < 0 or a.max() > np.iinfo(np.int32).max:
+        raise ValueError(f"{name} must hold n_seq + 1 offsets in int32 range")
+    return np.ascontiguousarray(a.astype(np.int32))
+
+
+def varlen_plan(cu_seqlens_q, cu_seqlens_k, Hq: int, Hkv: int, causal: bool):
+    """Schedule of a packed variable-length batch, computed on the host by
+    attn_varlen_plan: int32 [n_records, 8] tile records (n_records a multiple of 8)."""
+    lib = _load()
+    cq = _host_offsets(cu_seqlens_q, "cu_seqlens_q")
+    ck = _host_offsets(cu_seqlens_k, "cu_seqlens_k")
+    if cq.size != ck.size:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must have the same length")
+    n_seq = cq.size - 1
+    n = ctypes.c_int(0)
+    i32p = ctypes.POINTER(ctypes.c_int)
+    rc = lib.attn_varlen_plan(cq.ctypes.data_as(i32p), ck.ctypes.data_as(i32p), n_seq, int(Hq),
+                              int(Hkv), int(bool(causal)), None, 0, ctypes.byref(n))
+    if rc != ATTN_OK:
+        raise RuntimeError(f"attn_varlen_plan failed: {status_string(rc)} (code {rc})")
+    plan = np.zeros((n.value, VARLEN_RECORD_INTS), dtype=np.int32)
+    if n.value:
+        rc = lib.attn_varlen_plan(cq.ctypes.data_as(i32p), ck.ctypes.data_as(i32p), n_seq,
+                                  int(Hq), int(Hkv), int(bool(causal)),
+                                  plan.ctypes.data_as(i32p), n.value, ctypes.byref(n))
+        if rc != ATTN_OK:
+            raise RuntimeError(f"attn_varlen_plan failed: {status_string(rc)} (code {rc})")
+    return plan
+
+
+def attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, causal: bool = False,
+                    scale: float | None = None, plan=None, out=None, lse=None, stream=None):
+    """O [Tq, Hq, d_v] bf16 and lse [Hq, Tq] fp32 of a packed variable-length
+    batch: q [Tq, Hq, d_qk], k [Tk, Hkv, d_qk], v [Tk, Hkv, d_v] contiguous bf16
+    on one GPU; sequence s owns query tokens [cu_seqlens_q[s], cu_seqlens_q[s+1])
+    and key tokens [cu_seqlens_k[s], cu_seqlens_k[s+1]).  plan, if given, is the
+    device int32 [n, 8] result of varlen_plan for the same batch; otherwise it is
+    computed on the host and copied to q's device."""
+    lib = _load()
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.bfloat16:
+            raise TypeError(f"{name} must be a bfloat16 torch.Tensor")
+        if t.device.type != "cuda":
+            raise ValueError(f"{name} must be on a GPU device, got {t.device}")
+        if t.dim() != 3 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous token-major [T, H, d] tensor")
+    if not (q.device == k.device == v.device):
+        raise ValueError("q, k and v must be on the same device")
+    Tq, Hq, dqk = q.shape
+    Tk, Hkv, dk = k.shape
+    if dk != dqk or tuple(v.shape[:2]) != (Tk, Hkv):
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    dv = v.shape[2]
+    cq = _host_offsets(cu_seqlens_q, "cu_seqlens_q")
+    ck = _host_offsets(cu_seqlens_k, "cu_seqlens_k")
+    if int(cq[-1]) != Tq or int(ck[-1]) != Tk:
+        raise ValueError("the last offsets must equal the token counts of q and k")
+    if scale is None:
+        scale = 1.0 / math.sqrt(dqk)
+    if plan is None:
+        plan = torch.from_numpy(varlen_plan(cq, ck, Hq, Hkv, causal)).to(q.device)
+    if (not isinstance(plan, torch.Tensor) or plan.dtype != torch.int32 or plan.dim() != 2
+            or plan.shape[1] != VARLEN_RECORD_INTS or plan.device != q.device
+            or not plan.is_contiguous()):
+        raise ValueError("plan must be a contiguous int32 [n, 8] tensor on q's device")
+    if out is None:
+        out = torch.empty((Tq, Hq, dv), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((Hq, Tq), dtype=torch.float32, device=q.device)
+    if tuple(out.shape) != (Tq, Hq, dv) or out.dtype != torch.bfloat16 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous bf16 [Tq, Hq, d_v] tensor")
+    if tuple(lse.shape) != (Hq, Tq) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous fp32 [Hq, Tq] tensor")
+    with torch.cuda.device(q.device):
+        s = stream if stream is not None else torch.cuda.current_stream(q.device)
+        rc = lib.attn_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                 lse.data_ptr(), plan.data_ptr(), int(plan.shape[0]), Tq, Tk,
+                                 Hq, Hkv, dqk, dv, int(bool(causal)), float(scale),
+                                 s.cuda_stream)
+    if rc != ATTN_OK:
+        raise RuntimeError(f"attn_fwd_varlen failed: {status_string(rc)} (code {rc})")
+    return out, lse

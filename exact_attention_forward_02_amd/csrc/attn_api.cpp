@@ -7,7 +7,9 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <algorithm>
 #include <atomic>
+#include <vector>
 
 #include <hip/hip_runtime_api.h>
 
@@ -16,12 +18,14 @@
 
 namespace {
 
-constexpr int kAbiVersion = 4;
+constexpr int kAbiVersion = 5;
 constexpr int kMaxSplits = 4096;
 constexpr int kMaxDevices = 64;
 constexpr int kXcds = 8;                 // MI355X: 8 accelerator complex dies
 constexpr int kTilesPerXcdWave = 32;     // concurrent workgroups per XCD (32 CUs x 1)
 constexpr float kDefaultThreshold = 8.0f;  // log2 units: a factor of 256
+constexpr int kTileOverhead = 2;         // per-tile cost beyond its key blocks (Q in, O out),
+                                         // in key-block units, for the varlen schedule
 
 // -1 unknown, 0 not gfx950, 1 gfx950
 std::atomic<int> g_arch_ok[kMaxDevices];
@@ -126,11 +130,14 @@ int split_keys(int Lk, int n_split) {
     return attn::kBlockN * ((nb + n_split - 1) / n_split);
 }
 
+// Heads of one K/V head packed into a workgroup: Gp divides G and the 8 waves.
+int packed_heads(int G) { return (G % 8 == 0) ? 8 : (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1; }
+
 int fill_schedule(attn::FwdParams& p) {
     p.G = p.Hq / p.Hkv;
     // query heads that share a K/V head are packed into one workgroup, one
     // head per wave group, so the K/V block is loaded once for all of them
-    p.Gp = (p.G % 8 == 0) ? 8 : (p.G % 4 == 0) ? 4 : (p.G % 2 == 0) ? 2 : 1;
+    p.Gp = packed_heads(p.G);
     p.n_hg = p.G / p.Gp;
     p.bm_pos = attn::kRowsPerWave * attn::kWaves / p.Gp;
     p.n_m = (p.Lq + p.bm_pos - 1) / p.bm_pos;
@@ -221,6 +228,120 @@ int run(const void* q, const void* k, const void* v, void* o, float* lse, int B,
     hipError_t err = attn::launch_fwd(p, d_qk, d_v, causal != 0, debug, fp16,
                                       static_cast<hipStream_t>(stream));
     if (err != hipSuccess) return ATTN_ERR_HIP;
+    return ATTN_OK;
+}
+
+// Schedule of a packed variable-length batch ("Flash Attention 4 ..." review,
+// method part on scheduling: variable-length batches are ordered by the
+// execution time of their work tiles, longest first).  A tile is (sequence,
+// unit = (K/V head, head group), position block m); its cost is the number of
+// 64-key blocks it visits plus a fixed per-tile overhead.
+//  1. Units are dealt to the 8 XCDs longest first, each to the least loaded
+//     XCD, so each XCD streams whole K/V heads through its own L2.
+//  2. On each XCD, the units (longest first) are grouped into sections of at
+//     most kTilesPerXcdWave tiles (or one larger unit), so the tiles running
+//     at one time share few K/V heads.
+//  3. Section by section, tiles are assigned longest first to the least
+//     loaded of the XCD's kTilesPerXcdWave workgroups (LPT).
+//  4. The kernel gives workgroup slot s of an XCD, in round r, the local tile
+//     r * 32 + s (r even) or r * 32 + 31 - s (r odd); each slot's r-th
+//     assigned tile is written there, and slots with fewer tiles are padded
+//     with empty (all-zero) records.  Record 8 * local + x belongs to XCD x.
+// The balance assumes 32 workgroups per XCD (256 CUs); with fewer, the kernel
+// still runs every record exactly once, only less evenly.
+int build_varlen_plan(const int* cu_q, const int* cu_k, int n_seq, int Hq, int Hkv, int causal,
+                      std::vector<int>* out) {
+    if (!cu_q || !cu_k) return ATTN_ERR_NULL_PTR;
+    if (n_seq < 1 || Hq < 1 || Hkv < 1) return ATTN_ERR_BAD_SHAPE;
+    if (Hq % Hkv != 0) return ATTN_ERR_GQA_RATIO;
+    if (cu_q[0] != 0 || cu_k[0] != 0) return ATTN_ERR_BAD_SHAPE;
+    for (int s = 0; s < n_seq; ++s)
+        if (cu_q[s + 1] < cu_q[s] || cu_k[s + 1] < cu_k[s]) return ATTN_ERR_BAD_SHAPE;
+    const int G = Hq / Hkv, Gp = packed_heads(G), n_hg = G / Gp;
+    const int bm_pos = attn::kRowsPerWave * attn::kWaves / Gp;
+    const int units_per_seq = Hkv * n_hg;
+    // key blocks the tile at position block m of a (lq, lk) sequence visits
+    auto tile_blocks = [&](long long lq, long long lk, long long m) {
+        long long kend = lk;
+        if (causal) kend = std::min(lk, std::min(lq, (m + 1) * bm_pos) - 1 + lk - lq + 1);
+        return kend > 0 ? (kend + attn::kBlockN - 1) / attn::kBlockN : 0;
+    };
+    struct Unit {
+        long long cost;
+        int seq, ukv, n_m;
+    };
+    std::vector<Unit> units;
+    for (int s = 0; s < n_seq; ++s) {
+        const long long lq = cu_q[s + 1] - cu_q[s], lk = cu_k[s + 1] - cu_k[s];
+        if (lq == 0) continue;  // no query rows: nothing to compute or write
+        const int n_m = (int)((lq + bm_pos - 1) / bm_pos);
+        long long cost = 0;
+        for (int m = 0; m < n_m; ++m) cost += tile_blocks(lq, lk, m) + kTileOverhead;
+        for (int u = 0; u < units_per_seq; ++u) units.push_back({cost, s, u, n_m});
+    }
+    // 1. units longest first (ties: sequence, then unit), each to the least loaded XCD
+    std::stable_sort(units.begin(), units.end(),
+                     [](const Unit& a, const Unit& b) { return a.cost > b.cost; });
+    std::vector<std::vector<Unit>> xcd_units(kXcds);
+    long long xcd_load[kXcds] = {0};
+    for (const Unit& u : units) {
+        int best = 0;
+        for (int x = 1; x < kXcds; ++x)
+            if (xcd_load[x] < xcd_load[best]) best = x;
+        xcd_units[best].push_back(u);
+        xcd_load[best] += u.cost;
+    }
+    struct Tile {
+        long long cost;
+        int rec[attn::kPlanInts];
+    };
+    constexpr int kSlots = kTilesPerXcdWave;
+    // slot_tiles[x][s]: the tiles workgroup slot s of XCD x runs, in order
+    std::vector<std::vector<std::vector<Tile>>> slot_tiles(kXcds,
+                                                           std::vector<std::vector<Tile>>(kSlots));
+    size_t rounds = 0;
+    for (int x = 0; x < kXcds; ++x) {
+        long long load[kSlots] = {0};
+        std::vector<Tile> sec;
+        auto flush = [&]() {
+            // 3. the section's tiles longest first, each to the least loaded slot
+            std::stable_sort(sec.begin(), sec.end(),
+                             [](const Tile& a, const Tile& b) { return a.cost > b.cost; });
+            for (const Tile& t : sec) {
+                int best = 0;
+                for (int s = 1; s < kSlots; ++s)
+                    if (load[s] < load[best]) best = s;
+                slot_tiles[x][best].push_back(t);
+                load[best] += t.cost;
+            }
+            sec.clear();
+        };
+        for (const Unit& u : xcd_units[x]) {
+            // 2. a section holds at most kSlots tiles, or one unit
+            if (!sec.empty() && sec.size() + (size_t)u.n_m > (size_t)kSlots) flush();
+            const int lq = cu_q[u.seq + 1] - cu_q[u.seq], lk = cu_k[u.seq + 1] - cu_k[u.seq];
+            for (int m = 0; m < u.n_m; ++m) {
+                Tile t;
+                t.cost = tile_blocks(lq, lk, m) + kTileOverhead;
+                const int rec[attn::kPlanInts] = {cu_q[u.seq], lq, cu_k[u.seq], lk, u.ukv, m, 0, 0};
+                memcpy(t.rec, rec, sizeof rec);
+                sec.push_back(t);
+            }
+        }
+        if (!sec.empty()) flush();
+        for (int s = 0; s < kSlots; ++s) rounds = std::max(rounds, slot_tiles[x][s].size());
+    }
+    const size_t n_records = rounds * kSlots * kXcds;
+    if (n_records * attn::kPlanInts > (size_t)INT32_MAX) return ATTN_ERR_TOO_LARGE;
+    // 4. lay the records out where the kernel's round order looks for them
+    out->assign(n_records * attn::kPlanInts, 0);
+    for (int x = 0; x < kXcds; ++x)
+        for (int s = 0; s < kSlots; ++s)
+            for (size_t r = 0; r < slot_tiles[x][s].size(); ++r) {
+                const size_t local = r * kSlots + ((r & 1) ? kSlots - 1 - s : s);
+                memcpy(out->data() + (local * kXcds + x) * attn::kPlanInts,
+                       slot_tiles[x][s][r].rec, sizeof(int) * attn::kPlanInts);
+            }
     return ATTN_OK;
 }
 
@@ -329,6 +450,91 @@ int attn_merge(const float* o_part, const float* lse_part, void* o, float* lse, 
     if (rc != ATTN_OK) return rc;
     hipError_t err = attn::launch_merge(o_part, lse_part, static_cast<uint16_t*>(o), lse,
                                         n_split, rows, d_v, static_cast<hipStream_t>(stream));
+    if (err != hipSuccess) return ATTN_ERR_HIP;
+    return ATTN_OK;
+}
+
+int attn_varlen_plan(const int* cu_seqlens_q, const int* cu_seqlens_k, int n_seq, int Hq,
+                     int Hkv, int causal, int* plan, int capacity, int* n_records) {
+    if (!n_records) return ATTN_ERR_NULL_PTR;
+    std::vector<int> recs;
+    const int rc = build_varlen_plan(cu_seqlens_q, cu_seqlens_k, n_seq, Hq, Hkv, causal, &recs);
+    if (rc != ATTN_OK) return rc;
+    const int n = (int)(recs.size() / attn::kPlanInts);
+    *n_records = n;
+    if (plan == nullptr) return ATTN_OK;
+    if (capacity < n) return ATTN_ERR_BAD_ARGUMENT;
+    if (!recs.empty()) memcpy(plan, recs.data(), sizeof(int) * recs.size());
+    return ATTN_OK;
+}
+
+int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                    const int* plan, int n_records, int total_q, int total_k, int Hq, int Hkv,
+                    int d_qk, int d_v, int causal, float scale, void* stream) {
+    if (!plan) return ATTN_ERR_NULL_PTR;
+    if (total_q < 1 || total_k < 0 || n_records < 0) return ATTN_ERR_BAD_SHAPE;
+    if (n_records % kXcds != 0) return ATTN_ERR_BAD_ARGUMENT;
+    // the forward's argument rules on a batch of one token-major "sequence"
+    int rc = check_args(q, k, v, o, lse, 1, Hq, Hkv, total_q, total_k > 0 ? total_k : 1, d_qk,
+                        d_v, scale);
+    if (rc != ATTN_OK) return rc;
+    if (!aligned(plan, 16)) return ATTN_ERR_MISALIGNED;
+    // every sequence's K and V rows lie in one tensor of less than 2^31 bytes,
+    // so the kernel's 32-bit buffer offsets reach all of them
+    if ((long long)total_k * Hkv * d_qk * 2 > INT32_MAX ||
+        (long long)total_k * Hkv * d_v * 2 > INT32_MAX ||
+        (long long)total_q * Hq > INT32_MAX)
+        return ATTN_ERR_TOO_LARGE;
+    if (n_records == 0) return ATTN_OK;  // no query rows in the batch
+    attn::FwdParams p;
+    memset(&p, 0, sizeof p);
+    p.q = static_cast<const uint16_t*>(q);
+    p.k = static_cast<const uint16_t*>(k);
+    p.v = static_cast<const uint16_t*>(v);
+    p.o = static_cast<uint16_t*>(o);
+    p.lse = lse;
+    p.plan = plan;
+    p.total_q = total_q;
+    p.total_k = total_k;
+    // token-major [T, H, d]: a row is one token, heads are d apart
+    p.q_sh = d_qk;
+    p.q_sr = Hq * d_qk;
+    p.k_sh = d_qk;
+    p.k_sr = Hkv * d_qk;
+    p.v_sh = d_v;
+    p.v_sr = Hkv * d_v;
+    p.o_sh = d_v;
+    p.o_sr = Hq * d_v;
+    p.B = 1;
+    p.Hq = Hq;
+    p.Hkv = Hkv;
+    p.Lq = 1;
+    p.Lk = 1;
+    p.G = Hq / Hkv;
+    p.Gp = packed_heads(p.G);
+    p.n_hg = p.G / p.Gp;
+    p.bm_pos = attn::kRowsPerWave * attn::kWaves / p.Gp;
+    p.n_split = 1;
+    p.split_blocks = (total_k + attn::kBlockN - 1) / attn::kBlockN;
+    p.units_kv = Hkv * p.n_hg;
+    // the records are the tiles, interleaved by XCD
+    p.units = n_records;
+    p.n_m = 1;
+    p.xcd_mode = 1;
+    p.upx = n_records / kXcds;
+    p.sec_units = 1;
+    p.scale = scale;
+    p.scale_log2 = (float)((double)scale * 1.4426950408889634);  // log2(e)
+    p.threshold = kDefaultThreshold;
+    int n_cu = 0;
+    rc = check_device(&n_cu);
+    if (rc != ATTN_OK) return rc;
+    long long grid = n_records;
+    const long long slots = (long long)(n_cu / kXcds) * kXcds;
+    if (slots > 0 && grid > slots) grid = slots;
+    p.grid = (int)grid;
+    hipError_t err = attn::launch_fwd(p, d_qk, d_v, causal != 0, false, false,
+                                      static_cast<hipStream_t>(stream));
     if (err != hipSuccess) return ATTN_ERR_HIP;
     return ATTN_OK;
 }

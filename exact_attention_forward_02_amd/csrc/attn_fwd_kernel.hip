@@ -183,12 +183,41 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 // blocks in its L2.
 struct TileCoord {
     int split, bk, hq, pos0, qw;
+    int Lq, Lk;    // query rows and keys of the tile's sequence
     size_t qrow0;  // row of (b, hq, position 0) in lse
     size_t qbase, obase, kbase, vbase;  // element offsets of (b, head, row 0)
 };
 
-template <bool CAUSAL>
+template <bool CAUSAL, bool VARLEN>
 __device__ __forceinline__ TileCoord tile_coord(const FwdParams& p, int t, int wave) {
+    TileCoord c;
+    if constexpr (VARLEN) {
+        // A packed variable-length batch: the host's record of tile t gives
+        // its sequence's token offsets and lengths, its unit (K/V head, head
+        // group) and its position block, already in schedule order.  A record
+        // that does not fit the tensors becomes an empty tile.
+        const int* rec = p.plan + kPlanInts * t;
+        int q0 = rec[0], lq = rec[1], k0 = rec[2], lk = rec[3], unit = rec[4], m = rec[5];
+        const bool ok = q0 >= 0 && lq > 0 && lk >= 0 && k0 >= 0 && q0 <= p.total_q - lq &&
+                        k0 <= p.total_k - lk && unit >= 0 && unit < p.units_kv && m >= 0 &&
+                        m * p.bm_pos < lq;
+        if (!ok) q0 = lq = k0 = lk = unit = m = 0;
+        const int hg = unit % p.n_hg;
+        const int kvh = unit / p.n_hg;
+        c.Lq = lq;
+        c.Lk = lk;
+        c.split = 0;
+        c.bk = kvh;
+        c.hq = kvh * p.G + hg * p.Gp + (wave % p.Gp);
+        c.pos0 = m * p.bm_pos;
+        c.qw = c.pos0 + (wave / p.Gp) * kRowsPerWave;
+        c.qrow0 = (size_t)c.hq * p.total_q + q0;  // lse is [Hq, total_q]
+        c.qbase = (size_t)q0 * p.q_sr + (size_t)c.hq * p.q_sh;
+        c.obase = (size_t)q0 * p.o_sr + (size_t)c.hq * p.o_sh;
+        c.kbase = (size_t)k0 * p.k_sr + (size_t)kvh * p.k_sh;
+        c.vbase = (size_t)k0 * p.v_sr + (size_t)kvh * p.v_sh;
+        return c;
+    }
     const int per_sec = p.sec_units * p.n_m;
     int local = t, base = 0;
     if (p.xcd_mode) {
@@ -201,7 +230,8 @@ __device__ __forceinline__ TileCoord tile_coord(const FwdParams& p, int t, int w
     const int unit = base + sec * p.sec_units + (r - mo * p.sec_units);
     // causal tiles are ordered heaviest first (longest processing time first)
     const int m = CAUSAL ? (p.n_m - 1 - mo) : mo;
-    TileCoord c;
+    c.Lq = p.Lq;
+    c.Lk = p.Lk;
     c.split = unit / p.units_kv;  // key split of this tile (0 without splits)
     const int ukv = unit - c.split * p.units_kv;
     const int hg = ukv % p.n_hg;
@@ -232,23 +262,23 @@ __device__ __forceinline__ KeyRange key_range(const FwdParams& p, const TileCoor
     KeyRange r;
     r.jb0 = c.split * p.split_blocks;
     const int kbeg = r.jb0 * kBlockN;
-    const int ksplit = min(p.Lk, kbeg + p.split_blocks * kBlockN);
+    const int ksplit = min(c.Lk, kbeg + p.split_blocks * kBlockN);
     int kend = ksplit;
     int wend = ksplit;
     if (CAUSAL) {
-        const int off = p.Lk - p.Lq;
-        const int tile_last = min(p.Lq, c.pos0 + p.bm_pos) - 1;
+        const int off = c.Lk - c.Lq;
+        const int tile_last = min(c.Lq, c.pos0 + p.bm_pos) - 1;
         kend = min(ksplit, tile_last + off + 1);
-        const int wave_last = min(p.Lq, c.qw + kRowsPerWave) - 1;
+        const int wave_last = min(c.Lq, c.qw + kRowsPerWave) - 1;
         wend = min(ksplit, wave_last + off + 1);
     }
     r.nblk = kend > kbeg ? (kend - kbeg + kBlockN - 1) / kBlockN : 0;
-    r.nact = (c.qw < p.Lq && wend > kbeg) ? min(r.nblk, (wend - kbeg + kBlockN - 1) / kBlockN)
+    r.nact = (c.qw < c.Lq && wend > kbeg) ? min(r.nblk, (wend - kbeg + kBlockN - 1) / kBlockN)
                                           : 0;
     return r;
 }
 
-template <int DQK, int DV, bool CAUSAL, bool DEBUG, bool FP16>
+template <int DQK, int DV, bool CAUSAL, bool DEBUG, bool FP16, bool VARLEN>
 __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
     using S = Shape<DQK, DV>;
     using E = Elem<FP16>;
@@ -332,9 +362,22 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
     size_t qrow0;  // row index of (b, hq, position 0) in lse
     size_t qrow_w, orow_w;  // element offsets of this wave's first Q and O rows
     __amdgpu_buffer_rsrc_t krsrc, vrsrc;
-    const int off = p.Lk - p.Lq;  // causal diagonal offset
+    // query rows and keys of the tile's sequence (the launch's Lq and Lk
+    // unless the batch is packed with variable lengths)
+    int Lq_t = p.Lq, Lk_t = p.Lk;
+    int off = p.Lk - p.Lq;  // causal diagonal offset
+    // byte extent of a K (V) head's rows for its buffer descriptor; empty
+    // when a packed sequence has no keys
+    auto kv_bytes = [&](int lk, int rb, int row) __attribute__((always_inline)) {
+        return (VARLEN && lk <= 0) ? 0u : (uint32_t)(lk - 1) * rb + row;
+    };
     auto set_tile = [&](int t) __attribute__((always_inline)) {
-        const TileCoord c = tile_coord<CAUSAL>(p, t, wave);
+        const TileCoord c = tile_coord<CAUSAL, VARLEN>(p, t, wave);
+        if constexpr (VARLEN) {
+            Lq_t = c.Lq;
+            Lk_t = c.Lk;
+            off = c.Lk - c.Lq;
+        }
         split = c.split;
         qw = c.qw;
         qrow0 = c.qrow0;
@@ -346,8 +389,8 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
         nact = r.nact;
         // one descriptor per K/V head; a head spans less than 2^31 bytes
         // (checked on the host), so 32-bit byte offsets address all of it
-        krsrc = make_rsrc(p.k + c.kbase, (uint32_t)(p.Lk - 1) * k_rb + kRowK);
-        vrsrc = make_rsrc(p.v + c.vbase, (uint32_t)(p.Lk - 1) * v_rb + kRowV);
+        krsrc = make_rsrc(p.k + c.kbase, kv_bytes(c.Lk, k_rb, kRowK));
+        vrsrc = make_rsrc(p.v + c.vbase, kv_bytes(c.Lk, v_rb, kRowV));
     };
     set_tile(tile);
 
@@ -356,7 +399,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
     ex8 qf[S::kKSteps];
     auto load_q_global = [&]() __attribute__((always_inline)) {
         const int qi = qw + l32;
-        const bool ok = qi < p.Lq;
+        const bool ok = qi < Lq_t;
         // lanes past Lq point at row 0 of the head (never read past the tensor)
         const uint16_t* src =
             p.q + (ok ? qrow_w + (size_t)l32 * p.q_sr : qrow_w - (size_t)qw * p.q_sr) + 8 * hi;
@@ -400,7 +443,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
     // destination is a scalar too, so a copy needs no vector arithmetic.
     const int kdst = __builtin_amdgcn_readfirstlane(1024 * S::kKCopies * wq);
     const int vdst = __builtin_amdgcn_readfirstlane(1024 * S::kVCopies * wq);
-    auto copy_kblock = [&](__amdgpu_buffer_rsrc_t rs, int key0, unsigned char* dst)
+    auto copy_kblock = [&](__amdgpu_buffer_rsrc_t rs, int key0, int lk, unsigned char* dst)
                            __attribute__((always_inline)) {
         const uint32_t blk = (uint32_t)key0 * k_rb;
         // an opaque copy of the wave's offset: the destinations are formed
@@ -408,12 +451,12 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
         // and copy and held (or spilled) across the sweep
         int kd = kdst;
         asm volatile("" : "+s"(kd));
-        if (key0 + kBlockN <= p.Lk) {
+        if (key0 + kBlockN <= lk) {
 #pragma unroll
             for (int i = 0; i < S::kKCopies; ++i)
                 copy_to_lds(rs, koff[i], blk, dst + kd + 1024 * i);
         } else {
-            const int last = p.Lk - 1 - key0;
+            const int last = lk - 1 - key0;
 #pragma unroll
             for (int i = 0; i < S::kKCopies; ++i) {
                 const int r = (64 * (wq * S::kKCopies + i) + lane) / S::kChunksK;
@@ -424,19 +467,19 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
         }
     };
     auto copy_k = [&](int jl, unsigned char* dst) __attribute__((always_inline)) {
-        copy_kblock(krsrc, (jb0 + jl) * kBlockN, dst);
+        copy_kblock(krsrc, (jb0 + jl) * kBlockN, Lk_t, dst);
     };
     auto copy_v = [&](int jl, unsigned char* dst) __attribute__((always_inline)) {
         const int key0 = (jb0 + jl) * kBlockN;
         const uint32_t blk = (uint32_t)key0 * v_rb;
         int vd = vdst;
         asm volatile("" : "+s"(vd));
-        if (key0 + kBlockN <= p.Lk) {
+        if (key0 + kBlockN <= Lk_t) {
 #pragma unroll
             for (int i = 0; i < S::kVCopies; ++i)
                 copy_to_lds(vrsrc, voff_copy[i], blk, dst + vd + 1024 * i);
         } else {
-            const int last = p.Lk - 1 - key0;
+            const int last = Lk_t - 1 - key0;
 #pragma unroll
             for (int i = 0; i < S::kVCopies; ++i) {
                 const int r = (64 * (wq * S::kVCopies + i) + lane) / S::kChunksV;
@@ -610,10 +653,10 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
         const int key0 = (jb0 + j) * kBlockN;
         // mask keys past the end or past the causal diagonal
         const bool need_mask =
-            (key0 + kBlockN > p.Lk) || (CAUSAL && key0 + kBlockN - 1 > qw + off);
+            (key0 + kBlockN > Lk_t) || (CAUSAL && key0 + kBlockN - 1 > qw + off);
         if (need_mask) {
             const int qi = qw + l32;
-            const int klim = CAUSAL ? min(p.Lk, qi + off + 1) : p.Lk;
+            const int klim = CAUSAL ? min(Lk_t, qi + off + 1) : Lk_t;
 #pragma unroll
             for (int mb = 0; mb < kBlockN / 32; ++mb)
 #pragma unroll
@@ -644,7 +687,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
         const float acc_scale = moved ? __builtin_amdgcn_exp2f(delta) : 1.0f;
         if (DEBUG && rescale_count != nullptr) {
             // events count reference moves after the first one of a row
-            const unsigned long long ev = __ballot(moved && ref != kNegInf && qw + l32 < p.Lq);
+            const unsigned long long ev = __ballot(moved && ref != kNegInf && qw + l32 < Lq_t);
             if (lane == 0 && ev)
                 atomicAdd(rescale_count, (unsigned long long)__builtin_popcountll(ev & 0xffffffffull));
         }
@@ -752,6 +795,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
     int nq_rows = 0;
     bool nk_copy = false;
     int nk_key0 = 0;
+    int nk_lk = Lk_t;
     __amdgpu_buffer_rsrc_t nk_rsrc = krsrc;
     auto prefetch_q_chunk = [&](int k) __attribute__((always_inline)) {
         const int sl = 64 * k + lane;
@@ -806,13 +850,14 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
         nq_rows = 0;
         nk_copy = false;
         if (has_next) {
-            const TileCoord c = tile_coord<CAUSAL>(p, tile_n, wave);
+            const TileCoord c = tile_coord<CAUSAL, VARLEN>(p, tile_n, wave);
             const KeyRange r = key_range<CAUSAL>(p, c);
             nk_copy = r.nblk > 0;
             nk_key0 = r.jb0 * kBlockN;
-            nk_rsrc = make_rsrc(p.k + c.kbase, (uint32_t)(p.Lk - 1) * k_rb + kRowK);
+            nk_lk = c.Lk;
+            nk_rsrc = make_rsrc(p.k + c.kbase, kv_bytes(c.Lk, k_rb, kRowK));
             if (kStage) {
-                nq_rows = max(0, min(kRowsPerWave, p.Lq - c.qw));
+                nq_rows = max(0, min(kRowsPerWave, c.Lq - c.qw));
                 nq_src = p.q + c.qbase + (size_t)(nq_rows > 0 ? c.qw : 0) * p.q_sr;
             }
         }
@@ -835,7 +880,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
                     if (t + 1 < nblk)
                         copy_k(t + 1, lds_k1);
                     else if (t == nblk && nk_copy)
-                        copy_kblock(nk_rsrc, nk_key0, lds_k0);  // next tile's stage 0
+                        copy_kblock(nk_rsrc, nk_key0, nk_lk, lds_k0);  // next tile's stage 0
                 }
                 work(gc, C0{}, phi, lds_k0, lds_v0);
                 if constexpr (G == 0) {
@@ -851,7 +896,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
                     if (t + 2 < nblk)
                         copy_k(t + 2, lds_k0);
                     else if (t + 1 == nblk && nk_copy)
-                        copy_kblock(nk_rsrc, nk_key0, lds_k0);
+                        copy_kblock(nk_rsrc, nk_key0, nk_lk, lds_k0);
                 }
                 work(gc, C2{}, phi, lds_k1, lds_v1);
                 if constexpr (G == 0) {
@@ -881,7 +926,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
                     for (int k = 0; k < kSliceChunks; ++k) prefetch_q_chunk(k);
                 }
             }
-            if (nk_copy && grp == 1) copy_kblock(nk_rsrc, nk_key0, lds_k0);
+            if (nk_copy && grp == 1) copy_kblock(nk_rsrc, nk_key0, nk_lk, lds_k0);
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
         }
@@ -916,9 +961,9 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
                     }
                 }
                 pend = 1;
-                pend_rows = max(0, min(kRowsPerWave, p.Lq - qw));
+                pend_rows = max(0, min(kRowsPerWave, Lq_t - qw));
                 pend_dst = o_out + orow_w;
-            } else if (qi < p.Lq) {
+            } else if (qi < Lq_t) {
                 uint16_t* orow = o_out + orow_w + (size_t)l32 * p.o_sr;
 #pragma unroll
                 for (int i = 0; i < S::kDvBlocks; ++i) {
@@ -931,8 +976,8 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
                     }
                 }
             }
-            if (hi == 0 && qi < p.Lq) lse_out[qrow0 + qi] = lse_row;
-        } else if (qi < p.Lq) {
+            if (hi == 0 && qi < Lq_t) lse_out[qrow0 + qi] = lse_row;
+        } else if (qi < Lq_t) {
             // one split's state in fp32: its normalised output and lse
             const size_t prow = (size_t)split * p.B * p.Hq * p.Lq + qrow0 + qi;
             float* orow = o_part + prow * DV;
@@ -962,19 +1007,24 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
     }
 }
 
-template <int DQK, int DV, bool CAUSAL, bool DEBUG, bool FP16>
+template <int DQK, int DV, bool CAUSAL, bool DEBUG, bool FP16, bool VARLEN = false>
 hipError_t launch_one(const FwdParams& p, hipStream_t stream) {
     dim3 grid((unsigned)p.grid), block(kThreads);
     FwdParams arg = p;
     void* args[] = {&arg};
     return hipLaunchKernel(
-        reinterpret_cast<const void*>(&attn_fwd_kernel<DQK, DV, CAUSAL, DEBUG, FP16>), grid, block,
+        reinterpret_cast<const void*>(&attn_fwd_kernel<DQK, DV, CAUSAL, DEBUG, FP16, VARLEN>), grid, block,
         args, 0, stream);
 }
 
 template <int DQK, int DV>
 hipError_t launch_dims(const FwdParams& p, bool causal, bool debug, bool fp16,
                        hipStream_t stream) {
+    if (p.plan != nullptr) {  // packed variable-length batch (bf16)
+        if (debug || fp16) return hipErrorInvalidValue;
+        return causal ? launch_one<DQK, DV, true, false, false, true>(p, stream)
+                      : launch_one<DQK, DV, false, false, false, true>(p, stream);
+    }
     if (fp16) {
         if (debug) return hipErrorInvalidValue;  // the debug variant is bf16 only
         return causal ? launch_one<DQK, DV, true, false, true>(p, stream)

@@ -15,6 +15,8 @@ constexpr int kGroupWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kRowsPerWave = 32;     // query rows owned by one wave (MFMA N)
 constexpr int kBlockN = 64;          // keys per K/V block
+constexpr int kPlanInts = 8;         // ints per tile record of a packed variable-length
+                                     // batch: q0, Lq, k0, Lk, unit, position block, 0, 0
 
 struct FwdParams {
     // q, k, v, o: 16-bit elements (bf16 or fp16), element (b, h, i, c) at
@@ -26,6 +28,11 @@ struct FwdParams {
     float* o_part;       // [n_split, B, Hq, Lq, dv] fp32 (per-split output) when set
     float* lse;          // [B, Hq, Lq] fp32, or [n_split, B, Hq, Lq] with o_part
     unsigned long long* rescale_count;  // optional event counter
+    // Packed variable-length batch (nullptr otherwise): tile records in
+    // schedule order, kPlanInts ints each; q, k, v, o are token-major
+    // [T, H, d] and lse is [Hq, total_q].  The launch's Lq and Lk are unused.
+    const int* plan;
+    int total_q, total_k;  // query and key tokens of the packed batch
 
     int B, Hq, Hkv, Lq, Lk;
     int G;          // Hq / Hkv: query heads per K/V head

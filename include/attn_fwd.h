@@ -223,6 +223,54 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
              int B, int Hq, int Hkv, int Lq, int Lk, int d_qk, int d_v,
              int causal, float scale, void* stream);
 
+/*
+ * Packed variable-length batches ("Flash Attention 4 ..." review, method part
+ * on scheduling: variable-length batches are scheduled by the execution time
+ * of their work tiles, longest first).  n_seq sequences are packed along the
+ * token axis; sequence s owns query tokens [cu_seqlens_q[s], cu_seqlens_q[s+1])
+ * and key tokens [cu_seqlens_k[s], cu_seqlens_k[s+1]), and its queries attend
+ * only its own keys, with the causal mask aligned bottom-right inside the
+ * sequence (query i of Lq_s sees keys j <= i + Lk_s - Lq_s).  A sequence may
+ * be empty; rows of a sequence without visible keys get O = 0, lse = -inf.
+ *
+ * attn_varlen_plan -- host-side schedule of such a batch, computed on the
+ * CPU from HOST arrays cu_seqlens_q and cu_seqlens_k (n_seq + 1 ints each,
+ * starting at 0, non-decreasing).  Writes *n_records, the number of tile
+ * records (a multiple of 8), and, when plan is not NULL, the records
+ * themselves: ATTN_VARLEN_RECORD_INTS ints each into the host buffer plan of
+ * `capacity` records.  The order is the schedule: K/V heads dealt to the
+ * chip's 8 dies longest first, tiles longest first within each die's
+ * sections.  The plan depends on the sequence lengths, Hq, Hkv and causal.
+ * Returns ATTN_ERR_NULL_PTR (cu arrays or n_records NULL),
+ * ATTN_ERR_BAD_SHAPE (n_seq < 1, Hq or Hkv < 1, offsets not starting at 0 or
+ * decreasing), ATTN_ERR_GQA_RATIO, ATTN_ERR_BAD_ARGUMENT (capacity too small)
+ * or ATTN_ERR_TOO_LARGE.  No HIP call is made.
+ */
+#define ATTN_VARLEN_RECORD_INTS 8
+int attn_varlen_plan(const int* cu_seqlens_q, const int* cu_seqlens_k, int n_seq, int Hq,
+                     int Hkv, int causal, int* plan, int capacity, int* n_records);
+
+/*
+ * attn_fwd_varlen -- attention forward over a packed variable-length batch.
+ *   q    [total_q, Hq,  d_qk]  bfloat16, token-major and contiguous
+ *   k    [total_k, Hkv, d_qk]  bfloat16
+ *   v    [total_k, Hkv, d_v ]  bfloat16
+ *   o    [total_q, Hq,  d_v ]  bfloat16 (output)
+ *   lse  [Hq, total_q]         float32 (output)
+ *   plan the records of attn_varlen_plan for this batch, Hq, Hkv and causal,
+ *        copied to DEVICE memory (16-byte aligned); n_records of them
+ * A record that does not fit total_q / total_k / the head counts is treated as
+ * an empty tile, so a stale plan cannot make the kernel read or write out of
+ * bounds; a plan built for other lengths gives wrong rows.  Other arguments,
+ * ownership, asynchrony and errors as attn_fwd (one kernel on `stream`), with
+ * ATTN_ERR_BAD_SHAPE for total_q < 1 or total_k < 0, ATTN_ERR_BAD_ARGUMENT for
+ * n_records not a multiple of 8, and ATTN_ERR_TOO_LARGE when K or V spans
+ * 2^31 bytes or more.
+ */
+int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                    const int* plan, int n_records, int total_q, int total_k, int Hq, int Hkv,
+                    int d_qk, int d_v, int causal, float scale, void* stream);
+
 /* attn_status_string -- static, NUL-terminated description of a status code
  * (never NULL; unknown codes give "unknown attn status"). */
 const char* attn_status_string(int status);

@@ -40,7 +40,8 @@ def _exported_symbols(path):
 
 def test_header_declares_the_entry_points():
     assert {"attn_fwd", "attn_fwd_dbg", "attn_fwd_ex", "attn_bwd", "attn_split_keys", "attn_fwd_split",
-            "attn_merge", "attn_status_string", "attn_abi_version"} <= _declared_functions()
+            "attn_merge", "attn_varlen_plan", "attn_fwd_varlen", "attn_status_string",
+            "attn_abi_version"} <= _declared_functions()
 
 
 def test_status_codes_match_header():
@@ -59,7 +60,7 @@ def test_library_exports_every_declared_function():
 
 def test_abi_version_and_status_strings():
     lib = _binding.library()
-    assert lib.attn_abi_version() == 4
+    assert lib.attn_abi_version() == 5
     for code in CODES.values():
         s = _binding.status_string(code)
         assert s and s != "unknown attn status"
@@ -276,3 +277,116 @@ def test_valid_backward_call_without_a_gpu_reports_no_device():
         pytest.skip("a GPU is present")
     assert _call_bwd() == CODES["ATTN_ERR_NO_DEVICE"]
     assert _call_bwd(d_qk=64, d_v=64, causal=1) == CODES["ATTN_ERR_NO_DEVICE"]
+
+
+# --------------------------------------------------------------------------
+# Packed variable-length batches: the host planner and the entry point's checks
+# --------------------------------------------------------------------------
+
+def _plan_cost(rec, causal, bm_pos):
+    q0, lq, k0, lk, unit, m = rec[:6]
+    if lq == 0:
+        return None  # padding
+    kend = lk
+    if causal:
+        kend = min(lk, min(lq, (m + 1) * bm_pos) - 1 + lk - lq + 1)
+    return (max(kend, 0) + 63) // 64 + 2
+
+
+@pytest.mark.parametrize("lens_q,lens_k,Hq,Hkv,causal", [
+    ([7267, 4408, 2434, 1720, 3470, 527, 3413, 5988, 3541], None, 16, 16, True),
+    ([5, 0, 300, 1, 1000], [700, 4, 0, 1, 999], 32, 8, True),
+    ([129, 257, 64], None, 6, 3, False),
+    ([1], [1], 1, 1, False),
+])
+def test_varlen_plan_covers_every_tile_once(lens_q, lens_k, Hq, Hkv, causal):
+    import numpy as np
+    lens_k = lens_k or lens_q
+    cq = np.concatenate([[0], np.cumsum(lens_q)])
+    ck = np.concatenate([[0], np.cumsum(lens_k)])
+    plan = _binding.varlen_plan(cq, ck, Hq, Hkv, causal)
+    assert plan.shape[1] == 8 and plan.shape[0] % 8 == 0
+    G = Hq // Hkv
+    Gp = 8 if G % 8 == 0 else 4 if G % 4 == 0 else 2 if G % 2 == 0 else 1
+    bm_pos = 256 // Gp
+    units = Hkv * (G // Gp)
+    want = {(int(cq[s]), lq, int(ck[s]), lk, u, m)
+            for s, (lq, lk) in enumerate(zip(lens_q, lens_k)) if lq > 0
+            for u in range(units) for m in range(-(-lq // bm_pos))}
+    got = [tuple(int(x) for x in r[:6]) for r in plan if r[1] > 0]
+    assert len(got) == len(set(got)) == len(want) and set(got) == want
+    assert all(not r.any() for r in plan if r[1] == 0), "padding records must be all zero"
+    # Replay the kernel's order (32 workgroups per XCD; XCD x owns records
+    # x, x + 8, ...; round r gives slot s local tile 32 r + s, or 32 r + 31 - s
+    # in odd rounds).  Each tile went to the least loaded slot of its XCD, so
+    # no slot ends later than the XCD's mean load plus its largest tile.
+    loads = []
+    for x in range(8):
+        recs = plan[x::8]
+        assert len(recs) % 32 == 0
+        slot = np.zeros(32)
+        for r in range(len(recs) // 32):
+            for s in range(32):
+                c = _plan_cost(recs[32 * r + (31 - s if r & 1 else s)], causal, bm_pos)
+                slot[s] += c or 0
+        costs = [c for c in (_plan_cost(rec, causal, bm_pos) for rec in recs) if c]
+        if costs:
+            assert slot.max() <= slot.mean() + max(costs) + 1e-9
+        loads.append(slot.sum())
+    # and the XCDs' loads are balanced to within one unit of work
+    unit_cost = max(sum(_plan_cost((0, lq, 0, lk, 0, m), causal, bm_pos)
+                        for m in range(-(-lq // bm_pos))) for lq, lk in zip(lens_q, lens_k) if lq)
+    assert max(loads) - min(loads) <= unit_cost
+
+
+def test_varlen_plan_rejects_bad_offsets():
+    lib = _binding.library()
+    i32p = ctypes.POINTER(ctypes.c_int)
+    n = ctypes.c_int(-1)
+
+    def plan(cq, ck, n_seq, Hq=4, Hkv=2, cap=0, out=None):
+        aq = (ctypes.c_int * len(cq))(*cq)
+        ak = (ctypes.c_int * len(ck))(*ck)
+        return lib.attn_varlen_plan(ctypes.cast(aq, i32p), ctypes.cast(ak, i32p), n_seq, Hq, Hkv,
+                                    1, out, cap, ctypes.byref(n))
+
+    assert plan([0, 5], [0, 5], 1) == 0 and n.value == 256  # one round of 8 x 32
+    assert plan([1, 5], [0, 5], 1) == CODES["ATTN_ERR_BAD_SHAPE"]     # must start at 0
+    assert plan([0, 5, 3], [0, 5, 6], 2) == CODES["ATTN_ERR_BAD_SHAPE"]  # decreasing
+    assert plan([0, 5], [0, 5], 0) == CODES["ATTN_ERR_BAD_SHAPE"]
+    assert plan([0, 5], [0, 5], 1, Hq=3, Hkv=2) == CODES["ATTN_ERR_GQA_RATIO"]
+    small = (ctypes.c_int * 8)()
+    assert plan([0, 5], [0, 5], 1, cap=1, out=ctypes.cast(small, i32p)) == \
+        CODES["ATTN_ERR_BAD_ARGUMENT"]
+    assert lib.attn_varlen_plan(None, None, 1, 1, 1, 0, None, 0, ctypes.byref(n)) == \
+        CODES["ATTN_ERR_NULL_PTR"]
+
+
+VGOOD = dict(q=A, k=A * 2, v=A * 3, o=A * 4, lse=A * 5, plan=A * 6, n_records=8, total_q=100,
+             total_k=100, Hq=4, Hkv=2, d_qk=128, d_v=128, causal=1, scale=0.088, stream=None)
+VORDER = ["q", "k", "v", "o", "lse", "plan", "n_records", "total_q", "total_k", "Hq", "Hkv",
+          "d_qk", "d_v", "causal", "scale", "stream"]
+
+
+@pytest.mark.parametrize("over,code", [
+    ({"plan": None}, "ATTN_ERR_NULL_PTR"),
+    ({"q": None}, "ATTN_ERR_NULL_PTR"),
+    ({"total_q": 0}, "ATTN_ERR_BAD_SHAPE"),
+    ({"total_k": -1}, "ATTN_ERR_BAD_SHAPE"),
+    ({"n_records": 12}, "ATTN_ERR_BAD_ARGUMENT"),
+    ({"Hq": 3}, "ATTN_ERR_GQA_RATIO"),
+    ({"d_qk": 96}, "ATTN_ERR_UNSUPPORTED_HEAD_DIM"),
+    ({"scale": 0.0}, "ATTN_ERR_BAD_SCALE"),
+    ({"plan": A * 6 + 4}, "ATTN_ERR_MISALIGNED"),
+    ({"total_k": 1 << 22}, "ATTN_ERR_TOO_LARGE"),
+])
+def test_varlen_arguments_are_validated_first(over, code):
+    args = dict(VGOOD)
+    args.update(over)
+    assert _binding.library().attn_fwd_varlen(*[args[n] for n in VORDER]) == CODES[code]
+
+
+def test_valid_varlen_call_without_a_gpu_reports_no_device():
+    args = [VGOOD[n] for n in VORDER]
+    assert _binding.library().attn_fwd_varlen(*args) in (CODES["ATTN_ERR_NO_DEVICE"],
+                                                          CODES["ATTN_ERR_UNSUPPORTED_ARCH"])

@@ -1,0 +1,110 @@
+"""GPU parity of the packed variable-length forward (attn_fwd_varlen, on the
+host planner's schedule) against the fp64 oracle, through the C ABI.  Needs an
+MI355X."""
+import numpy as np
+import pytest
+import torch
+
+from exact_attention_forward_02_amd import attn_fwd, attn_fwd_varlen, varlen_plan
+from exact_attention_forward_02_amd.inputs import (VARLEN_WORKLOADS, make_varlen_qkv,
+                                                   varlen_workload_qkv)
+from parity import assert_parity
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+# (lens_q, lens_k, Hq, Hkv, dqk, dv, causal): ragged sequences spanning several
+# position tiles and key blocks with tails, empty sequences (no queries, or no
+# keys), Lq_s > Lk_s under the causal mask (rows without keys), Lq_s < Lk_s,
+# grouped-query packing (G = 4 and 8), d = 64 and (192, 128)
+SHAPES = [
+    ([300, 17, 1000, 64, 129], None, 4, 4, 128, 128, False),
+    ([300, 17, 1000, 64, 129], None, 4, 4, 128, 128, True),
+    ([513, 0, 77, 260], [600, 5, 0, 200], 8, 2, 128, 128, True),
+    ([513, 0, 77, 260], [600, 5, 0, 200], 8, 2, 128, 128, False),
+    ([1, 700, 33], [900, 650, 33], 16, 2, 64, 64, True),
+    ([450, 90], [450, 1100], 3, 1, 192, 128, True),
+    ([450, 90], [450, 1100], 2, 2, 192, 128, False),
+]
+
+
+def _ids(s):
+    return f"{len(s[0])}seq-H{s[2]}-{s[3]}-d{s[4]}-{s[5]}-{'causal' if s[6] else 'full'}"
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=_ids)
+def test_varlen_matches_the_oracle(orc, shape):
+    lens_q, lens_k, Hq, Hkv, dqk, dv, causal = shape
+    lens_k = lens_k or lens_q
+    print(f"[case] varlen {shape}", flush=True)
+    q, k, v, cu_q, cu_k = make_varlen_qkv(lens_q, lens_k, Hq, Hkv, dqk, dv,
+                                          seed=sum(lens_q) + 7 * Hq + dqk)
+    o, lse = attn_fwd_varlen(q.to(DEV), k.to(DEV), v.to(DEV), cu_q, cu_k, causal=causal)
+    torch.cuda.synchronize()
+    o_ref, l_ref = orc.attn_varlen(q, k, v, cu_q, cu_k, causal=causal)
+    # oracle rows are h * Tq + t: the GPU's lse [Hq, Tq] order; O is [Tq, Hq, dv]
+    og = o.permute(1, 0, 2).reshape(-1, dv).cpu()
+    assert_parity(f"varlen {shape}", og, lse.reshape(-1).cpu(), o_ref, l_ref)
+
+
+def test_varlen_q6_stress(orc):
+    """Q x 6: near one-hot rows whose references move inside sequences."""
+    lens = [333, 64, 700]
+    q, k, v, cu_q, cu_k = make_varlen_qkv(lens, lens, 4, 2, 64, 64, seed=66, q_mult=6.0)
+    print("[case] varlen q6", flush=True)
+    o, lse = attn_fwd_varlen(q.to(DEV), k.to(DEV), v.to(DEV), cu_q, cu_k, causal=True)
+    torch.cuda.synchronize()
+    o_ref, l_ref = orc.attn_varlen(q, k, v, cu_q, cu_k, causal=True)
+    assert_parity("varlen q6", o.permute(1, 0, 2).reshape(-1, 64).cpu(), lse.reshape(-1).cpu(),
+                  o_ref, l_ref, stress=True)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_equal_lengths_equal_the_batched_kernel_bitwise(causal):
+    """B sequences of one length: the same rows, blocks and arithmetic as the
+    batched kernel on the [B, H, L, d] copy, so identical bits."""
+    B, L, Hq, Hkv, d = 3, 700, 8, 2, 128
+    print(f"[case] varlen == batched, causal={causal}", flush=True)
+    q, k, v, cu_q, cu_k = make_varlen_qkv([L] * B, [L] * B, Hq, Hkv, d, d, seed=5)
+    o, lse = attn_fwd_varlen(q.to(DEV), k.to(DEV), v.to(DEV), cu_q, cu_k, causal=causal)
+    qb = q.view(B, L, Hq, d).transpose(1, 2).contiguous().to(DEV)
+    kb = k.view(B, L, Hkv, d).transpose(1, 2).contiguous().to(DEV)
+    vb = v.view(B, L, Hkv, d).transpose(1, 2).contiguous().to(DEV)
+    ob, lb = attn_fwd(qb, kb, vb, causal=causal)
+    torch.cuda.synchronize()
+    assert torch.equal(o.view(B, L, Hq, d).transpose(1, 2).cpu(), ob.cpu())
+    assert torch.equal(lse.view(Hq, B, L).transpose(0, 1).cpu(), lb.cpu())
+
+
+def test_explicit_device_plan_gives_the_same_bits():
+    lens = [100, 900, 40]
+    q, k, v, cu_q, cu_k = make_varlen_qkv(lens, lens, 4, 4, 128, 128, seed=9)
+    print("[case] varlen explicit plan", flush=True)
+    plan = torch.from_numpy(varlen_plan(cu_q, cu_k, 4, 4, True)).to(DEV)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    o1, l1 = attn_fwd_varlen(qd, kd, vd, cu_q, cu_k, causal=True, plan=plan)
+    o2, l2 = attn_fwd_varlen(qd, kd, vd, cu_q, cu_k, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_varlen_workload_in_bench_configuration(orc):
+    """varlen_32k at full size, in the launch the benchmark times, on sampled rows."""
+    w = VARLEN_WORKLOADS["varlen_32k"]
+    print(f"[case] {w.name} sampled rows", flush=True)
+    q, k, v, cu_q, cu_k = varlen_workload_qkv(w)
+    o, lse = attn_fwd_varlen(q.to(DEV), k.to(DEV), v.to(DEV), cu_q, cu_k, causal=w.causal)
+    torch.cuda.synchronize()
+    T = q.shape[0]
+    g = torch.Generator().manual_seed(4321)
+    rows = torch.randperm(w.Hq * T, generator=g)[:3000]
+    # each sequence's first and last token of the first and last head
+    edges = [h * T + int(t) for h in (0, w.Hq - 1) for s in range(len(cu_q) - 1)
+             for t in (cu_q[s], cu_q[s + 1] - 1)]
+    rows = torch.unique(torch.cat([rows, torch.tensor(edges)])).numpy()
+    o_ref, l_ref = orc.attn_varlen(q, k, v, cu_q, cu_k, causal=w.causal, rows=rows)
+    og = o.permute(1, 0, 2).reshape(-1, w.dv)[torch.from_numpy(rows).to(DEV)].cpu()
+    lg = lse.reshape(-1)[torch.from_numpy(rows).to(DEV)].cpu()
+    assert_parity(f"{w.name} ({len(rows)} rows)", og, lg, o_ref, l_ref)
+    assert np.isfinite(lse.cpu().numpy()).all()
