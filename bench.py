@@ -376,7 +376,7 @@ def bench_varlen(args, w) -> int:
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(w.name),
             "kernel": "attn_fwd_kernel (varlen)",
             "ms_per_launch": round(ms_launch, 4),
             "ms_per_launch_min": round(min(launch_ms), 4),
