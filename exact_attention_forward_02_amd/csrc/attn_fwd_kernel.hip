@@ -518,6 +518,12 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
     f32x16 oacc[S::kDvBlocks];
     float ref;  // exponent reference, raw q.k units
     float ell;  // this lane's share of sum P (fp32 P), for lse
+    // Compensation of ell (Kahan-Neumaier): minus the low-order part that the
+    // running fp32 sum has rounded away.  After the reference settles, later
+    // blocks can each add far less than half an ulp of ell (millions of keys
+    // with scores far below the maximum); uncompensated, that mass would be
+    // lost and lse biased low by up to its share of the sum.
+    float ell_c;
     // Row sums of the bf16 P that feed the PV product (they normalise O with
     // exactly the weights it was built from), accumulated by a 16x16x32 MFMA
     // with a 0/1 selector as A: in that shape lane l supplies B column l % 16
@@ -533,6 +539,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
             for (int r = 0; r < 16; ++r) oacc[i][r] = 0.0f;
         ref = kNegInf;
         ell = 0.0f;
+        ell_c = 0.0f;
         ell_o = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     };
     ex8 sel;
@@ -698,6 +705,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) oacc[i][r] *= acc_scale;
             ell *= acc_scale;
+            ell_c *= acc_scale;
             // only the register holding this lane's own query matters
             ell_o *= acc_scale;
         }
@@ -732,7 +740,11 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
                 for (int i = 0; i < 8; ++i) e[i] = s[mb][8 * t + i];
                 pb[2 * mb + t] = __builtin_convertvector(e, ex8);
             }
-        ell += ((rs[0] + rs[1]) + (rs[2] + rs[3])) + ((rs[4] + rs[5]) + (rs[6] + rs[7]));
+        const float bsum = ((rs[0] + rs[1]) + (rs[2] + rs[3])) + ((rs[4] + rs[5]) + (rs[6] + rs[7]));
+        const float y = bsum - ell_c;
+        const float t = ell + y;
+        ell_c = (t - ell) - y;
+        ell = t;
     };
 
     // ---- ping-pong sweep over key blocks ---------------------------------------
@@ -936,7 +948,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
         // The next tile's Q leaves the slice before this tile's O enters it.
         if (kStage && nq_rows > 0) load_q_slice();
         const int qi = qw + l32;
-        const float ell_row = pair_sum(ell);
+        const float ell_row = pair_sum(ell - ell_c);
         const float ell_o_row = ((lane >> 4) & 1) ? ell_o[1] : ell_o[0];
         const float inv = ell_o_row > 0.0f ? 1.0f / ell_o_row : 0.0f;
         const float lse_row = ell_row > 0.0f ? ref * scale + logf(ell_row) : kNegInf;

@@ -390,3 +390,11 @@ def test_valid_varlen_call_without_a_gpu_reports_no_device():
     args = [VGOOD[n] for n in VORDER]
     assert _binding.library().attn_fwd_varlen(*args) in (CODES["ATTN_ERR_NO_DEVICE"],
                                                           CODES["ATTN_ERR_UNSUPPORTED_ARCH"])
+
+
+def test_largest_head_is_accepted_and_one_more_key_is_not():
+    """d = 128: a head of 8388607 keys spans 2^31 - 256 bytes, the last size the
+    kernel's 32-bit buffer offsets address; 8388608 keys are rejected."""
+    ok = _call(B=1, Hq=1, Hkv=1, Lq=64, Lk=(2 ** 31 - 1) // 256)
+    assert ok in (CODES["ATTN_ERR_NO_DEVICE"], CODES["ATTN_ERR_UNSUPPORTED_ARCH"])
+    assert _call(B=1, Hq=1, Hkv=1, Lq=64, Lk=2 ** 23) == CODES["ATTN_ERR_TOO_LARGE"]
