@@ -215,7 +215,8 @@ def bench_split(args, w, qd, kd, vd) -> int:
             "unit": "GB/s",
             "frac": round(gbs / PEAK_HBM_GBS, 4),
             "traffic": None,
-            "kernel": "attn_fwd_kernel (split)",
+            "kernel": ("attn_decode_kernel" if w.Lq * (w.Hq // w.Hkv) <= 16 and w.dqk == w.dv
+                       and w.dqk in (64, 128) else "attn_fwd_kernel (split)"),
             "bytes_per_launch": split_bytes,
             "ms_per_launch": round(ms_split, 4),
             "ms_per_launch_min": round(min(split_ms), 4),

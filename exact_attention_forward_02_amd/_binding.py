@@ -59,6 +59,9 @@ def _load():
         lib.attn_fwd_split.restype = i
         lib.attn_fwd_split.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i,
                                        ctypes.c_float, i, vp]
+        lib.attn_fwd_decode.restype = i
+        lib.attn_fwd_decode.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i,
+                                        ctypes.c_float, i, vp]
         lib.attn_merge.restype = i
         lib.attn_merge.argtypes = [vp, vp, vp, vp, i, ctypes.c_longlong, i, vp]
         lib.attn_varlen_plan.restype = i
@@ -265,10 +268,7 @@ def split_keys(Lk: int, n_split: int) -> int:
     return w
 
 
-def attn_fwd_split(q, k, v, n_split: int, causal: bool = False, scale: float | None = None,
-                   o_part=None, lse_part=None, stream=None):
-    """Per-split states (o_part fp32 [n_split,B,Hq,Lq,d_v], lse_part fp32
-    [n_split,B,Hq,Lq]): the forward pass over each key split alone."""
+def _split_call(name, q, k, v, n_split, causal, scale, o_part, lse_part, stream):
     lib = _load()
     B, Hq, Hkv, Lq, Lk, dqk, dv = _check_inputs(q, k, v)
     if scale is None:
@@ -286,12 +286,29 @@ def attn_fwd_split(q, k, v, n_split: int, causal: bool = False, scale: float | N
         raise ValueError("lse_part must be a contiguous fp32 [n_split, B, Hq, Lq] tensor")
     with torch.cuda.device(q.device):
         s = stream if stream is not None else torch.cuda.current_stream(q.device)
-        rc = lib.attn_fwd_split(q.data_ptr(), k.data_ptr(), v.data_ptr(), o_part.data_ptr(),
+        rc = getattr(lib, name)(q.data_ptr(), k.data_ptr(), v.data_ptr(), o_part.data_ptr(),
                                 lse_part.data_ptr(), B, Hq, Hkv, Lq, Lk, dqk, dv,
                                 int(bool(causal)), float(scale), n, s.cuda_stream)
     if rc != ATTN_OK:
-        raise RuntimeError(f"attn_fwd_split failed: {status_string(rc)} (code {rc})")
+        raise RuntimeError(f"{name} failed: {status_string(rc)} (code {rc})")
     return o_part, lse_part
+
+
+def attn_fwd_split(q, k, v, n_split: int, causal: bool = False, scale: float | None = None,
+                   o_part=None, lse_part=None, stream=None):
+    """Per-split states (o_part fp32 [n_split,B,Hq,Lq,d_v], lse_part fp32
+    [n_split,B,Hq,Lq]): the forward pass over each key split alone."""
+    return _split_call("attn_fwd_split", q, k, v, n_split, causal, scale, o_part, lse_part,
+                       stream)
+
+
+def attn_fwd_decode(q, k, v, n_split: int, causal: bool = False, scale: float | None = None,
+                    o_part=None, lse_part=None, stream=None):
+    """attn_fwd_split's per-split states from the key-streaming decode kernel
+    (Lq * Hq / Hkv <= 16, d_qk == d_v in {64, 128}); attn_fwd_split selects it
+    by itself for such shapes."""
+    return _split_call("attn_fwd_decode", q, k, v, n_split, causal, scale, o_part, lse_part,
+                       stream)
 
 
 def attn_merge(o_part, lse_part, out=None, lse=None, stream=None):

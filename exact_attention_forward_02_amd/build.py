@@ -10,7 +10,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIBRARY = os.path.join(PKG, "libattn_fwd.so")
 SOURCES = [os.path.join(CSRC, "attn_fwd_kernel.hip"), os.path.join(CSRC, "attn_merge_kernel.hip"),
-           os.path.join(CSRC, "attn_bwd_kernel.hip"),
+           os.path.join(CSRC, "attn_bwd_kernel.hip"), os.path.join(CSRC, "attn_decode_kernel.hip"),
            os.path.join(CSRC, "attn_api.cpp")]
 ARCH = "gfx950"
 

@@ -431,10 +431,56 @@ int attn_split_keys(int Lk, int n_split) {
     return split_keys(Lk, n_split);
 }
 
+int attn_fwd_decode(const void* q, const void* k, const void* v, float* o_part, float* lse_part,
+                    int B, int Hq, int Hkv, int Lq, int Lk, int d_qk, int d_v, int causal,
+                    float scale, int n_split, void* stream) {
+    int rc = check_args(q, k, v, o_part, lse_part, B, Hq, Hkv, Lq, Lk, d_qk, d_v, scale);
+    if (rc != ATTN_OK) return rc;
+    if (!(d_qk == d_v && (d_qk == 64 || d_qk == 128))) return ATTN_ERR_UNSUPPORTED_HEAD_DIM;
+    if (n_split < 1 || n_split > kMaxSplits) return ATTN_ERR_BAD_ARGUMENT;
+    if ((long long)Lq * (Hq / Hkv) > attn::kDecRows) return ATTN_ERR_BAD_ARGUMENT;
+    rc = check_strides(contiguous_strides(Hq, Hkv, Lq, Lk, d_qk, d_v), B, Hq, Hkv, Lq, Lk, d_qk,
+                       d_v);
+    if (rc != ATTN_OK) return rc;
+    const long long grid = (long long)n_split * B * Hkv;
+    if ((long long)n_split * B * Hq * Lq > INT32_MAX || grid > INT32_MAX) return ATTN_ERR_TOO_LARGE;
+    attn::DecParams p;
+    memset(&p, 0, sizeof p);
+    p.q = static_cast<const uint16_t*>(q);
+    p.k = static_cast<const uint16_t*>(k);
+    p.v = static_cast<const uint16_t*>(v);
+    p.o_part = o_part;
+    p.lse_part = lse_part;
+    p.B = B;
+    p.Hq = Hq;
+    p.Hkv = Hkv;
+    p.Lq = Lq;
+    p.Lk = Lk;
+    p.G = Hq / Hkv;
+    p.R = Lq * p.G;
+    p.n_split = n_split;
+    p.split_w = split_keys(Lk, n_split);
+    p.grid = (int)grid;
+    p.scale = scale;
+    p.scale_log2 = (float)((double)scale * 1.4426950408889634);  // log2(e)
+    p.threshold = kDefaultThreshold;
+    rc = check_device();
+    if (rc != ATTN_OK) return rc;
+    if (attn::launch_decode(p, d_qk, causal != 0, static_cast<hipStream_t>(stream)) !=
+        hipSuccess)
+        return ATTN_ERR_HIP;
+    return ATTN_OK;
+}
+
 int attn_fwd_split(const void* q, const void* k, const void* v, float* o_part, float* lse_part,
                    int B, int Hq, int Hkv, int Lq, int Lk, int d_qk, int d_v, int causal,
                    float scale, int n_split, void* stream) {
     if (n_split < 1 || n_split > kMaxSplits) return ATTN_ERR_BAD_ARGUMENT;
+    // few query rows per K/V head: the key-streaming decode kernel
+    if (Hkv >= 1 && Hq % Hkv == 0 && Lq >= 1 && (long long)Lq * (Hq / Hkv) <= attn::kDecRows &&
+        d_qk == d_v && (d_qk == 64 || d_qk == 128))
+        return attn_fwd_decode(q, k, v, o_part, lse_part, B, Hq, Hkv, Lq, Lk, d_qk, d_v, causal,
+                               scale, n_split, stream);
     return run(q, k, v, o_part, lse_part, B, Hq, Hkv, Lq, Lk, d_qk, d_v, causal, scale, stream,
                kDefaultThreshold, nullptr, false, n_split);
 }

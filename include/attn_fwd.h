@@ -224,6 +224,22 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
              int causal, float scale, void* stream);
 
 /*
+ * attn_fwd_decode -- attn_fwd_split's per-split states, computed by a kernel
+ * that streams the keys for few query rows per K/V head: at most 16 rows,
+ * Lq * (Hq / Hkv) <= 16, as in decoding one or a few new tokens per sequence
+ * ("Infra: Flash Attention", section on prefill versus decode).  Arguments,
+ * layouts, splits and outputs as attn_fwd_split (contiguous bf16 tensors);
+ * d_qk == d_v in {64, 128} (ATTN_ERR_UNSUPPORTED_HEAD_DIM otherwise).
+ * Returns ATTN_ERR_BAD_ARGUMENT when Lq * (Hq / Hkv) > 16 or n_split is
+ * outside [1, 4096]; other errors as attn_fwd.  attn_fwd_split calls it by
+ * itself for every shape it accepts, so this entry point only pins the
+ * choice.  One kernel on `stream`.
+ */
+int attn_fwd_decode(const void* q, const void* k, const void* v, float* o_part, float* lse_part,
+                    int B, int Hq, int Hkv, int Lq, int Lk, int d_qk, int d_v,
+                    int causal, float scale, int n_split, void* stream);
+
+/*
  * Packed variable-length batches ("Flash Attention 4 ..." review, method part
  * on scheduling: variable-length batches are scheduled by the execution time
  * of their work tiles, longest first).  n_seq sequences are packed along the

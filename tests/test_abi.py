@@ -40,7 +40,8 @@ def _exported_symbols(path):
 
 def test_header_declares_the_entry_points():
     assert {"attn_fwd", "attn_fwd_dbg", "attn_fwd_ex", "attn_bwd", "attn_split_keys", "attn_fwd_split",
-            "attn_merge", "attn_varlen_plan", "attn_fwd_varlen", "attn_status_string",
+            "attn_merge", "attn_varlen_plan", "attn_fwd_varlen", "attn_fwd_decode",
+            "attn_status_string",
             "attn_abi_version"} <= _declared_functions()
 
 
@@ -398,3 +399,31 @@ def test_largest_head_is_accepted_and_one_more_key_is_not():
     ok = _call(B=1, Hq=1, Hkv=1, Lq=64, Lk=(2 ** 31 - 1) // 256)
     assert ok in (CODES["ATTN_ERR_NO_DEVICE"], CODES["ATTN_ERR_UNSUPPORTED_ARCH"])
     assert _call(B=1, Hq=1, Hkv=1, Lq=64, Lk=2 ** 23) == CODES["ATTN_ERR_TOO_LARGE"]
+
+
+def _call_decode(**over):
+    args = dict(GOOD, B=2, Hq=8, Hkv=2, Lq=1, Lk=1000, n_split=4)
+    args.update(over)
+    order = ["q", "k", "v", "o", "lse", "B", "Hq", "Hkv", "Lq", "Lk", "d_qk", "d_v", "causal",
+             "scale", "n_split", "stream"]
+    return _binding.library().attn_fwd_decode(*[args[n] for n in order])
+
+
+@pytest.mark.parametrize("over,code", [
+    ({"q": None}, "ATTN_ERR_NULL_PTR"),
+    ({"Lq": 0}, "ATTN_ERR_BAD_SHAPE"),
+    ({"Hq": 6, "Hkv": 4}, "ATTN_ERR_GQA_RATIO"),
+    ({"d_qk": 192, "d_v": 128}, "ATTN_ERR_UNSUPPORTED_HEAD_DIM"),
+    ({"Lq": 5}, "ATTN_ERR_BAD_ARGUMENT"),          # 5 x 4 = 20 rows per K/V head
+    ({"Hq": 34, "Hkv": 2}, "ATTN_ERR_BAD_ARGUMENT"),  # 17 rows
+    ({"n_split": 0}, "ATTN_ERR_BAD_ARGUMENT"),
+    ({"scale": float("nan")}, "ATTN_ERR_BAD_SCALE"),
+    ({"Lk": 2 ** 23}, "ATTN_ERR_TOO_LARGE"),
+])
+def test_decode_arguments_are_validated_first(over, code):
+    assert _call_decode(**over) == CODES[code]
+
+
+def test_valid_decode_call_without_a_gpu_reports_no_device():
+    assert _call_decode() in (CODES["ATTN_ERR_NO_DEVICE"], CODES["ATTN_ERR_UNSUPPORTED_ARCH"])
+    assert _call_decode(Lq=4) in (CODES["ATTN_ERR_NO_DEVICE"], CODES["ATTN_ERR_UNSUPPORTED_ARCH"])
