@@ -3,6 +3,7 @@ from __future__ import annotations
 
 import os
 import subprocess
+import tempfile
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -21,6 +22,15 @@ HIPCC_FLAGS = [
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]
 
+# Per-source code generation options.  The backward kernels keep their MFMA
+# results in VGPRs: with the default choice the score and dP accumulators land
+# in AGPRs and every softmax element is moved out and back (about 880 AGPR
+# moves per dK/dV loop body at d = 128, 360 with this option); measured 4%
+# faster on mha_l2k, causal_l8k and gqa_l16k with bit-identical gradients.
+SOURCE_FLAGS = {
+    "attn_bwd_kernel.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+}
+
 
 def hipcc() -> str:
     rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
@@ -28,12 +38,28 @@ def hipcc() -> str:
     return cand if os.path.exists(cand) else "hipcc"
 
 
+def source_flags(source: str):
+    return SOURCE_FLAGS.get(os.path.basename(source), [])
+
+
 def build(output: str = LIBRARY, extra_flags=()) -> str:
-    """Build libattn_fwd.so and return its path (always recompiles)."""
-    tmp = output + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, *extra_flags, "-o", tmp, *SOURCES]
-    subprocess.run(cmd, check=True)
-    os.replace(tmp, output)
+    """Build libattn_fwd.so and return its path (always recompiles): each
+    source to its own object with its own options, in parallel, then one link."""
+    compile_flags = [f for f in HIPCC_FLAGS if f != "-shared"]
+    with tempfile.TemporaryDirectory() as tmp:
+        objs, procs = [], []
+        for src in SOURCES:
+            obj = os.path.join(tmp, os.path.basename(src) + ".o")
+            cmd = [hipcc(), *compile_flags, *source_flags(src), *extra_flags, "-c", "-o", obj, src]
+            procs.append((subprocess.Popen(cmd), cmd))
+            objs.append(obj)
+        failed = [cmd for p, cmd in procs if p.wait() != 0]
+        if failed:
+            raise subprocess.CalledProcessError(1, failed[0])
+        tmp_out = output + ".tmp"
+        subprocess.run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp_out,
+                        *objs], check=True)
+    os.replace(tmp_out, output)
     return output
 
 

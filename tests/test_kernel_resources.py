@@ -12,7 +12,7 @@ from exact_attention_forward_02_amd import build
 
 def _remarks(source):
     cmd = [build.hipcc(), *[f for f in build.HIPCC_FLAGS if f not in ("-shared", "-fPIC")],
-           "-c", source, "-o", "/dev/null",
+           *build.source_flags(source), "-c", source, "-o", "/dev/null",
            "-Rpass-analysis=kernel-resource-usage"]
     out = subprocess.run(cmd, capture_output=True, text=True, check=True)
     return out.stderr
@@ -53,3 +53,14 @@ def test_decode_kernel_resources():
     scratch = [int(x) for x in re.findall(r"ScratchSize \[bytes/lane\]: (\d+)", text)]
     spills = [int(x) for x in re.findall(r"VGPRs Spill: (\d+)", text)]
     assert scratch == [0] * 4 and spills == [0] * 4, (scratch, spills)
+
+
+@pytest.mark.skipif(shutil.which(build.hipcc()) is None and not build.hipcc().startswith("/"),
+                    reason="hipcc not available")
+def test_backward_kernel_resources():
+    text = _remarks(build.SOURCES[2])
+    kernels = re.findall(r"Function Name: (\S+)", text)
+    assert len(kernels) == 10, kernels  # (D, dK/dV, dQ) x d = 64, 128, causal or not
+    scratch = [int(x) for x in re.findall(r"ScratchSize \[bytes/lane\]: (\d+)", text)]
+    spills = [int(x) for x in re.findall(r"VGPRs Spill: (\d+)", text)]
+    assert scratch == [0] * 10 and spills == [0] * 10, (scratch, spills)
