@@ -27,24 +27,26 @@ if ROOT not in sys.path:
 METRIC = "attention fwd TFLOP/s (bf16, 1 GPU) and % of MI355X dense bf16 MFMA peak"
 PEAK_BF16_TFLOPS = 2500.0  # MI355X published dense bf16 MFMA peak
 PEAK_HBM_GBS = 8000.0      # MI355X published HBM3E bandwidth
-KERNEL_SOURCE = os.path.join(ROOT, "exact_attention_forward_02_amd", "csrc",
-                             "attn_fwd_kernel.hip")
+CSRC = os.path.join(ROOT, "exact_attention_forward_02_amd", "csrc")
+KERNEL_SOURCE = os.path.join(CSRC, "attn_fwd_kernel.hip")
+DECODE_SOURCE = os.path.join(CSRC, "attn_decode_kernel.hip")
 
 
-def kernel_source_digest() -> str:
-    with open(KERNEL_SOURCE, "rb") as f:
+def kernel_source_digest(path: str = KERNEL_SOURCE) -> str:
+    with open(path, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def measured_traffic(workload: str):
-    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
-    taken on the current kernel source; otherwise None."""
-    path = os.path.join(ROOT, "profiles", f"traffic_attn_fwd_{workload}.json")
+def measured_traffic(workload: str, kernel: str = "attn_fwd", source: str = KERNEL_SOURCE):
+    """HBM bytes per launch from committed rocprofv3 counter runs
+    (profiles/traffic_<kernel>_<workload>.json), if they were taken on the
+    current kernel source; otherwise None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
     if not os.path.exists(path):
         return None
     with open(path, encoding="utf-8") as f:
         rec = json.load(f)
-    if rec.get("kernel_source_sha256") != kernel_source_digest():
+    if rec.get("kernel_source_sha256") != kernel_source_digest(source):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -192,6 +194,7 @@ def bench_split(args, w, qd, kd, vd) -> int:
                    + n * rows * (4 * w.dv + 4))
     merge_bytes = n * rows * (4 * w.dv + 4) + rows * (2 * w.dv + 4)
     gbs = split_bytes / (ms_split * 1e-3) / 1e9
+    decode = w.Lq * (w.Hq // w.Hkv) <= 16 and w.dqk == w.dv and w.dqk in (64, 128)
     result = {
         "metric": METRIC,
         "value": round(flops * args.steps / wall / 1e12, 3),
@@ -214,9 +217,9 @@ def bench_split(args, w, qd, kd, vd) -> int:
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": round(gbs / PEAK_HBM_GBS, 4),
-            "traffic": None,
-            "kernel": ("attn_decode_kernel" if w.Lq * (w.Hq // w.Hkv) <= 16 and w.dqk == w.dv
-                       and w.dqk in (64, 128) else "attn_fwd_kernel (split)"),
+            "traffic": (measured_traffic(w.name, "attn_decode", DECODE_SOURCE) if decode
+                        else None),
+            "kernel": "attn_decode_kernel" if decode else "attn_fwd_kernel (split)",
             "bytes_per_launch": split_bytes,
             "ms_per_launch": round(ms_split, 4),
             "ms_per_launch_min": round(min(split_ms), 4),

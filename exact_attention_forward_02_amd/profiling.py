@@ -32,8 +32,8 @@ KERNEL_SOURCE = os.path.join(ROOT, "exact_attention_forward_02_amd", "csrc",
                              "attn_fwd_kernel.hip")
 
 
-def kernel_source_digest() -> str:
-    with open(KERNEL_SOURCE, "rb") as f:
+def kernel_source_digest(path: str = KERNEL_SOURCE) -> str:
+    with open(path, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()
 
 
@@ -127,7 +127,8 @@ def cmd_traffic(args):
     rec = {
         "kernel": args.kernel,
         "workload": args.workload,
-        "kernel_source_sha256": kernel_source_digest(),
+        "kernel_source": os.path.basename(args.source),
+        "kernel_source_sha256": kernel_source_digest(args.source),
         "fetch_kib_per_dispatch": fetch["FETCH_SIZE"],
         "write_kib_per_dispatch": write["WRITE_SIZE"],
         "dispatches": [nf, nw],
@@ -171,6 +172,8 @@ def main(argv=None):
     c.add_argument("--copy-bytes", type=float, required=True)
     c.add_argument("--copy-kernel", default="neg")  # the calibration copy is torch.neg
     c.add_argument("--kernel", default="attn_fwd_kernel")
+    c.add_argument("--source", default=KERNEL_SOURCE,
+                   help="the kernel's source file, whose hash the record carries")
     c.add_argument("--workload", required=True)
     c.add_argument("--out")
     c.set_defaults(fn=cmd_traffic)
