@@ -79,7 +79,7 @@ def cpu_baseline(w, q, k, v, target_s: float = 12.0):
     n = int(min(total_rows, max(len(probe), len(probe) * target_s / max(t_probe, 1e-6))))
     rows = sample_rows(w.B, w.Hq, w.Lq, n, seed=54321).numpy()
     t0 = time.perf_counter()
-    orc.attn_rows(q, k, v, causal=w.causal, rows=rows, threads=threads)
+    o_ref, l_ref = orc.attn_rows(q, k, v, causal=w.causal, rows=rows, threads=threads)
     dt = time.perf_counter() - t0
     if dt < 0.5 * target_s and n < total_rows:
         # the small probe overstates the per-row cost (thread start-up): size
@@ -87,7 +87,7 @@ def cpu_baseline(w, q, k, v, target_s: float = 12.0):
         n = int(min(total_rows, n * target_s / max(dt, 1e-6)))
         rows = sample_rows(w.B, w.Hq, w.Lq, n, seed=54321).numpy()
         t0 = time.perf_counter()
-        orc.attn_rows(q, k, v, causal=w.causal, rows=rows, threads=threads)
+        o_ref, l_ref = orc.attn_rows(q, k, v, causal=w.causal, rows=rows, threads=threads)
         dt = time.perf_counter() - t0
     # exact FLOPs of the sampled rows
     if w.causal:
@@ -105,7 +105,34 @@ def cpu_baseline(w, q, k, v, target_s: float = 12.0):
         "sample": f"{len(rows)} of {total_rows} query rows of {w.name} drawn at random "
                   f"(seeded), fp64 materialised softmax, {dt:.1f} s",
         "seconds": dt,
+        # the oracle's rows, for the parity summary of the timed output
+        "_rows": rows, "_o": o_ref, "_lse": l_ref,
     }
+
+
+def parity_summary(o_gpu, lse_gpu, o_ref, lse_ref) -> dict:
+    """max / mean |dO| and max |dlse| of GPU rows against the oracle's (rows
+    without a visible key must be O = 0, lse = -inf)."""
+    import numpy as np
+
+    empty = np.isneginf(lse_ref)
+    full = ~empty
+    err = np.abs(o_gpu[full] - o_ref[full])
+    return {
+        "rows": int(len(lse_ref)),
+        "o_max": float(err.max()) if err.size else 0.0,
+        "o_mean": float(err.mean()) if err.size else 0.0,
+        "lse_max": float(np.abs(lse_gpu[full] - lse_ref[full]).max()) if full.any() else 0.0,
+        "empty_rows_exact": bool(np.all(o_gpu[empty] == 0.0) and np.all(np.isneginf(lse_gpu[empty]))),
+    }
+
+
+def environment(dev) -> dict:
+    import torch
+
+    prop = torch.cuda.get_device_properties(dev)
+    return {"device": prop.name, "compute_units": prop.multi_processor_count,
+            "torch": torch.__version__, "hip": getattr(torch.version, "hip", None)}
 
 
 COPY_BYTES = 1 << 30  # bytes read (and written) per calibration launch
@@ -373,6 +400,7 @@ def bench_varlen(args, w) -> int:
                    "seq_lens": lens, "Hq": w.Hq, "Hkv": w.Hkv, "d_qk": w.dqk, "d_v": w.dv,
                    "causal": w.causal, "layout": "thd", "flops_per_step": flops,
                    "tile_records": int(plan_host.shape[0]), "plan_ms": round(plan_ms, 3)},
+        "env": environment(dev),
         "pct_of_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "roofline": {
             "bound": "mfma",
@@ -383,6 +411,7 @@ def bench_varlen(args, w) -> int:
             "traffic": measured_traffic(w.name),
             "kernel": "attn_fwd_kernel (varlen)",
             "ms_per_launch": round(ms_launch, 4),
+            "ms_per_launch_median": round(sorted(launch_ms)[len(launch_ms) // 2], 4),
             "ms_per_launch_min": round(min(launch_ms), 4),
             "ms_per_launch_max": round(max(launch_ms), 4),
         },
@@ -394,7 +423,8 @@ def bench_varlen(args, w) -> int:
         n_rows = min(w.Hq * T, 10000 * threads)  # about 10 s of fp64 work
         rows = torch.randperm(w.Hq * T, generator=g)[:n_rows].numpy()
         t0 = time.perf_counter()
-        orc.attn_varlen(q, k, v, cu_q, cu_k, causal=w.causal, rows=rows, threads=threads)
+        o_ref, l_ref = orc.attn_varlen(q, k, v, cu_q, cu_k, causal=w.causal, rows=rows,
+                                       threads=threads)
         dt = time.perf_counter() - t0
         # exact FLOPs of the sampled rows: each sees its visible keys
         cq = np.asarray(cu_q)
@@ -409,6 +439,11 @@ def bench_varlen(args, w) -> int:
             "kind": "oracle",
             "sample": f"{len(rows)} of {w.Hq * T} query rows of {w.name} drawn at random "
                       f"(seeded), fp64 materialised softmax, {dt:.1f} s"}
+        ridx = torch.from_numpy(rows).to(dev)
+        og = o.permute(1, 0, 2).reshape(-1, w.dv).index_select(0, ridx)
+        lg = lse.reshape(-1).index_select(0, ridx)
+        result["parity"] = parity_summary(og.double().cpu().numpy(), lg.double().cpu().numpy(),
+                                          o_ref, l_ref)
     print(json.dumps(result), flush=True)
     return 0
 
@@ -502,6 +537,7 @@ def main() -> int:
     launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
     ms_launch = sum(launch_ms) / len(launch_ms)
     ms_step = wall * 1e3 / args.steps
+    import statistics
 
     flops = w.flops()
     value = flops * args.steps / wall / 1e12
@@ -535,15 +571,25 @@ def main() -> int:
             "traffic": traffic,
             "kernel": "attn_fwd_kernel",
             "ms_per_launch": round(ms_launch, 4),
+            "ms_per_launch_median": round(statistics.median(launch_ms), 4),
             "ms_per_launch_min": round(min(launch_ms), 4),
             "ms_per_launch_max": round(max(launch_ms), 4),
         },
+        "env": environment(dev),
     }
     if not args.no_cpu_baseline:
         cb = cpu_baseline(w, q, k, v)
         cb.pop("seconds", None)
         cb["value"] = float(f"{cb['value']:.4g}")
+        rows = torch.as_tensor(cb.pop("_rows"), dtype=torch.int64)
+        o_ref, l_ref = cb.pop("_o"), cb.pop("_lse")
+        og = o.contiguous().reshape(-1, w.dv).index_select(0, rows.to(dev))
+        lg = lse.reshape(-1).index_select(0, rows.to(dev))
         result["cpu_baseline"] = cb
+        # the timed launches' output on the oracle's rows (no assertion here:
+        # the tests hold the bar)
+        result["parity"] = parity_summary(og.double().cpu().numpy(), lg.double().cpu().numpy(),
+                                          o_ref, l_ref)
     print(json.dumps(result), flush=True)
     return 0
 

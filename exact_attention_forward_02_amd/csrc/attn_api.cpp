@@ -4,7 +4,10 @@
 // on the caller's stream.
 
 #include <math.h>
+#include <stdarg.h>
 #include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <algorithm>
@@ -33,6 +36,25 @@ std::atomic<int> g_arch_ok[kMaxDevices];
 std::atomic<int> g_cu_count[kMaxDevices];
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Launch log: with ATTN_LOG set to a non-empty value other than "0", every
+// launch prints its kernel, instantiation and grid to stderr.  Off by default.
+bool log_enabled() {
+    static const bool on = [] {
+        const char* e = getenv("ATTN_LOG");
+        return e != nullptr && e[0] != '\0' && strcmp(e, "0") != 0;
+    }();
+    return on;
+}
+void log_launch(const char* fmt, ...) {
+    if (!log_enabled()) return;
+    va_list ap;
+    va_start(ap, fmt);
+    fputs("[attn] ", stderr);
+    vfprintf(stderr, fmt, ap);
+    fputc('\n', stderr);
+    va_end(ap);
+}
 
 // Element strides of the four 16-bit tensors: (batch, head, row), head dim contiguous.
 struct Strides {
@@ -225,6 +247,10 @@ int run(const void* q, const void* k, const void* v, void* o, float* lse, int B,
     const long long slots = (long long)(n_cu / kXcds) * kXcds;
     if (slots > 0 && tiles > slots) grid = slots;
     p.grid = (int)grid;
+    log_launch("attn_fwd_kernel<%d,%d,%s%s%s> grid %d, %d tiles (units %d x position tiles %d), "
+               "splits %d, query heads per workgroup %d, xcd_mode %d",
+               d_qk, d_v, causal ? "causal" : "full", debug ? ",debug" : "", fp16 ? ",fp16" : "",
+               p.grid, p.units * p.n_m, p.units, p.n_m, p.n_split, p.Gp, p.xcd_mode);
     hipError_t err = attn::launch_fwd(p, d_qk, d_v, causal != 0, debug, fp16,
                                       static_cast<hipStream_t>(stream));
     if (err != hipSuccess) return ATTN_ERR_HIP;
@@ -421,6 +447,7 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
     p.G = Hq / Hkv;
     p.scale = scale;
     p.scale_log2 = (float)((double)scale * 1.4426950408889634);
+    log_launch("attn_bwd<%d,%s>: delta, dK/dV and dQ kernels", d_qk, causal ? "causal" : "full");
     hipError_t err = attn::launch_bwd(p, d_qk, causal != 0, static_cast<hipStream_t>(stream));
     return err == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
@@ -466,6 +493,8 @@ int attn_fwd_decode(const void* q, const void* k, const void* v, float* o_part, 
     p.threshold = kDefaultThreshold;
     rc = check_device();
     if (rc != ATTN_OK) return rc;
+    log_launch("attn_decode_kernel<%d,%s> grid %d (splits %d of %d keys), rows per K/V head %d",
+               d_qk, causal ? "causal" : "full", p.grid, p.n_split, p.split_w, p.R);
     if (attn::launch_decode(p, d_qk, causal != 0, static_cast<hipStream_t>(stream)) !=
         hipSuccess)
         return ATTN_ERR_HIP;
@@ -494,6 +523,7 @@ int attn_merge(const float* o_part, const float* lse_part, void* o, float* lse, 
         return ATTN_ERR_MISALIGNED;
     int rc = check_device();
     if (rc != ATTN_OK) return rc;
+    log_launch("attn_merge_kernel<%d>: %lld rows, %d splits", d_v, rows, n_split);
     hipError_t err = attn::launch_merge(o_part, lse_part, static_cast<uint16_t*>(o), lse,
                                         n_split, rows, d_v, static_cast<hipStream_t>(stream));
     if (err != hipSuccess) return ATTN_ERR_HIP;
@@ -579,6 +609,8 @@ int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float*
     const long long slots = (long long)(n_cu / kXcds) * kXcds;
     if (slots > 0 && grid > slots) grid = slots;
     p.grid = (int)grid;
+    log_launch("attn_fwd_kernel<%d,%d,%s,varlen> grid %d, %d tile records", d_qk, d_v,
+               causal ? "causal" : "full", p.grid, n_records);
     hipError_t err = attn::launch_fwd(p, d_qk, d_v, causal != 0, false, false,
                                       static_cast<hipStream_t>(stream));
     if (err != hipSuccess) return ATTN_ERR_HIP;

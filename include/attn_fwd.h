@@ -35,6 +35,9 @@
  * execution surface at the caller's next synchronisation.  The library keeps
  * no mutable state between calls except a per-device cache of the
  * architecture check, and may be called from several host threads.
+ *
+ * Logging: with the environment variable ATTN_LOG set (to anything but "0"),
+ * every launch prints its kernel, instantiation and grid to stderr.
  */
 #ifndef ATTN_FWD_H
 #define ATTN_FWD_H
