@@ -27,8 +27,11 @@ HIPCC_FLAGS = [
 # in AGPRs and every softmax element is moved out and back (about 880 AGPR
 # moves per dK/dV loop body at d = 128, 360 with this option); measured 4%
 # faster on mha_l2k, causal_l8k and gqa_l16k with bit-identical gradients.
+# The scheduler's AMDGPU register-pressure trackers add 1-2% on top (side by
+# side: mha_l2k 630-633 -> 639-648, gqa_l16k 637-642 -> 642-646 TFLOP/s).
 SOURCE_FLAGS = {
-    "attn_bwd_kernel.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+    "attn_bwd_kernel.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1",
+                            "-mllvm", "-amdgpu-use-amdgpu-trackers=1"],
 }
 
 
