@@ -155,7 +155,7 @@ int split_keys(int Lk, int n_split) {
 // Heads of one K/V head packed into a workgroup: Gp divides G and the 8 waves.
 int packed_heads(int G) { return (G % 8 == 0) ? 8 : (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1; }
 
-int fill_schedule(attn::FwdParams& p) {
+int fill_schedule(attn::FwdParams& p, bool causal) {
     p.G = p.Hq / p.Hkv;
     // query heads that share a K/V head are packed into one workgroup, one
     // head per wave group, so the K/V block is loaded once for all of them
@@ -171,7 +171,11 @@ int fill_schedule(attn::FwdParams& p) {
     p.units = (int)units;
     // XCD-aware order: workgroup i is dispatched to XCD i % 8; give each XCD
     // a contiguous range of units so the K/V blocks it streams stay in its L2.
-    p.xcd_mode = (p.units % kXcds == 0) ? 1 : 0;
+    // Under the causal mask the key splits of a head differ in work (a late
+    // split holds keys only the last position tiles see), so contiguous
+    // ranges of split units would leave some XCDs far busier than others:
+    // causal split launches keep the plain order.
+    p.xcd_mode = (p.units % kXcds == 0 && !(causal && p.n_split > 1)) ? 1 : 0;
     p.upx = p.xcd_mode ? p.units / kXcds : p.units;
     // units per cache section: enough tiles to occupy one XCD at a time
     int cap = kTilesPerXcdWave / p.n_m;
@@ -234,7 +238,7 @@ int run(const void* q, const void* k, const void* v, void* o, float* lse, int B,
     p.scale = scale;
     p.scale_log2 = (float)((double)scale * 1.4426950408889634);  // log2(e)
     p.threshold = threshold;
-    rc = fill_schedule(p);
+    rc = fill_schedule(p, causal != 0);
     if (rc != ATTN_OK) return rc;
     int n_cu = 0;
     rc = check_device(&n_cu);

@@ -71,7 +71,8 @@ def test_small_shapes(orc, shape):
     _full_check(f"small {shape}", q, k, v, causal, orc, stress=qm != 1.0)
 
 
-@pytest.mark.parametrize("name", ["mha_l2k", "causal_l8k", "gqa_l16k", "dsv3_l32k"])
+@pytest.mark.parametrize("name", ["mha_l2k", "causal_l8k", "gqa_l16k", "dsv3_l32k",
+                                  "dsv3_l32k_h2"])
 def test_full_size_workloads_sampled(orc, name):
     """Full-size workload on the GPU, checked on sampled rows the oracle
     computes one by one (always including the first and last rows)."""
