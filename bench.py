@@ -221,7 +221,7 @@ def bench_split(args, w, qd, kd, vd) -> int:
                    + n * rows * (4 * w.dv + 4))
     merge_bytes = n * rows * (4 * w.dv + 4) + rows * (2 * w.dv + 4)
     gbs = split_bytes / (ms_split * 1e-3) / 1e9
-    decode = w.Lq * (w.Hq // w.Hkv) <= 16 and w.dqk == w.dv and w.dqk in (64, 128)
+    decode = w.Lq * (w.Hq // w.Hkv) <= 16
     result = {
         "metric": METRIC,
         "value": round(flops * args.steps / wall / 1e12, 3),

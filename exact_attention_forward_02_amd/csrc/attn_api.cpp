@@ -467,7 +467,6 @@ int attn_fwd_decode(const void* q, const void* k, const void* v, float* o_part, 
                     float scale, int n_split, void* stream) {
     int rc = check_args(q, k, v, o_part, lse_part, B, Hq, Hkv, Lq, Lk, d_qk, d_v, scale);
     if (rc != ATTN_OK) return rc;
-    if (!(d_qk == d_v && (d_qk == 64 || d_qk == 128))) return ATTN_ERR_UNSUPPORTED_HEAD_DIM;
     if (n_split < 1 || n_split > kMaxSplits) return ATTN_ERR_BAD_ARGUMENT;
     if ((long long)Lq * (Hq / Hkv) > attn::kDecRows) return ATTN_ERR_BAD_ARGUMENT;
     rc = check_strides(contiguous_strides(Hq, Hkv, Lq, Lk, d_qk, d_v), B, Hq, Hkv, Lq, Lk, d_qk,
@@ -497,9 +496,9 @@ int attn_fwd_decode(const void* q, const void* k, const void* v, float* o_part, 
     p.threshold = kDefaultThreshold;
     rc = check_device();
     if (rc != ATTN_OK) return rc;
-    log_launch("attn_decode_kernel<%d,%s> grid %d (splits %d of %d keys), rows per K/V head %d",
-               d_qk, causal ? "causal" : "full", p.grid, p.n_split, p.split_w, p.R);
-    if (attn::launch_decode(p, d_qk, causal != 0, static_cast<hipStream_t>(stream)) !=
+    log_launch("attn_decode_kernel<%d,%d,%s> grid %d (splits %d of %d keys), rows per K/V head %d",
+               d_qk, d_v, causal ? "causal" : "full", p.grid, p.n_split, p.split_w, p.R);
+    if (attn::launch_decode(p, d_qk, d_v, causal != 0, static_cast<hipStream_t>(stream)) !=
         hipSuccess)
         return ATTN_ERR_HIP;
     return ATTN_OK;
@@ -510,8 +509,7 @@ int attn_fwd_split(const void* q, const void* k, const void* v, float* o_part, f
                    float scale, int n_split, void* stream) {
     if (n_split < 1 || n_split > kMaxSplits) return ATTN_ERR_BAD_ARGUMENT;
     // few query rows per K/V head: the key-streaming decode kernel
-    if (Hkv >= 1 && Hq % Hkv == 0 && Lq >= 1 && (long long)Lq * (Hq / Hkv) <= attn::kDecRows &&
-        d_qk == d_v && (d_qk == 64 || d_qk == 128))
+    if (Hkv >= 1 && Hq % Hkv == 0 && Lq >= 1 && (long long)Lq * (Hq / Hkv) <= attn::kDecRows)
         return attn_fwd_decode(q, k, v, o_part, lse_part, B, Hq, Hkv, Lq, Lk, d_qk, d_v, causal,
                                scale, n_split, stream);
     return run(q, k, v, o_part, lse_part, B, Hq, Hkv, Lq, Lk, d_qk, d_v, causal, scale, stream,

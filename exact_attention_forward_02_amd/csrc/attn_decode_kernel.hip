@@ -48,33 +48,41 @@ constexpr int kDecThreads = 64 * kDecWaves;
 constexpr int kDecStages = 3;  // LDS slots per wave: two steps in flight while one is computed
 constexpr int kDecLook = kDecStages - 1;
 
-template <int D>
+template <int DQK, int DV>
 struct Dec {
-    static constexpr int kChunks = D / 8;                  // 16-byte chunks per row
-    static constexpr int kRowBytes = D * 2;
-    static constexpr int kBlockBytes = kDecKeys * D * 2;   // 16 rows of K (or of V)
-    static constexpr int kCopies = kBlockBytes / 1024;     // 1 KiB wave copies per block
-    static constexpr int kStageBytes = 2 * kBlockBytes;    // K rows, then V rows
+    static constexpr int kChunksK = DQK / 8;               // 16-byte chunks per K row
+    static constexpr int kChunksV = DV / 8;                // and per V row
+    static constexpr int kRowK = DQK * 2;                  // bytes per K row
+    static constexpr int kRowV = DV * 2;                   // bytes per V row
+    static constexpr int kKBytes = kDecKeys * kRowK;       // 16 rows of K
+    static constexpr int kVBytes = kDecKeys * kRowV;       // 16 rows of V
+    static constexpr int kCopiesK = kKBytes / 1024;        // 1 KiB wave copies per block
+    static constexpr int kCopiesV = kVBytes / 1024;
+    static constexpr int kCopies = kCopiesK + kCopiesV;    // copy instructions per step
+    static constexpr int kStageBytes = kKBytes + kVBytes;  // K rows, then V rows
     static constexpr int kWaveBytes = kDecStages * kStageBytes;
-    static constexpr int kKSteps = D / 32;                 // k-steps of the score product
-    static constexpr int kDvBlocks = D / 16;               // 16-wide blocks of the output
-    // the final merge keeps each wave's O^T [D][16] and its row statistics in
+    static constexpr int kKSteps = DQK / 32;               // k-steps of the score product
+    static constexpr int kDvBlocks = DV / 16;              // 16-wide blocks of the output
+    static_assert(kKBytes % 1024 == 0 && kVBytes % 1024 == 0, "whole wave copies");
+    // the final merge keeps each wave's O^T [DV][16] and its row statistics in
     // the wave's own slots
-    static_assert(D * kDecRows * 4 + 3 * kDecRows * 4 <= kWaveBytes, "merge area fits");
+    static_assert(DV * kDecRows * 4 + 3 * kDecRows * 4 <= kWaveBytes, "merge area fits");
 };
 
 // K rows in LDS: chunk c of row r stored at slot c ^ kswz(r), so the 16 rows
-// one score operand read touches (same chunk) hit distinct bank groups.
-template <int D>
+// one score operand read touches (same chunk) hit distinct bank groups (8
+// distinct groups when the row has 8 or 24 chunks: the XOR must keep the slot
+// inside its aligned group of 8 and so inside the row).
+template <int DQK>
 __device__ __forceinline__ int kswz(int r) {
-    return (D == 128) ? (r & 15) : (r & 7);
+    return (DQK == 128) ? (r & 15) : (r & 7);
 }
 // V rows in LDS: chunk c of row r at slot c ^ vswz(r).  A transposed read
 // takes 8 bytes from each of 4 consecutive rows at two adjacent chunks; the
 // XOR moves consecutive rows to different 32-byte windows.
-template <int D>
+template <int DV>
 __device__ __forceinline__ int vswz(int r) {
-    return (D == 128) ? 2 * (r & 7) : 2 * (r & 3);
+    return (DV == 128) ? 2 * (r & 7) : 2 * (r & 3);
 }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
@@ -111,9 +119,9 @@ __device__ __forceinline__ float xor_sum(float x) {
     return x + __shfl_xor(x, 32);
 }
 
-template <int D, bool CAUSAL>
+template <int DQK, int DV, bool CAUSAL>
 __global__ __launch_bounds__(kDecThreads) void attn_decode_kernel(const DecParams p) {
-    using S = Dec<D>;
+    using S = Dec<DQK, DV>;
     __shared__ __attribute__((aligned(1024))) unsigned char lds[kDecWaves * S::kWaveBytes];
 
     const int tid = threadIdx.x;
@@ -128,9 +136,9 @@ __global__ __launch_bounds__(kDecThreads) void attn_decode_kernel(const DecParam
     const int kvh = unit % p.Hkv;
     const int b = unit / p.Hkv;
     const size_t head = (size_t)(b * p.Hkv + kvh) * p.Lk;  // row of key 0 of the head
-    const uint32_t head_bytes = (uint32_t)p.Lk * S::kRowBytes;  // < 2^31 (checked on the host)
-    const __amdgpu_buffer_rsrc_t krs = make_rsrc(p.k + head * D, head_bytes);
-    const __amdgpu_buffer_rsrc_t vrs = make_rsrc(p.v + head * D, head_bytes);
+    // one head's rows span less than 2^31 bytes (checked on the host)
+    const __amdgpu_buffer_rsrc_t krs = make_rsrc(p.k + head * DQK, (uint32_t)p.Lk * S::kRowK);
+    const __amdgpu_buffer_rsrc_t vrs = make_rsrc(p.v + head * DV, (uint32_t)p.Lk * S::kRowV);
 
     // Row n of the 16 is query position n % Lq of query head kvh * G + n / Lq;
     // rows n >= R are padding (zero queries, never stored).
@@ -145,7 +153,7 @@ __global__ __launch_bounds__(kDecThreads) void attn_decode_kernel(const DecParam
     // query rows as the B operand: lane l holds row l % 16, dims 32 ks + 8 lg .. + 7
     bf16x8 qf[S::kKSteps];
     {
-        const uint16_t* qrow = p.q + ((size_t)(b * p.Hq + hq) * p.Lq + qi) * D;
+        const uint16_t* qrow = p.q + ((size_t)(b * p.Hq + hq) * p.Lq + qi) * DQK;
 #pragma unroll
         for (int ks = 0; ks < S::kKSteps; ++ks) {
             const u32x4 w = row_ok ? *reinterpret_cast<const u32x4*>(qrow + 32 * ks + 8 * lg)
@@ -166,16 +174,23 @@ __global__ __launch_bounds__(kDecThreads) void attn_decode_kernel(const DecParam
 
     // per-lane copy offsets within a 16-row block: copy c, lane l fills LDS
     // slot 64 c + l = (row r, stored chunk c') from source chunk c' ^ swizzle(r)
-    uint32_t koff[S::kCopies], voff[S::kCopies];
-    int crow[S::kCopies];
+    uint32_t koff[S::kCopiesK], voff[S::kCopiesV];
+    int krow[S::kCopiesK], vrow[S::kCopiesV];
 #pragma unroll
-    for (int c = 0; c < S::kCopies; ++c) {
+    for (int c = 0; c < S::kCopiesK; ++c) {
         const int sl = 64 * c + lane;
-        const int r = sl / S::kChunks;
-        const int cs = sl - r * S::kChunks;
-        crow[c] = r;
-        koff[c] = r * S::kRowBytes + 16 * (cs ^ kswz<D>(r));
-        voff[c] = r * S::kRowBytes + 16 * (cs ^ vswz<D>(r));
+        const int r = sl / S::kChunksK;
+        const int cs = sl - r * S::kChunksK;
+        krow[c] = r;
+        koff[c] = r * S::kRowK + 16 * (cs ^ kswz<DQK>(r));
+    }
+#pragma unroll
+    for (int c = 0; c < S::kCopiesV; ++c) {
+        const int sl = 64 * c + lane;
+        const int r = sl / S::kChunksV;
+        const int cs = sl - r * S::kChunksV;
+        vrow[c] = r;
+        voff[c] = r * S::kRowV + 16 * (cs ^ vswz<DV>(r));
     }
     // copies of step t into slot t % kDecStages; rows past the last key repeat the
     // last key (masked to -inf, weighted by exactly 0)
@@ -183,17 +198,17 @@ __global__ __launch_bounds__(kDecThreads) void attn_decode_kernel(const DecParam
         const int key0 = wk0 + kDecKeys * t;
         unsigned char* slot = wlds + (t % kDecStages) * S::kStageBytes;
         int sd = __builtin_amdgcn_readfirstlane((int)(slot - lds));
-        const uint32_t soff = (uint32_t)key0 * S::kRowBytes;
         const int last = p.Lk - 1 - key0;
 #pragma unroll
-        for (int c = 0; c < S::kCopies; ++c) {
-            const uint32_t back = (uint32_t)(max(crow[c] - last, 0) * S::kRowBytes);
-            copy_to_lds(krs, koff[c] - back, soff, lds + sd + 1024 * c);
+        for (int c = 0; c < S::kCopiesK; ++c) {
+            const uint32_t back = (uint32_t)(max(krow[c] - last, 0) * S::kRowK);
+            copy_to_lds(krs, koff[c] - back, (uint32_t)key0 * S::kRowK, lds + sd + 1024 * c);
         }
 #pragma unroll
-        for (int c = 0; c < S::kCopies; ++c) {
-            const uint32_t back = (uint32_t)(max(crow[c] - last, 0) * S::kRowBytes);
-            copy_to_lds(vrs, voff[c] - back, soff, lds + sd + S::kBlockBytes + 1024 * c);
+        for (int c = 0; c < S::kCopiesV; ++c) {
+            const uint32_t back = (uint32_t)(max(vrow[c] - last, 0) * S::kRowV);
+            copy_to_lds(vrs, voff[c] - back, (uint32_t)key0 * S::kRowV,
+                        lds + sd + S::kKBytes + 1024 * c);
         }
     };
 
@@ -204,14 +219,14 @@ __global__ __launch_bounds__(kDecThreads) void attn_decode_kernel(const DecParam
     int kread[S::kKSteps];
 #pragma unroll
     for (int ks = 0; ks < S::kKSteps; ++ks)
-        kread[ks] = l16 * S::kRowBytes + 16 * ((4 * ks + lg) ^ kswz<D>(l16));
+        kread[ks] = l16 * S::kRowK + 16 * ((4 * ks + lg) ^ kswz<DQK>(l16));
     int vread[S::kDvBlocks];
     {
         const int r = 4 * lg + (l16 >> 2);
         const int j = l16 & 3;
 #pragma unroll
         for (int blk = 0; blk < S::kDvBlocks; ++blk)
-            vread[blk] = r * S::kRowBytes + 16 * ((2 * blk + (j >> 1)) ^ vswz<D>(r)) + 8 * (j & 1);
+            vread[blk] = r * S::kRowV + 16 * ((2 * blk + (j >> 1)) ^ vswz<DV>(r)) + 8 * (j & 1);
     }
 
     const float c2 = p.scale_log2;
@@ -225,10 +240,10 @@ __global__ __launch_bounds__(kDecThreads) void attn_decode_kernel(const DecParam
     for (int t = 0; t < min(kDecLook, nsteps); ++t) issue(t);
     for (int t = 0; t < nsteps; ++t) {
         // step t's copies have landed once only those of the steps issued
-        // after it remain in flight (2 kCopies instructions per step)
+        // after it remain in flight (kCopies instructions per step)
         static_assert(kDecLook == 2, "one wait per possible number of later steps");
         if (min(nsteps, t + kDecLook) - (t + 1) == 1)
-            wait_vmcnt<2 * S::kCopies>();
+            wait_vmcnt<S::kCopies>();
         else
             wait_vmcnt<0>();
         __builtin_amdgcn_sched_barrier(0);
@@ -236,7 +251,7 @@ __global__ __launch_bounds__(kDecThreads) void attn_decode_kernel(const DecParam
         if (t + kDecLook < nsteps) issue(t + kDecLook);
         __builtin_amdgcn_sched_barrier(0);
         const unsigned char* kl = wlds + (t % kDecStages) * S::kStageBytes;
-        const unsigned char* vl = kl + S::kBlockBytes;
+        const unsigned char* vl = kl + S::kKBytes;
         const int key0 = wk0 + kDecKeys * t;
 
         f32x4 s = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -292,61 +307,67 @@ __global__ __launch_bounds__(kDecThreads) void attn_decode_kernel(const DecParam
     const float ell_o_row = xor_sum(ell_o);
     wait_vmcnt<0>();
     __syncthreads();  // every wave is done with its slots
-    // wave w's area: O^T [D][16] fp32, then ref, ell and ell_o of the 16 rows
+    // wave w's area: O^T [DV][16] fp32, then ref, ell and ell_o of the 16 rows
     float* area = reinterpret_cast<float*>(wlds);
 #pragma unroll
     for (int blk = 0; blk < S::kDvBlocks; ++blk)
 #pragma unroll
         for (int i = 0; i < 4; ++i) area[(16 * blk + 4 * lg + i) * kDecRows + l16] = oacc[blk][i];
     if (lane < kDecRows) {
-        area[D * kDecRows + lane] = ref;
-        area[D * kDecRows + kDecRows + lane] = ell_row;
-        area[D * kDecRows + 2 * kDecRows + lane] = ell_o_row;
+        area[DV * kDecRows + lane] = ref;
+        area[DV * kDecRows + kDecRows + lane] = ell_row;
+        area[DV * kDecRows + 2 * kDecRows + lane] = ell_o_row;
     }
     __syncthreads();
 
-    // thread t covers output dim t % D of rows t / D, t / D + kDecThreads / D, ...
-    const int dim = tid % D;
-    for (int r = tid / D; r < p.R; r += kDecThreads / D) {
+    // thread t covers output dim t % DV of rows t / DV, t / DV + kDecThreads / DV, ...
+    const int dim = tid % DV;
+    for (int r = tid / DV; r < p.R; r += kDecThreads / DV) {
         float m = kNegInf;
 #pragma unroll
         for (int w = 0; w < kDecWaves; ++w) {
             const float* a = reinterpret_cast<const float*>(lds + w * S::kWaveBytes);
-            m = fmaxf(m, a[D * kDecRows + r]);
+            m = fmaxf(m, a[DV * kDecRows + r]);
         }
         float L = 0.0f, Lo = 0.0f, u = 0.0f;
         if (m != kNegInf) {
 #pragma unroll
             for (int w = 0; w < kDecWaves; ++w) {
                 const float* a = reinterpret_cast<const float*>(lds + w * S::kWaveBytes);
-                const float rw = a[D * kDecRows + r];
+                const float rw = a[DV * kDecRows + r];
                 const float e = (rw == kNegInf) ? 0.0f : __builtin_amdgcn_exp2f((rw - m) * c2);
-                L += e * a[D * kDecRows + kDecRows + r];
-                Lo += e * a[D * kDecRows + 2 * kDecRows + r];
+                L += e * a[DV * kDecRows + kDecRows + r];
+                Lo += e * a[DV * kDecRows + 2 * kDecRows + r];
                 u += e * a[dim * kDecRows + r];
             }
         }
         const int hq_r = kvh * p.G + r / p.Lq;
         const int qi_r = r % p.Lq;
         const size_t prow = (((size_t)split * p.B + b) * p.Hq + hq_r) * p.Lq + qi_r;
-        p.o_part[prow * D + dim] = Lo > 0.0f ? u / Lo : 0.0f;
+        p.o_part[prow * DV + dim] = Lo > 0.0f ? u / Lo : 0.0f;
         if (dim == 0) p.lse_part[prow] = L > 0.0f ? m * p.scale + logf(L) : kNegInf;
     }
 }
 
-template <int D, bool CAUSAL>
+template <int DQK, int DV, bool CAUSAL>
 hipError_t launch_d(const DecParams& p, hipStream_t stream) {
     DecParams arg = p;
     void* args[] = {&arg};
-    return hipLaunchKernel(reinterpret_cast<const void*>(&attn_decode_kernel<D, CAUSAL>),
+    return hipLaunchKernel(reinterpret_cast<const void*>(&attn_decode_kernel<DQK, DV, CAUSAL>),
                            dim3((unsigned)p.grid), dim3(kDecThreads), args, 0, stream);
+}
+
+template <int DQK, int DV>
+hipError_t launch_dims(const DecParams& p, bool causal, hipStream_t stream) {
+    return causal ? launch_d<DQK, DV, true>(p, stream) : launch_d<DQK, DV, false>(p, stream);
 }
 
 }  // namespace
 
-hipError_t launch_decode(const DecParams& p, int d, bool causal, hipStream_t stream) {
-    if (d == 64) return causal ? launch_d<64, true>(p, stream) : launch_d<64, false>(p, stream);
-    if (d == 128) return causal ? launch_d<128, true>(p, stream) : launch_d<128, false>(p, stream);
+hipError_t launch_decode(const DecParams& p, int dqk, int dv, bool causal, hipStream_t stream) {
+    if (dqk == 64 && dv == 64) return launch_dims<64, 64>(p, causal, stream);
+    if (dqk == 128 && dv == 128) return launch_dims<128, 128>(p, causal, stream);
+    if (dqk == 192 && dv == 128) return launch_dims<192, 128>(p, causal, stream);
     return hipErrorInvalidValue;
 }
 

@@ -85,17 +85,17 @@ hipError_t launch_bwd(const BwdParams& p, int d, bool causal, hipStream_t stream
 
 // Split-key forward for few query rows per K/V head (decoding): at most
 // kDecRows = Lq * Hq / Hkv rows, contiguous bf16 [B, H, L, d] tensors,
-// d_qk == d_v in {64, 128}.  Writes the same per-split states as the fused
-// kernel's split path.
+// (d_qk, d_v) in {(64, 64), (128, 128), (192, 128)}.  Writes the same
+// per-split states as the fused kernel's split path.
 constexpr int kDecWaves = 4;   // waves per workgroup, each streaming a quarter of the split
 constexpr int kDecKeys = 16;   // keys per wave step
 constexpr int kDecRows = 16;   // query rows served per K/V head
 
 struct DecParams {
-    const uint16_t* q;  // [B, Hq, Lq, d]
-    const uint16_t* k;  // [B, Hkv, Lk, d]
-    const uint16_t* v;  // [B, Hkv, Lk, d]
-    float* o_part;      // [n_split, B, Hq, Lq, d] fp32
+    const uint16_t* q;  // [B, Hq, Lq, d_qk]
+    const uint16_t* k;  // [B, Hkv, Lk, d_qk]
+    const uint16_t* v;  // [B, Hkv, Lk, d_v]
+    float* o_part;      // [n_split, B, Hq, Lq, d_v] fp32
     float* lse_part;    // [n_split, B, Hq, Lq]
     int B, Hq, Hkv, Lq, Lk;
     int G;        // Hq / Hkv
@@ -106,7 +106,7 @@ struct DecParams {
     float scale, scale_log2, threshold;
 };
 
-hipError_t launch_decode(const DecParams& p, int d, bool causal, hipStream_t stream);
+hipError_t launch_decode(const DecParams& p, int dqk, int dv, bool causal, hipStream_t stream);
 
 // Merges n_split partial states per row: o_part [n_split, rows, dv] fp32,
 // lse_part [n_split, rows] -> o [rows, dv] bf16, lse [rows].

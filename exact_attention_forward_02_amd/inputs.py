@@ -76,6 +76,10 @@ WORKLOADS = {
     # one decode step over a long key cache (split-key path): B8 Hq32 Hkv8,
     # one new query per sequence, 32k cached keys
     "decode_l32k": Workload("decode_l32k", 8, 32, 8, 1, 32768, 128, 128, False, seed=6),
+    # one decode step with the (192, 128) head shape: B8 H16, one new query per
+    # sequence, 32k cached keys per head
+    "decode_dsv3_l32k": Workload("decode_dsv3_l32k", 8, 16, 16, 1, 32768, 192, 128, False,
+                                 seed=9),
     # one GPU's share of dsv3_l32k when its 16 heads are sharded over 8 GPUs
     "dsv3_l32k_h2": Workload("dsv3_l32k_h2", 1, 2, 2, 32768, 32768, 192, 128, True, seed=8),
 }

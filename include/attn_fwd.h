@@ -231,8 +231,8 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
  * that streams the keys for few query rows per K/V head: at most 16 rows,
  * Lq * (Hq / Hkv) <= 16, as in decoding one or a few new tokens per sequence
  * ("Infra: Flash Attention", section on prefill versus decode).  Arguments,
- * layouts, splits and outputs as attn_fwd_split (contiguous bf16 tensors);
- * d_qk == d_v in {64, 128} (ATTN_ERR_UNSUPPORTED_HEAD_DIM otherwise).
+ * layouts, splits, head shapes and outputs as attn_fwd_split (contiguous
+ * bf16 tensors; (d_qk, d_v) one of (64,64), (128,128), (192,128)).
  * Returns ATTN_ERR_BAD_ARGUMENT when Lq * (Hq / Hkv) > 16 or n_split is
  * outside [1, 4096]; other errors as attn_fwd.  attn_fwd_split calls it by
  * itself for every shape it accepts, so this entry point only pins the

@@ -20,7 +20,7 @@ hipError_t launch_merge(const float*, const float*, uint16_t*, float*, int, long
                         hipStream_t) {
     abort();
 }
-hipError_t launch_decode(const DecParams&, int, bool, hipStream_t) { abort(); }
+hipError_t launch_decode(const DecParams&, int, int, bool, hipStream_t) { abort(); }
 }  // namespace attn
 
 static int failures = 0;

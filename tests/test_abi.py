@@ -413,7 +413,7 @@ def _call_decode(**over):
     ({"q": None}, "ATTN_ERR_NULL_PTR"),
     ({"Lq": 0}, "ATTN_ERR_BAD_SHAPE"),
     ({"Hq": 6, "Hkv": 4}, "ATTN_ERR_GQA_RATIO"),
-    ({"d_qk": 192, "d_v": 128}, "ATTN_ERR_UNSUPPORTED_HEAD_DIM"),
+    ({"d_qk": 192, "d_v": 192}, "ATTN_ERR_UNSUPPORTED_HEAD_DIM"),
     ({"Lq": 5}, "ATTN_ERR_BAD_ARGUMENT"),          # 5 x 4 = 20 rows per K/V head
     ({"Hq": 34, "Hkv": 2}, "ATTN_ERR_BAD_ARGUMENT"),  # 17 rows
     ({"n_split": 0}, "ATTN_ERR_BAD_ARGUMENT"),
@@ -427,3 +427,5 @@ def test_decode_arguments_are_validated_first(over, code):
 def test_valid_decode_call_without_a_gpu_reports_no_device():
     assert _call_decode() in (CODES["ATTN_ERR_NO_DEVICE"], CODES["ATTN_ERR_UNSUPPORTED_ARCH"])
     assert _call_decode(Lq=4) in (CODES["ATTN_ERR_NO_DEVICE"], CODES["ATTN_ERR_UNSUPPORTED_ARCH"])
+    assert _call_decode(d_qk=192, d_v=128) in (CODES["ATTN_ERR_NO_DEVICE"],
+                                                CODES["ATTN_ERR_UNSUPPORTED_ARCH"])

@@ -14,16 +14,18 @@ pytestmark = pytest.mark.gpu
 
 DEV = "cuda:0"
 
-# B, Hq, Hkv, Lq, Lk, d, causal, q_mult, n_split
+# B, Hq, Hkv, Lq, Lk, (d_qk, d_v), causal, q_mult, n_split
 SHAPES = [
-    (1, 1, 1, 1, 1000, 128, False, 1.0, 3),    # one row per K/V head, ragged last split
-    (2, 8, 2, 1, 777, 128, False, 1.0, 4),     # GQA 4: 4 rows
-    (1, 16, 2, 2, 300, 64, True, 1.0, 2),      # 16 rows, two positions under the mask
-    (1, 12, 4, 5, 129, 128, True, 1.0, 1),     # 15 rows, one split
-    (1, 4, 1, 4, 3, 64, True, 1.0, 2),         # Lq > Lk: rows without keys; an empty split
-    (2, 16, 1, 1, 5000, 128, False, 6.0, 7),   # MQA 16 rows, Q x 6: references move
-    (1, 8, 8, 2, 65, 64, False, 1.0, 9),       # more splits than key blocks
-    (3, 6, 3, 3, 2049, 128, True, 1.0, 5),     # 6 rows, tails in every wave's run
+    (1, 1, 1, 1, 1000, (128, 128), False, 1.0, 3),    # one row per K/V head, ragged last split
+    (2, 8, 2, 1, 777, (128, 128), False, 1.0, 4),     # GQA 4: 4 rows
+    (1, 16, 2, 2, 300, (64, 64), True, 1.0, 2),       # 16 rows, two positions under the mask
+    (1, 12, 4, 5, 129, (128, 128), True, 1.0, 1),     # 15 rows, one split
+    (1, 4, 1, 4, 3, (64, 64), True, 1.0, 2),          # Lq > Lk: rows without keys; an empty split
+    (2, 16, 1, 1, 5000, (128, 128), False, 6.0, 7),   # MQA 16 rows, Q x 6: references move
+    (1, 8, 8, 2, 65, (64, 64), False, 1.0, 9),        # more splits than key blocks
+    (3, 6, 3, 3, 2049, (128, 128), True, 1.0, 5),     # 6 rows, tails in every wave's run
+    (2, 4, 4, 1, 3001, (192, 128), False, 1.0, 4),    # the (192, 128) head shape, one row
+    (1, 16, 2, 2, 700, (192, 128), True, 6.0, 3),     # (192, 128), 16 rows, Q x 6
 ]
 
 
@@ -32,14 +34,14 @@ def _ids(s):
 
 
 def _inputs(shape):
-    B, Hq, Hkv, Lq, Lk, d, causal, qm, n = shape
-    return make_qkv(B, Hq, Hkv, Lq, Lk, d, d, seed=(B * 131 + Hq * 17 + Lq * 7 + Lk) % 10007,
+    B, Hq, Hkv, Lq, Lk, (dqk, dv), causal, qm, n = shape
+    return make_qkv(B, Hq, Hkv, Lq, Lk, dqk, dv, seed=(B * 131 + Hq * 17 + Lq * 7 + Lk) % 10007,
                     q_mult=qm)
 
 
 @pytest.mark.parametrize("shape", SHAPES, ids=_ids)
 def test_decode_split_states_match_the_oracle(orc, shape):
-    B, Hq, Hkv, Lq, Lk, d, causal, qm, n = shape
+    B, Hq, Hkv, Lq, Lk, (dqk, d), causal, qm, n = shape
     print(f"[case] decode states {shape}", flush=True)
     q, k, v = _inputs(shape)
     o_part, lse_part = attn_fwd_decode(q.to(DEV), k.to(DEV), v.to(DEV), n, causal=causal)
@@ -53,7 +55,7 @@ def test_decode_split_states_match_the_oracle(orc, shape):
 
 @pytest.mark.parametrize("shape", SHAPES, ids=_ids)
 def test_decode_then_merge_matches_the_definition(orc, shape):
-    B, Hq, Hkv, Lq, Lk, d, causal, qm, n = shape
+    B, Hq, Hkv, Lq, Lk, (dqk, d), causal, qm, n = shape
     print(f"[case] decode + merge {shape}", flush=True)
     q, k, v = _inputs(shape)
     o_part, lse_part = attn_fwd_decode(q.to(DEV), k.to(DEV), v.to(DEV), n, causal=causal)

@@ -49,10 +49,10 @@ def test_merge_kernel_resources():
 def test_decode_kernel_resources():
     text = _remarks(build.SOURCES[3])
     kernels = re.findall(r"Function Name: (\S+)", text)
-    assert len(kernels) == 4, kernels  # d = 64, 128 x causal or not
+    assert len(kernels) == 6, kernels  # (64,64), (128,128), (192,128) x causal or not
     scratch = [int(x) for x in re.findall(r"ScratchSize \[bytes/lane\]: (\d+)", text)]
     spills = [int(x) for x in re.findall(r"VGPRs Spill: (\d+)", text)]
-    assert scratch == [0] * 4 and spills == [0] * 4, (scratch, spills)
+    assert scratch == [0] * 6 and spills == [0] * 6, (scratch, spills)
 
 
 @pytest.mark.skipif(shutil.which(build.hipcc()) is None and not build.hipcc().startswith("/"),
