@@ -30,6 +30,7 @@ PEAK_HBM_GBS = 8000.0      # MI355X published HBM3E bandwidth
 CSRC = os.path.join(ROOT, "exact_attention_forward_02_amd", "csrc")
 KERNEL_SOURCE = os.path.join(CSRC, "attn_fwd_kernel.hip")
 DECODE_SOURCE = os.path.join(CSRC, "attn_decode_kernel.hip")
+BWD_SOURCE = os.path.join(CSRC, "attn_bwd_kernel.hip")
 
 
 def kernel_source_digest(path: str = KERNEL_SOURCE) -> str:
@@ -325,7 +326,7 @@ def bench_backward(args, w, qd, kd, vd) -> int:
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(w.name, "attn_bwd", BWD_SOURCE),
             "kernel": "attn_bwd (D, dK/dV and dQ kernels)",
             "ms_per_launch": round(ms_launch, 4),
             "ms_per_launch_min": round(min(launch_ms), 4),

@@ -12,7 +12,9 @@ run and prints the durations of the attention kernel over all its dispatches
 and over the last K (the timed steps, after the warmup launches that bring
 the clocks up).  `pmc` averages every counter per dispatch of the
 kernels whose name contains NAME.  `traffic` turns FETCH_SIZE / WRITE_SIZE
-(KiB per dispatch) of the attention kernel into HBM bytes per launch, each
+(KiB per dispatch) of the attention kernel (or the sum over a sequence of
+kernels that one call launches, such as the backward's) into HBM bytes per
+launch, each
 scaled by what the same counter reads for a plain copy kernel that moves a
 known number of bytes, and writes the JSON record bench.py reports while the
 kernel source is unchanged.
@@ -115,9 +117,23 @@ def cmd_pmc(args):
         print(f"{k:32s} {v:,.0f}")
 
 
+def read_counters_sum(path, kernels):
+    """Counters per call of a sequence of kernels (names separated by commas):
+    the per-dispatch means of each kernel, added up, and the dispatch counts."""
+    total, counts = defaultdict(float), []
+    for name in kernels.split(","):
+        mean, n, _ = read_counters(path, name)
+        if not n:
+            raise SystemExit(f"{path}: no dispatch of a kernel matching {name!r}")
+        for k, v in mean.items():
+            total[k] += v
+        counts.append(n)
+    return dict(total), counts
+
+
 def cmd_traffic(args):
-    fetch, nf, _ = read_counters(args.fetch, args.kernel)
-    write, nw, _ = read_counters(args.write, args.kernel)
+    fetch, nf = read_counters_sum(args.fetch, args.kernel)
+    write, nw = read_counters_sum(args.write, args.kernel)
     cfetch, _, _ = read_counters(args.copy_fetch, args.copy_kernel)
     cwrite, _, _ = read_counters(args.copy_write, args.copy_kernel)
     f_scale = args.copy_bytes / (cfetch["FETCH_SIZE"] * 1024.0)
@@ -131,7 +147,7 @@ def cmd_traffic(args):
         "kernel_source_sha256": kernel_source_digest(args.source),
         "fetch_kib_per_dispatch": fetch["FETCH_SIZE"],
         "write_kib_per_dispatch": write["WRITE_SIZE"],
-        "dispatches": [nf, nw],
+        "dispatches": [nf, nw],  # per kernel of the sequence, FETCH and WRITE runs
         "copy_bytes": args.copy_bytes,
         "copy_fetch_kib": cfetch["FETCH_SIZE"],
         "copy_write_kib": cwrite["WRITE_SIZE"],
@@ -171,7 +187,9 @@ def main(argv=None):
     c.add_argument("--copy-write", required=True)
     c.add_argument("--copy-bytes", type=float, required=True)
     c.add_argument("--copy-kernel", default="neg")  # the calibration copy is torch.neg
-    c.add_argument("--kernel", default="attn_fwd_kernel")
+    c.add_argument("--kernel", default="attn_fwd_kernel",
+                   help="kernel name, or several separated by commas: one call launches "
+                        "each once and the record holds their sum")
     c.add_argument("--source", default=KERNEL_SOURCE,
                    help="the kernel's source file, whose hash the record carries")
     c.add_argument("--workload", required=True)
