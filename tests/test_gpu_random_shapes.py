@@ -48,10 +48,12 @@ def test_random_shape_fused(orc, shape):
 
 
 SPLIT = [s for s in _shapes(77, 40) if s[5] == s[6] and s[5] in (64, 128)][:16]
+# the (192, 128) head shape through the same path: the decode kernel where a
+# K/V head serves at most 16 rows, the fused kernel's split path elsewhere
+SPLIT_WIDE = [s for s in _shapes(91, 80) if s[5] == 192][:10]
 
 
-@pytest.mark.parametrize("shape", SPLIT, ids=lambda s: "x".join(map(str, s)))
-def test_random_shape_split(orc, shape):
+def _check_split(orc, shape):
     B, Hq, Hkv, Lq, Lk, dqk, dv, causal = shape
     n = 1 + hash(shape) % 7
     print(f"[case] split {shape} n={n} rows/head={Lq * Hq // Hkv}", flush=True)
@@ -61,6 +63,16 @@ def test_random_shape_split(orc, shape):
     o_ref, l_ref = orc.attn_rows(q, k, v, causal=causal)
     assert_parity(f"split {shape} n={n}", o.reshape(-1, dv).cpu(), lse.reshape(-1).cpu(), o_ref,
                   l_ref)
+
+
+@pytest.mark.parametrize("shape", SPLIT, ids=lambda s: "x".join(map(str, s)))
+def test_random_shape_split(orc, shape):
+    _check_split(orc, shape)
+
+
+@pytest.mark.parametrize("shape", SPLIT_WIDE, ids=lambda s: "x".join(map(str, s)))
+def test_random_shape_split_wide(orc, shape):
+    _check_split(orc, shape)
 
 
 def _varlen_cases(seed, n):
