@@ -128,12 +128,52 @@ def parity_summary(o_gpu, lse_gpu, o_ref, lse_ref) -> dict:
     }
 
 
+HIP_ATTR_CLOCK_RATE = 5  # hipDeviceAttributeClockRate: peak clock in kHz
+
+
+def peak_clock_khz(index: int):
+    """The device's peak clock from the HIP runtime already loaded in this
+    process (hipDeviceGetAttribute), or None.  Only a runtime that is already
+    mapped is used, so no second copy of it is ever loaded."""
+    import ctypes
+
+    path = None
+    try:
+        with open("/proc/self/maps", encoding="utf-8") as f:
+            for line in f:
+                if "libamdhip64" in line and "/" in line:
+                    path = line[line.index("/"):].strip()
+                    break
+    except OSError:
+        return None
+    if path is None:
+        return None
+    try:
+        hip = ctypes.CDLL(path, mode=os.RTLD_NOLOAD | os.RTLD_GLOBAL)
+    except OSError:
+        return None
+    value = ctypes.c_int(0)
+    if hip.hipDeviceGetAttribute(ctypes.byref(value), HIP_ATTR_CLOCK_RATE, int(index)) != 0:
+        return None
+    return value.value
+
+
 def environment(dev) -> dict:
     import torch
 
     prop = torch.cuda.get_device_properties(dev)
-    return {"device": prop.name, "compute_units": prop.multi_processor_count,
-            "torch": torch.__version__, "hip": getattr(torch.version, "hip", None)}
+    khz = peak_clock_khz(dev.index or 0)
+    cus = prop.multi_processor_count
+    env = {"device": prop.name, "arch": prop.gcnArchName, "compute_units": cus,
+           "peak_clock_mhz": khz / 1000.0 if khz else None,
+           "torch": torch.__version__, "hip": getattr(torch.version, "hip", None)}
+    if khz:
+        # dense bf16 MFMA: 4 SIMDs per CU, 1024 flop per SIMD per clock
+        # (v_mfma_f32_32x32x16_bf16: 32768 flop in 32 cycles)
+        env["bf16_peak_formula"] = (f"{cus} CU x 4 SIMD x 1024 flop/clk x {khz / 1e6:.2f} GHz = "
+                                    f"{cus * 4 * 1024 * khz * 1e3 / 1e15:.3f} PFLOP/s "
+                                    f"(published {PEAK_BF16_TFLOPS / 1000:.1f})")
+    return env
 
 
 COPY_BYTES = 1 << 30  # bytes read (and written) per calibration launch
