@@ -601,7 +601,10 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Lq": w.Lq,
                    "Lk": w.Lk, "d_qk": w.dqk, "d_v": w.dv, "causal": w.causal,
-                   "layout": args.layout, "flops_per_step": flops},
+                   "layout": args.layout, "flops_per_step": flops,
+                   # the same count over the exact visible (query, key) pairs: under
+                   # the causal mask it exceeds the halved convention by about 1/L
+                   "flops_exact_pairs": 2.0 * w.B * w.Hq * w.valid_pairs() * (w.dqk + w.dv)},
         "pct_of_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "roofline": {
             "bound": "mfma",
