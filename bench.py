@@ -4,7 +4,10 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
 A step is one call of the whole hot path (one fused forward kernel) over the
-workload's seeded synthetic inputs, already resident in HBM.  Prints ONE JSON
+workload's seeded synthetic inputs, already resident in HBM.  Before the W
+warmup and K timed steps, an untimed clock-settle phase of fixed length
+(--settle-ms, default 250 ms of back-to-back steps) brings the chip to the
+clock it holds under this load; the line reports it.  Prints ONE JSON
 line: throughput in TFLOP/s (FLOPs = 2*B*Hq*Lq*Lk*(d_qk+d_v), halved when
 causal), the roofline object of the kernel (per-launch duration from HIP
 events on the launch stream), and the CPU oracle timed on a bounded sample of
@@ -60,6 +63,30 @@ def host_threads() -> int:
         return len(os.sched_getaffinity(0))
     except AttributeError:
         return os.cpu_count() or 1
+
+
+SETTLE_MS = 250.0  # default length of the untimed clock-settle phase
+
+
+def settle(launch, settle_ms: float) -> dict:
+    """Untimed clock-settle phase before the warmup: the step's launches run back
+    to back, in batches of 8 with a synchronisation after each, until
+    `settle_ms` of wall time have passed.  The MI355X raises its clock over the
+    first tens of milliseconds of load; this makes the timed steps, whatever
+    their number, run at the clock the chip holds under this load.  Its length
+    is fixed in time (the launch count it took is reported)."""
+    import torch
+
+    n = 0
+    t0 = time.perf_counter()
+    if settle_ms > 0:
+        while (time.perf_counter() - t0) * 1e3 < settle_ms:
+            for _ in range(8):
+                launch()
+            n += 8
+            torch.cuda.synchronize()
+    return {"ms": settle_ms, "launches": n,
+            "seconds": round(time.perf_counter() - t0, 4)}
 
 
 def cpu_baseline(w, q, k, v, target_s: float = 12.0):
@@ -238,6 +265,7 @@ def bench_split(args, w, qd, kd, vd) -> int:
         if ev is not None:
             ev[2].record(stream)
 
+    settled = settle(step, args.settle_ms)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -270,6 +298,7 @@ def bench_split(args, w, qd, kd, vd) -> int:
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle": settled,
         "ms_per_step": round(wall * 1e3 / args.steps, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -325,6 +354,7 @@ def bench_backward(args, w, qd, kd, vd) -> int:
         attn_bwd(qd, kd, vd, o, lse, dout, causal=w.causal, dq=dq, dk=dk, dv=dv, delta=delta,
                  stream=stream)
 
+    settled = settle(step, args.settle_ms)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -350,6 +380,7 @@ def bench_backward(args, w, qd, kd, vd) -> int:
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle": settled,
         "ms_per_step": round(wall * 1e3 / args.steps, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -405,6 +436,7 @@ def bench_varlen(args, w) -> int:
         attn_fwd_varlen(qd, kd, vd, cu_q, cu_k, causal=w.causal, plan=plan, out=o, lse=lse,
                         stream=stream)
 
+    settled = settle(step, args.settle_ms)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -431,6 +463,7 @@ def bench_varlen(args, w) -> int:
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle": settled,
         "ms_per_step": round(wall * 1e3 / args.steps, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -492,8 +525,11 @@ def bench_varlen(args, w) -> int:
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--settle-ms", type=float, default=SETTLE_MS,
+                    help="length of the untimed clock-settle phase before the warmup, in ms "
+                         "of back-to-back steps (0: none)")
     ap.add_argument("--workload", default="mha_l2k")
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle timing (for profiler runs)")
@@ -561,8 +597,12 @@ def main() -> int:
     lse = torch.empty((w.B, w.Hq, w.Lq), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
 
-    for _ in range(args.warmup):
+    def step():
         fwd(qd, kd, vd, causal=w.causal, out=o, lse=lse, stream=stream)
+
+    settled = settle(step, args.settle_ms)
+    for _ in range(args.warmup):
+        step()
     torch.cuda.synchronize()
 
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
@@ -571,7 +611,7 @@ def main() -> int:
     t0 = time.perf_counter()
     for i in range(args.steps):
         starts[i].record(stream)
-        fwd(qd, kd, vd, causal=w.causal, out=o, lse=lse, stream=stream)
+        step()
         ends[i].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -593,6 +633,7 @@ def main() -> int:
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle": settled,
         "ms_per_step": round(ms_step, 4),
         "higher_is_better": True,
         "scaling": "weak",

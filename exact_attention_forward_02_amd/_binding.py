@@ -48,7 +48,7 @@ def _load():
         lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, ctypes.c_float, vp]
         lib.attn_fwd_dbg.restype = i
         lib.attn_fwd_dbg.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i,
-                                     ctypes.c_float, vp, ctypes.c_float, vp]
+                                     ctypes.c_float, vp, ctypes.c_float, i, vp]
         lib.attn_fwd_ex.restype = i
         lib.attn_fwd_ex.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i,
                                     Strides, Strides, Strides, Strides, i, i, ctypes.c_float, vp]
@@ -106,12 +106,23 @@ def _check_inputs(q, k, v):
     return B, Hq, Hkv, Lq, Lk, dqk, v.shape[3]
 
 
+def _require_device(t, device, name):
+    """Caller-supplied buffers must live on the device of the inputs: the
+    kernels write through their addresses."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+
+
 def _outputs(q, dv, out, lse):
     B, Hq, Lq, _ = q.shape
     if out is None:
         out = torch.empty((B, Hq, Lq, dv), dtype=torch.bfloat16, device=q.device)
     if lse is None:
         lse = torch.empty((B, Hq, Lq), dtype=torch.float32, device=q.device)
+    _require_device(out, q.device, "out")
+    _require_device(lse, q.device, "lse")
     if out.shape != (B, Hq, Lq, dv) or out.dtype != torch.bfloat16 or not out.is_contiguous():
         raise ValueError("out must be a contiguous bf16 [B, Hq, Lq, d_v] tensor")
     if lse.shape != (B, Hq, Lq) or lse.dtype != torch.float32 or not lse.is_contiguous():
@@ -143,9 +154,10 @@ def attn_fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None
 
 def attn_fwd_dbg(q, k, v, causal: bool = False, scale: float | None = None,
                  rescale_threshold: float = 8.0, rescale_count=None, out=None, lse=None,
-                 stream=None):
+                 stream=None, exp_mode: int = 0):
     """attn_fwd with the rescale threshold exposed; rescale_count, if given, is a
-    zeroed int64 GPU tensor of one element that receives the event count."""
+    zeroed int64 GPU tensor of one element that receives the event count.
+    exp_mode 0 (v_exp_f32) is the only mode the library builds."""
     lib = _load()
     B, Hq, Hkv, Lq, Lk, dqk, dv = _check_inputs(q, k, v)
     if scale is None:
@@ -161,7 +173,8 @@ def attn_fwd_dbg(q, k, v, causal: bool = False, scale: float | None = None,
         s = stream if stream is not None else torch.cuda.current_stream(q.device)
         rc = lib.attn_fwd_dbg(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                               lse.data_ptr(), B, Hq, Hkv, Lq, Lk, dqk, dv, int(bool(causal)),
-                              float(scale), s.cuda_stream, float(rescale_threshold), cnt)
+                              float(scale), s.cuda_stream, float(rescale_threshold),
+                              int(exp_mode), cnt)
     if rc != ATTN_OK:
         raise RuntimeError(f"attn_fwd_dbg failed: {status_string(rc)} (code {rc})")
     return out, lse
@@ -207,10 +220,12 @@ def attn_fwd_ex(q, k, v, causal: bool = False, scale: float | None = None, out=N
             out = torch.empty((B, Lq, Hq, dv), dtype=q.dtype, device=q.device).transpose(1, 2)
         else:
             out = torch.empty((B, Hq, Lq, dv), dtype=q.dtype, device=q.device)
-    if tuple(out.shape) != (B, Hq, Lq, dv) or out.dtype != q.dtype or out.device != q.device:
+    _require_device(out, q.device, "out")
+    if tuple(out.shape) != (B, Hq, Lq, dv) or out.dtype != q.dtype:
         raise ValueError("out must be a [B, Hq, Lq, d_v] view of q's dtype on q's device")
     if lse is None:
         lse = torch.empty((B, Hq, Lq), dtype=torch.float32, device=q.device)
+    _require_device(lse, q.device, "lse")
     if lse.shape != (B, Hq, Lq) or lse.dtype != torch.float32 or not lse.is_contiguous():
         raise ValueError("lse must be a contiguous fp32 [B, Hq, Lq] tensor")
     dtype = ATTN_DTYPE_FP16 if q.dtype == torch.float16 else ATTN_DTYPE_BF16
@@ -278,6 +293,8 @@ def _split_call(name, q, k, v, n_split, causal, scale, o_part, lse_part, stream)
         o_part = torch.empty((n, B, Hq, Lq, dv), dtype=torch.float32, device=q.device)
     if lse_part is None:
         lse_part = torch.empty((n, B, Hq, Lq), dtype=torch.float32, device=q.device)
+    _require_device(o_part, q.device, "o_part")
+    _require_device(lse_part, q.device, "lse_part")
     if (o_part.shape != (n, B, Hq, Lq, dv) or o_part.dtype != torch.float32
             or not o_part.is_contiguous()):
         raise ValueError("o_part must be a contiguous fp32 [n_split, B, Hq, Lq, d_v] tensor")
@@ -315,6 +332,12 @@ def attn_merge(o_part, lse_part, out=None, lse=None, stream=None):
     """Merge per-split states [n_split, ..., d_v] / [n_split, ...] into the bf16
     output [..., d_v] and lse [...] (leading dims as in the per-split tensors)."""
     lib = _load()
+    for name, t in (("o_part", o_part), ("lse_part", lse_part)):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch.Tensor")
+    if o_part.device.type != "cuda":
+        raise ValueError(f"o_part must be on a GPU device, got {o_part.device}")
+    _require_device(lse_part, o_part.device, "lse_part")
     if o_part.dtype != torch.float32 or lse_part.dtype != torch.float32:
         raise TypeError("o_part and lse_part must be float32")
     if not (o_part.is_contiguous() and lse_part.is_contiguous()):
@@ -331,6 +354,8 @@ def attn_merge(o_part, lse_part, out=None, lse=None, stream=None):
         out = torch.empty(lead + (dv,), dtype=torch.bfloat16, device=o_part.device)
     if lse is None:
         lse = torch.empty(lead, dtype=torch.float32, device=o_part.device)
+    _require_device(out, o_part.device, "out")
+    _require_device(lse, o_part.device, "lse")
     if tuple(out.shape) != lead + (dv,) or out.dtype != torch.bfloat16 or not out.is_contiguous():
         raise ValueError("out must be a contiguous bf16 tensor of the merged shape")
     if tuple(lse.shape) != lead or lse.dtype != torch.float32 or not lse.is_contiguous():
@@ -426,6 +451,8 @@ def attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, causal: bool = False,
         out = torch.empty((Tq, Hq, dv), dtype=torch.bfloat16, device=q.device)
     if lse is None:
         lse = torch.empty((Hq, Tq), dtype=torch.float32, device=q.device)
+    _require_device(out, q.device, "out")
+    _require_device(lse, q.device, "lse")
     if tuple(out.shape) != (Tq, Hq, dv) or out.dtype != torch.bfloat16 or not out.is_contiguous():
         raise ValueError("out must be a contiguous bf16 [Tq, Hq, d_v] tensor")
     if tuple(lse.shape) != (Hq, Tq) or lse.dtype != torch.float32 or not lse.is_contiguous():

@@ -21,7 +21,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 5;
+constexpr int kAbiVersion = 6;
 constexpr int kMaxSplits = 4096;
 constexpr int kMaxDevices = 64;
 constexpr int kXcds = 8;                 // MI355X: 8 accelerator complex dies
@@ -395,9 +395,11 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
 
 int attn_fwd_dbg(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                  int Hq, int Hkv, int Lq, int Lk, int d_qk, int d_v, int causal, float scale,
-                 void* stream, float rescale_threshold, unsigned long long* rescale_count) {
+                 void* stream, float rescale_threshold, int exp_mode,
+                 unsigned long long* rescale_count) {
     if (!(rescale_threshold >= 0.0f) || !isfinite(rescale_threshold))
         return ATTN_ERR_BAD_ARGUMENT;
+    if (exp_mode != 0) return ATTN_ERR_BAD_ARGUMENT;  // only v_exp_f32 is built
     return run(q, k, v, o, lse, B, Hq, Hkv, Lq, Lk, d_qk, d_v, causal, scale, stream,
                rescale_threshold, rescale_count, true, 0);
 }
@@ -635,8 +637,8 @@ const char* attn_status_string(int status) {
         case ATTN_ERR_UNSUPPORTED_ARCH: return "the current device is not gfx950 (MI355X)";
         case ATTN_ERR_HIP: return "the HIP runtime reported an error";
         case ATTN_ERR_BAD_ARGUMENT:
-            return "argument out of range (rescale threshold finite and >= 0, split count in "
-                   "[1, 4096], merge rows >= 0, dtype bf16 or fp16)";
+            return "argument out of range (rescale threshold finite and >= 0, exp mode 0, split "
+                   "count in [1, 4096], merge rows >= 0, dtype bf16 or fp16)";
         case ATTN_ERR_BAD_STRIDE:
             return "strides must be >= 0 and multiples of 8 elements, with row strides of at "
                    "least the head dim";

@@ -98,6 +98,17 @@ def make_qkv(B: int, Hq: int, Hkv: int, Lq: int, Lk: int, dqk: int, dv: int,
     return q, k, v
 
 
+def make_qkv_fp16(B: int, Hq: int, Hkv: int, Lq: int, Lk: int, dqk: int, dv: int, seed: int):
+    """Seeded fp16 CPU tensors with the full fp16 precision: float32 N(0, 1)
+    draws (Q, then K, then V) rounded to float16 with RNE, so most values carry
+    mantissa bits that bf16 cannot hold."""
+    g = torch.Generator(device="cpu").manual_seed(int(seed))
+    q = torch.randn((B, Hq, Lq, dqk), generator=g, dtype=torch.float32).to(torch.float16)
+    k = torch.randn((B, Hkv, Lk, dqk), generator=g, dtype=torch.float32).to(torch.float16)
+    v = torch.randn((B, Hkv, Lk, dv), generator=g, dtype=torch.float32).to(torch.float16)
+    return q, k, v
+
+
 @dataclass(frozen=True)
 class VarlenWorkload:
     """A packed batch of sequences of different lengths (self-attention: each

@@ -105,18 +105,24 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
  *                      moves when (ref - cand) * scale * log2(e) < -tau.
  *                      0 rescales at every increase of the running max; the
  *                      production entry point uses 8.
+ *   exp_mode           how the exponentials 2^x are evaluated: 0 = the
+ *                      hardware v_exp_f32 for every element (the only mode
+ *                      built; the FA4 review's exp-emulation section describes
+ *                      a partial polynomial, which on gfx950 would cost more
+ *                      VALU time than it saves).  Any other value returns
+ *                      ATTN_ERR_BAD_ARGUMENT.
  *   rescale_count      device pointer to one unsigned 64-bit counter, or NULL.
  *                      When given, the kernel atomically adds the number of
  *                      (query row, key block) pairs, after the row's first
  *                      visible block, at which the row's reference moved.  The
  *                      caller zeroes it beforehand.
  * Other arguments and returns as attn_fwd; ATTN_ERR_BAD_ARGUMENT for a bad
- * threshold.
+ * threshold or exp_mode.
  */
 int attn_fwd_dbg(const void* q, const void* k, const void* v, void* o, float* lse,
                  int B, int Hq, int Hkv, int Lq, int Lk, int d_qk, int d_v,
                  int causal, float scale, void* stream,
-                 float rescale_threshold, unsigned long long* rescale_count);
+                 float rescale_threshold, int exp_mode, unsigned long long* rescale_count);
 
 /*
  * attn_fwd_ex -- attn_fwd for any element strides and for fp16 as well as

@@ -151,6 +151,48 @@ def pin_conditional_cases(orc):
         _close(o[0, 0], 11269 / 3075, 1e-14, f"firing case mode {mode}")
 
 
+def pin_group_decision(orc):
+    """The shared decision (mode 2) on a hand-built group of two rows, where
+    only one row's block maximum jumps past the threshold.  With scale = ln 2
+    (scale*log2(e) = 1), d = 1, keys (0, 1, 10, 9) and blocks of two:
+      row A, q = 1:    scores (0, 1 | 10, 9): the jump 1 -> 10 is 9 > 8, so A
+                       moves its reference to 10 in both modes;
+      row B, q = 1/4:  scores (0, 1/4 | 5/2, 9/4): the jump is 9/4 < 8, so on
+                       its own (mode 1) B keeps 1/4; in a group with A (mode 2)
+                       it moves to its own candidate 5/2 because A moved.
+    Final (reference, l) of both rows follow by hand; O and lse equal the
+    definition whatever the decision."""
+    q = _bf([1.0, 0.25], (1, 1, 2, 1))
+    k = _bf([0.0, 1.0, 10.0, 9.0], (1, 1, 4, 1))
+    v = _bf([1.0, 2.0, 3.0, 4.0], (1, 1, 4, 1))
+    x = {"A": [0.0, 1.0, 10.0, 9.0], "B": [0.0, 0.25, 2.5, 2.25]}
+    # l relative to the final reference r: sum_j 2^(x_j - r) (every key is
+    # visible); the first block's terms were accumulated at its max and scaled
+    # by 2^(r_first - r) when the reference moved, which is the same sum
+    def ell(xs, r):
+        return sum(2.0 ** (xj - r) for xj in xs)
+    want = {
+        1: {"A": (10.0, ell(x["A"], 10.0)), "B": (0.25, ell(x["B"], 0.25))},
+        2: {"A": (10.0, ell(x["A"], 10.0)), "B": (2.5, ell(x["B"], 2.5))},
+    }
+    want_events = {1: 1, 2: 2}
+    o_def, l_def = orc.attn_rows(q, k, v, causal=False, scale=LN2)
+    for mode in (1, 2):
+        o, lse, st, ev = orc.online_rows(q, k, v, causal=False, scale=LN2, bn=2, mode=mode,
+                                         tau=8.0, group=2)
+        for row, name in enumerate(("A", "B")):
+            r, l = want[mode][name]
+            _close(st[row, 0], r, 0.0, f"mode {mode} row {name}: final reference")
+            _close(st[row, 1], l, 1e-14 * l, f"mode {mode} row {name}: final l")
+        assert ev == want_events[mode], f"mode {mode}: {ev} rescale events"
+        _close(o, o_def, 1e-14, f"mode {mode}: O")
+        _close(lse, l_def, 1e-14, f"mode {mode}: lse")
+    # a group of one is the per-row rule
+    _, _, st1, _ = orc.online_rows(q, k, v, causal=False, scale=LN2, bn=2, mode=2, tau=8.0,
+                                   group=1)
+    _close(st1[1, 0], 0.25, 0.0, "mode 2 group 1 row B: final reference")
+
+
 # --------------------------------------------------------------------------
 # Closed forms
 # --------------------------------------------------------------------------
@@ -696,6 +738,7 @@ def pin_varlen_zero_query(orc):
 ALL_PINS = [
     pin_worked_example,
     pin_conditional_cases,
+    pin_group_decision,
     pin_zero_query,
     pin_causal_first_row,
     pin_powers_of_two,

@@ -96,7 +96,9 @@ int main() {
                               nullptr)));
     unsigned long long cnt = 0;
     EXPECT(is_no_dev(attn_fwd_dbg(q, k, v, o, lse, 1, 1, 1, 256, 256, 64, 64, 0, 0.125f, nullptr,
-                                  0.0f, &cnt)));
+                                  0.0f, 0, &cnt)));
+    EXPECT(attn_fwd_dbg(q, k, v, o, lse, 1, 1, 1, 256, 256, 64, 64, 0, 0.125f, nullptr, 0.0f, 1,
+                        &cnt) == ATTN_ERR_BAD_ARGUMENT);
     attn_strides sq = {3LL * 100 * 4 * 128, 128, 3 * 4 * 128}, so = {100LL * 4 * 128, 128, 512};
     EXPECT(is_no_dev(attn_fwd_ex(q, k, v, o, lse, 1, 4, 4, 100, 100, 128, 128, sq, sq, sq, so, 1,
                                  0, 0.1f, nullptr)));

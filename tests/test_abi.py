@@ -61,7 +61,7 @@ def test_library_exports_every_declared_function():
 
 def test_abi_version_and_status_strings():
     lib = _binding.library()
-    assert lib.attn_abi_version() == 5
+    assert lib.attn_abi_version() == 6
     for code in CODES.values():
         s = _binding.status_string(code)
         assert s and s != "unknown attn status"
@@ -82,10 +82,10 @@ def _call(**over):
     return _binding.library().attn_fwd(*[args[n] for n in ORDER])
 
 
-def _call_dbg(threshold, **over):
+def _call_dbg(threshold, exp_mode=0, **over):
     args = dict(GOOD)
     args.update(over)
-    return _binding.library().attn_fwd_dbg(*[args[n] for n in ORDER], threshold, None)
+    return _binding.library().attn_fwd_dbg(*[args[n] for n in ORDER], threshold, exp_mode, None)
 
 
 @pytest.mark.parametrize("over,code", [
@@ -122,6 +122,12 @@ def test_debug_threshold_is_validated():
     assert _call_dbg(float("inf")) == CODES["ATTN_ERR_BAD_ARGUMENT"]
 
 
+def test_debug_exp_mode_is_validated():
+    # only the hardware exponential (mode 0) is built; every other mode is refused
+    for mode in (1, 2, -1, 7):
+        assert _call_dbg(8.0, exp_mode=mode) == CODES["ATTN_ERR_BAD_ARGUMENT"]
+
+
 def test_valid_call_without_a_gpu_reports_no_device():
     import torch
 
@@ -139,6 +145,30 @@ def test_python_binding_rejects_bad_tensors():
         _binding.attn_fwd(q, q, q)  # CPU tensors are refused before any call
     with pytest.raises(TypeError):
         _binding.attn_fwd(q.float(), q, q)
+
+
+def test_binding_refuses_outputs_off_the_input_device():
+    """Caller-supplied outputs on another device than the inputs are refused
+    before any library call (the kernels would write through a host or foreign
+    address).  Without a GPU the rule is checked on the binding's output
+    helper, with inputs on the meta device standing in for a GPU."""
+    import torch
+
+    q = torch.empty((1, 2, 8, 64), dtype=torch.bfloat16, device="meta")
+    good_o = torch.empty((1, 2, 8, 64), dtype=torch.bfloat16, device="meta")
+    good_l = torch.empty((1, 2, 8), dtype=torch.float32, device="meta")
+    out, lse = _binding._outputs(q, 64, good_o, good_l)
+    assert out is good_o and lse is good_l
+    with pytest.raises(ValueError, match="out must be on"):
+        _binding._outputs(q, 64, torch.empty((1, 2, 8, 64), dtype=torch.bfloat16), good_l)
+    with pytest.raises(ValueError, match="lse must be on"):
+        _binding._outputs(q, 64, good_o, torch.empty((1, 2, 8), dtype=torch.float32))
+    with pytest.raises(TypeError):
+        _binding._require_device(None, q.device, "out")
+    # merge takes its device from o_part, which must be a GPU tensor
+    o_part = torch.zeros((2, 4, 64), dtype=torch.float32)
+    with pytest.raises(ValueError, match="GPU"):
+        _binding.attn_merge(o_part, torch.zeros((2, 4), dtype=torch.float32))
 
 
 def test_split_keys_arithmetic():

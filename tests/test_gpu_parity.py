@@ -8,7 +8,7 @@ import torch
 
 from exact_attention_forward_02_amd import attn_fwd, attn_fwd_dbg
 from exact_attention_forward_02_amd.inputs import WORKLOADS, make_qkv, sample_rows, workload_qkv
-from parity import assert_parity, gather_rows
+from parity import assert_parity, default_scale, dense_bound, gather_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -26,13 +26,19 @@ def _run(q, k, v, causal, scale=None):
     return o.cpu(), lse.cpu()
 
 
-def _full_check(tag, q, k, v, causal, orc, scale=None, stress=False):
+def _full_check(tag, q, k, v, causal, orc, scale=None, bounded=False):
+    """bounded: hold each element to max(1e-2, the bf16-weight bound) instead of
+    the absolute 1e-2 (only for inputs where that bound passes 1e-2)."""
     print(f"[case] {tag} q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)} "
           f"causal={causal}", flush=True)
     o, lse = _run(q, k, v, causal, scale)
     o_ref, l_ref = orc.attn_rows(q, k, v, causal=causal, scale=scale)
+    bound = None
+    if bounded:
+        sc = default_scale(q.shape[-1]) if scale is None else scale
+        bound = dense_bound(q, k, v, causal, sc, o_ref)
     return assert_parity(tag, o.reshape(-1, o.shape[-1]), lse.reshape(-1), o_ref, l_ref,
-                         stress=stress)
+                         bound=bound)
 
 
 def test_tiny_workload(orc):
@@ -64,31 +70,69 @@ SMALL = [
 ]
 
 
+# Inputs on which a correct kernel with bf16 weights and output can pass 1e-2:
+# rows split between two keys with large, opposite V values (measured 1.557e-2,
+# one bf16 ulp at |O| in [2, 4)).  Held to max(1e-2, the bf16-weight bound).
+BOUNDED = {(2, 4, 4, 513, 513, 128, 128, True, 6.0)}
+
+
 @pytest.mark.parametrize("shape", SMALL, ids=lambda s: "x".join(map(str, s)))
 def test_small_shapes(orc, shape):
     B, Hq, Hkv, Lq, Lk, dqk, dv, causal, qm = shape
     q, k, v = make_qkv(B, Hq, Hkv, Lq, Lk, dqk, dv, seed=hash(shape) % 10007, q_mult=qm)
-    _full_check(f"small {shape}", q, k, v, causal, orc, stress=qm != 1.0)
+    _full_check(f"small {shape}", q, k, v, causal, orc, bounded=shape in BOUNDED)
 
 
-@pytest.mark.parametrize("name", ["mha_l2k", "causal_l8k", "gqa_l16k", "dsv3_l32k",
-                                  "dsv3_l32k_h2"])
-def test_full_size_workloads_sampled(orc, name):
-    """Full-size workload on the GPU, checked on sampled rows the oracle
-    computes one by one (always including the first and last rows)."""
+# Full-size workloads, every query row against the oracle.  The GPU output of
+# a workload is computed once (the launch the benchmark times) and the rows are
+# compared in chunks of whole heads, so that each test stays well under a
+# minute of oracle time on the host's cores.
+FULL_CHUNKS = {"mha_l2k": 2, "causal_l8k": 2, "gqa_l16k": 8, "dsv3_l32k": 8, "dsv3_l32k_h2": 2}
+_full_out = {}
+_full_stats = {}
+
+
+def _full_output(name):
+    if name not in _full_out:
+        _full_out.clear()  # keep one workload's tensors at a time
+        w = WORKLOADS[name]
+        q, k, v = workload_qkv(w)
+        qd, kd, vd = _gpu(q, k, v)
+        o, lse = attn_fwd(qd, kd, vd, causal=w.causal)
+        torch.cuda.synchronize()
+        assert torch.isfinite(o).all().item() and torch.isfinite(lse).all().item()
+        _full_out[name] = (q, k, v, o.reshape(-1, w.dv).cpu(), lse.reshape(-1).cpu())
+    return _full_out[name]
+
+
+@pytest.mark.parametrize("name,chunk", [(n, c) for n, nc in FULL_CHUNKS.items()
+                                        for c in range(nc)],
+                         ids=lambda x: str(x))
+def test_full_size_workloads_all_rows(orc, name, chunk):
+    """Full-size workload on the GPU in the benchmark's launch configuration;
+    every query row is compared with the oracle, one chunk of whole heads per
+    test.  The last chunk prints the workload's totals."""
     w = WORKLOADS[name]
-    print(f"[case] {name} {w.as_dict()}", flush=True)
-    q, k, v = workload_qkv(w)
-    qd, kd, vd = _gpu(q, k, v)
-    o, lse = attn_fwd(qd, kd, vd, causal=w.causal)
-    torch.cuda.synchronize()
-    rows = sample_rows(w.B, w.Hq, w.Lq, 384, seed=w.seed)
-    og, lg = gather_rows(o, lse, rows)
-    o_ref, l_ref = orc.attn_rows(q, k, v, causal=w.causal, rows=rows.numpy())
-    assert_parity(name, og, lg, o_ref, l_ref)
-    # every row is finite (or 0/-inf where it has no key) across the whole output
-    assert torch.isfinite(o).all().item()
-    assert torch.isfinite(lse).all().item()
+    n_chunks = FULL_CHUNKS[name]
+    heads = w.B * w.Hq
+    assert heads % n_chunks == 0
+    per = heads // n_chunks
+    print(f"[case] {name} all rows, heads {chunk * per}..{(chunk + 1) * per - 1} of {heads} "
+          f"{w.as_dict()}", flush=True)
+    q, k, v, o, lse = _full_output(name)
+    r0, r1 = chunk * per * w.Lq, (chunk + 1) * per * w.Lq
+    rows = np.arange(r0, r1, dtype=np.int64)
+    o_ref, l_ref = orc.attn_rows(q, k, v, causal=w.causal, rows=rows)
+    st = assert_parity(f"{name} rows {r0}..{r1 - 1}", o[r0:r1], lse[r0:r1], o_ref, l_ref)
+    acc = _full_stats.setdefault(name, {"rows": 0, "o_max": 0.0, "o_sum": 0.0, "lse_max": 0.0})
+    acc["rows"] += r1 - r0
+    acc["o_max"] = max(acc["o_max"], st["o_max"])
+    acc["o_sum"] += st["o_mean"] * (r1 - r0)
+    acc["lse_max"] = max(acc["lse_max"], st["lse_max"])
+    if chunk == n_chunks - 1 and acc["rows"] == heads * w.Lq:
+        print(f"[full] {name}: all {acc['rows']} rows, o_max={acc['o_max']:.3e} "
+              f"o_mean={acc['o_sum'] / acc['rows']:.3e} lse_max={acc['lse_max']:.3e}",
+              flush=True)
 
 
 # More than 256 tiles: one workgroup per CU loops over several tiles,
@@ -115,7 +159,7 @@ def test_persistent_shapes_sampled(orc, shape):
     rows = sample_rows(B, Hq, Lq, 512, seed=hash(shape) % 997)
     og, lg = gather_rows(o, lse, rows)
     o_ref, l_ref = orc.attn_rows(q, k, v, causal=causal, rows=rows.numpy())
-    assert_parity(f"persistent {shape}", og, lg, o_ref, l_ref, stress=qm != 1.0)
+    assert_parity(f"persistent {shape}", og, lg, o_ref, l_ref)
     if Lq <= Lk:
         assert torch.isfinite(o).all().item() and torch.isfinite(lse).all().item()
 
@@ -206,3 +250,38 @@ def test_rescale_threshold_and_events(orc):
         assert abs(counts[thr] - want) <= max(2, want // 50)
     assert counts[8.0] > 0
     assert counts[0.0] >= counts[8.0]
+
+
+def test_outputs_off_the_input_device_are_refused():
+    """Caller-supplied outputs on the host are refused before any launch, for
+    every entry point that takes them."""
+    from exact_attention_forward_02_amd import (attn_fwd_ex, attn_fwd_split, attn_fwd_varlen,
+                                                attn_merge)
+
+    q, k, v = _gpu(*make_qkv(1, 2, 2, 64, 64, 64, 64, seed=3))
+    o_host = torch.empty((1, 2, 64, 64), dtype=torch.bfloat16)
+    l_host = torch.empty((1, 2, 64), dtype=torch.float32)
+    o_dev = torch.empty_like(o_host, device=DEV)
+    l_dev = torch.empty_like(l_host, device=DEV)
+    with pytest.raises(ValueError):
+        attn_fwd(q, k, v, out=o_host)
+    with pytest.raises(ValueError):
+        attn_fwd(q, k, v, out=o_dev, lse=l_host)
+    with pytest.raises(ValueError):
+        attn_fwd_dbg(q, k, v, out=o_host)
+    with pytest.raises(ValueError):
+        attn_fwd_ex(q, k, v, out=o_host)
+    with pytest.raises(ValueError):
+        attn_fwd_ex(q, k, v, lse=l_host)
+    with pytest.raises(ValueError):
+        attn_fwd_split(q, k, v, 2, o_part=torch.empty((2, 1, 2, 64, 64)))
+    o_part, lse_part = attn_fwd_split(q, k, v, 2)
+    with pytest.raises(ValueError):
+        attn_merge(o_part, lse_part, out=o_host)
+    with pytest.raises(ValueError):
+        attn_merge(o_part, lse_part.cpu())
+    qv, kv, vv = (t[0].transpose(0, 1).contiguous() for t in (q, k, v))
+    with pytest.raises(ValueError):
+        attn_fwd_varlen(qv, kv, vv, [0, 64], [0, 64], out=torch.empty((64, 2, 64),
+                                                                       dtype=torch.bfloat16))
+    torch.cuda.synchronize()

@@ -8,7 +8,7 @@ import torch
 from exact_attention_forward_02_amd import attn_fwd, attn_fwd_varlen, varlen_plan
 from exact_attention_forward_02_amd.inputs import (VARLEN_WORKLOADS, make_varlen_qkv,
                                                    varlen_workload_qkv)
-from parity import assert_parity
+from parity import assert_parity, default_scale, dense_bound
 
 pytestmark = pytest.mark.gpu
 
@@ -48,16 +48,37 @@ def test_varlen_matches_the_oracle(orc, shape):
     assert_parity(f"varlen {shape}", og, lse.reshape(-1).cpu(), o_ref, l_ref)
 
 
+def _varlen_bound(q, k, v, cu_q, cu_k, causal, o_ref):
+    """The bf16-weight bound of every row (oracle order h * Tq + t), sequence by
+    sequence on [1, H, L, d] views."""
+    Tq, Hq, dqk = q.shape
+    bound = np.zeros_like(o_ref)
+    cq, ck = [int(x) for x in cu_q], [int(x) for x in cu_k]
+    for s in range(len(cq) - 1):
+        lq, lk = cq[s + 1] - cq[s], ck[s + 1] - ck[s]
+        if lq == 0 or lk == 0:
+            continue
+        qs, ks, vs = (t.permute(1, 0, 2).unsqueeze(0) for t in
+                      (q[cq[s]:cq[s + 1]], k[ck[s]:ck[s + 1]], v[ck[s]:ck[s + 1]]))
+        rows = (np.arange(Hq)[:, None] * Tq + cq[s] + np.arange(lq)[None, :]).ravel()
+        bound[rows] = dense_bound(qs, ks, vs, causal, default_scale(dqk), o_ref[rows])
+    return bound
+
+
 def test_varlen_q6_stress(orc):
-    """Q x 6: near one-hot rows whose references move inside sequences."""
+    """Q x 6: near one-hot rows whose references move inside sequences.  Rows
+    split between two keys with large, opposite V values pass 1e-2 for any
+    kernel with bf16 weights and output (measured 1.287e-2), so each element
+    is held to max(1e-2, the bf16-weight bound)."""
     lens = [333, 64, 700]
     q, k, v, cu_q, cu_k = make_varlen_qkv(lens, lens, 4, 2, 64, 64, seed=66, q_mult=6.0)
     print("[case] varlen q6", flush=True)
     o, lse = attn_fwd_varlen(q.to(DEV), k.to(DEV), v.to(DEV), cu_q, cu_k, causal=True)
     torch.cuda.synchronize()
     o_ref, l_ref = orc.attn_varlen(q, k, v, cu_q, cu_k, causal=True)
+    bound = _varlen_bound(q, k, v, cu_q, cu_k, True, o_ref)
     assert_parity("varlen q6", o.permute(1, 0, 2).reshape(-1, 64).cpu(), lse.reshape(-1).cpu(),
-                  o_ref, l_ref, stress=True)
+                  o_ref, l_ref, bound=bound)
 
 
 @pytest.mark.parametrize("causal", [False, True])

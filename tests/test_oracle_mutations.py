@@ -29,6 +29,8 @@ MUTATIONS = {
     "rescale_dropped": ("acc_scale = exp2((s->ref - cand) * scale_log2);", "acc_scale = 1.0;"),
     "online_lse_units": ("lse[t] = (mode == 0) ? s->ref + log(s->l)\n                                         : scale * s->ref + log(s->l);",
                          "lse[t] = s->ref + log(s->l);"),
+    "group_decision_ignored": ("int do_switch = (mode == 1) ? wants[a] : any_switch;",
+                               "int do_switch = wants[a];"),
     "first_block_not_adopted": ("s->ref = bmax[a];\n                acc_scale = 1.0;",
                                 "s->ref = 0.0;\n                acc_scale = 1.0;"),
     "segment_start_ignored": ("    if (j0 < 0)\n        j0 = 0;", "    j0 = 0;"),
