@@ -54,6 +54,8 @@ def _load():
                                     Strides, Strides, Strides, Strides, i, i, ctypes.c_float, vp]
         lib.attn_bwd.restype = i
         lib.attn_bwd.argtypes = [vp] * 10 + [i] * 8 + [ctypes.c_float, vp]
+        lib.attn_bwd_noalloc.restype = i
+        lib.attn_bwd_noalloc.argtypes = [vp] * 9 + [i] * 8 + [ctypes.c_float, vp]
         lib.attn_split_keys.restype = i
         lib.attn_split_keys.argtypes = [i, i]
         lib.attn_fwd_split.restype = i
@@ -273,6 +275,43 @@ def attn_bwd(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = 
     if rc != ATTN_OK:
         raise RuntimeError(f"attn_bwd failed: {status_string(rc)} (code {rc})")
     return dq, dk, dv, delta
+
+
+BWD_NOALLOC_MAX_ROWS = 4 << 20  # ATTN_BWD_NOALLOC_MAX_ROWS of include/attn_fwd.h
+
+
+def attn_bwd_noalloc(q, k, v, o, lse, dout, dq, dk, dv, causal: bool = False,
+                     scale: float | None = None, stream=None):
+    """attn_bwd for callers that cannot allocate: dq, dk and dv (caller-owned,
+    contiguous, on q's device) are written by the same kernels, with D kept in
+    the library's static device scratch (B * Hq * Lq <= BWD_NOALLOC_MAX_ROWS).
+    Calls that overlap on one device race on that scratch."""
+    lib = _load()
+    B, Hq, Hkv, Lq, Lk, dqk, dvd = _check_inputs(q, k, v)
+    for name, t, shape in (("o", o, (B, Hq, Lq, dvd)), ("dout", dout, (B, Hq, Lq, dvd))):
+        if (not isinstance(t, torch.Tensor) or t.dtype != torch.bfloat16 or t.device != q.device
+                or tuple(t.shape) != shape or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous bf16 {shape} tensor on q's device")
+    if (not isinstance(lse, torch.Tensor) or lse.dtype != torch.float32
+            or tuple(lse.shape) != (B, Hq, Lq) or not lse.is_contiguous()
+            or lse.device != q.device):
+        raise ValueError("lse must be the forward's contiguous fp32 [B, Hq, Lq] tensor")
+    for name, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        if (not isinstance(t, torch.Tensor) or t.shape != ref.shape or t.dtype != ref.dtype
+                or not t.is_contiguous() or t.device != q.device):
+            raise ValueError(f"{name} must be a contiguous tensor like {tuple(ref.shape)} on "
+                             "q's device")
+    if scale is None:
+        scale = 1.0 / math.sqrt(dqk)
+    with torch.cuda.device(q.device):
+        s = stream if stream is not None else torch.cuda.current_stream(q.device)
+        rc = lib.attn_bwd_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                  dout.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                                  dv.data_ptr(), B, Hq, Hkv, Lq, Lk, dqk, dvd,
+                                  int(bool(causal)), float(scale), s.cuda_stream)
+    if rc != ATTN_OK:
+        raise RuntimeError(f"attn_bwd_noalloc failed: {status_string(rc)} (code {rc})")
+    return dq, dk, dv
 
 
 def split_keys(Lk: int, n_split: int) -> int:

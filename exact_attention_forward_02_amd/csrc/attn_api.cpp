@@ -21,7 +21,9 @@
 
 namespace {
 
-constexpr int kAbiVersion = 6;
+static_assert(attn::kBwdScratchRows == ATTN_BWD_NOALLOC_MAX_ROWS,
+              "the header states the scratch size of attn_bwd_noalloc");
+constexpr int kAbiVersion = 7;
 constexpr int kMaxSplits = 4096;
 constexpr int kMaxDevices = 64;
 constexpr int kXcds = 8;                 // MI355X: 8 accelerator complex dies
@@ -414,16 +416,23 @@ int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse
                kDefaultThreshold, nullptr, false, 0, &st, dtype == ATTN_DTYPE_FP16);
 }
 
-int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
-             const float* lse, void* dq, void* dk, void* dv, float* delta, int B, int Hq, int Hkv,
-             int Lq, int Lk, int d_qk, int d_v, int causal, float scale, void* stream) {
-    if (!dout || !dq || !dk || !dv || !delta) return ATTN_ERR_NULL_PTR;
+}  // extern "C"
+
+namespace {
+
+// Validation and launch of the backward pass; delta == nullptr takes D's rows
+// from the library's static device scratch instead of a caller buffer.
+int run_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+            const float* lse, void* dq, void* dk, void* dv, float* delta, int B, int Hq, int Hkv,
+            int Lq, int Lk, int d_qk, int d_v, int causal, float scale, void* stream) {
+    const bool own_delta = delta == nullptr;
+    if (!dout || !dq || !dk || !dv) return ATTN_ERR_NULL_PTR;
     // the forward's argument rules, with o and lse as inputs here
     int rc = check_args(q, k, v, o, lse, B, Hq, Hkv, Lq, Lk, d_qk, d_v, scale);
     if (rc != ATTN_OK) return rc;
     if (!(d_qk == d_v && (d_qk == 64 || d_qk == 128))) return ATTN_ERR_UNSUPPORTED_HEAD_DIM;
     if (!aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) ||
-        !aligned(delta, 4))
+        (!own_delta && !aligned(delta, 4)))
         return ATTN_ERR_MISALIGNED;
     const Strides st = contiguous_strides(Hq, Hkv, Lq, Lk, d_qk, d_v);
     rc = check_strides(st, B, Hq, Hkv, Lq, Lk, d_qk, d_v);
@@ -431,8 +440,10 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
     if ((long long)B * Hkv * ((Lk + 127) / 128) > INT32_MAX ||
         (long long)B * Hq * ((Lq + 127) / 128) > INT32_MAX)
         return ATTN_ERR_TOO_LARGE;
+    if (own_delta && (long long)B * Hq * Lq > attn::kBwdScratchRows) return ATTN_ERR_SCRATCH;
     rc = check_device();
     if (rc != ATTN_OK) return rc;
+    if (own_delta && attn::bwd_scratch_rows(&delta) != hipSuccess) return ATTN_ERR_HIP;
     attn::BwdParams p;
     memset(&p, 0, sizeof p);
     p.q = static_cast<const uint16_t*>(q);
@@ -453,9 +464,30 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
     p.G = Hq / Hkv;
     p.scale = scale;
     p.scale_log2 = (float)((double)scale * 1.4426950408889634);
-    log_launch("attn_bwd<%d,%s>: delta, dK/dV and dQ kernels", d_qk, causal ? "causal" : "full");
+    log_launch("attn_bwd<%d,%s>: delta, dK/dV and dQ kernels%s", d_qk,
+               causal ? "causal" : "full", own_delta ? " (D in the static scratch)" : "");
     hipError_t err = attn::launch_bwd(p, d_qk, causal != 0, static_cast<hipStream_t>(stream));
     return err == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+             const float* lse, void* dq, void* dk, void* dv, float* delta, int B, int Hq, int Hkv,
+             int Lq, int Lk, int d_qk, int d_v, int causal, float scale, void* stream) {
+    if (!delta) return ATTN_ERR_NULL_PTR;
+    return run_bwd(q, k, v, o, dout, lse, dq, dk, dv, delta, B, Hq, Hkv, Lq, Lk, d_qk, d_v,
+                   causal, scale, stream);
+}
+
+int attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                     const void* dout, const float* lse, void* dq, void* dk, void* dv, int B,
+                     int Hq, int Hkv, int Lq, int Lk, int d_qk, int d_v, int causal, float scale,
+                     void* stream) {
+    return run_bwd(q, k, v, o, dout, lse, dq, dk, dv, nullptr, B, Hq, Hkv, Lq, Lk, d_qk, d_v,
+                   causal, scale, stream);
 }
 
 int attn_split_keys(int Lk, int n_split) {
@@ -642,6 +674,9 @@ const char* attn_status_string(int status) {
         case ATTN_ERR_BAD_STRIDE:
             return "strides must be >= 0 and multiples of 8 elements, with row strides of at "
                    "least the head dim";
+        case ATTN_ERR_SCRATCH:
+            return "B * Hq * Lq exceeds the rows of the allocation-free entry point's static "
+                   "scratch (ATTN_BWD_NOALLOC_MAX_ROWS)";
         default: return "unknown attn status";
     }
 }

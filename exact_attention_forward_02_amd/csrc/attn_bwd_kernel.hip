@@ -29,9 +29,38 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "attn_params.h"
 
 namespace attn {
+
+// D_i of the allocation-free entry point (attn_bwd_noalloc): one float per
+// query row, a fixed 16 MiB that each device running the library holds until
+// the process ends.  Host code never passes this name to a kernel (in host
+// code it is only a stand-in for the symbol): it looks up the device address
+// once per device (bwd_scratch_rows) and passes that.
+static __device__ __align__(256) float scratch[kBwdScratchRows];
+
+hipError_t bwd_scratch_rows(float** rows) {
+    constexpr int kMaxDev = 64;
+    static std::mutex mu;
+    static float* addr[kMaxDev] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDev) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (addr[dev] == nullptr) {
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (ptr == nullptr) return hipErrorInvalidSymbol;
+        addr[dev] = static_cast<float*>(ptr);
+    }
+    *rows = addr[dev];
+    return hipSuccess;
+}
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));

@@ -83,6 +83,14 @@ struct BwdParams {
 
 hipError_t launch_bwd(const BwdParams& p, int d, bool causal, hipStream_t stream);
 
+// Rows of D (one float each) that the file-scope device array `scratch` of the
+// allocation-free backward entry point holds: 4 Mi rows, 16 MiB per device.
+constexpr long long kBwdScratchRows = 4LL << 20;
+
+// Device address of the current device's copy of that array, looked up with
+// hipGetSymbolAddress on the first call per device and kept; allocates nothing.
+hipError_t bwd_scratch_rows(float** rows);
+
 // Split-key forward for few query rows per K/V head (decoding): at most
 // kDecRows = Lq * Hq / Hkv rows, contiguous bf16 [B, H, L, d] tensors,
 // (d_qk, d_v) in {(64, 64), (128, 128), (192, 128)}.  Writes the same

@@ -61,9 +61,11 @@ enum attn_status {
     ATTN_ERR_HIP = 10,                  /* the HIP runtime reported an error at launch */
     ATTN_ERR_BAD_ARGUMENT = 11,         /* a debug-only argument, a split count, a
                                            merge row count or a dtype is out of range */
-    ATTN_ERR_BAD_STRIDE = 12            /* a stride is negative, not a multiple of 8
+    ATTN_ERR_BAD_STRIDE = 12,           /* a stride is negative, not a multiple of 8
                                            elements, or a row stride is below the
                                            head dim */
+    ATTN_ERR_SCRATCH = 13               /* attn_bwd_noalloc: B * Hq * Lq exceeds
+                                           ATTN_BWD_NOALLOC_MAX_ROWS */
 };
 
 /* Element types of attn_fwd_ex. */
@@ -231,6 +233,30 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
              const float* lse, void* dq, void* dk, void* dv, float* delta,
              int B, int Hq, int Hkv, int Lq, int Lk, int d_qk, int d_v,
              int causal, float scale, void* stream);
+
+/*
+ * attn_bwd_noalloc -- attn_bwd for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight loops, harnesses that forbid
+ * hipMalloc): the same kernels and the same dq, dk and dv, bit for bit, with
+ * D = rowsum(dout * o) kept in a fixed device array inside the library instead
+ * of a caller's delta buffer.  Nothing is allocated by this call or by the
+ * library: the array is a file-scope device variable of
+ * ATTN_BWD_NOALLOC_MAX_ROWS floats (16 MiB), which each device the library
+ * runs on holds until the process ends; its device address is looked up once
+ * per device on the first call there.
+ *   Arguments as attn_bwd without delta.
+ *   Returns ATTN_ERR_SCRATCH when B * Hq * Lq > ATTN_BWD_NOALLOC_MAX_ROWS
+ *   (checked before any HIP call); other errors as attn_bwd.
+ * Every call on one device shares that device's array, and D is written in
+ * full by each call before its kernels read it, so no clearing is needed; but
+ * calls that overlap on one device (on different streams, or from different
+ * host threads without ordering) race on the array and must not be issued.
+ */
+#define ATTN_BWD_NOALLOC_MAX_ROWS (4LL << 20)
+int attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                     const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                     int B, int Hq, int Hkv, int Lq, int Lk, int d_qk, int d_v,
+                     int causal, float scale, void* stream);
 
 /*
  * attn_fwd_decode -- attn_fwd_split's per-split states, computed by a kernel

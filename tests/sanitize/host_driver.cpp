@@ -21,6 +21,7 @@ hipError_t launch_merge(const float*, const float*, uint16_t*, float*, int, long
     abort();
 }
 hipError_t launch_decode(const DecParams&, int, int, bool, hipStream_t) { abort(); }
+hipError_t bwd_scratch_rows(float**) { abort(); }
 }  // namespace attn
 
 static int failures = 0;
@@ -94,6 +95,13 @@ int main() {
     EXPECT(is_no_dev(attn_fwd(q, k, v, o, lse, 2, 8, 2, 300, 500, 128, 128, 1, 0.1f, nullptr)));
     EXPECT(is_no_dev(attn_fwd(q, k, v, o, lse, 1, 16, 16, 32768, 32768, 192, 128, 1, 0.07f,
                               nullptr)));
+    // the allocation-free backward: its row limit is checked before any device call
+    EXPECT(attn_bwd_noalloc(q, k, v, o, o, lse, o, o, o, 1, 64, 64, 65537, 64, 128, 128, 0, 0.1f,
+                            nullptr) == ATTN_ERR_SCRATCH);
+    EXPECT(is_no_dev(attn_bwd_noalloc(q, k, v, o, o, lse, o, o, o, 1, 64, 64, 65536, 64, 128,
+                                      128, 0, 0.1f, nullptr)));
+    EXPECT(attn_bwd_noalloc(q, k, v, o, o, nullptr, o, o, o, 1, 2, 2, 64, 64, 128, 128, 0, 0.1f,
+                            nullptr) == ATTN_ERR_NULL_PTR);
     unsigned long long cnt = 0;
     EXPECT(is_no_dev(attn_fwd_dbg(q, k, v, o, lse, 1, 1, 1, 256, 256, 64, 64, 0, 0.125f, nullptr,
                                   0.0f, 0, &cnt)));

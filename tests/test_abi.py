@@ -18,6 +18,7 @@ CODES = {
     "ATTN_ERR_UNSUPPORTED_HEAD_DIM": 4, "ATTN_ERR_BAD_SCALE": 5, "ATTN_ERR_MISALIGNED": 6,
     "ATTN_ERR_TOO_LARGE": 7, "ATTN_ERR_NO_DEVICE": 8, "ATTN_ERR_UNSUPPORTED_ARCH": 9,
     "ATTN_ERR_HIP": 10, "ATTN_ERR_BAD_ARGUMENT": 11, "ATTN_ERR_BAD_STRIDE": 12,
+    "ATTN_ERR_SCRATCH": 13,
 }
 
 
@@ -39,7 +40,8 @@ def _exported_symbols(path):
 
 
 def test_header_declares_the_entry_points():
-    assert {"attn_fwd", "attn_fwd_dbg", "attn_fwd_ex", "attn_bwd", "attn_split_keys", "attn_fwd_split",
+    assert {"attn_fwd", "attn_fwd_dbg", "attn_fwd_ex", "attn_bwd", "attn_bwd_noalloc",
+            "attn_split_keys", "attn_fwd_split",
             "attn_merge", "attn_varlen_plan", "attn_fwd_varlen", "attn_fwd_decode",
             "attn_status_string",
             "attn_abi_version"} <= _declared_functions()
@@ -61,7 +63,7 @@ def test_library_exports_every_declared_function():
 
 def test_abi_version_and_status_strings():
     lib = _binding.library()
-    assert lib.attn_abi_version() == 6
+    assert lib.attn_abi_version() == 7
     for code in CODES.values():
         s = _binding.status_string(code)
         assert s and s != "unknown attn status"
@@ -169,6 +171,27 @@ def test_binding_refuses_outputs_off_the_input_device():
     o_part = torch.zeros((2, 4, 64), dtype=torch.float32)
     with pytest.raises(ValueError, match="GPU"):
         _binding.attn_merge(o_part, torch.zeros((2, 4), dtype=torch.float32))
+
+
+def test_noalloc_backward_row_limit_comes_before_any_device_call():
+    """attn_bwd_noalloc refuses problems whose D rows exceed its static scratch
+    (ATTN_BWD_NOALLOC_MAX_ROWS) before touching a device; a problem at the limit
+    passes validation and, without a GPU, stops at the device check."""
+    import torch
+
+    lib = _binding.library()
+    mx = _binding.BWD_NOALLOC_MAX_ROWS
+    header = open(os.path.join(ROOT, "include", "attn_fwd.h"), encoding="utf-8").read()
+    assert "#define ATTN_BWD_NOALLOC_MAX_ROWS (4LL << 20)" in header and mx == 4 << 20
+
+    def call(Hq, Lq, lse=A * 5):
+        return lib.attn_bwd_noalloc(A, A * 2, A * 3, A * 4, A * 6, lse, A * 7, A * 8, A * 9,
+                                    1, Hq, 1, Lq, 64, 128, 128, 0, 0.088, None)
+
+    assert call(64, mx // 64 + 1) == CODES["ATTN_ERR_SCRATCH"]
+    assert call(64, mx // 64, lse=None) == CODES["ATTN_ERR_NULL_PTR"]
+    if not torch.cuda.is_available():
+        assert call(64, mx // 64) == CODES["ATTN_ERR_NO_DEVICE"]
 
 
 def test_split_keys_arithmetic():
