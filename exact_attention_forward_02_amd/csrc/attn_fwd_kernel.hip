@@ -353,12 +353,28 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
         const int local = first + ((r & 1) ? cnt - 1 - slot : slot);
         return p.xcd_mode ? (local << 3) | xcd : local;
     };
+    // Causal tiles of odd rounds sweep their keys from the last block down.
+    // Round r and r + 1 pair heavy with light tiles (the snake above), so the
+    // tiles of an odd round, which start as the previous round's tiles finish,
+    // all finish together; swept downward they all reach block 0 at that
+    // moment and so visit the same key block at the same time, which keeps a
+    // head's K/V blocks shared in the XCD's L2 instead of fetched once per
+    // tile.  The online softmax takes the keys in any order: rows whose
+    // first blocks are masked keep an empty state until their first visible
+    // key adopts its maximum.
+    auto sweep_down = [&](int r) __attribute__((always_inline)) {
+        return CAUSAL && !VARLEN && (r & 1) != 0;
+    };
     int round = 0;
     int tile = tile_of_round(0);
     if (tile < 0) return;  // only if the grid exceeds the tiles (workgroup-uniform)
 
-    // per-tile values of this wave (set_tile)
-    int split, qw, jb0, nblk, nact;
+    // per-tile values of this wave (set_tile).  The sweep visits the tile's
+    // blocks in local order j = 0 .. nblk - 1, key block jb0 + blk(j); the
+    // wave computes on local blocks [jact0, jact1).
+    int split, qw, jb0, nblk, jact1;
+    int jact0 = 0;
+    bool desc = false;  // the sweep runs from the last key block down
     size_t qrow0;  // row index of (b, hq, position 0) in lse
     size_t qrow_w, orow_w;  // element offsets of this wave's first Q and O rows
     __amdgpu_buffer_rsrc_t krsrc, vrsrc;
@@ -386,7 +402,14 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
         const KeyRange r = key_range<CAUSAL>(p, c);
         jb0 = r.jb0;
         nblk = r.nblk;
-        nact = r.nact;
+        // the wave's own blocks are the first nact in key order: a prefix of an
+        // upward sweep, a suffix of a downward one
+        jact1 = r.nact;
+        if constexpr (CAUSAL && !VARLEN) {
+            desc = sweep_down(round);
+            jact0 = desc ? r.nblk - r.nact : 0;
+            jact1 = desc ? r.nblk : r.nact;
+        }
         // one descriptor per K/V head; a head spans less than 2^31 bytes
         // (checked on the host), so 32-bit byte offsets address all of it
         krsrc = make_rsrc(p.k + c.kbase, kv_bytes(c.Lk, k_rb, kRowK));
@@ -443,9 +466,13 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
     // destination is a scalar too, so a copy needs no vector arithmetic.
     const int kdst = __builtin_amdgcn_readfirstlane(1024 * S::kKCopies * wq);
     const int vdst = __builtin_amdgcn_readfirstlane(1024 * S::kVCopies * wq);
+    // key block (relative to jb0) of local block j of the sweep
+    auto blk = [&](int j) __attribute__((always_inline)) {
+        return (CAUSAL && !VARLEN && desc) ? nblk - 1 - j : j;
+    };
     auto copy_kblock = [&](__amdgpu_buffer_rsrc_t rs, int key0, int lk, unsigned char* dst)
                            __attribute__((always_inline)) {
-        const uint32_t blk = (uint32_t)key0 * k_rb;
+        const uint32_t boff = (uint32_t)key0 * k_rb;
         // an opaque copy of the wave's offset: the destinations are formed
         // here with one scalar add each, not precomputed for every buffer
         // and copy and held (or spilled) across the sweep
@@ -454,37 +481,37 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
         if (key0 + kBlockN <= lk) {
 #pragma unroll
             for (int i = 0; i < S::kKCopies; ++i)
-                copy_to_lds(rs, koff[i], blk, dst + kd + 1024 * i);
+                copy_to_lds(rs, koff[i], boff, dst + kd + 1024 * i);
         } else {
             const int last = lk - 1 - key0;
 #pragma unroll
             for (int i = 0; i < S::kKCopies; ++i) {
                 const int r = (64 * (wq * S::kKCopies + i) + lane) / S::kChunksK;
                 const int rr = min(r, last);
-                copy_to_lds(rs, koff[i] - (uint32_t)((r - rr) * k_rb), blk,
+                copy_to_lds(rs, koff[i] - (uint32_t)((r - rr) * k_rb), boff,
                             dst + kd + 1024 * i);
             }
         }
     };
     auto copy_k = [&](int jl, unsigned char* dst) __attribute__((always_inline)) {
-        copy_kblock(krsrc, (jb0 + jl) * kBlockN, Lk_t, dst);
+        copy_kblock(krsrc, (jb0 + blk(jl)) * kBlockN, Lk_t, dst);
     };
     auto copy_v = [&](int jl, unsigned char* dst) __attribute__((always_inline)) {
-        const int key0 = (jb0 + jl) * kBlockN;
-        const uint32_t blk = (uint32_t)key0 * v_rb;
+        const int key0 = (jb0 + blk(jl)) * kBlockN;
+        const uint32_t boff = (uint32_t)key0 * v_rb;
         int vd = vdst;
         asm volatile("" : "+s"(vd));
         if (key0 + kBlockN <= Lk_t) {
 #pragma unroll
             for (int i = 0; i < S::kVCopies; ++i)
-                copy_to_lds(vrsrc, voff_copy[i], blk, dst + vd + 1024 * i);
+                copy_to_lds(vrsrc, voff_copy[i], boff, dst + vd + 1024 * i);
         } else {
             const int last = Lk_t - 1 - key0;
 #pragma unroll
             for (int i = 0; i < S::kVCopies; ++i) {
                 const int r = (64 * (wq * S::kVCopies + i) + lane) / S::kChunksV;
                 const int rr = min(r, last);
-                copy_to_lds(vrsrc, voff_copy[i] - (uint32_t)((r - rr) * v_rb), blk,
+                copy_to_lds(vrsrc, voff_copy[i] - (uint32_t)((r - rr) * v_rb), boff,
                             dst + vd + 1024 * i);
             }
         }
@@ -579,8 +606,9 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
                                                 mb * 32 * kRowK);
     };
     auto m_phase = [&](int j, const unsigned char* kl, const unsigned char* vl) __attribute__((always_inline)) {
-        const bool do_pv = j >= 0 && j < nact;
-        const bool do_s = j + 1 < nact;
+        constexpr bool kDown = CAUSAL && !VARLEN;  // launches that may sweep downward
+        const bool do_pv = j >= (kDown ? jact0 : 0) && j < jact1;
+        const bool do_s = (!kDown || j + 1 >= jact0) && j + 1 < jact1;
         const f32x16 zero = {};
         // one MFMA unit: PV unit u < kPvUnits, else score unit u - kPvUnits; the
         // first k-step of a score block starts from an inline zero accumulator
@@ -656,8 +684,11 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
 
     // ---- VALU phase V(j): online softmax of block j's scores -----------------
     auto v_phase = [&](int j) __attribute__((always_inline)) {
-        if (j >= nact) return;
-        const int key0 = (jb0 + j) * kBlockN;
+        if (j >= jact1) return;
+        if constexpr (CAUSAL && !VARLEN) {
+            if (j < jact0) return;
+        }
+        const int key0 = (jb0 + blk(j)) * kBlockN;
         // mask keys past the end or past the causal diagonal
         const bool need_mask =
             (key0 + kBlockN > Lk_t) || (CAUSAL && key0 + kBlockN - 1 > qw + off);
@@ -865,7 +896,8 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
             const TileCoord c = tile_coord<CAUSAL, VARLEN>(p, tile_n, wave);
             const KeyRange r = key_range<CAUSAL>(p, c);
             nk_copy = r.nblk > 0;
-            nk_key0 = r.jb0 * kBlockN;
+            // its first block: the first or the last of its key range
+            nk_key0 = (r.jb0 + (sweep_down(round + 1) ? r.nblk - 1 : 0)) * kBlockN;
             nk_lk = c.Lk;
             nk_rsrc = make_rsrc(p.k + c.kbase, kv_bytes(c.Lk, k_rb, kRowK));
             if (kStage) {

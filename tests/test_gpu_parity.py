@@ -137,7 +137,8 @@ def test_full_size_workloads_all_rows(orc, name, chunk):
 
 # More than 256 tiles: one workgroup per CU loops over several tiles,
 # prefetching each next tile's queries and draining each output tile through
-# LDS.  Checked on sampled rows (always including the first and last).
+# LDS; causal tiles of odd rounds sweep their keys downward.  Every row is
+# compared with the oracle.
 PERSISTENT = [
     (2, 16, 16, 2100, 700, 128, 128, False, 1.0),   # 288 tiles, ragged Lq and Lk
     (4, 8, 8, 2304, 300, 128, 128, True, 1.0),      # Lq > Lk: tiles with 0, 1, 2 blocks
@@ -145,38 +146,46 @@ PERSISTENT = [
     (1, 32, 32, 2304, 512, 128, 128, False, 6.0),   # Q x 6
     (3, 12, 6, 2000, 2000, 128, 128, True, 1.0),    # causal square, GQA 2
     (1, 16, 16, 4200, 1000, 192, 128, True, 1.0),   # (192, 128): Q loaded per tile
+    (2, 16, 16, 6000, 6100, 128, 128, True, 1.0),   # causal, ragged, three rounds
 ]
+# Q x 6 over all 73,728 rows: rows split between two keys with large, opposite V
+# values take the bf16-weight bound past 1e-2 (emulated: 1.53e-2)
+PERSISTENT_BOUNDED = {(1, 32, 32, 2304, 512, 128, 128, False, 6.0)}
 
 
 @pytest.mark.parametrize("shape", PERSISTENT, ids=lambda s: "x".join(map(str, s)))
-def test_persistent_shapes_sampled(orc, shape):
+def test_persistent_shapes(orc, shape):
     B, Hq, Hkv, Lq, Lk, dqk, dv, causal, qm = shape
-    print(f"[case] persistent {shape}", flush=True)
     q, k, v = make_qkv(B, Hq, Hkv, Lq, Lk, dqk, dv, seed=hash(shape) % 10007, q_mult=qm)
-    qd, kd, vd = _gpu(q, k, v)
-    o, lse = attn_fwd(qd, kd, vd, causal=causal)
-    torch.cuda.synchronize()
-    rows = sample_rows(B, Hq, Lq, 512, seed=hash(shape) % 997)
-    og, lg = gather_rows(o, lse, rows)
-    o_ref, l_ref = orc.attn_rows(q, k, v, causal=causal, rows=rows.numpy())
-    assert_parity(f"persistent {shape}", og, lg, o_ref, l_ref)
-    if Lq <= Lk:
-        assert torch.isfinite(o).all().item() and torch.isfinite(lse).all().item()
+    _full_check(f"persistent {shape}", q, k, v, causal, orc,
+                bounded=shape in PERSISTENT_BOUNDED)
 
 
-def test_persistent_equals_one_tile_per_workgroup():
+def test_persistent_equals_one_tile_per_workgroup(orc):
     """The same rows computed in a launch of 288 tiles (workgroups loop over
     tiles) and, batch by batch, in launches of 144 tiles (one tile per
-    workgroup) agree bit for bit."""
+    workgroup): bit for bit without the causal mask; with it, the tiles of the
+    second round sweep their keys downward, so both launches are held to the
+    oracle instead."""
     q, k, v = make_qkv(2, 16, 16, 2100, 700, 128, 128, seed=123)
     qd, kd, vd = _gpu(q, k, v)
     for causal in (False, True):
         o, lse = attn_fwd(qd, kd, vd, causal=causal)
+        parts = []
         for b in range(2):
             ob, lb = attn_fwd(qd[b:b + 1].contiguous(), kd[b:b + 1].contiguous(),
                               vd[b:b + 1].contiguous(), causal=causal)
             torch.cuda.synchronize()
-            assert torch.equal(o[b:b + 1], ob) and torch.equal(lse[b:b + 1], lb)
+            if not causal:
+                assert torch.equal(o[b:b + 1], ob) and torch.equal(lse[b:b + 1], lb)
+            parts.append((ob, lb))
+        if causal:
+            o_ref, l_ref = orc.attn_rows(q, k, v, causal=True)
+            assert_parity("288 tiles causal", o.cpu().reshape(-1, 128), lse.cpu().reshape(-1),
+                          o_ref, l_ref)
+            ob = torch.cat([p_[0] for p_ in parts]).cpu().reshape(-1, 128)
+            lb = torch.cat([p_[1] for p_ in parts]).cpu().reshape(-1)
+            assert_parity("2 x 144 tiles causal", ob, lb, o_ref, l_ref)
 
 
 def test_zero_query_closed_form():
