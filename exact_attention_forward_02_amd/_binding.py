@@ -54,6 +54,8 @@ def _load():
                                     Strides, Strides, Strides, Strides, i, i, ctypes.c_float, vp]
         lib.attn_bwd.restype = i
         lib.attn_bwd.argtypes = [vp] * 10 + [i] * 8 + [ctypes.c_float, vp]
+        lib.attn_bwd_ex.restype = i
+        lib.attn_bwd_ex.argtypes = [vp] * 10 + [i] * 9 + [ctypes.c_float, vp]
         lib.attn_bwd_noalloc.restype = i
         lib.attn_bwd_noalloc.argtypes = [vp] * 9 + [i] * 8 + [ctypes.c_float, vp]
         lib.attn_split_keys.restype = i
@@ -89,12 +91,12 @@ def status_string(rc: int) -> str:
     return _load().attn_status_string(int(rc)).decode()
 
 
-def _check_inputs(q, k, v):
+def _check_inputs(q, k, v, dtypes=(torch.bfloat16,)):
     for name, t in (("q", q), ("k", k), ("v", v)):
         if not isinstance(t, torch.Tensor):
             raise TypeError(f"{name} must be a torch.Tensor")
-        if t.dtype != torch.bfloat16:
-            raise TypeError(f"{name} must be bfloat16, got {t.dtype}")
+        if t.dtype not in dtypes or t.dtype != q.dtype:
+            raise TypeError(f"{name} must be one of {dtypes} (as q), got {t.dtype}")
         if t.device.type != "cuda":
             raise ValueError(f"{name} must be on a GPU device, got {t.device}")
         if t.dim() != 4 or not t.is_contiguous():
@@ -245,14 +247,16 @@ def attn_fwd_ex(q, k, v, causal: bool = False, scale: float | None = None, out=N
 def attn_bwd(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = None,
              dq=None, dk=None, dv=None, delta=None, stream=None):
     """dq, dk, dv (and delta = rowsum(dout * o)) of the attention forward pass
-    that produced o and lse from q, k, v: contiguous bf16 [B, H, L, d] tensors,
-    d_qk == d_v in (64, 128)."""
+    that produced o and lse from q, k, v: contiguous [B, H, L, d] tensors, all
+    bf16 (attn_bwd) or all fp16 (attn_bwd_ex), (d_qk, d_v) one of (64, 64),
+    (128, 128), (192, 128)."""
     lib = _load()
-    B, Hq, Hkv, Lq, Lk, dqk, dvd = _check_inputs(q, k, v)
+    B, Hq, Hkv, Lq, Lk, dqk, dvd = _check_inputs(q, k, v, (torch.bfloat16, torch.float16))
     for name, t, shape in (("o", o, (B, Hq, Lq, dvd)), ("dout", dout, (B, Hq, Lq, dvd))):
-        if (not isinstance(t, torch.Tensor) or t.dtype != torch.bfloat16 or t.device != q.device
+        if (not isinstance(t, torch.Tensor) or t.dtype != q.dtype or t.device != q.device
                 or tuple(t.shape) != shape or not t.is_contiguous()):
-            raise ValueError(f"{name} must be a contiguous bf16 {shape} tensor on q's device")
+            raise ValueError(f"{name} must be a contiguous {q.dtype} {shape} tensor on q's "
+                             "device")
     if (lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq, Lq) or not lse.is_contiguous()
             or lse.device != q.device):
         raise ValueError("lse must be the forward's contiguous fp32 [B, Hq, Lq] tensor")
@@ -266,14 +270,20 @@ def attn_bwd(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = 
         if t.shape != ref.shape or t.dtype != ref.dtype or not t.is_contiguous() \
                 or t.device != q.device:
             raise ValueError(f"{name} must be a contiguous tensor like {tuple(ref.shape)}")
+    ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
+            lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(),
+            B, Hq, Hkv, Lq, Lk, dqk, dvd)
     with torch.cuda.device(q.device):
         s = stream if stream is not None else torch.cuda.current_stream(q.device)
-        rc = lib.attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
-                          dout.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
-                          dv.data_ptr(), delta.data_ptr(), B, Hq, Hkv, Lq, Lk, dqk, dvd,
-                          int(bool(causal)), float(scale), s.cuda_stream)
+        if q.dtype == torch.bfloat16:
+            name = "attn_bwd"
+            rc = lib.attn_bwd(*ptrs, int(bool(causal)), float(scale), s.cuda_stream)
+        else:
+            name = "attn_bwd_ex"
+            rc = lib.attn_bwd_ex(*ptrs, ATTN_DTYPE_FP16, int(bool(causal)), float(scale),
+                                 s.cuda_stream)
     if rc != ATTN_OK:
-        raise RuntimeError(f"attn_bwd failed: {status_string(rc)} (code {rc})")
+        raise RuntimeError(f"{name} failed: {status_string(rc)} (code {rc})")
     return dq, dk, dv, delta
 
 

@@ -23,7 +23,7 @@ namespace {
 
 static_assert(attn::kBwdScratchRows == ATTN_BWD_NOALLOC_MAX_ROWS,
               "the header states the scratch size of attn_bwd_noalloc");
-constexpr int kAbiVersion = 7;
+constexpr int kAbiVersion = 8;
 constexpr int kMaxSplits = 4096;
 constexpr int kMaxDevices = 64;
 constexpr int kXcds = 8;                 // MI355X: 8 accelerator complex dies
@@ -424,13 +424,13 @@ namespace {
 // from the library's static device scratch instead of a caller buffer.
 int run_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
             const float* lse, void* dq, void* dk, void* dv, float* delta, int B, int Hq, int Hkv,
-            int Lq, int Lk, int d_qk, int d_v, int causal, float scale, void* stream) {
+            int Lq, int Lk, int d_qk, int d_v, int causal, float scale, void* stream,
+            bool fp16 = false) {
     const bool own_delta = delta == nullptr;
     if (!dout || !dq || !dk || !dv) return ATTN_ERR_NULL_PTR;
     // the forward's argument rules, with o and lse as inputs here
     int rc = check_args(q, k, v, o, lse, B, Hq, Hkv, Lq, Lk, d_qk, d_v, scale);
     if (rc != ATTN_OK) return rc;
-    if (!(d_qk == d_v && (d_qk == 64 || d_qk == 128))) return ATTN_ERR_UNSUPPORTED_HEAD_DIM;
     if (!aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) ||
         (!own_delta && !aligned(delta, 4)))
         return ATTN_ERR_MISALIGNED;
@@ -439,6 +439,10 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const vo
     if (rc != ATTN_OK) return rc;
     if ((long long)B * Hkv * ((Lk + 127) / 128) > INT32_MAX ||
         (long long)B * Hq * ((Lq + 127) / 128) > INT32_MAX)
+        return ATTN_ERR_TOO_LARGE;
+    // the dK/dV kernel addresses one query head of Q and of dO with 32-bit
+    // buffer offsets
+    if ((long long)Lq * d_qk * 2 > INT32_MAX || (long long)Lq * d_v * 2 > INT32_MAX)
         return ATTN_ERR_TOO_LARGE;
     if (own_delta && (long long)B * Hq * Lq > attn::kBwdScratchRows) return ATTN_ERR_SCRATCH;
     rc = check_device();
@@ -464,9 +468,11 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const vo
     p.G = Hq / Hkv;
     p.scale = scale;
     p.scale_log2 = (float)((double)scale * 1.4426950408889634);
-    log_launch("attn_bwd<%d,%s>: delta, dK/dV and dQ kernels%s", d_qk,
-               causal ? "causal" : "full", own_delta ? " (D in the static scratch)" : "");
-    hipError_t err = attn::launch_bwd(p, d_qk, causal != 0, static_cast<hipStream_t>(stream));
+    log_launch("attn_bwd<%d,%d,%s%s>: delta, dK/dV and dQ kernels%s", d_qk, d_v,
+               causal ? "causal" : "full", fp16 ? ",fp16" : "",
+               own_delta ? " (D in the static scratch)" : "");
+    hipError_t err = attn::launch_bwd(p, d_qk, d_v, causal != 0, fp16,
+                                      static_cast<hipStream_t>(stream));
     return err == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
@@ -480,6 +486,16 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
     if (!delta) return ATTN_ERR_NULL_PTR;
     return run_bwd(q, k, v, o, dout, lse, dq, dk, dv, delta, B, Hq, Hkv, Lq, Lk, d_qk, d_v,
                    causal, scale, stream);
+}
+
+int attn_bwd_ex(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                const float* lse, void* dq, void* dk, void* dv, float* delta, int B, int Hq,
+                int Hkv, int Lq, int Lk, int d_qk, int d_v, int dtype, int causal, float scale,
+                void* stream) {
+    if (dtype != ATTN_DTYPE_BF16 && dtype != ATTN_DTYPE_FP16) return ATTN_ERR_BAD_ARGUMENT;
+    if (!delta) return ATTN_ERR_NULL_PTR;
+    return run_bwd(q, k, v, o, dout, lse, dq, dk, dv, delta, B, Hq, Hkv, Lq, Lk, d_qk, d_v,
+                   causal, scale, stream, dtype == ATTN_DTYPE_FP16);
 }
 
 int attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,

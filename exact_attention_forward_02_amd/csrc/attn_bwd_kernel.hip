@@ -20,11 +20,14 @@
 // Both main kernels stream their blocks of 64 rows through two LDS stages,
 // filled by direct-to-LDS buffer copies while the other stage is computed on,
 // with one barrier per block.
-// MFMA v_mfma_f32_32x32x16_bf16 with fp32 accumulation.  Operand A is read
-// from LDS (rows with ds_read_b128, transposed with ds_read_b64_tr_b16);
-// operand B is a register fragment: the wave's own K/V or Q/dO rows, or the
-// bf16 P / dS fragments, whose row order the transposed reads follow.  The
-// causal mask is bottom-right aligned (query i sees keys j <= i + Lk - Lq).
+// MFMA v_mfma_f32_32x32x16 (bf16 or fp16 inputs) with fp32 accumulation.
+// Operand A is read from LDS (rows with ds_read_b128, transposed with
+// ds_read_b64_tr_b16); operand B is a register fragment: the wave's own K/V
+// or Q/dO rows, or the 16-bit P / dS fragments, whose row order the
+// transposed reads follow.  The causal mask is bottom-right aligned (query i
+// sees keys j <= i + Lk - Lq).  Q and K rows have d_qk elements, V, O and dO
+// rows d_v (64/64, 128/128 or 192/128); P and dS enter the products in the
+// inputs' 16-bit type.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -71,6 +74,29 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+
+// The 16-bit element type of the tensors and of P and dS in the products,
+// with its MFMA form; conversions from fp32 round to nearest even.
+template <bool FP16>
+struct Elem;
+template <>
+struct Elem<false> {
+    using x8 = bf16x8;
+    using x4 = bf16x4;
+    static __device__ __forceinline__ f32x16 mfma(x8 a, x8 b, f32x16 c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+    }
+};
+template <>
+struct Elem<true> {
+    using x8 = f16x8;
+    using x4 = f16x4;
+    static __device__ __forceinline__ f32x16 mfma(x8 a, x8 b, f32x16 c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+    }
+};
 
 constexpr int kBwdThreads = 256;  // 4 waves, one per SIMD
 constexpr int kBlk = 64;          // rows of a staged Q/dO (or K/V) block
@@ -82,8 +108,13 @@ constexpr float kLog2e = 1.4426950408889634f;
 // 32 lanes reading 8 bytes of 4 consecutive rows at 4 adjacent chunks).
 // With 64 banks of 4 bytes, the row read is conflict-free when the 16 rows
 // land on 16 distinct bank groups, and the transposed read when the 4 rows
-// have distinct chunk bits 2-3 (d = 128); for d = 64 two rows share the bank
-// space.  These swizzles satisfy both (swz(r) depends on r mod 16).
+// have distinct chunk bits 2-3 (d = 128).  For 128-byte (d = 64) and
+// 384-byte (d = 192) rows, rows r and r + 1 start half a bank space apart, so
+// the even rows of 16 need distinct swizzles in the low 3 bits (row reads),
+// and rows r and r + 2 of a transposed read's 4 must differ in bit 2 (the
+// two 16-byte chunks of a row stay together): 4 ((r >> 1) & 1) | ((r >> 2) & 3)
+// does both.  The XOR only touches the low 3 bits, so a chunk stays in its
+// row (d / 8 is a multiple of 8).
 template <int D>
 __device__ __forceinline__ int swz(int r) {
     return (D == 128) ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
@@ -160,11 +191,11 @@ struct BlockCopies {
 
 // A operand from rows of an LDS block: lane l reads row m0 + (l & 31),
 // elements 16 ks + 8 (l >> 5) .. +7.
-template <int D>
-__device__ __forceinline__ bf16x8 row_frag(const unsigned char* blk, int m0, int ks, int lane) {
+template <int D, typename X8>
+__device__ __forceinline__ X8 row_frag(const unsigned char* blk, int m0, int ks, int lane) {
     const int m = m0 + (lane & 31);
     const int ch = 2 * ks + (lane >> 5);
-    return *reinterpret_cast<const bf16x8*>(blk + m * (D * 2) + 16 * (ch ^ swz<D>(m)));
+    return *reinterpret_cast<const X8*>(blk + m * (D * 2) + 16 * (ch ^ swz<D>(m)));
 }
 
 // Per-lane byte offsets of the transposed reads: with 16-lane group g = l / 16
@@ -192,16 +223,15 @@ struct TrOffsets {
 // lane l receives column 32 i + (l & 31) at the 8 rows whose values the
 // B fragment g (rows 8 (r >> 2) + 4 (l >> 5) + (r & 3) of an accumulator)
 // carries in the same order.
-template <int D>
-__device__ __forceinline__ bf16x8 tr_frag(const unsigned char* blk, const TrOffsets<D>& tro,
-                                          int i, int g) {
+template <int D, typename X8>
+__device__ __forceinline__ X8 tr_frag(const unsigned char* blk, const TrOffsets<D>& tro, int i,
+                                      int g) {
     i16x4 part[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t)
         part[t] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (lds_i16x4*)(blk + tro.off[i][t] + 16 * g * (D * 2)));
-    return __builtin_bit_cast(bf16x8,
-                              __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
+    return __builtin_bit_cast(X8, __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
 // Workgroup order.  The hardware deals workgroups round-robin over the 8
@@ -216,24 +246,21 @@ __device__ __forceinline__ int xcd_contiguous(int x, int n) {
     return k * q + min(k, r) + x / 8;
 }
 
-__device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-
 // Row of accumulator register r for lane half hi: 8 (r >> 2) + 4 hi + (r & 3).
 __device__ __forceinline__ int acc_row(int r, int hi) { return 8 * (r >> 2) + 4 * hi + (r & 3); }
 
 // ---- D_i = dO_i . O_i --------------------------------------------------------
-template <int D>
+template <int D, bool FP16>
 __global__ __launch_bounds__(256) void attn_bwd_delta_kernel(const BwdParams p, long long rows) {
+    using X8 = typename Elem<FP16>::x8;
     constexpr int kLanes = D / 8;  // lanes per row, 16 bytes each
     constexpr int kRows = 256 / kLanes;
     const long long row = (long long)blockIdx.x * kRows + threadIdx.x / kLanes;
     const int c = threadIdx.x % kLanes;
     float acc = 0.0f;
     if (row < rows) {
-        const bf16x8 a = __builtin_bit_cast(bf16x8, load16(p.dout + row * D + 8 * c));
-        const bf16x8 b = __builtin_bit_cast(bf16x8, load16(p.o + row * D + 8 * c));
+        const X8 a = __builtin_bit_cast(X8, load16(p.dout + row * D + 8 * c));
+        const X8 b = __builtin_bit_cast(X8, load16(p.o + row * D + 8 * c));
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc += (float)a[e] * (float)b[e];
     }
@@ -243,15 +270,28 @@ __global__ __launch_bounds__(256) void attn_bwd_delta_kernel(const BwdParams p, 
 }
 
 // ---- dK, dV ------------------------------------------------------------------
-template <int D, bool CAUSAL>
+// PART selects the outputs: kBwdBoth computes dK and dV together; kBwdOnlyDV
+// and kBwdOnlyDK split them over two launches that each recompute S (the
+// second also dP), for head shapes whose dK and dV accumulators, K and V rows
+// and pipeline state do not fit one wave's registers together (d_qk = 192).
+constexpr int kBwdBoth = 0, kBwdOnlyDV = 1, kBwdOnlyDK = 2;
+
+template <int DQK, int DV, bool FP16, bool CAUSAL, int PART>
 __global__ __launch_bounds__(kBwdThreads, 1) void attn_bwd_dkdv_kernel(const BwdParams p) {
-    constexpr int kKs = D / 16;   // k-steps over the head dim
-    constexpr int kDb = D / 32;   // 32-wide output blocks
+    using E = Elem<FP16>;
+    using X8 = typename E::x8;
+    using X4 = typename E::x4;
+    constexpr bool kDoDV = PART != kBwdOnlyDK;
+    constexpr bool kDoDK = PART != kBwdOnlyDV;
+    constexpr int kKsQ = DQK / 16;                // k-steps of S = Q K^T
+    constexpr int kKsV = kDoDK ? DV / 16 : 0;     // k-steps of dP = dO V^T
+    constexpr int kDbQ = kDoDK ? DQK / 32 : 0;    // 32-wide blocks of dK
+    constexpr int kDbV = kDoDV ? DV / 32 : 0;     // 32-wide blocks of dV
     // two stages of (Q block, dO block, lse, D), filled by direct-to-LDS copies
-    __shared__ __attribute__((aligned(1024))) unsigned char qbuf0[kBlk * D * 2];
-    __shared__ __attribute__((aligned(1024))) unsigned char dobuf0[kBlk * D * 2];
-    __shared__ __attribute__((aligned(1024))) unsigned char qbuf1[kBlk * D * 2];
-    __shared__ __attribute__((aligned(1024))) unsigned char dobuf1[kBlk * D * 2];
+    __shared__ __attribute__((aligned(1024))) unsigned char qbuf0[kBlk * DQK * 2];
+    __shared__ __attribute__((aligned(1024))) unsigned char dobuf0[kBlk * DV * 2];
+    __shared__ __attribute__((aligned(1024))) unsigned char qbuf1[kBlk * DQK * 2];
+    __shared__ __attribute__((aligned(1024))) unsigned char dobuf1[kBlk * DV * 2];
     __shared__ __attribute__((aligned(256))) float lse0[kBlk], dl0[kBlk], lse1[kBlk], dl1[kBlk];
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -276,23 +316,33 @@ __global__ __launch_bounds__(kBwdThreads, 1) void attn_bwd_dkdv_kernel(const Bwd
 
     // the wave's K and V rows as B operands (rows past Lk repeat the last key)
     const int krow = min(key, p.Lk - 1);
-    const uint16_t* kh = p.k + (size_t)bk * p.Lk * D;
-    const uint16_t* vh = p.v + (size_t)bk * p.Lk * D;
-    bf16x8 kf[kKs], vf[kKs];
+    const uint16_t* kh = p.k + (size_t)bk * p.Lk * DQK;
+    const uint16_t* vh = p.v + (size_t)bk * p.Lk * DV;
+    // (arrays a pass does not use keep one unused element)
+    X8 kf[kKsQ], vf[kKsV > 0 ? kKsV : 1];
 #pragma unroll
-    for (int ks = 0; ks < kKs; ++ks) {
-        kf[ks] = __builtin_bit_cast(bf16x8, load16(kh + (size_t)krow * D + 16 * ks + 8 * hi));
-        vf[ks] = __builtin_bit_cast(bf16x8, load16(vh + (size_t)krow * D + 16 * ks + 8 * hi));
-    }
-    f32x16 dkt[kDb], dvt[kDb];
+    for (int ks = 0; ks < kKsQ; ++ks)
+        kf[ks] = __builtin_bit_cast(X8, load16(kh + (size_t)krow * DQK + 16 * ks + 8 * hi));
 #pragma unroll
-    for (int i = 0; i < kDb; ++i)
+    for (int ks = 0; ks < kKsV; ++ks)
+        vf[ks] = __builtin_bit_cast(X8, load16(vh + (size_t)krow * DV + 16 * ks + 8 * hi));
+    f32x16 dkt[kDbQ > 0 ? kDbQ : 1], dvt[kDbV > 0 ? kDbV : 1];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) dkt[i][r] = dvt[i][r] = 0.0f;
-    TrOffsets<D> tro;
-    tro.init(lane);
-    BlockCopies<D> cp;
-    cp.init(wave, lane);
+    for (int i = 0; i < kDbQ; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dkt[i][r] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kDbV; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dvt[i][r] = 0.0f;
+    TrOffsets<DQK> troq;
+    troq.init(lane);
+    TrOffsets<DV> trov;
+    trov.init(lane);
+    BlockCopies<DQK> cpq;
+    cpq.init(wave, lane);
+    BlockCopies<DV> cpv;
+    cpv.init(wave, lane);
 
     // causal: query blocks before qb0 see none of this workgroup's keys
     int qb0 = 0;
@@ -309,9 +359,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) void attn_bwd_dkdv_kernel(const Bwd
         const int g = t / nq;
         const int i0 = (qb0 + t % nq) * kBlk;
         const size_t r0 = head0 + (size_t)g * p.Lq;
-        const uint32_t bytes = (uint32_t)p.Lq * (D * 2);
-        cp.issue(make_rsrc(uniform(p.q + r0 * D), bytes), i0, p.Lq, qb);
-        cp.issue(make_rsrc(uniform(p.dout + r0 * D), bytes), i0, p.Lq, dob);
+        cpq.issue(make_rsrc(uniform(p.q + r0 * DQK), (uint32_t)p.Lq * (DQK * 2)), i0, p.Lq, qb);
+        cpv.issue(make_rsrc(uniform(p.dout + r0 * DV), (uint32_t)p.Lq * (DV * 2)), i0, p.Lq, dob);
         if (wave < 2) {
             const float* src = wave == 0 ? p.lse : p.delta;
             float* dst = wave == 0 ? lb : db;
@@ -320,73 +369,119 @@ __global__ __launch_bounds__(kBwdThreads, 1) void attn_bwd_dkdv_kernel(const Bwd
         }
     };
     // One step (64 query rows = sub-blocks 0 and 1 of 32 rows) is a sequence
-    // of 64 MFMA units, each with one LDS operand:
-    //   units  0..15  S(0), dP(0)        A = Q / dO rows of sub-block 0
-    //   units 16..31  S(1), dP(1)        (sub-block 1), with P(0), dS(0) formed
-    //                                    one element per unit on the VALU
-    //   units 32..47  dV(0), dK(0)       A = dO^T / Q^T of sub-block 0, B = P(0) /
-    //                                    dS(0), with P(1), dS(1) formed likewise
-    //   units 48..63  dV(1), dK(1)
+    // of MFMA units in four quarters, each unit with one LDS operand:
+    //   quarter 0  S(0), dP(0)     A = Q / dO rows of sub-block 0 (the k-steps
+    //                              of S and dP alternate while both last)
+    //   quarter 1  S(1), dP(1)     (sub-block 1), with P(0), dS(0) formed on
+    //                              the VALU, spread over its units
+    //   quarter 2  dV(0), dK(0)    A = dO^T / Q^T of sub-block 0, B = P(0) /
+    //                              dS(0), with P(1), dS(1) formed likewise
+    //   quarter 3  dV(1), dK(1)
     // Operands are loaded kAhead units before their MFMA into a register ring
     // and scheduling barriers keep that order, so LDS latency and the
     // softmax arithmetic overlap earlier MFMAs instead of stalling each one.
     constexpr int kAhead = 4;
-    constexpr int kUnits = 64;
+    constexpr int kSD = kKsQ + kKsV;           // units of an S / dP quarter
+    constexpr int kVK = 2 * (kDbV + kDbQ);     // units of a dV / dK quarter
+    constexpr int kUnits = 2 * kSD + 2 * kVK;
     // query rows i that see this lane's key: i >= imin (and i < Lq); none
     // for a key past Lk
     const int imin = key >= p.Lk ? INT32_MAX : (CAUSAL ? key - off : INT32_MIN);
     const f32x16 zero = {};
     f32x16 sacc[2], dpacc[2], pv, dsv;
-    bf16x8 pb[2][2], db[2][2];
+    X8 pb[2][2], db[2][2];
     f32x4 l4[4], d4[4];
+    // unit n -> (quarter, position in it)
+    auto quarter = [](int n) { return n < kSD ? 0 : n < 2 * kSD ? 1 : n < 2 * kSD + kVK ? 2 : 3; };
+    auto qpos = [](int n) {
+        return n < kSD ? n : n < 2 * kSD ? n - kSD : n < 2 * kSD + kVK ? n - 2 * kSD
+                                                                        : n - 2 * kSD - kVK;
+    };
+    // S / dP quarter position u: S(k-step) or dP(k-step), alternating while
+    // both have k-steps left
+    auto sd_unit = [](int u, bool* is_dp, int* ks) {
+        constexpr int kBoth = 2 * (kKsQ < kKsV ? kKsQ : kKsV);
+        if (u < kBoth) {
+            *is_dp = (u & 1) != 0;
+            *ks = u >> 1;
+        } else {
+            *is_dp = kKsV > kKsQ;
+            *ks = kBoth / 2 + (u - kBoth);
+        }
+    };
+    // dV / dK quarter position u: row group t2 (16 query rows), then dV(i) and
+    // dK(i) alternating while both have blocks left
+    auto vk_unit = [](int u, bool* is_dk, int* t2, int* i) {
+        constexpr int kPer = kDbV + kDbQ;
+        constexpr int kBoth = 2 * (kDbV < kDbQ ? kDbV : kDbQ);
+        *t2 = u / kPer;
+        const int w = u % kPer;
+        if (w < kBoth) {
+            *is_dk = (w & 1) != 0;
+            *i = w >> 1;
+        } else {
+            *is_dk = kDbQ > kDbV;
+            *i = kBoth / 2 + (w - kBoth);
+        }
+    };
     auto load = [&](int n, const unsigned char* qbuf, const unsigned char* dobuf)
                     __attribute__((always_inline)) {
-        const int u = n & 15, sub = (n >> 4) & 1;
-        if (n < 32)  // S / dP unit: k-step u >> 1 of sub-block sub
-            return row_frag<D>((u & 1) ? dobuf : qbuf, 32 * sub, u >> 1, lane);
-        // dV / dK unit: rows 16 (2 sub + t2) .., output block i
-        const int t2 = u >> 3, i = (u >> 1) & 3;
-        return tr_frag<D>((u & 1) ? qbuf : dobuf, tro, i % kDb, 2 * sub + t2);
+        const int qt = quarter(n), u = qpos(n);
+        const int sub = qt & 1;
+        if (qt < 2) {  // S / dP unit of sub-block sub
+            bool is_dp;
+            int ks;
+            sd_unit(u, &is_dp, &ks);
+            return is_dp ? row_frag<DV, X8>(dobuf, 32 * sub, ks, lane)
+                         : row_frag<DQK, X8>(qbuf, 32 * sub, ks, lane);
+        }
+        bool is_dk;
+        int t2, i;
+        vk_unit(u, &is_dk, &t2, &i);
+        return is_dk ? tr_frag<DQK, X8>(qbuf, troq, i, 2 * sub + t2)
+                     : tr_frag<DV, X8>(dobuf, trov, i, 2 * sub + t2);
     };
-    auto mfma_unit = [&](int n, bf16x8 a) __attribute__((always_inline)) {
-        const int u = n & 15, sub = (n >> 4) & 1;
-        if (n < 32) {
-            const int ks = u >> 1;
-            if (ks < kKs) {
-                if (u & 1)
-                    dpacc[sub] = mfma(a, vf[ks], ks == 0 ? zero : dpacc[sub]);
-                else
-                    sacc[sub] = mfma(a, kf[ks], ks == 0 ? zero : sacc[sub]);
-            }
+    auto mfma_unit = [&](int n, X8 a) __attribute__((always_inline)) {
+        const int qt = quarter(n), u = qpos(n);
+        const int sub = qt & 1;
+        if (qt < 2) {
+            bool is_dp;
+            int ks;
+            sd_unit(u, &is_dp, &ks);
+            if (is_dp)
+                dpacc[sub] = E::mfma(a, vf[ks], ks == 0 ? zero : dpacc[sub]);
+            else
+                sacc[sub] = E::mfma(a, kf[ks], ks == 0 ? zero : sacc[sub]);
         } else {
-            const int t2 = u >> 3, i = (u >> 1) & 3;
-            if (i < kDb) {
-                if (u & 1)
-                    dkt[i] = mfma(a, db[sub][t2], dkt[i]);
-                else
-                    dvt[i] = mfma(a, pb[sub][t2], dvt[i]);
-            }
+            bool is_dk;
+            int t2, i;
+            vk_unit(u, &is_dk, &t2, &i);
+            if (is_dk)
+                dkt[i] = E::mfma(a, db[sub][t2], dkt[i]);
+            else
+                dvt[i] = E::mfma(a, pb[sub][t2], dvt[i]);
         }
     };
     // P and dS of sub-block sub at accumulator element r (row i0 + 32 sub +
-    // acc_row(r), column key); after elements 7 and 15, their bf16 fragments
+    // acc_row(r), column key); after elements 7 and 15, their 16-bit fragments
+    // (P for the dV products, dS for the dK products)
     auto softmax_elem = [&](int sub, int r, int i0) __attribute__((always_inline)) {
         const int i = i0 + 32 * sub + acc_row(r, hi);
         const bool ok = i >= imin && i < p.Lq;
         const float pr = ok ? __builtin_amdgcn_exp2f(sacc[sub][r] * c2 - l4[r >> 2][r & 3] * kLog2e)
                             : 0.0f;
         pv[r] = pr;
-        dsv[r] = pr * (dpacc[sub][r] - d4[r >> 2][r & 3]);
+        if constexpr (kDoDK) dsv[r] = pr * (dpacc[sub][r] - d4[r >> 2][r & 3]);
         if ((r & 7) == 7) {
             const int t2 = r >> 3;
             f32x8 e1, e2;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 e1[e] = pv[8 * t2 + e];
-                e2[e] = dsv[8 * t2 + e];
+                if constexpr (kDoDK) e2[e] = dsv[8 * t2 + e];
             }
-            pb[sub][t2] = __builtin_convertvector(e1, bf16x8);
-            db[sub][t2] = __builtin_convertvector(e2, bf16x8);
+            if constexpr (kDoDV) pb[sub][t2] = __builtin_convertvector(e1, X8);
+            if constexpr (kDoDK) db[sub][t2] = __builtin_convertvector(e2, X8);
         }
     };
     auto load_rowstats = [&](int sub, const float* lsebuf, const float* dbuf)
@@ -394,33 +489,42 @@ __global__ __launch_bounds__(kBwdThreads, 1) void attn_bwd_dkdv_kernel(const Bwd
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
             l4[g4] = *reinterpret_cast<const f32x4*>(lsebuf + 32 * sub + 8 * g4 + 4 * hi);
-            d4[g4] = *reinterpret_cast<const f32x4*>(dbuf + 32 * sub + 8 * g4 + 4 * hi);
+            if constexpr (kDoDK)
+                d4[g4] = *reinterpret_cast<const f32x4*>(dbuf + 32 * sub + 8 * g4 + 4 * hi);
         }
     };
     auto compute = [&](int t, const unsigned char* qbuf, const unsigned char* dobuf,
                        const float* lsebuf, const float* dbuf) __attribute__((always_inline)) {
         const int i0 = (qb0 + t % nq) * kBlk;
-        bf16x8 ring[kAhead];
+        X8 ring[kAhead];
 #pragma unroll
         for (int n = 0; n < kAhead; ++n) ring[n] = load(n, qbuf, dobuf);
         auto unit = [&](int n) __attribute__((always_inline)) {
-            const bf16x8 a = ring[n % kAhead];
+            const X8 a = ring[n % kAhead];
             if (n + kAhead < kUnits) ring[n % kAhead] = load(n + kAhead, qbuf, dobuf);
             mfma_unit(n, a);
-            if (n >= 16 && n < 48) softmax_elem((n >> 4) - 1, n & 15, i0);
+            // the 16 softmax elements of the previous sub-block, spread over
+            // the units of quarters 1 and 2 in order
+            const int qt = quarter(n), u = qpos(n);
+            if (qt == 1 || qt == 2) {
+                const int len = qt == 1 ? kSD : kVK;
+#pragma unroll
+                for (int r = (16 * u + len - 1) / len; r < (16 * (u + 1) + len - 1) / len; ++r)
+                    softmax_elem(qt - 1, r, i0);
+            }
             __builtin_amdgcn_sched_barrier(0);
         };
-        // four loops of 16 units, each short enough to be unrolled in full
+        // four loops, one per quarter, each short enough to be unrolled in full
 #pragma unroll
-        for (int n = 0; n < 16; ++n) unit(n);
+        for (int n = 0; n < kSD; ++n) unit(n);
         load_rowstats(0, lsebuf, dbuf);
 #pragma unroll
-        for (int n = 16; n < 32; ++n) unit(n);
+        for (int n = kSD; n < 2 * kSD; ++n) unit(n);
         load_rowstats(1, lsebuf, dbuf);
 #pragma unroll
-        for (int n = 32; n < 48; ++n) unit(n);
+        for (int n = 2 * kSD; n < 2 * kSD + kVK; ++n) unit(n);
 #pragma unroll
-        for (int n = 48; n < 64; ++n) unit(n);
+        for (int n = 2 * kSD + kVK; n < kUnits; ++n) unit(n);
     };
     // One barrier per step: every wave's copies of stage t have landed (each
     // wave waits for its own before the barrier) and every wave is done with
@@ -438,34 +542,46 @@ __global__ __launch_bounds__(kBwdThreads, 1) void attn_bwd_dkdv_kernel(const Bwd
     }
     // lane holds key `key`, columns 32 i + 8 (r >> 2) + 4 hi + (r & 3)
     if (key < p.Lk) {
-        uint16_t* dkrow = p.dk + ((size_t)bk * p.Lk + key) * D;
-        uint16_t* dvrow = p.dv + ((size_t)bk * p.Lk + key) * D;
+        uint16_t* dkrow = p.dk + ((size_t)bk * p.Lk + key) * DQK;
+        uint16_t* dvrow = p.dv + ((size_t)bk * p.Lk + key) * DV;
 #pragma unroll
-        for (int i = 0; i < kDb; ++i)
+        for (int i = 0; i < kDbQ; ++i)
 #pragma unroll
             for (int r4 = 0; r4 < 4; ++r4) {
                 const f32x4 xk = {dkt[i][4 * r4] * p.scale, dkt[i][4 * r4 + 1] * p.scale,
                                   dkt[i][4 * r4 + 2] * p.scale, dkt[i][4 * r4 + 3] * p.scale};
+                *reinterpret_cast<X4*>(dkrow + 32 * i + 8 * r4 + 4 * hi) =
+                    __builtin_convertvector(xk, X4);
+            }
+#pragma unroll
+        for (int i = 0; i < kDbV; ++i)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
                 const f32x4 xv = {dvt[i][4 * r4], dvt[i][4 * r4 + 1], dvt[i][4 * r4 + 2],
                                   dvt[i][4 * r4 + 3]};
-                *reinterpret_cast<bf16x4*>(dkrow + 32 * i + 8 * r4 + 4 * hi) =
-                    __builtin_convertvector(xk, bf16x4);
-                *reinterpret_cast<bf16x4*>(dvrow + 32 * i + 8 * r4 + 4 * hi) =
-                    __builtin_convertvector(xv, bf16x4);
+                *reinterpret_cast<X4*>(dvrow + 32 * i + 8 * r4 + 4 * hi) =
+                    __builtin_convertvector(xv, X4);
             }
     }
 }
 
 // ---- dQ ----------------------------------------------------------------------
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kBwdThreads, 2) void attn_bwd_dq_kernel(const BwdParams p) {
-    constexpr int kKs = D / 16;
-    constexpr int kDb = D / 32;
+// Two waves per SIMD where the registers allow (d_qk <= 128), one otherwise.
+template <int DQK, int DV, bool FP16, bool CAUSAL>
+__global__ __launch_bounds__(kBwdThreads, (DQK <= 128 ? 2 : 1)) void attn_bwd_dq_kernel(
+    const BwdParams p) {
+    using E = Elem<FP16>;
+    using X8 = typename E::x8;
+    using X4 = typename E::x4;
+    constexpr int kKsQ = DQK / 16;
+    constexpr int kKsV = DV / 16;
+    constexpr int kKsMax = kKsQ > kKsV ? kKsQ : kKsV;
+    constexpr int kDbQ = DQK / 32;
     // two stages of (K block, V block), filled by direct-to-LDS copies
-    __shared__ __attribute__((aligned(1024))) unsigned char kbuf0[kBlk * D * 2];
-    __shared__ __attribute__((aligned(1024))) unsigned char vbuf0[kBlk * D * 2];
-    __shared__ __attribute__((aligned(1024))) unsigned char kbuf1[kBlk * D * 2];
-    __shared__ __attribute__((aligned(1024))) unsigned char vbuf1[kBlk * D * 2];
+    __shared__ __attribute__((aligned(1024))) unsigned char kbuf0[kBlk * DQK * 2];
+    __shared__ __attribute__((aligned(1024))) unsigned char vbuf0[kBlk * DV * 2];
+    __shared__ __attribute__((aligned(1024))) unsigned char kbuf1[kBlk * DQK * 2];
+    __shared__ __attribute__((aligned(1024))) unsigned char vbuf1[kBlk * DV * 2];
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int l32 = lane & 31, hi = lane >> 5;
@@ -491,23 +607,26 @@ __global__ __launch_bounds__(kBwdThreads, 2) void attn_bwd_dq_kernel(const BwdPa
 
     // Q and dO rows as B operands (rows past Lq read row 0 and are not stored)
     const int qr = qi < p.Lq ? qi : 0;
-    bf16x8 qf[kKs], gf[kKs];
+    X8 qf[kKsQ], gf[kKsV];
 #pragma unroll
-    for (int ks = 0; ks < kKs; ++ks) {
-        qf[ks] = __builtin_bit_cast(bf16x8, load16(p.q + (qrow0 + qr) * D + 16 * ks + 8 * hi));
-        gf[ks] = __builtin_bit_cast(bf16x8, load16(p.dout + (qrow0 + qr) * D + 16 * ks + 8 * hi));
-    }
+    for (int ks = 0; ks < kKsQ; ++ks)
+        qf[ks] = __builtin_bit_cast(X8, load16(p.q + (qrow0 + qr) * DQK + 16 * ks + 8 * hi));
+#pragma unroll
+    for (int ks = 0; ks < kKsV; ++ks)
+        gf[ks] = __builtin_bit_cast(X8, load16(p.dout + (qrow0 + qr) * DV + 16 * ks + 8 * hi));
     const float lse_q = p.lse[qrow0 + qr];
     const float d_q = p.delta[qrow0 + qr];
-    f32x16 dqt[kDb];
+    f32x16 dqt[kDbQ];
 #pragma unroll
-    for (int i = 0; i < kDb; ++i)
+    for (int i = 0; i < kDbQ; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r) dqt[i][r] = 0.0f;
-    TrOffsets<D> tro;
+    TrOffsets<DQK> tro;
     tro.init(lane);
-    BlockCopies<D> cp;
-    cp.init(wave, lane);
+    BlockCopies<DQK> cpk;
+    cpk.init(wave, lane);
+    BlockCopies<DV> cpv;
+    cpv.init(wave, lane);
 
     // keys of the workgroup and of this wave
     int kend = p.Lk, wend = p.Lk;
@@ -516,27 +635,29 @@ __global__ __launch_bounds__(kBwdThreads, 2) void attn_bwd_dq_kernel(const BwdPa
         wend = min(p.Lk, min(p.Lq, q0 + 32) - 1 + off + 1);
     }
     const int nkb = kend > 0 ? (kend + kBlk - 1) / kBlk : 0;
-    const uint32_t bytes = (uint32_t)p.Lk * (D * 2);
-    const __amdgpu_buffer_rsrc_t krs = make_rsrc(uniform(p.k + (size_t)bk * p.Lk * D), bytes);
-    const __amdgpu_buffer_rsrc_t vrs = make_rsrc(uniform(p.v + (size_t)bk * p.Lk * D), bytes);
+    const __amdgpu_buffer_rsrc_t krs =
+        make_rsrc(uniform(p.k + (size_t)bk * p.Lk * DQK), (uint32_t)p.Lk * (DQK * 2));
+    const __amdgpu_buffer_rsrc_t vrs =
+        make_rsrc(uniform(p.v + (size_t)bk * p.Lk * DV), (uint32_t)p.Lk * (DV * 2));
     auto issue = [&](int jb, unsigned char* kbuf, unsigned char* vbuf)
                      __attribute__((always_inline)) {
-        cp.issue(krs, jb * kBlk, p.Lk, kbuf);
-        cp.issue(vrs, jb * kBlk, p.Lk, vbuf);
+        cpk.issue(krs, jb * kBlk, p.Lk, kbuf);
+        cpv.issue(vrs, jb * kBlk, p.Lk, vbuf);
     };
     const f32x16 zero = {};
     auto compute = [&](int jb, const unsigned char* kbuf, const unsigned char* vbuf)
                        __attribute__((always_inline)) {
         const int j0 = jb * kBlk;
         if (q0 >= p.Lq || j0 >= wend) return;  // no visible key of this block for the wave
-        bf16x8 db[4];
+        X8 db[4];
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) {
             f32x16 st = zero, dpt = zero;
 #pragma unroll
-            for (int ks = 0; ks < kKs; ++ks) {
-                st = mfma(row_frag<D>(kbuf, 32 * mb, ks, lane), qf[ks], st);
-                dpt = mfma(row_frag<D>(vbuf, 32 * mb, ks, lane), gf[ks], dpt);
+            for (int ks = 0; ks < kKsMax; ++ks) {
+                if (ks < kKsQ) st = E::mfma(row_frag<DQK, X8>(kbuf, 32 * mb, ks, lane), qf[ks], st);
+                if (ks < kKsV)
+                    dpt = E::mfma(row_frag<DV, X8>(vbuf, 32 * mb, ks, lane), gf[ks], dpt);
             }
             f32x16 ds;
 #pragma unroll
@@ -552,14 +673,15 @@ __global__ __launch_bounds__(kBwdThreads, 2) void attn_bwd_dq_kernel(const BwdPa
                 f32x8 e;
 #pragma unroll
                 for (int x = 0; x < 8; ++x) e[x] = ds[8 * t + x];
-                db[2 * mb + t] = __builtin_convertvector(e, bf16x8);
+                db[2 * mb + t] = __builtin_convertvector(e, X8);
             }
         }
         // dQ^T += K^T dS^T
 #pragma unroll
         for (int g = 0; g < 4; ++g)
 #pragma unroll
-            for (int i = 0; i < kDb; ++i) dqt[i] = mfma(tr_frag<D>(kbuf, tro, i, g), db[g], dqt[i]);
+            for (int i = 0; i < kDbQ; ++i)
+                dqt[i] = E::mfma(tr_frag<DQK, X8>(kbuf, tro, i, g), db[g], dqt[i]);
     };
     // one barrier per block, as in the dK/dV kernel
     if (nkb > 0) issue(0, kbuf0, vbuf0);
@@ -574,50 +696,74 @@ __global__ __launch_bounds__(kBwdThreads, 2) void attn_bwd_dq_kernel(const BwdPa
         }
     }
     if (qi < p.Lq) {
-        uint16_t* row = p.dq + (qrow0 + qi) * D;
+        uint16_t* row = p.dq + (qrow0 + qi) * DQK;
 #pragma unroll
-        for (int i = 0; i < kDb; ++i)
+        for (int i = 0; i < kDbQ; ++i)
 #pragma unroll
             for (int r4 = 0; r4 < 4; ++r4) {
                 const f32x4 x = {dqt[i][4 * r4] * p.scale, dqt[i][4 * r4 + 1] * p.scale,
                                  dqt[i][4 * r4 + 2] * p.scale, dqt[i][4 * r4 + 3] * p.scale};
-                *reinterpret_cast<bf16x4*>(row + 32 * i + 8 * r4 + 4 * hi) =
-                    __builtin_convertvector(x, bf16x4);
+                *reinterpret_cast<X4*>(row + 32 * i + 8 * r4 + 4 * hi) =
+                    __builtin_convertvector(x, X4);
             }
     }
 }
 
-template <int D, bool CAUSAL>
+template <int DQK, int DV, bool FP16, bool CAUSAL>
 hipError_t launch_bwd_t(const BwdParams& p, hipStream_t stream) {
     BwdParams arg = p;
     const long long rows = (long long)p.B * p.Hq * p.Lq;
     {
-        constexpr int kRows = 256 / (D / 8);
+        constexpr int kRows = 256 / (DV / 8);
         const long long blocks = (rows + kRows - 1) / kRows;
         void* args[] = {&arg, const_cast<long long*>(&rows)};
-        hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&attn_bwd_delta_kernel<D>),
-                                       dim3((unsigned)blocks), dim3(256), args, 0, stream);
+        hipError_t e =
+            hipLaunchKernel(reinterpret_cast<const void*>(&attn_bwd_delta_kernel<DV, FP16>),
+                            dim3((unsigned)blocks), dim3(256), args, 0, stream);
         if (e != hipSuccess) return e;
     }
     void* args[] = {&arg};
     {
         const long long blocks = (long long)p.B * p.Hkv * ((p.Lk + 127) / 128);
-        hipError_t e =
-            hipLaunchKernel(reinterpret_cast<const void*>(&attn_bwd_dkdv_kernel<D, CAUSAL>),
-                            dim3((unsigned)blocks), dim3(kBwdThreads), args, 0, stream);
+        auto launch = [&](const void* kernel) {
+            return hipLaunchKernel(kernel, dim3((unsigned)blocks), dim3(kBwdThreads), args, 0,
+                                   stream);
+        };
+        hipError_t e;
+        if constexpr (DQK > 128) {
+            // dV, then dK, in launches of their own (see PART)
+            e = launch(reinterpret_cast<const void*>(
+                &attn_bwd_dkdv_kernel<DQK, DV, FP16, CAUSAL, kBwdOnlyDV>));
+            if (e != hipSuccess) return e;
+            e = launch(reinterpret_cast<const void*>(
+                &attn_bwd_dkdv_kernel<DQK, DV, FP16, CAUSAL, kBwdOnlyDK>));
+        } else {
+            e = launch(reinterpret_cast<const void*>(
+                &attn_bwd_dkdv_kernel<DQK, DV, FP16, CAUSAL, kBwdBoth>));
+        }
         if (e != hipSuccess) return e;
     }
     const long long blocks = (long long)p.B * p.Hq * ((p.Lq + 127) / 128);
-    return hipLaunchKernel(reinterpret_cast<const void*>(&attn_bwd_dq_kernel<D, CAUSAL>),
+    return hipLaunchKernel(reinterpret_cast<const void*>(&attn_bwd_dq_kernel<DQK, DV, FP16, CAUSAL>),
                            dim3((unsigned)blocks), dim3(kBwdThreads), args, 0, stream);
+}
+
+template <int DQK, int DV>
+hipError_t launch_bwd_dims(const BwdParams& p, bool causal, bool fp16, hipStream_t stream) {
+    if (fp16)
+        return causal ? launch_bwd_t<DQK, DV, true, true>(p, stream)
+                      : launch_bwd_t<DQK, DV, true, false>(p, stream);
+    return causal ? launch_bwd_t<DQK, DV, false, true>(p, stream)
+                  : launch_bwd_t<DQK, DV, false, false>(p, stream);
 }
 
 }  // namespace
 
-hipError_t launch_bwd(const BwdParams& p, int d, bool causal, hipStream_t stream) {
-    if (d == 64) return causal ? launch_bwd_t<64, true>(p, stream) : launch_bwd_t<64, false>(p, stream);
-    if (d == 128)
-        return causal ? launch_bwd_t<128, true>(p, stream) : launch_bwd_t<128, false>(p, stream);
+hipError_t launch_bwd(const BwdParams& p, int dqk, int dv, bool causal, bool fp16,
+                      hipStream_t stream) {
+    if (dqk == 64 && dv == 64) return launch_bwd_dims<64, 64>(p, causal, fp16, stream);
+    if (dqk == 128 && dv == 128) return launch_bwd_dims<128, 128>(p, causal, fp16, stream);
+    if (dqk == 192 && dv == 128) return launch_bwd_dims<192, 128>(p, causal, fp16, stream);
     return hipErrorInvalidValue;
 }
 

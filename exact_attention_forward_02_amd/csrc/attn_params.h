@@ -65,23 +65,25 @@ struct FwdParams {
 hipError_t launch_fwd(const FwdParams& p, int dqk, int dv, bool causal, bool debug, bool fp16,
                       hipStream_t stream);
 
-// Backward pass (contiguous [B, H, L, d] bf16 tensors, d_qk == d_v).
+// Backward pass (contiguous [B, H, L, d] tensors, bf16 or fp16; q, k, dq, dk
+// rows of d_qk elements, v, o, dout, dv rows of d_v).
 struct BwdParams {
-    const uint16_t* q;     // [B, Hq, Lq, d]
-    const uint16_t* k;     // [B, Hkv, Lk, d]
-    const uint16_t* v;     // [B, Hkv, Lk, d]
-    const uint16_t* o;     // [B, Hq, Lq, d]  forward output
-    const uint16_t* dout;  // [B, Hq, Lq, d]  gradient of the loss w.r.t. o
-    const float* lse;      // [B, Hq, Lq]     forward lse
-    float* delta;          // [B, Hq, Lq]     D_i = dO_i . O_i (written)
-    uint16_t* dq;          // [B, Hq, Lq, d]
-    uint16_t* dk;          // [B, Hkv, Lk, d]
-    uint16_t* dv;          // [B, Hkv, Lk, d]
+    const uint16_t* q;     // [B, Hq, Lq, d_qk]
+    const uint16_t* k;     // [B, Hkv, Lk, d_qk]
+    const uint16_t* v;     // [B, Hkv, Lk, d_v]
+    const uint16_t* o;     // [B, Hq, Lq, d_v]  forward output
+    const uint16_t* dout;  // [B, Hq, Lq, d_v]  gradient of the loss w.r.t. o
+    const float* lse;      // [B, Hq, Lq]       forward lse
+    float* delta;          // [B, Hq, Lq]       D_i = dO_i . O_i (written)
+    uint16_t* dq;          // [B, Hq, Lq, d_qk]
+    uint16_t* dk;          // [B, Hkv, Lk, d_qk]
+    uint16_t* dv;          // [B, Hkv, Lk, d_v]
     int B, Hq, Hkv, Lq, Lk, G;
     float scale, scale_log2;
 };
 
-hipError_t launch_bwd(const BwdParams& p, int d, bool causal, hipStream_t stream);
+hipError_t launch_bwd(const BwdParams& p, int dqk, int dv, bool causal, bool fp16,
+                      hipStream_t stream);
 
 // Rows of D (one float each) that the file-scope device array `scratch` of the
 // allocation-free backward entry point holds: 4 Mi rows, 16 MiB per device.

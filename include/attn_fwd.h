@@ -223,16 +223,30 @@ int attn_merge(const float* o_part, const float* lse_part, void* o, float* lse,
  *   dk, dv           bfloat16 [B, Hkv, Lk, d_qk] and [B, Hkv, Lk, d_v] (output)
  *   delta            float32 [B, Hq, Lq] (output, and the kernels' scratch:
  *                    D_i = dout_i . o_i)
- *   d_qk == d_v, 64 or 128 (ATTN_ERR_UNSUPPORTED_HEAD_DIM otherwise)
+ *   (d_qk, d_v)      (64,64), (128,128) or (192,128)
+ *                    (ATTN_ERR_UNSUPPORTED_HEAD_DIM otherwise)
  * All pointers are caller-owned device pointers; outputs must not overlap
  * the inputs or each other; every 16-bit tensor is 16-byte aligned, lse and
- * delta 4-byte aligned.  Three kernels are enqueued on `stream`; errors as
- * attn_fwd.
+ * delta 4-byte aligned.  One query head of Q and of dout must span less than
+ * 2^31 bytes (ATTN_ERR_TOO_LARGE).  Three kernels are enqueued on `stream`;
+ * errors as attn_fwd.
  */
 int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
              const float* lse, void* dq, void* dk, void* dv, float* delta,
              int B, int Hq, int Hkv, int Lq, int Lk, int d_qk, int d_v,
              int causal, float scale, void* stream);
+
+/*
+ * attn_bwd_ex -- attn_bwd for bf16 or fp16 tensors: dtype ATTN_DTYPE_BF16 or
+ * ATTN_DTYPE_FP16 is the element type of q, k, v, o, dout, dq, dk and dv, and
+ * of P and dS in the products (the FA4 chapter's usage example runs fp16).
+ * Other arguments, layouts and errors as attn_bwd; ATTN_ERR_BAD_ARGUMENT for
+ * another dtype.
+ */
+int attn_bwd_ex(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                const float* lse, void* dq, void* dk, void* dv, float* delta,
+                int B, int Hq, int Hkv, int Lq, int Lk, int d_qk, int d_v,
+                int dtype, int causal, float scale, void* stream);
 
 /*
  * attn_bwd_noalloc -- attn_bwd for callers that cannot allocate device memory

@@ -734,7 +734,8 @@ int oracle_online_rows(const uint16_t* q, const uint16_t* k, const uint16_t* v,
  * nothing.  Inputs are 16-bit bit patterns (elem as in
  * oracle_attn_rows_elem): q, k, v, dout contiguous [B, H, L, d]; outputs in
  * double: dq [B, Hq, Lq, dqk], dk [B, Hkv, Lk, dqk], dv [B, Hkv, Lk, dv], and
- * delta [B, Hq, Lq] (the D_i above).  Parallel over (b, K/V head).
+ * delta [B, Hq, Lq] (the D_i above).  Parallel over the query rows of one
+ * K/V head at a time.
  */
 int oracle_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                     const uint16_t* dout, int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq,
@@ -752,95 +753,128 @@ int oracle_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
 #ifdef _OPENMP
     if (n_threads > 0)
         omp_set_num_threads(n_threads);
+    const int nthr = omp_get_max_threads();
 #else
     (void)n_threads;
+    const int nthr = 1;
 #endif
     const int64_t group = Hq / Hkv;
     int failed = 0;
+    /* One K/V head at a time; its query rows (of every query head it serves)
+     * are shared out over the threads, each summing its rows' dK and dV
+     * contributions into a buffer of its own, added up afterwards. */
+    double* part_k = (double*)malloc(sizeof(double) * (size_t)(nthr * Lk * dqk));
+    double* part_v = (double*)malloc(sizeof(double) * (size_t)(nthr * Lk * dv));
+    if (!part_k || !part_v) {
+        free(part_k);
+        free(part_v);
+        return 7;
+    }
+    for (int64_t bk = 0; bk < B * Hkv && !failed; ++bk) {
+        const int64_t b = bk / Hkv, hk = bk % Hkv;
+        const uint16_t* kh = k + bk * Lk * dqk;
+        const uint16_t* vh = v + bk * Lk * dv;
+        for (int64_t t = 0; t < nthr * Lk * dqk; ++t)
+            part_k[t] = 0.0;
+        for (int64_t t = 0; t < nthr * Lk * dv; ++t)
+            part_v[t] = 0.0;
 #pragma omp parallel
-    {
-        double* qd = (double*)malloc(sizeof(double) * (size_t)dqk);
-        double* gd = (double*)malloc(sizeof(double) * (size_t)dv);
-        double* p = (double*)malloc(sizeof(double) * (size_t)Lk);
-        double* dp = (double*)malloc(sizeof(double) * (size_t)Lk);
-        int ok = qd && gd && p && dp;
-#pragma omp for schedule(dynamic, 1)
-        for (int64_t bk = 0; bk < B * Hkv; ++bk) {
-            if (!ok) {
+        {
+#ifdef _OPENMP
+            const int tid = omp_get_thread_num();
+#else
+            const int tid = 0;
+#endif
+            double* dkh = part_k + (int64_t)tid * Lk * dqk;
+            double* dvh = part_v + (int64_t)tid * Lk * dv;
+            double* qd = (double*)malloc(sizeof(double) * (size_t)dqk);
+            double* gd = (double*)malloc(sizeof(double) * (size_t)dv);
+            double* p = (double*)malloc(sizeof(double) * (size_t)Lk);
+            double* dp = (double*)malloc(sizeof(double) * (size_t)Lk);
+            int ok = qd && gd && p && dp;
+#pragma omp for schedule(static, 16)
+            for (int64_t hi = 0; hi < group * Lq; ++hi) {
+                if (!ok) {
 #pragma omp atomic write
-                failed = 1;
-                continue;
-            }
-            const int64_t b = bk / Hkv, hk = bk % Hkv;
-            const uint16_t* kh = k + bk * Lk * dqk;
-            const uint16_t* vh = v + bk * Lk * dv;
-            double* dkh = dk + bk * Lk * dqk;
-            double* dvh = dvo + bk * Lk * dv;
-            for (int64_t t = 0; t < Lk * dqk; ++t)
-                dkh[t] = 0.0;
-            for (int64_t t = 0; t < Lk * dv; ++t)
-                dvh[t] = 0.0;
-            for (int64_t h = hk * group; h < (hk + 1) * group; ++h) {
-                for (int64_t i = 0; i < Lq; ++i) {
-                    const int64_t r = (b * Hq + h) * Lq + i;
-                    const uint16_t* qrow = q + r * dqk;
-                    const uint16_t* grow = dout + r * dv;
-                    double* dqrow = dq + r * dqk;
+                    failed = 1;
+                    continue;
+                }
+                const int64_t h = hk * group + hi / Lq, i = hi % Lq;
+                const int64_t r = (b * Hq + h) * Lq + i;
+                const uint16_t* qrow = q + r * dqk;
+                const uint16_t* grow = dout + r * dv;
+                double* dqrow = dq + r * dqk;
+                for (int64_t c = 0; c < dqk; ++c)
+                    dqrow[c] = 0.0;
+                const int64_t n = valid_keys(&d, i);
+                if (n == 0) {
+                    delta[r] = 0.0;
+                    continue;
+                }
+                for (int64_t c = 0; c < dqk; ++c)
+                    qd[c] = widen(&d, qrow[c]);
+                for (int64_t c = 0; c < dv; ++c)
+                    gd[c] = widen(&d, grow[c]);
+                /* P_i. over the visible keys (safe softmax) */
+                double m = -INFINITY;
+                for (int64_t j = 0; j < n; ++j) {
+                    double dot = 0.0;
                     for (int64_t c = 0; c < dqk; ++c)
-                        dqrow[c] = 0.0;
-                    const int64_t n = valid_keys(&d, i);
-                    if (n == 0) {
-                        delta[r] = 0.0;
-                        continue;
-                    }
-                    for (int64_t c = 0; c < dqk; ++c)
-                        qd[c] = widen(&d, qrow[c]);
+                        dot += qd[c] * widen(&d, kh[j * dqk + c]);
+                    p[j] = scale * dot;
+                    if (p[j] > m)
+                        m = p[j];
+                }
+                double l = 0.0;
+                for (int64_t j = 0; j < n; ++j) {
+                    p[j] = exp(p[j] - m);
+                    l += p[j];
+                }
+                for (int64_t j = 0; j < n; ++j)
+                    p[j] /= l;
+                /* dP_ij = dO_i . V_j and D_i = sum_j P_ij dP_ij */
+                double di = 0.0;
+                for (int64_t j = 0; j < n; ++j) {
+                    double dot = 0.0;
                     for (int64_t c = 0; c < dv; ++c)
-                        gd[c] = widen(&d, grow[c]);
-                    /* P_i. over the visible keys (safe softmax) */
-                    double m = -INFINITY;
-                    for (int64_t j = 0; j < n; ++j) {
-                        double dot = 0.0;
-                        for (int64_t c = 0; c < dqk; ++c)
-                            dot += qd[c] * widen(&d, kh[j * dqk + c]);
-                        p[j] = scale * dot;
-                        if (p[j] > m)
-                            m = p[j];
-                    }
-                    double l = 0.0;
-                    for (int64_t j = 0; j < n; ++j) {
-                        p[j] = exp(p[j] - m);
-                        l += p[j];
-                    }
-                    for (int64_t j = 0; j < n; ++j)
-                        p[j] /= l;
-                    /* dP_ij = dO_i . V_j and D_i = sum_j P_ij dP_ij */
-                    double di = 0.0;
-                    for (int64_t j = 0; j < n; ++j) {
-                        double dot = 0.0;
-                        for (int64_t c = 0; c < dv; ++c)
-                            dot += gd[c] * widen(&d, vh[j * dv + c]);
-                        dp[j] = dot;
-                        di += p[j] * dot;
-                    }
-                    delta[r] = di;
-                    for (int64_t j = 0; j < n; ++j) {
-                        const double ds = p[j] * (dp[j] - di);
-                        /* dV_j += P_ij dO_i;  dK_j += scale dS_ij Q_i;  dQ_i += scale dS_ij K_j */
-                        for (int64_t c = 0; c < dv; ++c)
-                            dvh[j * dv + c] += p[j] * gd[c];
-                        for (int64_t c = 0; c < dqk; ++c) {
-                            dkh[j * dqk + c] += scale * ds * qd[c];
-                            dqrow[c] += scale * ds * widen(&d, kh[j * dqk + c]);
-                        }
+                        dot += gd[c] * widen(&d, vh[j * dv + c]);
+                    dp[j] = dot;
+                    di += p[j] * dot;
+                }
+                delta[r] = di;
+                for (int64_t j = 0; j < n; ++j) {
+                    const double ds = p[j] * (dp[j] - di);
+                    /* dV_j += P_ij dO_i;  dK_j += scale dS_ij Q_i;  dQ_i += scale dS_ij K_j */
+                    for (int64_t c = 0; c < dv; ++c)
+                        dvh[j * dv + c] += p[j] * gd[c];
+                    for (int64_t c = 0; c < dqk; ++c) {
+                        dkh[j * dqk + c] += scale * ds * qd[c];
+                        dqrow[c] += scale * ds * widen(&d, kh[j * dqk + c]);
                     }
                 }
             }
+            free(qd);
+            free(gd);
+            free(p);
+            free(dp);
         }
-        free(qd);
-        free(gd);
-        free(p);
-        free(dp);
+        /* the threads' partial sums, in thread order */
+        double* dkh = dk + bk * Lk * dqk;
+        double* dvh = dvo + bk * Lk * dv;
+        for (int64_t t = 0; t < Lk * dqk; ++t) {
+            double acc = 0.0;
+            for (int th = 0; th < nthr; ++th)
+                acc += part_k[(int64_t)th * Lk * dqk + t];
+            dkh[t] = acc;
+        }
+        for (int64_t t = 0; t < Lk * dv; ++t) {
+            double acc = 0.0;
+            for (int th = 0; th < nthr; ++th)
+                acc += part_v[(int64_t)th * Lk * dv + t];
+            dvh[t] = acc;
+        }
     }
+    free(part_k);
+    free(part_v);
     return failed ? 7 : 0;
 }

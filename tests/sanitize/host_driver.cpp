@@ -15,7 +15,7 @@
 
 namespace attn {
 hipError_t launch_fwd(const FwdParams&, int, int, bool, bool, bool, hipStream_t) { abort(); }
-hipError_t launch_bwd(const BwdParams&, int, bool, hipStream_t) { abort(); }
+hipError_t launch_bwd(const BwdParams&, int, int, bool, bool, hipStream_t) { abort(); }
 hipError_t launch_merge(const float*, const float*, uint16_t*, float*, int, long long, int,
                         hipStream_t) {
     abort();
@@ -102,6 +102,17 @@ int main() {
                                       128, 0, 0.1f, nullptr)));
     EXPECT(attn_bwd_noalloc(q, k, v, o, o, nullptr, o, o, o, 1, 2, 2, 64, 64, 128, 128, 0, 0.1f,
                             nullptr) == ATTN_ERR_NULL_PTR);
+    // the backward of every head shape and element type validates, then stops at the device
+    EXPECT(is_no_dev(attn_bwd(q, k, v, o, o, lse, o, o, o, lse, 1, 16, 16, 2048, 2048, 192, 128,
+                              1, 0.07f, nullptr)));
+    EXPECT(is_no_dev(attn_bwd_ex(q, k, v, o, o, lse, o, o, o, lse, 1, 8, 2, 300, 200, 64, 64, 1,
+                                 0, 0.125f, nullptr)));
+    EXPECT(attn_bwd_ex(q, k, v, o, o, lse, o, o, o, lse, 1, 8, 2, 300, 200, 64, 64, 2, 0, 0.125f,
+                       nullptr) == ATTN_ERR_BAD_ARGUMENT);
+    EXPECT(attn_bwd(q, k, v, o, o, lse, o, o, o, lse, 1, 8, 2, 300, 200, 192, 192, 0, 0.1f,
+                    nullptr) == ATTN_ERR_UNSUPPORTED_HEAD_DIM);
+    EXPECT(attn_bwd(q, k, v, o, o, lse, o, o, o, lse, 1, 1, 1, 6000000, 64, 192, 128, 0, 0.1f,
+                    nullptr) == ATTN_ERR_TOO_LARGE);
     unsigned long long cnt = 0;
     EXPECT(is_no_dev(attn_fwd_dbg(q, k, v, o, lse, 1, 1, 1, 256, 256, 64, 64, 0, 0.125f, nullptr,
                                   0.0f, 0, &cnt)));

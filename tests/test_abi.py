@@ -40,7 +40,7 @@ def _exported_symbols(path):
 
 
 def test_header_declares_the_entry_points():
-    assert {"attn_fwd", "attn_fwd_dbg", "attn_fwd_ex", "attn_bwd", "attn_bwd_noalloc",
+    assert {"attn_fwd", "attn_fwd_dbg", "attn_fwd_ex", "attn_bwd", "attn_bwd_ex", "attn_bwd_noalloc",
             "attn_split_keys", "attn_fwd_split",
             "attn_merge", "attn_varlen_plan", "attn_fwd_varlen", "attn_fwd_decode",
             "attn_status_string",
@@ -63,7 +63,7 @@ def test_library_exports_every_declared_function():
 
 def test_abi_version_and_status_strings():
     lib = _binding.library()
-    assert lib.attn_abi_version() == 7
+    assert lib.attn_abi_version() == 8
     for code in CODES.values():
         s = _binding.status_string(code)
         assert s and s != "unknown attn status"
@@ -312,7 +312,8 @@ def _call_bwd(**over):
     (dict(lse=None), "ATTN_ERR_NULL_PTR"),
     (dict(Lq=0), "ATTN_ERR_BAD_SHAPE"),
     (dict(Hq=6, Hkv=4), "ATTN_ERR_GQA_RATIO"),
-    (dict(d_qk=192, d_v=128), "ATTN_ERR_UNSUPPORTED_HEAD_DIM"),  # forward only
+    (dict(d_qk=192, d_v=192), "ATTN_ERR_UNSUPPORTED_HEAD_DIM"),
+    (dict(d_qk=128, d_v=64), "ATTN_ERR_UNSUPPORTED_HEAD_DIM"),
     (dict(d_qk=96, d_v=96), "ATTN_ERR_UNSUPPORTED_HEAD_DIM"),
     (dict(scale=float("nan")), "ATTN_ERR_BAD_SCALE"),
     (dict(dout=A * 6 + 2), "ATTN_ERR_MISALIGNED"),

@@ -4,8 +4,8 @@ import numpy as np
 import pytest
 import torch
 
-from exact_attention_forward_02_amd import attn_bwd, attn_fwd
-from exact_attention_forward_02_amd.inputs import make_qkv
+from exact_attention_forward_02_amd import attn_bwd, attn_fwd, attn_fwd_ex
+from exact_attention_forward_02_amd.inputs import make_qkv, make_qkv_fp16
 
 pytestmark = pytest.mark.gpu
 
@@ -21,15 +21,30 @@ DEV = "cuda:0"
 # allows five of those.
 TOL_MAX = 1.5e-2
 TOL_MEAN = 5e-3
+# fp16 (u = 2^-11): the same four roundings bound the max error by 4 * 2^-11 and
+# five average ones the mean error by 5 * 2^-13
+TOL_MAX_FP16 = 2e-3
+TOL_MEAN_FP16 = 6.5e-4
 
-# B, Hq, Hkv, Lq, Lk, d, causal
+# B, Hq, Hkv, Lq, Lk, d_qk, d_v, causal
 SHAPES = [
-    (1, 2, 2, 200, 300, 128, False),
-    (2, 4, 2, 256, 256, 128, True),    # GQA 2
-    (1, 4, 1, 130, 700, 64, False),    # MQA, d = 64
-    (1, 2, 2, 300, 129, 64, True),     # Lq > Lk: rows without keys
-    (1, 2, 2, 64, 64, 128, True),      # one block
-    (2, 8, 8, 1024, 1024, 128, True),  # several blocks per workgroup and wave
+    (1, 2, 2, 200, 300, 128, 128, False),
+    (2, 4, 2, 256, 256, 128, 128, True),    # GQA 2
+    (1, 4, 1, 130, 700, 64, 64, False),     # MQA, d = 64
+    (1, 2, 2, 300, 129, 64, 64, True),      # Lq > Lk: rows without keys
+    (1, 2, 2, 64, 64, 128, 128, True),      # one block
+    (2, 8, 8, 1024, 1024, 128, 128, True),  # several blocks per workgroup and wave
+    (1, 2, 2, 200, 300, 192, 128, False),   # (192, 128): dV and dK in two passes
+    (2, 4, 2, 333, 333, 192, 128, True),    # (192, 128), GQA 2, ragged
+    (1, 2, 2, 300, 129, 192, 128, True),    # (192, 128), rows without keys
+    (1, 4, 4, 1024, 1024, 192, 128, True),  # (192, 128), several blocks
+]
+# fp16 at full precision (inputs drawn straight into fp16)
+SHAPES_FP16 = [
+    (1, 2, 2, 200, 300, 128, 128, False),
+    (2, 4, 2, 256, 256, 128, 128, True),
+    (1, 4, 1, 130, 700, 64, 64, False),
+    (2, 4, 2, 333, 333, 192, 128, True),
 ]
 
 
@@ -37,7 +52,7 @@ def _ids(s):
     return "x".join(map(str, s))
 
 
-def _stats(name, got, ref):
+def _stats(name, got, ref, tol_max=TOL_MAX, tol_mean=TOL_MEAN):
     g = got.detach().cpu().double().numpy()
     err = np.abs(g - ref)
     scale_max = float(np.abs(ref).max())
@@ -46,26 +61,46 @@ def _stats(name, got, ref):
           "ref_mean": scale_mean}
     print(f"[bwd parity] {name}: " + ", ".join(f"{k}={v:.3e}" for k, v in st.items()), flush=True)
     assert np.all(np.isfinite(g)), f"{name}: non-finite gradient"
-    assert st["max"] <= TOL_MAX * scale_max, f"{name}: max error {st['max']:.3e}"
-    assert st["mean"] <= TOL_MEAN * scale_mean, f"{name}: mean error {st['mean']:.3e}"
+    assert st["max"] <= tol_max * scale_max, f"{name}: max error {st['max']:.3e}"
+    assert st["mean"] <= tol_mean * scale_mean, f"{name}: mean error {st['mean']:.3e}"
+
+
+def _check_backward(orc, shape, dtype):
+    B, Hq, Hkv, Lq, Lk, dqk, dvd, causal = shape
+    print(f"[case] bwd {dtype} {shape}", flush=True)
+    if dtype == torch.float16:
+        q, k, v = make_qkv_fp16(B, Hq, Hkv, Lq, Lk, dqk, dvd, seed=hash(shape) % 10007)
+        tol = (TOL_MAX_FP16, TOL_MEAN_FP16)
+    else:
+        q, k, v = make_qkv(B, Hq, Hkv, Lq, Lk, dqk, dvd, seed=hash(shape) % 10007)
+        tol = (TOL_MAX, TOL_MEAN)
+    g = torch.Generator().manual_seed(hash(shape) % 997)
+    dout = torch.randn((B, Hq, Lq, dvd), generator=g).to(dtype)
+    qd, kd, vd, gd = (t.to(DEV) for t in (q, k, v, dout))
+    if dtype == torch.float16:
+        o, lse = attn_fwd_ex(qd, kd, vd, causal=causal)
+    else:
+        o, lse = attn_fwd(qd, kd, vd, causal=causal)
+    dq, dk, dv, delta = attn_bwd(qd, kd, vd, o, lse, gd, causal=causal)
+    torch.cuda.synchronize()
+    assert dq.dtype == dk.dtype == dv.dtype == dtype
+    want_dq, want_dk, want_dv, want_delta = orc.attn_bwd(q, k, v, dout, causal=causal)
+    tag = f"{'fp16' if dtype == torch.float16 else 'bf16'} {shape}"
+    _stats(f"dq {tag}", dq, want_dq, *tol)
+    _stats(f"dk {tag}", dk, want_dk, *tol)
+    _stats(f"dv {tag}", dv, want_dv, *tol)
+    _stats(f"delta {tag}", delta, want_delta, *tol)
 
 
 @pytest.mark.parametrize("shape", SHAPES, ids=_ids)
 def test_backward_matches_the_oracle(orc, shape):
-    B, Hq, Hkv, Lq, Lk, d, causal = shape
-    print(f"[case] bwd {shape}", flush=True)
-    q, k, v = make_qkv(B, Hq, Hkv, Lq, Lk, d, d, seed=hash(shape) % 10007)
-    g = torch.Generator().manual_seed(hash(shape) % 997)
-    dout = torch.randn((B, Hq, Lq, d), generator=g).to(torch.bfloat16)
-    qd, kd, vd, gd = (t.to(DEV) for t in (q, k, v, dout))
-    o, lse = attn_fwd(qd, kd, vd, causal=causal)
-    dq, dk, dv, delta = attn_bwd(qd, kd, vd, o, lse, gd, causal=causal)
-    torch.cuda.synchronize()
-    want_dq, want_dk, want_dv, want_delta = orc.attn_bwd(q, k, v, dout, causal=causal)
-    _stats(f"dq {shape}", dq, want_dq)
-    _stats(f"dk {shape}", dk, want_dk)
-    _stats(f"dv {shape}", dv, want_dv)
-    _stats(f"delta {shape}", delta, want_delta)
+    _check_backward(orc, shape, torch.bfloat16)
+
+
+@pytest.mark.parametrize("shape", SHAPES_FP16, ids=_ids)
+def test_backward_fp16_matches_the_oracle(orc, shape):
+    """fp16 tensors (attn_bwd_ex) with values bf16 cannot hold, to the fp16 bar."""
+    _check_backward(orc, shape, torch.float16)
 
 
 def test_backward_gqa_equals_repeated_heads_summed():
@@ -90,7 +125,7 @@ def test_backward_gqa_equals_repeated_heads_summed():
             assert err <= 2e-2 * summed.abs().max().item(), err
 
 
-@pytest.mark.parametrize("name,n_heads", [("mha_l2k", 2), ("causal_l8k", 1)])
+@pytest.mark.parametrize("name,n_heads", [("mha_l2k", 2), ("causal_l8k", 1), ("dsv3_l32k", 1)])
 def test_backward_full_size_sampled_heads(orc, name, n_heads):
     """The backward at a full workload size, as bench.py --backward runs it:
     gradients of one head depend only on that head's q, k, v and dout, so

@@ -48,8 +48,10 @@ MUTATIONS = {
                           "dvh[j * dv + c] += p[j] * gd[dv - 1 - c];"),
     "bwd_dk_unscaled": ("dkh[j * dqk + c] += scale * ds * qd[c];",
                         "dkh[j * dqk + c] += ds * qd[c];"),
-    "bwd_gqa_first_head_only": ("for (int64_t h = hk * group; h < (hk + 1) * group; ++h) {",
-                                "for (int64_t h = hk * group; h < hk * group + 1; ++h) {"),
+    "bwd_dk_one_thread_partial": ("for (int th = 0; th < nthr; ++th)\n                acc += part_k",
+                                  "for (int th = 0; th < 1; ++th)\n                acc += part_k"),
+    "bwd_gqa_first_head_only": ("for (int64_t hi = 0; hi < group * Lq; ++hi) {",
+                                "for (int64_t hi = 0; hi < Lq; ++hi) {"),
     "fp16_read_as_bf16": ("return d->elem == ELEM_FP16 ? fp16_bits_to_double(bits) : "
                           "bf16_bits_to_double(bits);", "return bf16_bits_to_double(bits);"),
     "varlen_keys_at_query_offset": (
