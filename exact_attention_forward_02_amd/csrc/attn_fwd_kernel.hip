@@ -420,19 +420,21 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
     // ---- Q fragment, resident in registers for the whole sweep -----------
     // lane holds Q[qw + l32][16 ks + 8 hi .. +7] for every k-step ks
     ex8 qf[S::kKSteps];
-    auto load_q_global = [&]() __attribute__((always_inline)) {
-        const int qi = qw + l32;
-        const bool ok = qi < Lq_t;
+    // rows qw_ .. of the tile whose first Q row of this wave is at element
+    // qrow_w_ (lq_ query rows in its sequence)
+    auto load_q_rows = [&](int qw_, size_t qrow_w_, int lq_) __attribute__((always_inline)) {
+        const int qi = qw_ + l32;
+        const bool ok = qi < lq_;
         // lanes past Lq point at row 0 of the head (never read past the tensor)
         const uint16_t* src =
-            p.q + (ok ? qrow_w + (size_t)l32 * p.q_sr : qrow_w - (size_t)qw * p.q_sr) + 8 * hi;
+            p.q + (ok ? qrow_w_ + (size_t)l32 * p.q_sr : qrow_w_ - (size_t)qw_ * p.q_sr) + 8 * hi;
 #pragma unroll
         for (int ks = 0; ks < S::kKSteps; ++ks) {
             u32x4 w = ok ? load16(src + 16 * ks) : u32x4{0u, 0u, 0u, 0u};
             qf[ks] = __builtin_bit_cast(ex8, w);
         }
     };
-    load_q_global();
+    load_q_rows(qw, qrow_w, Lq_t);
 
     // ---- direct global -> LDS copies of one K or V block -------------------
     // The copies are issued by the waves whose phase at that moment is the
@@ -883,6 +885,15 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
         }
     };
 
+    // next tile's Q rows of this wave, for head shapes without slices: loaded
+    // straight into the Q registers once the sweep is over, so that the loads
+    // run under the epilogue (packed variable-length batches load them after
+    // the epilogue: their registers have no room to carry the coordinates
+    // through the sweep)
+    constexpr bool kQEarly = !kStage && !VARLEN;
+    int nq_qw = 0, nq_lq = 0;
+    size_t nq_qrow = 0;
+
     // ---- ping-pong sweep over key blocks, tile after tile -----------------------
     if (nblk > 0 && grp == 1) copy_k(0, lds_k0);
     __builtin_amdgcn_s_waitcnt(0);
@@ -903,6 +914,10 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
             if (kStage) {
                 nq_rows = max(0, min(kRowsPerWave, c.Lq - c.qw));
                 nq_src = p.q + c.qbase + (size_t)(nq_rows > 0 ? c.qw : 0) * p.q_sr;
+            } else if (kQEarly) {
+                nq_qw = c.qw;
+                nq_qrow = c.qbase + (size_t)c.qw * p.q_sr;
+                nq_lq = c.Lq;
             }
         }
         reset_state();
@@ -975,6 +990,8 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
             __syncthreads();
         }
         pend = 0;
+        // the sweep no longer reads Q: the next tile's rows load now
+        if (kQEarly && has_next) load_q_rows(nq_qw, nq_qrow, nq_lq);
 
         // ---- epilogue: O = U / l (bf16), lse = scale * ref + ln l ------------
         // The next tile's Q leaves the slice before this tile's O enters it.
@@ -1040,7 +1057,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
         ++round;
         tile = tile_n;
         set_tile(tile);
-        if (!kStage) load_q_global();
+        if (!kStage && !kQEarly) load_q_rows(qw, qrow_w, Lq_t);
     }
     // the last tile's output
     if constexpr (kStage) {
