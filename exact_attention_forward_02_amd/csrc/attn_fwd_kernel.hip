@@ -312,6 +312,14 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
     // drain all outstanding LDS reads instead of only the oldest ones.
     const float c2 = p.scale_log2;
     const float threshold = p.threshold;
+    // Weight bound of the softmax fast path: a row whose weights against its
+    // reference all stay below 2^(threshold - 1/64) cannot move, whatever the
+    // rounding of the exact rule's own test, which the rows closer to the
+    // boundary take.
+    // (Not with the (192, 128) head shape, whose registers the fast path
+    // would overflow; there the weights overwrite the scores.)
+    constexpr bool kFastMax = DQK <= 128;
+    const float thr_weight = kFastMax ? __builtin_amdgcn_exp2f(threshold - 0.015625f) : 0.0f;
     const float scale = p.scale;
     float* const lse_out = p.lse;
     uint16_t* const o_out = p.o;
@@ -319,6 +327,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
     unsigned long long* const rescale_count = p.rescale_count;
     asm volatile("" ::"s"(c2), "s"(threshold), "s"(scale), "s"(lse_out), "s"(o_out),
                  "s"(o_part), "s"(rescale_count));
+    if constexpr (kFastMax) asm volatile("" ::"s"(thr_weight));
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
@@ -706,74 +715,117 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
                 }
         }
 
-        // block max of this row (raw units), two independent chains
-        float bm0 = fmaxf(s[0][0], s[0][1]);
-        float bm1 = fmaxf(s[kBlockN / 32 - 1][0], s[kBlockN / 32 - 1][1]);
+        // P = 2^(x * c2 - refc), rounded to bf16 in registers, with this lane's
+        // share of their fp32 sum (returned).  The scores stay in s, so the
+        // weights can be formed again against another reference.  Groups of 8
+        // independent instructions back to back, since this wave is the only
+        // VALU issuer on its SIMD while the other wave runs MFMAs.
+        auto weights = [&](float refc) __attribute__((always_inline)) {
+            float rs[8];
+            if constexpr (!kFastMax) {
 #pragma unroll
-        for (int r = 2; r < 16; r += 2) {
-            bm0 = fmaxf(fmaxf(bm0, s[0][r]), s[0][r + 1]);
-            bm1 = fmaxf(fmaxf(bm1, s[kBlockN / 32 - 1][r]), s[kBlockN / 32 - 1][r + 1]);
-        }
-        static_assert(kBlockN / 32 == 2, "two 32-key score blocks per key block");
-        const float bmax = pair_max(fmaxf(bm0, bm1));
-
-        // Conditional rescale decision, branch-free.  delta is -inf when the
-        // row had no reference yet (the first block with a visible key adopts
-        // its own max: scale 0 applied to an empty state) and NaN while the
-        // row has seen no visible key at all (nothing moves).
-        const float cand = fmaxf(ref, bmax);
-        const float delta = (ref - cand) * c2;
-        const bool moved = delta < -threshold;
-        const float acc_scale = moved ? __builtin_amdgcn_exp2f(delta) : 1.0f;
-        if (DEBUG && rescale_count != nullptr) {
-            // events count reference moves after the first one of a row
-            const unsigned long long ev = __ballot(moved && ref != kNegInf && qw + l32 < Lq_t);
-            if (lane == 0 && ev)
-                atomicAdd(rescale_count, (unsigned long long)__builtin_popcountll(ev & 0xffffffffull));
-        }
-        ref = moved ? cand : ref;
-        if (__ballot(moved)) {  // wave-uniform: some row of this wave moved its reference
+                for (int mb = 0; mb < kBlockN / 32; ++mb)
 #pragma unroll
-            for (int i = 0; i < S::kDvBlocks; ++i)
+                    for (int r = 0; r < 16; ++r) s[mb][r] = fmaf(s[mb][r], c2, -refc);
 #pragma unroll
-                for (int r = 0; r < 16; ++r) oacc[i][r] *= acc_scale;
-            ell *= acc_scale;
-            ell_c *= acc_scale;
-            // only the register holding this lane's own query matters
-            ell_o *= acc_scale;
-        }
-
-        // P = 2^(x * c2 - ref * c2), rounded to bf16 in registers; the fp32
-        // P are summed here for lse, the bf16 P by the MFMA phase.  Computed in
-        // place, all exponent arguments first, then all exponentials, then the
-        // sums: independent instructions back to back, since this wave is the
-        // only VALU issuer on its SIMD while the other wave runs MFMAs.
-        const float refc = (ref == kNegInf) ? 0.0f : ref * c2;
+                for (int mb = 0; mb < kBlockN / 32; ++mb)
 #pragma unroll
-        for (int mb = 0; mb < kBlockN / 32; ++mb)
+                    for (int r = 0; r < 16; ++r) s[mb][r] = __builtin_amdgcn_exp2f(s[mb][r]);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) s[mb][r] = fmaf(s[mb][r], c2, -refc);
+                for (int i = 0; i < 8; ++i) rs[i] = s[0][i] + s[0][i + 8];
 #pragma unroll
-        for (int mb = 0; mb < kBlockN / 32; ++mb)
+                for (int mb = 1; mb < kBlockN / 32; ++mb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) s[mb][r] = __builtin_amdgcn_exp2f(s[mb][r]);
-        float rs[8];
+                    for (int r = 0; r < 16; ++r) rs[r & 7] += s[mb][r];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) rs[i] = s[0][i] + s[0][i + 8];
+                for (int mb = 0; mb < kBlockN / 32; ++mb)
 #pragma unroll
-        for (int mb = 1; mb < kBlockN / 32; ++mb)
+                    for (int t = 0; t < 2; ++t) {
+                        f32x8 e;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) rs[r & 7] += s[mb][r];
+                        for (int i = 0; i < 8; ++i) e[i] = s[mb][8 * t + i];
+                        pb[2 * mb + t] = __builtin_convertvector(e, ex8);
+                    }
+                return ((rs[0] + rs[1]) + (rs[2] + rs[3])) + ((rs[4] + rs[5]) + (rs[6] + rs[7]));
+            }
+            static_assert(sizeof(pb) / sizeof(pb[0]) == 2 * (kBlockN / 32),
+                          "one group of 8 weights per half score block");
 #pragma unroll
-        for (int mb = 0; mb < kBlockN / 32; ++mb)
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
+            for (int g = 0; g < kBlockN / 16; ++g) {
+                const int mb = g >> 1, t = g & 1;
                 f32x8 e;
 #pragma unroll
-                for (int i = 0; i < 8; ++i) e[i] = s[mb][8 * t + i];
-                pb[2 * mb + t] = __builtin_convertvector(e, ex8);
+                for (int i = 0; i < 8; ++i) e[i] = fmaf(s[mb][8 * t + i], c2, -refc);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) e[i] = __builtin_amdgcn_exp2f(e[i]);
+                if (g == 0) {
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) rs[i] = e[i];
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) rs[i] += e[i];
+                }
+                pb[g] = __builtin_convertvector(e, ex8);
             }
-        const float bsum = ((rs[0] + rs[1]) + (rs[2] + rs[3])) + ((rs[4] + rs[5]) + (rs[6] + rs[7]));
+            return ((rs[0] + rs[1]) + (rs[2] + rs[3])) + ((rs[4] + rs[5]) + (rs[6] + rs[7]));
+        };
+        // The reference moves only when the block maximum exceeds it by more
+        // than the threshold, i.e. when some weight against the current
+        // reference exceeds 2^threshold.  So once every row of the wave has a
+        // reference, the weights are formed against it first: if no lane's
+        // sum of them reaches thr_weight, no weight does and no row moves,
+        // and the block maximum is never needed.  Otherwise (or while some
+        // row has no reference yet) the rule runs in full below and decides
+        // exactly as it would alone.
+        float bsum = 0.0f;
+        bool done = false;
+        const bool attempted = kFastMax && !__ballot(ref == kNegInf);
+        if (attempted) {
+            bsum = weights(ref * c2);
+            done = !__ballot(!(bsum <= thr_weight));
+        }
+        if (!done) {
+            // block max of this row (raw units), two independent chains
+            float bm0 = fmaxf(s[0][0], s[0][1]);
+            float bm1 = fmaxf(s[kBlockN / 32 - 1][0], s[kBlockN / 32 - 1][1]);
+#pragma unroll
+            for (int r = 2; r < 16; r += 2) {
+                bm0 = fmaxf(fmaxf(bm0, s[0][r]), s[0][r + 1]);
+                bm1 = fmaxf(fmaxf(bm1, s[kBlockN / 32 - 1][r]), s[kBlockN / 32 - 1][r + 1]);
+            }
+            static_assert(kBlockN / 32 == 2, "two 32-key score blocks per key block");
+            const float bmax = pair_max(fmaxf(bm0, bm1));
+
+            // Conditional rescale decision, branch-free.  delta is -inf when
+            // the row had no reference yet (the first block with a visible key
+            // adopts its own max: scale 0 applied to an empty state) and NaN
+            // while the row has seen no visible key at all (nothing moves).
+            const float cand = fmaxf(ref, bmax);
+            const float delta = (ref - cand) * c2;
+            const bool moved = delta < -threshold;
+            const float acc_scale = moved ? __builtin_amdgcn_exp2f(delta) : 1.0f;
+            if (DEBUG && rescale_count != nullptr) {
+                // events count reference moves after the first one of a row
+                const unsigned long long ev = __ballot(moved && ref != kNegInf && qw + l32 < Lq_t);
+                if (lane == 0 && ev)
+                    atomicAdd(rescale_count, (unsigned long long)__builtin_popcountll(ev & 0xffffffffull));
+            }
+            ref = moved ? cand : ref;
+            const bool any_moved = __ballot(moved) != 0;
+            if (any_moved) {  // wave-uniform: some row of this wave moved its reference
+#pragma unroll
+                for (int i = 0; i < S::kDvBlocks; ++i)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) oacc[i][r] *= acc_scale;
+                ell *= acc_scale;
+                ell_c *= acc_scale;
+                // only the register holding this lane's own query matters
+                ell_o *= acc_scale;
+            }
+            // the weights against the final references (unless the attempt
+            // above formed them and no row moved)
+            if (!attempted || any_moved) bsum = weights((ref == kNegInf) ? 0.0f : ref * c2);
+        }
         const float y = bsum - ell_c;
         const float t = ell + y;
         ell_c = (t - ell) - y;
