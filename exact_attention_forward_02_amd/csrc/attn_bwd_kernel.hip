@@ -294,7 +294,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) void attn_bwd_dkdv_kernel(const Bwd
     __shared__ __attribute__((aligned(1024))) unsigned char dobuf1[kBlk * DV * 2];
     __shared__ __attribute__((aligned(256))) float lse0[kBlk], dl0[kBlk], lse1[kBlk], dl1[kBlk];
 
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, hi = lane >> 5;
     const int nkb = (p.Lk + 127) / 128;
     const int nbk = p.B * p.Hkv;
@@ -352,20 +353,30 @@ __global__ __launch_bounds__(kBwdThreads, 1) void attn_bwd_dkdv_kernel(const Bwd
     const int nt = p.G * nq;    // steps: (query head of the group, query block)
     const size_t head0 = (size_t)(b * p.Hq + hk * p.G) * p.Lq;
 
-    // stage t: Q and dO rows of its block by every wave, lse by wave 0 and
-    // D by wave 1 (one 4-byte copy of 64 rows each)
-    auto issue = [&](int t, unsigned char* qb, unsigned char* dob, float* lb, float* db)
+    // stage t: Q and dO rows of its block by every wave, and D by wave 1
+    // (one 4-byte copy of 64 rows).  Wave 0 loads the block's lse into a
+    // register instead; just before the barrier that publishes the stage it
+    // stores the exponent's row term lse * log2(e), or +inf for a row past
+    // Lq, whose weights then come out exactly 0 (publish_lse).  Each score
+    // then needs one fma before its exponential, and no test for the query
+    // tail.
+    float lse_pend = 0.0f;
+    auto issue = [&](int t, unsigned char* qb, unsigned char* dob, float* db)
                      __attribute__((always_inline)) {
         const int g = t / nq;
         const int i0 = (qb0 + t % nq) * kBlk;
         const size_t r0 = head0 + (size_t)g * p.Lq;
+        if (wave == 0) lse_pend = p.lse[r0 + min(i0 + lane, p.Lq - 1)];
         cpq.issue(make_rsrc(uniform(p.q + r0 * DQK), (uint32_t)p.Lq * (DQK * 2)), i0, p.Lq, qb);
         cpv.issue(make_rsrc(uniform(p.dout + r0 * DV), (uint32_t)p.Lq * (DV * 2)), i0, p.Lq, dob);
-        if (wave < 2) {
-            const float* src = wave == 0 ? p.lse : p.delta;
-            float* dst = wave == 0 ? lb : db;
-            copy4_to_lds(make_rsrc(uniform(src + r0), (uint32_t)p.Lq * 4),
-                           (uint32_t)min(i0 + lane, p.Lq - 1) * 4, dst);
+        if (wave == 1)
+            copy4_to_lds(make_rsrc(uniform(p.delta + r0), (uint32_t)p.Lq * 4),
+                         (uint32_t)min(i0 + lane, p.Lq - 1) * 4, db);
+    };
+    auto publish_lse = [&](int t, float* lb) __attribute__((always_inline)) {
+        if (wave == 0) {
+            const int i0 = (qb0 + t % nq) * kBlk;
+            lb[lane] = i0 + lane < p.Lq ? lse_pend * kLog2e : __builtin_inff();
         }
     };
     // One step (64 query rows = sub-blocks 0 and 1 of 32 rows) is a sequence
@@ -384,9 +395,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) void attn_bwd_dkdv_kernel(const Bwd
     constexpr int kSD = kKsQ + kKsV;           // units of an S / dP quarter
     constexpr int kVK = 2 * (kDbV + kDbQ);     // units of a dV / dK quarter
     constexpr int kUnits = 2 * kSD + 2 * kVK;
-    // query rows i that see this lane's key: i >= imin (and i < Lq); none
-    // for a key past Lk
-    const int imin = key >= p.Lk ? INT32_MAX : (CAUSAL ? key - off : INT32_MIN);
+    // causal: query rows i that see this lane's key: i >= imin
+    const int imin = key - off;
     const f32x16 zero = {};
     f32x16 sacc[2], dpacc[2], pv, dsv;
     X8 pb[2][2], db[2][2];
@@ -464,16 +474,30 @@ __global__ __launch_bounds__(kBwdThreads, 1) void attn_bwd_dkdv_kernel(const Bwd
     };
     // P and dS of sub-block sub at accumulator element r (row i0 + 32 sub +
     // acc_row(r), column key); after elements 7 and 15, their 16-bit fragments
-    // (P for the dV products, dS for the dK products)
-    auto softmax_elem = [&](int sub, int r, int i0) __attribute__((always_inline)) {
-        const int i = i0 + 32 * sub + acc_row(r, hi);
-        const bool ok = i >= imin && i < p.Lq;
-        const float pr = ok ? __builtin_amdgcn_exp2f(sacc[sub][r] * c2 - l4[r >> 2][r & 3] * kLog2e)
-                            : 0.0f;
+    // (P for the dV products, dS for the dK products).  Rows past Lq carry an
+    // infinite row term (weight 0).  A key past Lk only ever meets its own
+    // accumulator column, which is never stored, so it needs no mask.  Under
+    // the causal mask, the steps whose rows do not all see the wave's last
+    // key (diag, wave-uniform) zero the weights of the rows before each
+    // lane's key, 8 at a time, with selects: a row that sees no key at all
+    // has lse = -inf and an infinite weight there.
+    auto softmax_elem = [&](int sub, int r, int i0, bool diag) __attribute__((always_inline)) {
+        const float pr = __builtin_amdgcn_exp2f(fmaf(sacc[sub][r], c2, -l4[r >> 2][r & 3]));
         pv[r] = pr;
         if constexpr (kDoDK) dsv[r] = pr * (dpacc[sub][r] - d4[r >> 2][r & 3]);
         if ((r & 7) == 7) {
             const int t2 = r >> 3;
+            if (CAUSAL && diag) {
+                // element r is row i0 + 32 sub + acc_row(r, hi)
+                const int lo = imin - i0 - 32 * sub - 4 * hi;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int r2 = 8 * t2 + e;
+                    const bool ok = acc_row(r2, 0) >= lo;
+                    pv[r2] = ok ? pv[r2] : 0.0f;
+                    if constexpr (kDoDK) dsv[r2] = ok ? dsv[r2] : 0.0f;
+                }
+            }
             f32x8 e1, e2;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
@@ -496,6 +520,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void attn_bwd_dkdv_kernel(const Bwd
     auto compute = [&](int t, const unsigned char* qbuf, const unsigned char* dobuf,
                        const float* lsebuf, const float* dbuf) __attribute__((always_inline)) {
         const int i0 = (qb0 + t % nq) * kBlk;
+        const bool diag = CAUSAL && i0 < key0 + 31 - off;
         X8 ring[kAhead];
 #pragma unroll
         for (int n = 0; n < kAhead; ++n) ring[n] = load(n, qbuf, dobuf);
@@ -510,7 +535,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void attn_bwd_dkdv_kernel(const Bwd
                 const int len = qt == 1 ? kSD : kVK;
 #pragma unroll
                 for (int r = (16 * u + len - 1) / len; r < (16 * (u + 1) + len - 1) / len; ++r)
-                    softmax_elem(qt - 1, r, i0);
+                    softmax_elem(qt - 1, r, i0, diag);
             }
             __builtin_amdgcn_sched_barrier(0);
         };
@@ -527,16 +552,19 @@ __global__ __launch_bounds__(kBwdThreads, 1) void attn_bwd_dkdv_kernel(const Bwd
         for (int n = 2 * kSD + kVK; n < kUnits; ++n) unit(n);
     };
     // One barrier per step: every wave's copies of stage t have landed (each
-    // wave waits for its own before the barrier) and every wave is done with
-    // stage t - 1, whose buffers the copies of stage t + 1 then refill.
-    issue(0, qbuf0, dobuf0, lse0, dl0);
+    // wave waits for its own before the barrier), its row terms are stored,
+    // and every wave is done with stage t - 1, whose buffers the copies of
+    // stage t + 1 then refill.
+    issue(0, qbuf0, dobuf0, dl0);
     for (int t = 0; t < nt; t += 2) {
+        publish_lse(t, lse0);
         wait_copies_and_sync();
-        if (t + 1 < nt) issue(t + 1, qbuf1, dobuf1, lse1, dl1);
+        if (t + 1 < nt) issue(t + 1, qbuf1, dobuf1, dl1);
         compute(t, qbuf0, dobuf0, lse0, dl0);
         if (t + 1 < nt) {
+            publish_lse(t + 1, lse1);
             wait_copies_and_sync();
-            if (t + 2 < nt) issue(t + 2, qbuf0, dobuf0, lse0, dl0);
+            if (t + 2 < nt) issue(t + 2, qbuf0, dobuf0, dl0);
             compute(t + 1, qbuf1, dobuf1, lse1, dl1);
         }
     }
@@ -583,7 +611,8 @@ __global__ __launch_bounds__(kBwdThreads, (DQK <= 128 ? 2 : 1)) void attn_bwd_dq
     __shared__ __attribute__((aligned(1024))) unsigned char kbuf1[kBlk * DQK * 2];
     __shared__ __attribute__((aligned(1024))) unsigned char vbuf1[kBlk * DV * 2];
 
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, hi = lane >> 5;
     const int nqb = (p.Lq + 127) / 128;
     const int nbh = p.B * p.Hq;
@@ -614,8 +643,11 @@ __global__ __launch_bounds__(kBwdThreads, (DQK <= 128 ? 2 : 1)) void attn_bwd_dq
 #pragma unroll
     for (int ks = 0; ks < kKsV; ++ks)
         gf[ks] = __builtin_bit_cast(X8, load16(p.dout + (qrow0 + qr) * DV + 16 * ks + 8 * hi));
-    const float lse_q = p.lse[qrow0 + qr];
+    const float lse2_q = p.lse[qrow0 + qr] * kLog2e;  // the exponent's row term
     const float d_q = p.delta[qrow0 + qr];
+    // the last key this lane's query sees (a lane past Lq reads row 0 and is
+    // never stored)
+    const int jlast = CAUSAL ? min(p.Lk - 1, qi + off) : p.Lk - 1;
     f32x16 dqt[kDbQ];
 #pragma unroll
     for (int i = 0; i < kDbQ; ++i)
@@ -659,14 +691,14 @@ __global__ __launch_bounds__(kBwdThreads, (DQK <= 128 ? 2 : 1)) void attn_bwd_dq
                 if (ks < kKsV)
                     dpt = E::mfma(row_frag<DV, X8>(vbuf, 32 * mb, ks, lane), gf[ks], dpt);
             }
+            // element r holds key j0 + 32 mb + acc_row(r, hi), visible iff
+            // acc_row(r, 0) <= lim: one compare with a constant
+            const int lim = jlast - j0 - 32 * mb - 4 * hi;
             f32x16 ds;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int j = j0 + 32 * mb + acc_row(r, hi);
-                bool ok = j < p.Lk && qi < p.Lq;
-                if (CAUSAL) ok = ok && j <= qi + off;
-                const float pr = ok ? __builtin_amdgcn_exp2f(st[r] * c2 - lse_q * kLog2e) : 0.0f;
-                ds[r] = pr * (dpt[r] - d_q);
+                const float pr = __builtin_amdgcn_exp2f(fmaf(st[r], c2, -lse2_q));
+                ds[r] = (acc_row(r, 0) <= lim ? pr : 0.0f) * (dpt[r] - d_q);
             }
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
