@@ -677,20 +677,60 @@ __global__ __launch_bounds__(kBwdThreads, (DQK <= 128 ? 2 : 1)) void attn_bwd_dq
         cpv.issue(vrs, jb * kBlk, p.Lk, vbuf);
     };
     const f32x16 zero = {};
+    // A block is a list of MFMA units, each with one LDS operand: the S / dP
+    // units of key rows 0..31 (the k-steps of S and dP alternate while both
+    // last), those of rows 32..63, then the dQ units (row group g, output
+    // block i).  Operands are loaded kAhead units before their MFMA into a
+    // register ring, and scheduling barriers keep that order, so the loads of
+    // the next units are in flight while the softmax of a row group runs and
+    // while earlier MFMAs execute, instead of each MFMA waiting for its own.
+    constexpr int kAheadQ = 2;
+    constexpr int kSDq = kKsQ + kKsV;
+    constexpr int kUnitsQ = 2 * kSDq + 4 * kDbQ;
+    auto sd_unit = [](int u, bool* is_dp, int* ks) {
+        constexpr int kBoth = 2 * (kKsQ < kKsV ? kKsQ : kKsV);
+        if (u < kBoth) {
+            *is_dp = (u & 1) != 0;
+            *ks = u >> 1;
+        } else {
+            *is_dp = kKsV > kKsQ;
+            *ks = kBoth / 2 + (u - kBoth);
+        }
+    };
     auto compute = [&](int jb, const unsigned char* kbuf, const unsigned char* vbuf)
                        __attribute__((always_inline)) {
         const int j0 = jb * kBlk;
         if (q0 >= p.Lq || j0 >= wend) return;  // no visible key of this block for the wave
         X8 db[4];
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
-            f32x16 st = zero, dpt = zero;
-#pragma unroll
-            for (int ks = 0; ks < kKsMax; ++ks) {
-                if (ks < kKsQ) st = E::mfma(row_frag<DQK, X8>(kbuf, 32 * mb, ks, lane), qf[ks], st);
-                if (ks < kKsV)
-                    dpt = E::mfma(row_frag<DV, X8>(vbuf, 32 * mb, ks, lane), gf[ks], dpt);
+        f32x16 st, dpt;
+        auto load = [&](int n) __attribute__((always_inline)) {
+            if (n < 2 * kSDq) {
+                const int mb = n / kSDq;
+                bool is_dp;
+                int ks;
+                sd_unit(n % kSDq, &is_dp, &ks);
+                return is_dp ? row_frag<DV, X8>(vbuf, 32 * mb, ks, lane)
+                             : row_frag<DQK, X8>(kbuf, 32 * mb, ks, lane);
             }
+            const int g = (n - 2 * kSDq) / kDbQ, i = (n - 2 * kSDq) % kDbQ;
+            return tr_frag<DQK, X8>(kbuf, tro, i, g);
+        };
+        auto mfma_unit = [&](int n, X8 a) __attribute__((always_inline)) {
+            if (n < 2 * kSDq) {
+                bool is_dp;
+                int ks;
+                sd_unit(n % kSDq, &is_dp, &ks);
+                if (is_dp)
+                    dpt = E::mfma(a, gf[ks], ks == 0 ? zero : dpt);
+                else
+                    st = E::mfma(a, qf[ks], ks == 0 ? zero : st);
+            } else {
+                const int g = (n - 2 * kSDq) / kDbQ, i = (n - 2 * kSDq) % kDbQ;
+                dqt[i] = E::mfma(a, db[g], dqt[i]);
+            }
+        };
+        // dS of key rows 32 mb .. 32 mb + 31 from the finished S and dP
+        auto softmax = [&](int mb) __attribute__((always_inline)) {
             // element r holds key j0 + 32 mb + acc_row(r, hi), visible iff
             // acc_row(r, 0) <= lim: one compare with a constant
             const int lim = jlast - j0 - 32 * mb - 4 * hi;
@@ -707,13 +747,27 @@ __global__ __launch_bounds__(kBwdThreads, (DQK <= 128 ? 2 : 1)) void attn_bwd_dq
                 for (int x = 0; x < 8; ++x) e[x] = ds[8 * t + x];
                 db[2 * mb + t] = __builtin_convertvector(e, X8);
             }
-        }
-        // dQ^T += K^T dS^T
+        };
+        X8 ring[kAheadQ];
 #pragma unroll
-        for (int g = 0; g < 4; ++g)
+        for (int n = 0; n < kAheadQ; ++n) ring[n] = load(n);
+        auto unit = [&](int n) __attribute__((always_inline)) {
+            const X8 a = ring[n % kAheadQ];
+            if (n + kAheadQ < kUnitsQ) ring[n % kAheadQ] = load(n + kAheadQ);
+            mfma_unit(n, a);
+            __builtin_amdgcn_sched_barrier(0);
+        };
+        // three loops, each short enough to be unrolled in full
 #pragma unroll
-            for (int i = 0; i < kDbQ; ++i)
-                dqt[i] = E::mfma(tr_frag<DQK, X8>(kbuf, tro, i, g), db[g], dqt[i]);
+        for (int n = 0; n < kSDq; ++n) unit(n);
+        softmax(0);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int n = kSDq; n < 2 * kSDq; ++n) unit(n);
+        softmax(1);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int n = 2 * kSDq; n < kUnitsQ; ++n) unit(n);
     };
     // one barrier per block, as in the dK/dV kernel
     if (nkb > 0) issue(0, kbuf0, vbuf0);
