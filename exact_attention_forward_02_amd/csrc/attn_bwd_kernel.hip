@@ -603,7 +603,6 @@ __global__ __launch_bounds__(kBwdThreads, (DQK <= 128 ? 2 : 1)) void attn_bwd_dq
     using X4 = typename E::x4;
     constexpr int kKsQ = DQK / 16;
     constexpr int kKsV = DV / 16;
-    constexpr int kKsMax = kKsQ > kKsV ? kKsQ : kKsV;
     constexpr int kDbQ = DQK / 32;
     // two stages of (K block, V block), filled by direct-to-LDS copies
     __shared__ __attribute__((aligned(1024))) unsigned char kbuf0[kBlk * DQK * 2];
