@@ -33,6 +33,7 @@
 #include <stdint.h>
 
 #include <mutex>
+#include <type_traits>
 
 #include "attn_params.h"
 
@@ -729,7 +730,8 @@ __global__ __launch_bounds__(kBwdThreads, (DQK <= 128 ? 2 : 1)) void attn_bwd_dq
             }
         };
         // dS of key rows 32 mb .. 32 mb + 31 from the finished S and dP
-        auto softmax = [&](int mb) __attribute__((always_inline)) {
+        auto softmax_m = [&](int mb, auto maskc) __attribute__((always_inline)) {
+            constexpr bool kMask = decltype(maskc)::value;
             // element r holds key j0 + 32 mb + acc_row(r, hi), visible iff
             // acc_row(r, 0) <= lim: one compare with a constant
             const int lim = jlast - j0 - 32 * mb - 4 * hi;
@@ -737,7 +739,7 @@ __global__ __launch_bounds__(kBwdThreads, (DQK <= 128 ? 2 : 1)) void attn_bwd_dq
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const float pr = __builtin_amdgcn_exp2f(fmaf(st[r], c2, -lse2_q));
-                ds[r] = (acc_row(r, 0) <= lim ? pr : 0.0f) * (dpt[r] - d_q);
+                ds[r] = (!kMask || acc_row(r, 0) <= lim ? pr : 0.0f) * (dpt[r] - d_q);
             }
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
@@ -746,6 +748,16 @@ __global__ __launch_bounds__(kBwdThreads, (DQK <= 128 ? 2 : 1)) void attn_bwd_dq
                 for (int x = 0; x < 8; ++x) e[x] = ds[8 * t + x];
                 db[2 * mb + t] = __builtin_convertvector(e, X8);
             }
+        };
+        // blocks whose keys all exist and, under the causal mask, all lie at
+        // or before every row's last visible key need no test (wave-uniform)
+        const bool full = j0 + kBlk <= p.Lk && (!CAUSAL || j0 + kBlk - 1 <= q0 + off) &&
+                          q0 + 32 <= p.Lq;
+        auto softmax = [&](int mb) __attribute__((always_inline)) {
+            if (full)
+                softmax_m(mb, std::false_type{});
+            else
+                softmax_m(mb, std::true_type{});
         };
         X8 ring[kAheadQ];
 #pragma unroll
