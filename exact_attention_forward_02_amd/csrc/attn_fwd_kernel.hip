@@ -316,10 +316,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
     // reference all stay below 2^(threshold - 1/64) cannot move, whatever the
     // rounding of the exact rule's own test, which the rows closer to the
     // boundary take.
-    // (Not with the (192, 128) head shape, whose registers the fast path
-    // would overflow; there the weights overwrite the scores.)
-    constexpr bool kFastMax = DQK <= 128;
-    const float thr_weight = kFastMax ? __builtin_amdgcn_exp2f(threshold - 0.015625f) : 0.0f;
+    const float thr_weight = __builtin_amdgcn_exp2f(threshold - 0.015625f);
     const float scale = p.scale;
     float* const lse_out = p.lse;
     uint16_t* const o_out = p.o;
@@ -327,7 +324,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
     unsigned long long* const rescale_count = p.rescale_count;
     asm volatile("" ::"s"(c2), "s"(threshold), "s"(scale), "s"(lse_out), "s"(o_out),
                  "s"(o_part), "s"(rescale_count));
-    if constexpr (kFastMax) asm volatile("" ::"s"(thr_weight));
+    asm volatile("" ::"s"(thr_weight));
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
@@ -454,8 +451,9 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
     // c' ^ swizzle(r) of key row key0 + r (rows are row-stride bytes apart in
     // HBM and DQK * 2 apart in LDS).  The per-lane byte offsets within a
     // block are fixed, so they are computed once.  In a block that runs
-    // past the last key, rows are clamped to the last key: those rows are
-    // masked to -inf (K) or weighted by exactly 0 (V).
+    // past the last key, the rows past it lie beyond the descriptor's range
+    // and arrive as zeros: their scores are masked to -inf and their weights
+    // are exactly 0.
     const int wq = wave % kGroupWaves;  // index of the wave within its group
     uint32_t koff[S::kKCopies], voff_copy[S::kVCopies];
 #pragma unroll
@@ -481,7 +479,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
     auto blk = [&](int j) __attribute__((always_inline)) {
         return (CAUSAL && !VARLEN && desc) ? nblk - 1 - j : j;
     };
-    auto copy_kblock = [&](__amdgpu_buffer_rsrc_t rs, int key0, int lk, unsigned char* dst)
+    auto copy_kblock = [&](__amdgpu_buffer_rsrc_t rs, int key0, unsigned char* dst)
                            __attribute__((always_inline)) {
         const uint32_t boff = (uint32_t)key0 * k_rb;
         // an opaque copy of the wave's offset: the destinations are formed
@@ -489,43 +487,20 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
         // and copy and held (or spilled) across the sweep
         int kd = kdst;
         asm volatile("" : "+s"(kd));
-        if (key0 + kBlockN <= lk) {
 #pragma unroll
-            for (int i = 0; i < S::kKCopies; ++i)
-                copy_to_lds(rs, koff[i], boff, dst + kd + 1024 * i);
-        } else {
-            const int last = lk - 1 - key0;
-#pragma unroll
-            for (int i = 0; i < S::kKCopies; ++i) {
-                const int r = (64 * (wq * S::kKCopies + i) + lane) / S::kChunksK;
-                const int rr = min(r, last);
-                copy_to_lds(rs, koff[i] - (uint32_t)((r - rr) * k_rb), boff,
-                            dst + kd + 1024 * i);
-            }
-        }
+        for (int i = 0; i < S::kKCopies; ++i)
+            copy_to_lds(rs, koff[i], boff, dst + kd + 1024 * i);
     };
     auto copy_k = [&](int jl, unsigned char* dst) __attribute__((always_inline)) {
-        copy_kblock(krsrc, (jb0 + blk(jl)) * kBlockN, Lk_t, dst);
+        copy_kblock(krsrc, (jb0 + blk(jl)) * kBlockN, dst);
     };
     auto copy_v = [&](int jl, unsigned char* dst) __attribute__((always_inline)) {
-        const int key0 = (jb0 + blk(jl)) * kBlockN;
-        const uint32_t boff = (uint32_t)key0 * v_rb;
+        const uint32_t boff = (uint32_t)((jb0 + blk(jl)) * kBlockN) * v_rb;
         int vd = vdst;
         asm volatile("" : "+s"(vd));
-        if (key0 + kBlockN <= Lk_t) {
 #pragma unroll
-            for (int i = 0; i < S::kVCopies; ++i)
-                copy_to_lds(vrsrc, voff_copy[i], boff, dst + vd + 1024 * i);
-        } else {
-            const int last = Lk_t - 1 - key0;
-#pragma unroll
-            for (int i = 0; i < S::kVCopies; ++i) {
-                const int r = (64 * (wq * S::kVCopies + i) + lane) / S::kChunksV;
-                const int rr = min(r, last);
-                copy_to_lds(vrsrc, voff_copy[i] - (uint32_t)((r - rr) * v_rb), boff,
-                            dst + vd + 1024 * i);
-            }
-        }
+        for (int i = 0; i < S::kVCopies; ++i)
+            copy_to_lds(vrsrc, voff_copy[i], boff, dst + vd + 1024 * i);
     };
 
     // ---- LDS read offsets (bytes within a block buffer) -----------------------
@@ -599,7 +574,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
     // of stalling each one.
     constexpr int kPvUnits = (kBlockN / 16) * S::kDvBlocks;
     constexpr int kSUnits = S::kKSteps * (kBlockN / 32);
-    constexpr int kAhead = DQK > 128 ? 3 : 4;  // wide heads have fewer spare VGPRs
+    constexpr int kAhead = 4;
     auto load_pv = [&](int u, const unsigned char* vl) __attribute__((always_inline)) {
         const int g = u / S::kDvBlocks, i = u % S::kDvBlocks;
         i16x4 part[2];
@@ -722,32 +697,6 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
         // VALU issuer on its SIMD while the other wave runs MFMAs.
         auto weights = [&](float refc) __attribute__((always_inline)) {
             float rs[8];
-            if constexpr (!kFastMax) {
-#pragma unroll
-                for (int mb = 0; mb < kBlockN / 32; ++mb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) s[mb][r] = fmaf(s[mb][r], c2, -refc);
-#pragma unroll
-                for (int mb = 0; mb < kBlockN / 32; ++mb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) s[mb][r] = __builtin_amdgcn_exp2f(s[mb][r]);
-#pragma unroll
-                for (int i = 0; i < 8; ++i) rs[i] = s[0][i] + s[0][i + 8];
-#pragma unroll
-                for (int mb = 1; mb < kBlockN / 32; ++mb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) rs[r & 7] += s[mb][r];
-#pragma unroll
-                for (int mb = 0; mb < kBlockN / 32; ++mb)
-#pragma unroll
-                    for (int t = 0; t < 2; ++t) {
-                        f32x8 e;
-#pragma unroll
-                        for (int i = 0; i < 8; ++i) e[i] = s[mb][8 * t + i];
-                        pb[2 * mb + t] = __builtin_convertvector(e, ex8);
-                    }
-                return ((rs[0] + rs[1]) + (rs[2] + rs[3])) + ((rs[4] + rs[5]) + (rs[6] + rs[7]));
-            }
             static_assert(sizeof(pb) / sizeof(pb[0]) == 2 * (kBlockN / 32),
                           "one group of 8 weights per half score block");
 #pragma unroll
@@ -779,7 +728,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
         // exactly as it would alone.
         float bsum = 0.0f;
         bool done = false;
-        const bool attempted = kFastMax && !__ballot(ref == kNegInf);
+        const bool attempted = !__ballot(ref == kNegInf);
         if (attempted) {
             bsum = weights(ref * c2);
             done = !__ballot(!(bsum <= thr_weight));
@@ -892,7 +841,6 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
     int nq_rows = 0;
     bool nk_copy = false;
     int nk_key0 = 0;
-    int nk_lk = Lk_t;
     __amdgpu_buffer_rsrc_t nk_rsrc = krsrc;
     auto prefetch_q_chunk = [&](int k) __attribute__((always_inline)) {
         const int sl = 64 * k + lane;
@@ -961,7 +909,6 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
             nk_copy = r.nblk > 0;
             // its first block: the first or the last of its key range
             nk_key0 = (r.jb0 + (sweep_down(round + 1) ? r.nblk - 1 : 0)) * kBlockN;
-            nk_lk = c.Lk;
             nk_rsrc = make_rsrc(p.k + c.kbase, kv_bytes(c.Lk, k_rb, kRowK));
             if (kStage) {
                 nq_rows = max(0, min(kRowsPerWave, c.Lq - c.qw));
@@ -991,7 +938,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
                     if (t + 1 < nblk)
                         copy_k(t + 1, lds_k1);
                     else if (t == nblk && nk_copy)
-                        copy_kblock(nk_rsrc, nk_key0, nk_lk, lds_k0);  // next tile's stage 0
+                        copy_kblock(nk_rsrc, nk_key0, lds_k0);  // next tile's stage 0
                 }
                 work(gc, C0{}, phi, lds_k0, lds_v0);
                 if constexpr (G == 0) {
@@ -1007,7 +954,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
                     if (t + 2 < nblk)
                         copy_k(t + 2, lds_k0);
                     else if (t + 1 == nblk && nk_copy)
-                        copy_kblock(nk_rsrc, nk_key0, nk_lk, lds_k0);
+                        copy_kblock(nk_rsrc, nk_key0, lds_k0);
                 }
                 work(gc, C2{}, phi, lds_k1, lds_v1);
                 if constexpr (G == 0) {
@@ -1037,7 +984,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
                     for (int k = 0; k < kSliceChunks; ++k) prefetch_q_chunk(k);
                 }
             }
-            if (nk_copy && grp == 1) copy_kblock(nk_rsrc, nk_key0, nk_lk, lds_k0);
+            if (nk_copy && grp == 1) copy_kblock(nk_rsrc, nk_key0, lds_k0);
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
         }
