@@ -261,6 +261,35 @@ def test_rescale_threshold_and_events(orc):
     assert counts[0.0] >= counts[8.0]
 
 
+@pytest.mark.parametrize("dims", [(128, 128), (192, 128)], ids=lambda d: f"{d[0]}x{d[1]}")
+def test_rescale_events_each_head_shape(orc, dims):
+    """The softmax fast path (weights against the current reference first,
+    the block maximum only where some weight could move it) takes the same
+    decisions as the per-row rule at every head shape: on Q x 6 inputs that
+    fire rescales, the event count matches the oracle's for the same block
+    size, and the output its values.  Q x 6 makes rows nearly one-hot, where
+    bf16 weights cannot reach the absolute 1e-2 everywhere, so O is held to
+    max(1e-2, the bf16-weight bound)."""
+    dqk, dv = dims
+    q, k, v = make_qkv(1, 2, 2, 256, 320, dqk, dv, seed=4242 + dqk, q_mult=6.0)
+    qd, kd, vd = _gpu(q, k, v)
+    o_ref, l_ref = orc.attn_rows(q, k, v, causal=False)
+    cnt = torch.zeros(1, dtype=torch.int64, device=DEV)
+    o, lse = attn_fwd_dbg(qd, kd, vd, causal=False, rescale_threshold=8.0, rescale_count=cnt)
+    torch.cuda.synchronize()
+    bound = dense_bound(q, k, v, False, default_scale(dqk), o_ref)
+    err = np.abs(o.cpu().double().numpy().reshape(-1, dv) - np.asarray(o_ref))
+    print(f"[bound] {dims}: elements above 1e-2: {100.0 * float((err > 1e-2).mean()):.2f}%",
+          flush=True)
+    assert_parity(f"q6 {dims}", o.cpu().reshape(-1, dv), lse.cpu().reshape(-1), o_ref, l_ref,
+                  bound=bound)
+    _, _, _, want = orc.online_rows(q, k, v, causal=False, bn=64, mode=1, tau=8.0)
+    got = int(cnt.item())
+    print(f"[events] {dims}: gpu {got} oracle {want}", flush=True)
+    assert want > 0
+    assert abs(got - want) <= max(2, want // 50)
+
+
 def test_outputs_off_the_input_device_are_refused():
     """Caller-supplied outputs on the host are refused before any launch, for
     every entry point that takes them."""
