@@ -46,3 +46,17 @@ def test_committed_traffic_records_name_their_kernel_and_workload():
         assert rec["hbm_bytes_per_launch"] == pytest.approx(
             rec["hbm_read_bytes_per_launch"] + rec["hbm_write_bytes_per_launch"])
         assert len(rec["kernel_source_sha256"]) == 64
+
+
+def test_committed_traffic_records_match_the_current_kernel_sources():
+    """Every committed traffic record was taken on the kernel source as it
+    stands, so each bench line reports it (a kernel change since the counters
+    were taken would turn the line's traffic into null)."""
+    csrc = os.path.join(ROOT, "exact_attention_forward_02_amd", "csrc")
+    for name in sorted(os.listdir(os.path.join(ROOT, "profiles"))):
+        if not (name.startswith("traffic_") and name.endswith(".json")):
+            continue
+        with open(os.path.join(ROOT, "profiles", name)) as f:
+            rec = json.load(f)
+        src = os.path.join(csrc, rec["kernel_source"])
+        assert rec["kernel_source_sha256"] == bench.kernel_source_digest(src), name
