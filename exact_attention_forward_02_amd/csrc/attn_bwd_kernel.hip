@@ -176,15 +176,17 @@ struct BlockCopies {
         slot0 = 64 * kCopies * wave + lane;
         dst = __builtin_amdgcn_readfirstlane(1024 * kCopies * wave);
     }
-    // rows [row0, row0 + 64) of the head that rs covers (L rows) into blk
+    // rows [row0, row0 + 64) of the head that rs covers (L rows) into blk;
+    // rows past L lie beyond the descriptor's range and arrive as zeros
     __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t rs, int row0, int L,
                                           unsigned char* blk) const {
+        (void)L;
 #pragma unroll
         for (int i = 0; i < kCopies; ++i) {
             const int slot = slot0 + 64 * i;
             const int r = slot / kChunks;
             const uint32_t col = 16u * (uint32_t)((slot % kChunks) ^ swz<D>(r));
-            const uint32_t off = (uint32_t)min(row0 + r, L - 1) * (D * 2) + col;
+            const uint32_t off = (uint32_t)(row0 + r) * (D * 2) + col;
             copy16_to_lds(rs, off, blk + dst + 1024 * i);
         }
     }
