@@ -176,11 +176,10 @@ struct BlockCopies {
         slot0 = 64 * kCopies * wave + lane;
         dst = __builtin_amdgcn_readfirstlane(1024 * kCopies * wave);
     }
-    // rows [row0, row0 + 64) of the head that rs covers (L rows) into blk;
-    // rows past L lie beyond the descriptor's range and arrive as zeros
-    __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t rs, int row0, int L,
+    // rows [row0, row0 + 64) of the head that rs covers into blk; rows past
+    // the head's last row lie beyond the descriptor's range and arrive as zeros
+    __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t rs, int row0,
                                           unsigned char* blk) const {
-        (void)L;
 #pragma unroll
         for (int i = 0; i < kCopies; ++i) {
             const int slot = slot0 + 64 * i;
@@ -370,8 +369,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) void attn_bwd_dkdv_kernel(const Bwd
         const int i0 = (qb0 + t % nq) * kBlk;
         const size_t r0 = head0 + (size_t)g * p.Lq;
         if (wave == 0) lse_pend = p.lse[r0 + min(i0 + lane, p.Lq - 1)];
-        cpq.issue(make_rsrc(uniform(p.q + r0 * DQK), (uint32_t)p.Lq * (DQK * 2)), i0, p.Lq, qb);
-        cpv.issue(make_rsrc(uniform(p.dout + r0 * DV), (uint32_t)p.Lq * (DV * 2)), i0, p.Lq, dob);
+        cpq.issue(make_rsrc(uniform(p.q + r0 * DQK), (uint32_t)p.Lq * (DQK * 2)), i0, qb);
+        cpv.issue(make_rsrc(uniform(p.dout + r0 * DV), (uint32_t)p.Lq * (DV * 2)), i0, dob);
         if (wave == 1)
             copy4_to_lds(make_rsrc(uniform(p.delta + r0), (uint32_t)p.Lq * 4),
                          (uint32_t)min(i0 + lane, p.Lq - 1) * 4, db);
@@ -675,8 +674,8 @@ __global__ __launch_bounds__(kBwdThreads, (DQK <= 128 ? 2 : 1)) void attn_bwd_dq
         make_rsrc(uniform(p.v + (size_t)bk * p.Lk * DV), (uint32_t)p.Lk * (DV * 2));
     auto issue = [&](int jb, unsigned char* kbuf, unsigned char* vbuf)
                      __attribute__((always_inline)) {
-        cpk.issue(krs, jb * kBlk, p.Lk, kbuf);
-        cpv.issue(vrs, jb * kBlk, p.Lk, vbuf);
+        cpk.issue(krs, jb * kBlk, kbuf);
+        cpv.issue(vrs, jb * kBlk, vbuf);
     };
     const f32x16 zero = {};
     // A block is a list of MFMA units, each with one LDS operand: the S / dP
