@@ -157,6 +157,16 @@ int split_keys(int Lk, int n_split) {
 // Heads of one K/V head packed into a workgroup: Gp divides G and the 8 waves.
 int packed_heads(int G) { return (G % 8 == 0) ? 8 : (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1; }
 
+// The kernel divides by these launch constants with a multiply and a shift.
+void set_divisors(attn::FwdParams& p) {
+    p.div_sec = attn::make_fast_div((uint32_t)(p.sec_units * p.n_m));
+    p.div_sec_units = attn::make_fast_div((uint32_t)p.sec_units);
+    p.div_units_kv = attn::make_fast_div((uint32_t)p.units_kv);
+    p.div_hg = attn::make_fast_div((uint32_t)p.n_hg);
+    p.div_hkv = attn::make_fast_div((uint32_t)p.Hkv);
+    p.div_gp = attn::make_fast_div((uint32_t)p.Gp);
+}
+
 int fill_schedule(attn::FwdParams& p, bool causal) {
     p.G = p.Hq / p.Hkv;
     // query heads that share a K/V head are packed into one workgroup, one
@@ -183,6 +193,7 @@ int fill_schedule(attn::FwdParams& p, bool causal) {
     int cap = kTilesPerXcdWave / p.n_m;
     if (cap < 1) cap = 1;
     p.sec_units = largest_divisor_at_most(p.upx, cap);
+    set_divisors(p);
     return ATTN_OK;
 }
 
@@ -254,9 +265,10 @@ int run(const void* q, const void* k, const void* v, void* o, float* lse, int B,
     if (slots > 0 && tiles > slots) grid = slots;
     p.grid = (int)grid;
     log_launch("attn_fwd_kernel<%d,%d,%s%s%s> grid %d, %d tiles (units %d x position tiles %d), "
-               "splits %d, query heads per workgroup %d, xcd_mode %d",
+               "splits %d, query heads per workgroup %d, xcd_mode %d, chained %d",
                d_qk, d_v, causal ? "causal" : "full", debug ? ",debug" : "", fp16 ? ",fp16" : "",
-               p.grid, p.units * p.n_m, p.units, p.n_m, p.n_split, p.Gp, p.xcd_mode);
+               p.grid, p.units * p.n_m, p.units, p.n_m, p.n_split, p.Gp, p.xcd_mode,
+               attn::fwd_chained(p, d_qk, d_v, causal != 0) ? 1 : 0);
     hipError_t err = attn::launch_fwd(p, d_qk, d_v, causal != 0, debug, fp16,
                                       static_cast<hipStream_t>(stream));
     if (err != hipSuccess) return ATTN_ERR_HIP;
@@ -651,6 +663,7 @@ int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float*
     p.xcd_mode = 1;
     p.upx = n_records / kXcds;
     p.sec_units = 1;
+    set_divisors(p);
     p.scale = scale;
     p.scale_log2 = (float)((double)scale * 1.4426950408889634);  // log2(e)
     p.threshold = kDefaultThreshold;

@@ -174,6 +174,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
 }
 
+// n / d for 0 <= n < 2^31 with f = make_fast_div(d)
+__device__ __forceinline__ int fdiv(int n, FastDiv f) {
+    return (int)((__umulhi((uint32_t)n, f.mul) + (uint32_t)n) >> f.shift);
+}
+
 // Tile t of the launch -> its key split, K/V head, and this wave's query head
 // and first query row.  With xcd_mode, tile t runs on XCD t % 8 (the
 // hardware deals workgroups round-robin over the 8 XCDs, and a persistent
@@ -202,15 +207,16 @@ __device__ __forceinline__ TileCoord tile_coord(const FwdParams& p, int t, int w
                         k0 <= p.total_k - lk && unit >= 0 && unit < p.units_kv && m >= 0 &&
                         m * p.bm_pos < lq;
         if (!ok) q0 = lq = k0 = lk = unit = m = 0;
-        const int hg = unit % p.n_hg;
-        const int kvh = unit / p.n_hg;
+        const int kvh = fdiv(unit, p.div_hg);
+        const int hg = unit - kvh * p.n_hg;
         c.Lq = lq;
         c.Lk = lk;
         c.split = 0;
         c.bk = kvh;
-        c.hq = kvh * p.G + hg * p.Gp + (wave % p.Gp);
+        const int wg = fdiv(wave, p.div_gp);
+        c.hq = kvh * p.G + hg * p.Gp + (wave - wg * p.Gp);
         c.pos0 = m * p.bm_pos;
-        c.qw = c.pos0 + (wave / p.Gp) * kRowsPerWave;
+        c.qw = c.pos0 + wg * kRowsPerWave;
         c.qrow0 = (size_t)c.hq * p.total_q + q0;  // lse is [Hq, total_q]
         c.qbase = (size_t)q0 * p.q_sr + (size_t)c.hq * p.q_sh;
         c.obase = (size_t)q0 * p.o_sr + (size_t)c.hq * p.o_sh;
@@ -224,23 +230,24 @@ __device__ __forceinline__ TileCoord tile_coord(const FwdParams& p, int t, int w
         local = t >> 3;
         base = (t & 7) * p.upx;
     }
-    const int sec = local / per_sec;
+    const int sec = fdiv(local, p.div_sec);
     const int r = local - sec * per_sec;
-    const int mo = r / p.sec_units;
+    const int mo = fdiv(r, p.div_sec_units);
     const int unit = base + sec * p.sec_units + (r - mo * p.sec_units);
     // causal tiles are ordered heaviest first (longest processing time first)
     const int m = CAUSAL ? (p.n_m - 1 - mo) : mo;
     c.Lq = p.Lq;
     c.Lk = p.Lk;
-    c.split = unit / p.units_kv;  // key split of this tile (0 without splits)
+    c.split = fdiv(unit, p.div_units_kv);  // key split of this tile (0 without splits)
     const int ukv = unit - c.split * p.units_kv;
-    const int hg = ukv % p.n_hg;
-    c.bk = ukv / p.n_hg;  // b * Hkv + kv head
-    const int kvh = c.bk % p.Hkv;
-    const int b = c.bk / p.Hkv;
-    c.hq = kvh * p.G + hg * p.Gp + (wave % p.Gp);
+    c.bk = fdiv(ukv, p.div_hg);  // b * Hkv + kv head
+    const int hg = ukv - c.bk * p.n_hg;
+    const int b = fdiv(c.bk, p.div_hkv);
+    const int kvh = c.bk - b * p.Hkv;
+    const int wg = fdiv(wave, p.div_gp);
+    c.hq = kvh * p.G + hg * p.Gp + (wave - wg * p.Gp);
     c.pos0 = m * p.bm_pos;
-    c.qw = c.pos0 + (wave / p.Gp) * kRowsPerWave;  // first row of this wave
+    c.qw = c.pos0 + wg * kRowsPerWave;  // first row of this wave
     c.qrow0 = (size_t)(b * p.Hq + c.hq) * p.Lq;
     c.qbase = (size_t)(b * p.q_sb + c.hq * p.q_sh);
     c.obase = (size_t)(b * p.o_sb + c.hq * p.o_sh);
@@ -278,7 +285,7 @@ __device__ __forceinline__ KeyRange key_range(const FwdParams& p, const TileCoor
     return r;
 }
 
-template <int DQK, int DV, bool CAUSAL, bool DEBUG, bool FP16, bool VARLEN>
+template <int DQK, int DV, bool CAUSAL, bool DEBUG, bool FP16, bool VARLEN, bool CHAIN>
 __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
     using S = Shape<DQK, DV>;
     using E = Elem<FP16>;
@@ -334,6 +341,10 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
     // waves are spread round-robin over the 4 SIMDs: waves w and w + 4 share
     // one; the two wave groups alternate between MFMA and VALU phases
     const int grp = wave / kGroupWaves;
+    // The wave index for the tile coordinates.  The chained sweep computes
+    // them inside its sweep, where the pointers derived from it would
+    // otherwise take vector registers: there it is made wave-uniform.
+    const int wave_t = CHAIN ? __builtin_amdgcn_readfirstlane(wave) : wave;
 
     // ---- tiles of this workgroup ---------------------------------------------
     // With one workgroup per CU the grid is persistent: each workgroup runs
@@ -394,7 +405,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
         return (VARLEN && lk <= 0) ? 0u : (uint32_t)(lk - 1) * rb + row;
     };
     auto set_tile = [&](int t) __attribute__((always_inline)) {
-        const TileCoord c = tile_coord<CAUSAL, VARLEN>(p, t, wave);
+        const TileCoord c = tile_coord<CAUSAL, VARLEN>(p, t, wave_t);
         if constexpr (VARLEN) {
             Lq_t = c.Lq;
             Lk_t = c.Lk;
@@ -494,13 +505,17 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
     auto copy_k = [&](int jl, unsigned char* dst) __attribute__((always_inline)) {
         copy_kblock(krsrc, (jb0 + blk(jl)) * kBlockN, dst);
     };
-    auto copy_v = [&](int jl, unsigned char* dst) __attribute__((always_inline)) {
-        const uint32_t boff = (uint32_t)((jb0 + blk(jl)) * kBlockN) * v_rb;
+    auto copy_vblock = [&](__amdgpu_buffer_rsrc_t rs, int key0, unsigned char* dst)
+                           __attribute__((always_inline)) {
+        const uint32_t boff = (uint32_t)key0 * v_rb;
         int vd = vdst;
         asm volatile("" : "+s"(vd));
 #pragma unroll
         for (int i = 0; i < S::kVCopies; ++i)
-            copy_to_lds(vrsrc, voff_copy[i], boff, dst + vd + 1024 * i);
+            copy_to_lds(rs, voff_copy[i], boff, dst + vd + 1024 * i);
+    };
+    auto copy_v = [&](int jl, unsigned char* dst) __attribute__((always_inline)) {
+        copy_vblock(vrsrc, (jb0 + blk(jl)) * kBlockN, dst);
     };
 
     // ---- LDS read offsets (bytes within a block buffer) -----------------------
@@ -545,15 +560,20 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
     // rows those of query l % 16 + 16 (groups 1, 3).  Lane l then finds its
     // own query's sum in register (l / 16) & 1 of the accumulator.
     f32x4 ell_o;
+    // the per-row state; O itself is cleared separately (reset_state), or not
+    // at all where the tile's first PV product starts from a zero accumulator
+    auto reset_rows = [&]() __attribute__((always_inline)) {
+        ref = kNegInf;
+        ell = 0.0f;
+        ell_c = 0.0f;
+        ell_o = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    };
     auto reset_state = [&]() __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < S::kDvBlocks; ++i)
 #pragma unroll
             for (int r = 0; r < 16; ++r) oacc[i][r] = 0.0f;
-        ref = kNegInf;
-        ell = 0.0f;
-        ell_c = 0.0f;
-        ell_o = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        reset_rows();
     };
     ex8 sel;
     {
@@ -591,17 +611,18 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
                                                 (ks / kReadTable) * kReadTable * 32 +
                                                 mb * 32 * kRowK);
     };
-    auto m_phase = [&](int j, const unsigned char* kl, const unsigned char* vl) __attribute__((always_inline)) {
-        constexpr bool kDown = CAUSAL && !VARLEN;  // launches that may sweep downward
-        const bool do_pv = j >= (kDown ? jact0 : 0) && j < jact1;
-        const bool do_s = (!kDown || j + 1 >= jact0) && j + 1 < jact1;
+    // pvz: the PV product is the tile's first, its first k-step starts O from
+    // an inline zero accumulator
+    auto m_units = [&](bool do_pv, bool do_s, const unsigned char* kl, const unsigned char* vl,
+                       auto pvz) __attribute__((always_inline)) {
+        constexpr bool kPvZero = decltype(pvz)::value;
         const f32x16 zero = {};
         // one MFMA unit: PV unit u < kPvUnits, else score unit u - kPvUnits; the
         // first k-step of a score block starts from an inline zero accumulator
         auto mfma_unit = [&](int u, ex8 a) __attribute__((always_inline)) {
             if (u < kPvUnits) {
                 const int g = u / S::kDvBlocks, i = u % S::kDvBlocks;
-                oacc[i] = E::mfma32(a, pb[g], oacc[i]);
+                oacc[i] = E::mfma32(a, pb[g], (kPvZero && g == 0) ? zero : oacc[i]);
             } else {
                 const int v = u - kPvUnits;
                 const int ks = v / (kBlockN / 32), mb = v % (kBlockN / 32);
@@ -668,12 +689,17 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
         }
     };
 
+    auto m_phase = [&](int j, const unsigned char* kl, const unsigned char* vl) __attribute__((always_inline)) {
+        constexpr bool kDown = CAUSAL && !VARLEN;  // launches that may sweep downward
+        const bool do_pv = j >= (kDown ? jact0 : 0) && j < jact1;
+        const bool do_s = (!kDown || j + 1 >= jact0) && j + 1 < jact1;
+        m_units(do_pv, do_s, kl, vl, std::false_type{});
+    };
+
     // ---- VALU phase V(j): online softmax of block j's scores -----------------
-    auto v_phase = [&](int j) __attribute__((always_inline)) {
-        if (j >= jact1) return;
-        if constexpr (CAUSAL && !VARLEN) {
-            if (j < jact0) return;
-        }
+    // fresh: the tile's first block, whose O is not read (its PV product
+    // starts from zero), so a reference move need not rescale it
+    auto softmax = [&](int j, bool fresh) __attribute__((always_inline)) {
         const int key0 = (jb0 + blk(j)) * kBlockN;
         // mask keys past the end or past the causal diagonal
         const bool need_mask =
@@ -762,10 +788,12 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
             ref = moved ? cand : ref;
             const bool any_moved = __ballot(moved) != 0;
             if (any_moved) {  // wave-uniform: some row of this wave moved its reference
+                if (!fresh) {
 #pragma unroll
-                for (int i = 0; i < S::kDvBlocks; ++i)
+                    for (int i = 0; i < S::kDvBlocks; ++i)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) oacc[i][r] *= acc_scale;
+                        for (int r = 0; r < 16; ++r) oacc[i][r] *= acc_scale;
+                }
                 ell *= acc_scale;
                 ell_c *= acc_scale;
                 // only the register holding this lane's own query matters
@@ -779,6 +807,13 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
         const float t = ell + y;
         ell_c = (t - ell) - y;
         ell = t;
+    };
+    auto v_phase = [&](int j) __attribute__((always_inline)) {
+        if (j >= jact1) return;
+        if constexpr (CAUSAL && !VARLEN) {
+            if (j < jact0) return;
+        }
+        softmax(j, false);
     };
 
     // ---- ping-pong sweep over key blocks ---------------------------------------
@@ -894,10 +929,241 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
     int nq_qw = 0, nq_lq = 0;
     size_t nq_qrow = 0;
 
+    // ---- epilogue of a tile: O = U / l (bf16), lse = scale * ref + ln l -------
+    auto epilogue = [&]() __attribute__((always_inline)) {
+        const int qi = qw + l32;
+        const float ell_row = pair_sum(ell - ell_c);
+        const float ell_o_row = ((lane >> 4) & 1) ? ell_o[1] : ell_o[0];
+        const float inv = ell_o_row > 0.0f ? 1.0f / ell_o_row : 0.0f;
+        const float lse_row = ell_row > 0.0f ? ref * scale + logf(ell_row) : kNegInf;
+        if (o_part == nullptr) {
+            if constexpr (kStage) {
+                // row l32 of the slice; this lane's 4 columns 32 i + 8 r4 + 4 hi
+                // are the half hi of 16-byte chunk 4 i + r4.  The row index goes
+                // through an empty asm so that these per-lane addresses are
+                // computed here, not hoisted out of the tile loop and kept in
+                // registers across the sweep.
+                int orow = l32;
+                asm volatile("" : "+v"(orow));
+#pragma unroll
+                for (int i = 0; i < S::kDvBlocks; ++i) {
+#pragma unroll
+                    for (int r4 = 0; r4 < 4; ++r4) {
+                        f32x4 x = {oacc[i][4 * r4 + 0] * inv, oacc[i][4 * r4 + 1] * inv,
+                                   oacc[i][4 * r4 + 2] * inv, oacc[i][4 * r4 + 3] * inv};
+                        const ex4 y = __builtin_convertvector(x, ex4);
+                        *reinterpret_cast<ex4*>(slice + orow * kRowQ +
+                                                   16 * ((4 * i + r4) ^ kswz<DV>(orow)) + 8 * hi) = y;
+                    }
+                }
+                pend = 1;
+                pend_rows = max(0, min(kRowsPerWave, Lq_t - qw));
+                pend_dst = o_out + orow_w;
+            } else if (qi < Lq_t) {
+                uint16_t* orow = o_out + orow_w + (size_t)l32 * p.o_sr;
+#pragma unroll
+                for (int i = 0; i < S::kDvBlocks; ++i) {
+#pragma unroll
+                    for (int r4 = 0; r4 < 4; ++r4) {
+                        f32x4 x = {oacc[i][4 * r4 + 0] * inv, oacc[i][4 * r4 + 1] * inv,
+                                   oacc[i][4 * r4 + 2] * inv, oacc[i][4 * r4 + 3] * inv};
+                        const ex4 y = __builtin_convertvector(x, ex4);
+                        *reinterpret_cast<ex4*>(orow + 32 * i + 8 * r4 + 4 * hi) = y;
+                    }
+                }
+            }
+            if (hi == 0 && qi < Lq_t) lse_out[qrow0 + qi] = lse_row;
+        } else if (qi < Lq_t) {
+            // one split's state in fp32: its normalised output and lse
+            const size_t prow = (size_t)split * p.B * p.Hq * p.Lq + qrow0 + qi;
+            float* orow = o_part + prow * DV;
+#pragma unroll
+            for (int i = 0; i < S::kDvBlocks; ++i) {
+#pragma unroll
+                for (int r4 = 0; r4 < 4; ++r4) {
+                    f32x4 x = {oacc[i][4 * r4 + 0] * inv, oacc[i][4 * r4 + 1] * inv,
+                               oacc[i][4 * r4 + 2] * inv, oacc[i][4 * r4 + 3] * inv};
+                    *reinterpret_cast<f32x4*>(orow + 32 * i + 8 * r4 + 4 * hi) = x;
+                }
+            }
+            if (hi == 0) lse_out[prow] = lse_row;
+        }
+    };
+
     // ---- ping-pong sweep over key blocks, tile after tile -----------------------
     if (nblk > 0 && grp == 1) copy_k(0, lds_k0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+
+    // ---- chained sweep: all tiles of the workgroup as one sequence of blocks ---
+    // Without the causal mask and without key splits every tile visits the
+    // same nblk blocks, so the workgroup's tiles form one sweep over
+    // n_mine * nblk blocks, block J being local block J - tstart of the tile
+    // that starts at tstart.  The ping-pong above then runs unchanged across
+    // tile boundaries: the MFMA phase with the PV product of a tile's last
+    // block also computes the scores of the next tile's first block, with the
+    // next tile's Q, which the wave loaded from its slice at the end of the
+    // softmax phase before; and the softmax phase of the next tile's first
+    // block starts by finishing the previous tile (O into the slice, lse) and
+    // resetting the running state.  The pipeline neither drains nor refills
+    // between tiles.  A wave's hand-offs are keyed to the local block l of its
+    // softmax phase: output chunk k leaves in l = k + 1 and the next tile's Q
+    // chunk k arrives in l = nblk - 1 - C + k (C chunks per slice), so the
+    // two never overlap when nblk >= 2 C + 2; the copies of a block that
+    // belongs to the next tile (K is copied up to two blocks ahead) use that
+    // tile's descriptors.  Every wave computes every block, also a wave whose
+    // rows lie past Lq (it stores nothing).
+    if constexpr (CHAIN) {
+        static_assert(!CAUSAL && !VARLEN && kStage, "chained sweeps are for non-causal launches with slices");
+        {
+            const int nb = nblk;
+            const int n_mine = (n_local - slot + per_round - 1) / per_round;
+            const int total = n_mine * nb;
+            int tstart = 0;   // sweep index of this wave's current tile's block 0
+            int tile_n = -1;  // the tile after it, or -1
+            __amdgpu_buffer_rsrc_t nv_rsrc = vrsrc;
+            // the next tile's rows as set_tile would set them: the switch to
+            // it then only copies
+            int nx_qw = 0;
+            size_t nx_qrow0 = 0, nx_orow_w = 0;
+            auto prepare_next = [&]() __attribute__((always_inline)) {
+                tile_n = tile_of_round(round + 1);
+                nq_rows = 0;
+                if (tile_n >= 0) {
+                    const TileCoord c = tile_coord<CAUSAL, VARLEN>(p, tile_n, wave_t);
+                    nk_rsrc = make_rsrc(p.k + c.kbase, kv_bytes(c.Lk, k_rb, kRowK));
+                    nv_rsrc = make_rsrc(p.v + c.vbase, kv_bytes(c.Lk, v_rb, kRowV));
+                    nq_rows = max(0, min(kRowsPerWave, c.Lq - c.qw));
+                    nq_src = p.q + c.qbase + (size_t)(nq_rows > 0 ? c.qw : 0) * p.q_sr;
+                    nx_qw = c.qw;
+                    nx_qrow0 = c.qrow0;
+                    nx_orow_w = c.obase + (size_t)c.qw * p.o_sr;
+                }
+            };
+            prepare_next();
+            reset_state();
+            auto copy_k_at = [&](int J, unsigned char* dst) __attribute__((always_inline)) {
+                const int l = J - tstart;
+                if (l < nb)
+                    copy_kblock(krsrc, l * kBlockN, dst);
+                else if (tile_n >= 0)
+                    copy_kblock(nk_rsrc, (l - nb) * kBlockN, dst);
+            };
+            auto copy_v_at = [&](int J, unsigned char* dst) __attribute__((always_inline)) {
+                const int l = J - tstart;
+                if (l < nb)
+                    copy_vblock(vrsrc, l * kBlockN, dst);
+                else if (tile_n >= 0)
+                    copy_vblock(nv_rsrc, (l - nb) * kBlockN, dst);
+            };
+            auto hand_off = [&](int l) __attribute__((always_inline)) {
+                if (pend && l >= 1 && l <= kSliceChunks) store_o_chunk(l - 1);
+                __builtin_amdgcn_sched_barrier(0);
+                const int k = l - (nb - 1 - kSliceChunks);
+                if (nq_rows > 0 && k >= 0 && k < kSliceChunks) prefetch_q_chunk(k);
+            };
+            // V(J).  Only edge pairs (see below) hold a tile's first or last
+            // block for some wave, so only they test for the tile switch and
+            // for the load of the next tile's Q.
+            auto v_chain = [&](int J, auto edgec) __attribute__((always_inline)) {
+                constexpr bool kEdge = decltype(edgec)::value;
+                if constexpr (kEdge) {
+                    if (J >= total) return;
+                    if (J - tstart == nb) {  // the next tile's first block
+                        epilogue();
+                        ++round;
+                        tile = tile_n;
+                        qw = nx_qw;
+                        qrow0 = nx_qrow0;
+                        orow_w = nx_orow_w;
+                        krsrc = nk_rsrc;
+                        vrsrc = nv_rsrc;
+                        tstart += nb;
+                        prepare_next();
+                        reset_rows();
+                    }
+                }
+                softmax(J - tstart, kEdge && J == tstart);
+                if constexpr (kEdge) {
+                    // the scores of the next tile's first block, in the coming
+                    // MFMA phase, take the next tile's Q
+                    if (J - tstart == nb - 1 && nq_rows > 0) load_q_slice();
+                }
+            };
+            // Pair t of the sweep (phases 2 t, 2 t + 1) reads stage t from the
+            // buffers kl, vl and fills stage t + 1 into kn, vn.  Group 0 runs
+            // M(t - 1) then V(t), group 1 V(t - 1) then M(t - 1).  MK selects
+            // the MFMA units of M(t - 1): 0 both products, 1 scores only (the
+            // first pair), 2 PV only (the last pair), 3 both with the PV
+            // product starting O from zero (M(t - 1) holds a tile's first PV).
+            auto pair = [&](auto gc, auto mk, auto edgec, int t, const unsigned char* kl,
+                            const unsigned char* vl, unsigned char* kn, unsigned char* vn)
+                            __attribute__((always_inline)) {
+                constexpr int G = decltype(gc)::value;
+                constexpr int MK = decltype(mk)::value;
+                auto m = [&]() __attribute__((always_inline)) {
+                    __builtin_amdgcn_s_setprio(2);
+                    m_units(MK != 1, MK != 2, kl, vl, std::integral_constant<bool, MK == 3>{});
+                };
+                if constexpr (G == 0) {
+                    m();
+                    hand_off(t - tstart);
+                    if (MK != 2) {
+                        copy_v_at(t, vn);
+                        __builtin_amdgcn_s_setprio(0);
+                        v_chain(t, edgec);
+                    }
+                } else {
+                    hand_off(t - 1 - tstart);
+                    copy_k_at(t + 1, kn);
+                    if (MK != 1) {
+                        __builtin_amdgcn_s_setprio(0);
+                        v_chain(t - 1, edgec);
+                    }
+                    m();
+                }
+                __builtin_amdgcn_s_waitcnt(0);
+                __syncthreads();
+            };
+            // The pairs of the tile whose first block is tb (nblk is even, so
+            // every tile starts on stage buffers 0).  A wave's tile switch falls
+            // in pair tb (group 0) or tb + 1 (group 1), its load of the next Q
+            // in pair tb + nb - 1 (group 0) or the next tile's pair tb + nb
+            // (group 1): these are the edge pairs, and the loop between them
+            // holds only the steady form of a pair.
+            auto tile_pairs = [&](auto gc, auto firstc, int tb) __attribute__((always_inline)) {
+                using Both = std::integral_constant<int, 0>;
+                using SOnly = std::integral_constant<int, 1>;
+                using First = std::conditional_t<decltype(firstc)::value, SOnly, Both>;
+                using Edge = std::true_type;
+                using Plain = std::false_type;
+                using PvFirst = std::integral_constant<int, 3>;
+                pair(gc, First{}, Edge{}, tb, lds_k0, lds_v0, lds_k1, lds_v1);
+                pair(gc, PvFirst{}, Edge{}, tb + 1, lds_k1, lds_v1, lds_k0, lds_v0);
+                for (int t = tb + 2; t < tb + nb - 2; t += 2) {
+                    pair(gc, Both{}, Plain{}, t, lds_k0, lds_v0, lds_k1, lds_v1);
+                    pair(gc, Both{}, Plain{}, t + 1, lds_k1, lds_v1, lds_k0, lds_v0);
+                }
+                pair(gc, Both{}, Plain{}, tb + nb - 2, lds_k0, lds_v0, lds_k1, lds_v1);
+                pair(gc, Both{}, Edge{}, tb + nb - 1, lds_k1, lds_v1, lds_k0, lds_v0);
+            };
+            auto chain_sweep = [&](auto gc) __attribute__((always_inline)) {
+                tile_pairs(gc, std::true_type{}, 0);
+                for (int tb = nb; tb < total; tb += nb) tile_pairs(gc, std::false_type{}, tb);
+                pair(gc, std::integral_constant<int, 2>{}, std::true_type{}, total, lds_k0,
+                     lds_v0, lds_k1, lds_v1);
+            };
+            if (grp == 0)
+                chain_sweep(std::integral_constant<int, 0>{});
+            else
+                chain_sweep(std::integral_constant<int, 1>{});
+            epilogue();
+#pragma unroll 1
+            for (int k = 0; k < kSliceChunks; ++k) store_o_chunk(k);
+            return;
+        }
+    }
+
     for (;;) {
         const int tile_n = tile_of_round(round + 1);
         const bool has_next = tile_n >= 0;
@@ -992,66 +1258,9 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
         // the sweep no longer reads Q: the next tile's rows load now
         if (kQEarly && has_next) load_q_rows(nq_qw, nq_qrow, nq_lq);
 
-        // ---- epilogue: O = U / l (bf16), lse = scale * ref + ln l ------------
         // The next tile's Q leaves the slice before this tile's O enters it.
         if (kStage && nq_rows > 0) load_q_slice();
-        const int qi = qw + l32;
-        const float ell_row = pair_sum(ell - ell_c);
-        const float ell_o_row = ((lane >> 4) & 1) ? ell_o[1] : ell_o[0];
-        const float inv = ell_o_row > 0.0f ? 1.0f / ell_o_row : 0.0f;
-        const float lse_row = ell_row > 0.0f ? ref * scale + logf(ell_row) : kNegInf;
-        if (o_part == nullptr) {
-            if constexpr (kStage) {
-                // row l32 of the slice; this lane's 4 columns 32 i + 8 r4 + 4 hi
-                // are the half hi of 16-byte chunk 4 i + r4.  The row index goes
-                // through an empty asm so that these per-lane addresses are
-                // computed here, not hoisted out of the tile loop and kept in
-                // registers across the sweep.
-                int orow = l32;
-                asm volatile("" : "+v"(orow));
-#pragma unroll
-                for (int i = 0; i < S::kDvBlocks; ++i) {
-#pragma unroll
-                    for (int r4 = 0; r4 < 4; ++r4) {
-                        f32x4 x = {oacc[i][4 * r4 + 0] * inv, oacc[i][4 * r4 + 1] * inv,
-                                   oacc[i][4 * r4 + 2] * inv, oacc[i][4 * r4 + 3] * inv};
-                        const ex4 y = __builtin_convertvector(x, ex4);
-                        *reinterpret_cast<ex4*>(slice + orow * kRowQ +
-                                                   16 * ((4 * i + r4) ^ kswz<DV>(orow)) + 8 * hi) = y;
-                    }
-                }
-                pend = 1;
-                pend_rows = max(0, min(kRowsPerWave, Lq_t - qw));
-                pend_dst = o_out + orow_w;
-            } else if (qi < Lq_t) {
-                uint16_t* orow = o_out + orow_w + (size_t)l32 * p.o_sr;
-#pragma unroll
-                for (int i = 0; i < S::kDvBlocks; ++i) {
-#pragma unroll
-                    for (int r4 = 0; r4 < 4; ++r4) {
-                        f32x4 x = {oacc[i][4 * r4 + 0] * inv, oacc[i][4 * r4 + 1] * inv,
-                                   oacc[i][4 * r4 + 2] * inv, oacc[i][4 * r4 + 3] * inv};
-                        const ex4 y = __builtin_convertvector(x, ex4);
-                        *reinterpret_cast<ex4*>(orow + 32 * i + 8 * r4 + 4 * hi) = y;
-                    }
-                }
-            }
-            if (hi == 0 && qi < Lq_t) lse_out[qrow0 + qi] = lse_row;
-        } else if (qi < Lq_t) {
-            // one split's state in fp32: its normalised output and lse
-            const size_t prow = (size_t)split * p.B * p.Hq * p.Lq + qrow0 + qi;
-            float* orow = o_part + prow * DV;
-#pragma unroll
-            for (int i = 0; i < S::kDvBlocks; ++i) {
-#pragma unroll
-                for (int r4 = 0; r4 < 4; ++r4) {
-                    f32x4 x = {oacc[i][4 * r4 + 0] * inv, oacc[i][4 * r4 + 1] * inv,
-                               oacc[i][4 * r4 + 2] * inv, oacc[i][4 * r4 + 3] * inv};
-                    *reinterpret_cast<f32x4*>(orow + 32 * i + 8 * r4 + 4 * hi) = x;
-                }
-            }
-            if (hi == 0) lse_out[prow] = lse_row;
-        }
+        epilogue();
         if (!has_next) break;
         ++round;
         tile = tile_n;
@@ -1067,14 +1276,34 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
     }
 }
 
-template <int DQK, int DV, bool CAUSAL, bool DEBUG, bool FP16, bool VARLEN = false>
+template <int DQK, int DV, bool CAUSAL, bool DEBUG, bool FP16, bool VARLEN = false,
+          bool CHAIN = false>
 hipError_t launch_one(const FwdParams& p, hipStream_t stream) {
     dim3 grid((unsigned)p.grid), block(kThreads);
     FwdParams arg = p;
     void* args[] = {&arg};
     return hipLaunchKernel(
-        reinterpret_cast<const void*>(&attn_fwd_kernel<DQK, DV, CAUSAL, DEBUG, FP16, VARLEN>), grid, block,
-        args, 0, stream);
+        reinterpret_cast<const void*>(&attn_fwd_kernel<DQK, DV, CAUSAL, DEBUG, FP16, VARLEN, CHAIN>),
+        grid, block, args, 0, stream);
+}
+
+// Non-causal launches without key splits run the chained sweep when every
+// tile's key range is long enough for its hand-offs (2 C + 2 blocks, C =
+// d / 16 one-KiB chunks per wave slice) and an even number of blocks (every
+// tile then starts on the same stage buffers); equal head dims only.
+bool chained(const FwdParams& p, int dqk, int dv) {
+    if (dqk != dv || p.plan != nullptr || p.n_split != 1 || p.o_part != nullptr) return false;
+    const int nblk = (p.Lk + kBlockN - 1) / kBlockN;
+    return nblk >= 2 * (dqk / 16) + 2 && nblk % 2 == 0;
+}
+
+template <int DQK, int DV, bool DEBUG, bool FP16>
+hipError_t launch_noncausal(const FwdParams& p, hipStream_t stream) {
+    if constexpr (DQK == DV) {
+        if (chained(p, DQK, DV))
+            return launch_one<DQK, DV, false, DEBUG, FP16, false, true>(p, stream);
+    }
+    return launch_one<DQK, DV, false, DEBUG, FP16>(p, stream);
 }
 
 template <int DQK, int DV>
@@ -1088,16 +1317,20 @@ hipError_t launch_dims(const FwdParams& p, bool causal, bool debug, bool fp16,
     if (fp16) {
         if (debug) return hipErrorInvalidValue;  // the debug variant is bf16 only
         return causal ? launch_one<DQK, DV, true, false, true>(p, stream)
-                      : launch_one<DQK, DV, false, false, true>(p, stream);
+                      : launch_noncausal<DQK, DV, false, true>(p, stream);
     }
     if (causal)
         return debug ? launch_one<DQK, DV, true, true, false>(p, stream)
                      : launch_one<DQK, DV, true, false, false>(p, stream);
-    return debug ? launch_one<DQK, DV, false, true, false>(p, stream)
-                 : launch_one<DQK, DV, false, false, false>(p, stream);
+    return debug ? launch_noncausal<DQK, DV, true, false>(p, stream)
+                 : launch_noncausal<DQK, DV, false, false>(p, stream);
 }
 
 }  // namespace
+
+bool fwd_chained(const FwdParams& p, int dqk, int dv, bool causal) {
+    return !causal && chained(p, dqk, dv);
+}
 
 hipError_t launch_fwd(const FwdParams& p, int dqk, int dv, bool causal, bool debug, bool fp16,
                       hipStream_t stream) {

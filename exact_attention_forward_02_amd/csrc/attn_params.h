@@ -18,6 +18,26 @@ constexpr int kBlockN = 64;          // keys per K/V block
 constexpr int kPlanInts = 8;         // ints per tile record of a packed variable-length
                                      // batch: q0, Lq, k0, Lk, unit, position block, 0, 0
 
+// Division by a launch constant d >= 1 as a multiply and a shift, exact for
+// numerators n < 2^31: n / d = (mulhi(n, mul) + n) >> shift, with shift =
+// ceil(log2 d) and mul = floor(2^32 (2^shift - d) / d) + 1 (T. Granlund and
+// P. Montgomery, "Division by invariant integers using multiplication",
+// PLDI 1994, section 4).  (mul + 2^32) / 2^(32 + shift) exceeds 1 / d by at
+// most 2^-(32 + shift), so for n < 2^31 the product exceeds n / d by less than
+// 2^-(shift + 1) <= 1 / (2 d): too little to reach the next multiple of 1 / d.
+// mulhi(n, mul) < n keeps the sum below 2^32.
+struct FastDiv {
+    uint32_t mul;
+    uint32_t shift;
+};
+
+inline FastDiv make_fast_div(uint32_t d) {
+    uint32_t l = 0;
+    while ((1ull << l) < d) ++l;
+    const unsigned long long m = (((1ull << 32) * ((1ull << l) - d)) / d) + 1;
+    return FastDiv{(uint32_t)m, l};
+}
+
 struct FwdParams {
     // q, k, v, o: 16-bit elements (bf16 or fp16), element (b, h, i, c) at
     // b * s_b + h * s_h + i * s_r + c with the strides below
@@ -50,6 +70,9 @@ struct FwdParams {
     int sec_units;  // units per cache section (divides upx, or units)
     int grid;       // workgroups launched; each processes tiles i, i + grid, ...
                     // (a multiple of 8 when smaller than the tile count)
+    // the divisors of a tile's coordinates: sec_units * n_m, sec_units,
+    // units_kv, n_hg, Hkv and Gp
+    FastDiv div_sec, div_sec_units, div_units_kv, div_hg, div_hkv, div_gp;
 
     long long q_sb, q_sh, k_sb, k_sh, v_sb, v_sh, o_sb, o_sh;  // batch and head strides
     int q_sr, k_sr, v_sr, o_sr;  // row strides (elements); one K or V head spans
@@ -64,6 +87,11 @@ struct FwdParams {
 // element type); debug is bf16 only.
 hipError_t launch_fwd(const FwdParams& p, int dqk, int dv, bool causal, bool debug, bool fp16,
                       hipStream_t stream);
+
+// Whether launch_fwd runs the workgroups' tiles as one chained sweep (non-causal,
+// no key splits, equal head dims, an even number of at least 2 d / 16 + 2 key
+// blocks).
+bool fwd_chained(const FwdParams& p, int dqk, int dv, bool causal);
 
 // Backward pass (contiguous [B, H, L, d] tensors, bf16 or fp16; q, k, dq, dk
 // rows of d_qk elements, v, o, dout, dv rows of d_v).

@@ -59,7 +59,9 @@ def test_fp16_contiguous(orc, shape):
 # Shapes of the true-fp16 test: B, Hq, Hkv, Lq, Lk, dqk, dv, causal
 FP16_SHAPES = [(1, 2, 2, 300, 300, 128, 128, False), (1, 4, 4, 513, 513, 128, 128, True),
                (1, 3, 1, 517, 517, 64, 64, False), (2, 8, 2, 200, 333, 128, 128, True),
-               (1, 2, 2, 100, 517, 192, 128, False)]
+               (1, 2, 2, 100, 517, 192, 128, False),
+               # chained sweeps over 2-3 tiles per workgroup
+               (2, 160, 160, 300, 1100, 128, 128, False), (4, 64, 16, 500, 640, 64, 64, False)]
 
 
 @pytest.mark.parametrize("layout", ["bhsd", "bshd"])

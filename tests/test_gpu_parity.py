@@ -188,6 +188,62 @@ def test_persistent_equals_one_tile_per_workgroup(orc):
             assert_parity("2 x 144 tiles causal", ob, lb, o_ref, l_ref)
 
 
+# Non-causal launches whose key range is an even number of blocks, at least
+# 2 C + 2 of them (C = d / 16 slice chunks: 18 blocks at d = 128, 10 at d = 64),
+# run all tiles of a workgroup as one chained sweep: the scores of a tile's
+# first block are computed in the MFMA phase of the previous tile's last PV
+# product, and the previous tile is finished in the softmax phase of the next
+# one's first block.  More than 256 tiles, so workgroups chain several tiles;
+# every row is compared with the oracle.
+CHAINED = [
+    (1, 520, 520, 300, 1100, 128, 128, False, 1.0),  # 1040 tiles (4-5 per workgroup),
+                                                     # ragged Lq and Lk, waves past Lq
+    (4, 32, 8, 1000, 640, 64, 64, False, 1.0),       # d = 64, GQA 4: 512 tiles
+    (3, 40, 8, 700, 1240, 128, 128, False, 1.0),     # GQA 5 (one query head per
+                                                     # workgroup): 360 tiles
+    (1, 300, 300, 256, 1152, 128, 128, False, 6.0),  # Q x 6, 300 units: plain tile order
+]
+
+
+@pytest.mark.parametrize("shape", CHAINED, ids=lambda s: "x".join(map(str, s)))
+def test_chained_shapes(orc, shape):
+    B, Hq, Hkv, Lq, Lk, dqk, dv, causal, qm = shape
+    q, k, v = make_qkv(B, Hq, Hkv, Lq, Lk, dqk, dv, seed=hash(shape) % 10007, q_mult=qm)
+    _full_check(f"chained {shape}", q, k, v, causal, orc, bounded=qm != 1.0)
+
+
+def test_chained_equals_one_tile_per_workgroup():
+    """A launch of 288 tiles, whose workgroups chain up to two tiles, and per
+    batch launches of 144 tiles (one tile per workgroup, no tile switch) give
+    the same rows bit for bit."""
+    q, k, v = _gpu(*make_qkv(2, 16, 16, 2100, 1100, 128, 128, seed=321))
+    o, lse = attn_fwd(q, k, v)
+    for b in range(2):
+        ob, lb = attn_fwd(q[b:b + 1].contiguous(), k[b:b + 1].contiguous(),
+                          v[b:b + 1].contiguous())
+        torch.cuda.synchronize()
+        assert torch.equal(o[b:b + 1], ob) and torch.equal(lse[b:b + 1], lb)
+
+
+def test_chained_rescale_events(orc):
+    """The debug kernel's chained sweep counts the same rescale events as the
+    oracle's tiled method with 64-key blocks, over 300 heads of Q x 6 rows
+    (the counter and the fast path run across tile switches)."""
+    q, k, v = make_qkv(1, 300, 300, 256, 1152, 128, 128, seed=4343, q_mult=6.0)
+    qd, kd, vd = _gpu(q, k, v)
+    cnt = torch.zeros(1, dtype=torch.int64, device=DEV)
+    o, lse = attn_fwd_dbg(qd, kd, vd, causal=False, rescale_threshold=8.0, rescale_count=cnt)
+    torch.cuda.synchronize()
+    o2, lse2 = attn_fwd(qd, kd, vd)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(lse, lse2)
+    _, _, _, want = orc.online_rows(q, k, v, causal=False, bn=64, mode=1, tau=8.0)
+    got = int(cnt.item())
+    print(f"[events] chained: gpu {got} oracle {want}", flush=True)
+    assert want > 0
+    assert abs(got - want) <= max(2, want // 50)
+
+
 def test_zero_query_closed_form():
     """Q = 0: O is the mean of the visible V rows and lse = ln(#visible)."""
     for causal in (False, True):

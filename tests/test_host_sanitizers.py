@@ -1,8 +1,10 @@
 """Host code under AddressSanitizer and UndefinedBehaviorSanitizer, on the CPU:
-the oracle (every entry point, tests/sanitize/oracle_driver.c) and the C
+the oracle (every entry point, tests/sanitize/oracle_driver.c), the C
 ABI's host side (validation, the varlen planner, split arithmetic;
-tests/sanitize/host_driver.cpp, with the kernel launchers stubbed).  Built
-with gcc / g++ on lines of their own, no GPU code involved."""
+tests/sanitize/host_driver.cpp, with the kernel launchers stubbed) and the
+multiply-and-shift division the kernels use for tile coordinates
+(tests/sanitize/fast_div_driver.cpp).  Built with gcc / g++ on lines of their
+own, no GPU code involved."""
 import os
 import shutil
 import subprocess
@@ -51,3 +53,13 @@ def test_host_abi_under_sanitizers(tmp_path):
     # the HIP runtime's own allocations outlive main; leaks are not this code's
     out = _run(exe, {"ASAN_OPTIONS": "detect_leaks=0"})
     assert "all checks passed" in out
+
+
+@pytest.mark.skipif(shutil.which("g++") is None, reason="g++ not available")
+def test_fast_division_is_exact(tmp_path):
+    exe = str(tmp_path / "fast_div_driver")
+    subprocess.run(["g++", *SAN, "-std=c++17", "-Wall", "-D__HIP_PLATFORM_AMD__",
+                    f"-I{ROCM}/include", f"-I{ROOT}/exact_attention_forward_02_amd/csrc",
+                    "-o", exe, os.path.join(HERE, "fast_div_driver.cpp")], check=True)
+    out = _run(exe, {"ASAN_OPTIONS": "detect_leaks=1"})
+    assert "all quotients exact" in out
