@@ -612,10 +612,13 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
                                                 mb * 32 * kRowK);
     };
     // pvz: the PV product is the tile's first, its first k-step starts O from
-    // an inline zero accumulator
+    // an inline zero accumulator.  epic: the PV product is the tile's last; all
+    // PV units run first, then epi(-1) and, after score unit k, epi(k) (the
+    // tile's epilogue in pieces beside the score MFMAs)
     auto m_units = [&](bool do_pv, bool do_s, const unsigned char* kl, const unsigned char* vl,
-                       auto pvz) __attribute__((always_inline)) {
+                       auto pvz, auto epic, auto&& epi) __attribute__((always_inline)) {
         constexpr bool kPvZero = decltype(pvz)::value;
+        constexpr bool kEpi = decltype(epic)::value;
         const f32x16 zero = {};
         // one MFMA unit: PV unit u < kPvUnits, else score unit u - kPvUnits; the
         // first k-step of a score block starts from an inline zero accumulator
@@ -648,6 +651,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
                 constexpr int kUnits = kPvUnits + kSUnits;
                 static_assert(kSUnits >= kPvUnits, "every PV unit has a score partner");
                 auto order = [](int n) {
+                    if (kEpi) return n;
                     return n < 2 * kPvUnits ? ((n & 1) ? kPvUnits + (n >> 1) : (n >> 1))
                                             : kPvUnits + n - kPvUnits;
                 };
@@ -661,6 +665,12 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
                     if (n + kAhead < kUnits) ring[n % kAhead] = load(order(n + kAhead));
                     mfma_unit(order(n), a);
                     __builtin_amdgcn_sched_barrier(0);
+                    if constexpr (kEpi) {
+                        if (n >= kPvUnits - 1) {
+                            epi(n - kPvUnits);
+                            __builtin_amdgcn_sched_barrier(0);
+                        }
+                    }
                 }
             } else if (do_pv) {
                 ex8 ring[kAhead];
@@ -693,7 +703,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
         constexpr bool kDown = CAUSAL && !VARLEN;  // launches that may sweep downward
         const bool do_pv = j >= (kDown ? jact0 : 0) && j < jact1;
         const bool do_s = (!kDown || j + 1 >= jact0) && j + 1 < jact1;
-        m_units(do_pv, do_s, kl, vl, std::false_type{});
+        m_units(do_pv, do_s, kl, vl, std::false_type{}, std::false_type{}, [](int) {});
     };
 
     // ---- VALU phase V(j): online softmax of block j's scores -----------------
@@ -930,6 +940,29 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
     size_t nq_qrow = 0;
 
     // ---- epilogue of a tile: O = U / l (bf16), lse = scale * ref + ln l -------
+    // Piece k of the output into the slice: row l32 of the slice; this lane's
+    // 4 columns 32 i + 8 r4 + 4 hi (i = k / 4, r4 = k % 4) are the half hi of
+    // 16-byte chunk 4 i + r4.  The caller's row index orow comes through an
+    // empty asm, so that these per-lane addresses are computed where they are
+    // used, not hoisted out of the tile loop and kept in registers.
+    auto out_piece = [&](int k, float inv, int orow) __attribute__((always_inline)) {
+        const int i = k >> 2, r4 = k & 3;
+        f32x4 x = {oacc[i][4 * r4 + 0] * inv, oacc[i][4 * r4 + 1] * inv,
+                   oacc[i][4 * r4 + 2] * inv, oacc[i][4 * r4 + 3] * inv};
+        const ex4 y = __builtin_convertvector(x, ex4);
+        *reinterpret_cast<ex4*>(slice + orow * kRowQ + 16 * ((4 * i + r4) ^ kswz<DV>(orow)) +
+                                8 * hi) = y;
+    };
+    // 1 / l for O's normalisation; lse stored (the output rows' head)
+    auto out_head = [&]() __attribute__((always_inline)) {
+        const int qi = qw + l32;
+        const float ell_row = pair_sum(ell - ell_c);
+        const float ell_o_row = ((lane >> 4) & 1) ? ell_o[1] : ell_o[0];
+        const float inv = ell_o_row > 0.0f ? 1.0f / ell_o_row : 0.0f;
+        const float lse_row = ell_row > 0.0f ? ref * scale + logf(ell_row) : kNegInf;
+        if (hi == 0 && qi < Lq_t) lse_out[qrow0 + qi] = lse_row;
+        return inv;
+    };
     auto epilogue = [&]() __attribute__((always_inline)) {
         const int qi = qw + l32;
         const float ell_row = pair_sum(ell - ell_c);
@@ -938,24 +971,10 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
         const float lse_row = ell_row > 0.0f ? ref * scale + logf(ell_row) : kNegInf;
         if (o_part == nullptr) {
             if constexpr (kStage) {
-                // row l32 of the slice; this lane's 4 columns 32 i + 8 r4 + 4 hi
-                // are the half hi of 16-byte chunk 4 i + r4.  The row index goes
-                // through an empty asm so that these per-lane addresses are
-                // computed here, not hoisted out of the tile loop and kept in
-                // registers across the sweep.
                 int orow = l32;
                 asm volatile("" : "+v"(orow));
 #pragma unroll
-                for (int i = 0; i < S::kDvBlocks; ++i) {
-#pragma unroll
-                    for (int r4 = 0; r4 < 4; ++r4) {
-                        f32x4 x = {oacc[i][4 * r4 + 0] * inv, oacc[i][4 * r4 + 1] * inv,
-                                   oacc[i][4 * r4 + 2] * inv, oacc[i][4 * r4 + 3] * inv};
-                        const ex4 y = __builtin_convertvector(x, ex4);
-                        *reinterpret_cast<ex4*>(slice + orow * kRowQ +
-                                                   16 * ((4 * i + r4) ^ kswz<DV>(orow)) + 8 * hi) = y;
-                    }
-                }
+                for (int k = 0; k < 4 * S::kDvBlocks; ++k) out_piece(k, inv, orow);
                 pend = 1;
                 pend_rows = max(0, min(kRowsPerWave, Lq_t - qw));
                 pend_dst = o_out + orow_w;
@@ -1003,10 +1022,12 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
     // tile boundaries: the MFMA phase with the PV product of a tile's last
     // block also computes the scores of the next tile's first block, with the
     // next tile's Q, which the wave loaded from its slice at the end of the
-    // softmax phase before; and the softmax phase of the next tile's first
-    // block starts by finishing the previous tile (O into the slice, lse) and
-    // resetting the running state.  The pipeline neither drains nor refills
-    // between tiles.  A wave's hand-offs are keyed to the local block l of its
+    // softmax phase before.  That MFMA phase runs its PV units first and then,
+    // beside its score MFMAs, finishes the tile: lse stored, O normalised
+    // into the slice piece by piece.  The softmax phase of the next tile's
+    // first block switches the wave's tile and resets the row state; the next
+    // tile's first PV product starts O from zero.  The pipeline neither
+    // drains nor refills between tiles.  A wave's hand-offs are keyed to the local block l of its
     // softmax phase: output chunk k leaves in l = k + 1 and the next tile's Q
     // chunk k arrives in l = nblk - 1 - C + k (C chunks per slice), so the
     // two never overlap when nblk >= 2 C + 2; the copies of a block that
@@ -1070,7 +1091,8 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
                 if constexpr (kEdge) {
                     if (J >= total) return;
                     if (J - tstart == nb) {  // the next tile's first block
-                        epilogue();
+                        // (the previous tile's output is in the slice already:
+                        // the MFMA phase before wrote it, see tile_pairs)
                         ++round;
                         tile = tile_n;
                         qw = nx_qw;
@@ -1095,7 +1117,10 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
             // M(t - 1) then V(t), group 1 V(t - 1) then M(t - 1).  MK selects
             // the MFMA units of M(t - 1): 0 both products, 1 scores only (the
             // first pair), 2 PV only (the last pair), 3 both with the PV
-            // product starting O from zero (M(t - 1) holds a tile's first PV).
+            // product starting O from zero (M(t - 1) holds a tile's first PV),
+            // 4 both with the PV units first and the finished tile's output
+            // written into the slice in pieces beside the score units (M(t - 1)
+            // holds a tile's last PV and the next tile's first scores).
             auto pair = [&](auto gc, auto mk, auto edgec, int t, const unsigned char* kl,
                             const unsigned char* vl, unsigned char* kn, unsigned char* vn)
                             __attribute__((always_inline)) {
@@ -1103,7 +1128,22 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
                 constexpr int MK = decltype(mk)::value;
                 auto m = [&]() __attribute__((always_inline)) {
                     __builtin_amdgcn_s_setprio(2);
-                    m_units(MK != 1, MK != 2, kl, vl, std::integral_constant<bool, MK == 3>{});
+                    float inv = 0.0f;
+                    int orow = 0;
+                    m_units(MK != 1, MK != 2, kl, vl, std::integral_constant<bool, MK == 3>{},
+                            std::integral_constant<bool, MK == 4>{},
+                            [&](int k) __attribute__((always_inline)) {
+                                if (k < 0) {
+                                    inv = out_head();
+                                    orow = l32;
+                                    asm volatile("" : "+v"(orow));
+                                    pend = 1;
+                                    pend_rows = max(0, min(kRowsPerWave, Lq_t - qw));
+                                    pend_dst = o_out + orow_w;
+                                } else {
+                                    out_piece(k, inv, orow);
+                                }
+                            });
                 };
                 if constexpr (G == 0) {
                     m();
@@ -1126,7 +1166,9 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
                 __syncthreads();
             };
             // The pairs of the tile whose first block is tb (nblk is even, so
-            // every tile starts on stage buffers 0).  A wave's tile switch falls
+            // every tile starts on stage buffers 0).  In pair tb both groups' MFMA
+            // phase holds the previous tile's last PV product, and writes that
+            // tile's output (MK 4); a wave's tile switch falls
             // in pair tb (group 0) or tb + 1 (group 1), its load of the next Q
             // in pair tb + nb - 1 (group 0) or the next tile's pair tb + nb
             // (group 1): these are the edge pairs, and the loop between them
@@ -1134,7 +1176,8 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
             auto tile_pairs = [&](auto gc, auto firstc, int tb) __attribute__((always_inline)) {
                 using Both = std::integral_constant<int, 0>;
                 using SOnly = std::integral_constant<int, 1>;
-                using First = std::conditional_t<decltype(firstc)::value, SOnly, Both>;
+                using Finish = std::integral_constant<int, 4>;
+                using First = std::conditional_t<decltype(firstc)::value, SOnly, Finish>;
                 using Edge = std::true_type;
                 using Plain = std::false_type;
                 using PvFirst = std::integral_constant<int, 3>;
