@@ -264,11 +264,11 @@ int run(const void* q, const void* k, const void* v, void* o, float* lse, int B,
     const long long slots = (long long)(n_cu / kXcds) * kXcds;
     if (slots > 0 && tiles > slots) grid = slots;
     p.grid = (int)grid;
+    p.chain = attn::fwd_chained(p, d_qk, d_v, causal != 0) ? 1 : 0;
     log_launch("attn_fwd_kernel<%d,%d,%s%s%s> grid %d, %d tiles (units %d x position tiles %d), "
                "splits %d, query heads per workgroup %d, xcd_mode %d, chained %d",
                d_qk, d_v, causal ? "causal" : "full", debug ? ",debug" : "", fp16 ? ",fp16" : "",
-               p.grid, p.units * p.n_m, p.units, p.n_m, p.n_split, p.Gp, p.xcd_mode,
-               attn::fwd_chained(p, d_qk, d_v, causal != 0) ? 1 : 0);
+               p.grid, p.units * p.n_m, p.units, p.n_m, p.n_split, p.Gp, p.xcd_mode, p.chain);
     hipError_t err = attn::launch_fwd(p, d_qk, d_v, causal != 0, debug, fp16,
                                       static_cast<hipStream_t>(stream));
     if (err != hipSuccess) return ATTN_ERR_HIP;

@@ -1330,21 +1330,12 @@ hipError_t launch_one(const FwdParams& p, hipStream_t stream) {
         grid, block, args, 0, stream);
 }
 
-// Non-causal launches without key splits run the chained sweep when every
-// tile's key range is long enough for its hand-offs (2 C + 2 blocks, C =
-// d / 16 one-KiB chunks per wave slice) and an even number of blocks (every
-// tile then starts on the same stage buffers); equal head dims only.
-bool chained(const FwdParams& p, int dqk, int dv) {
-    if (dqk != dv || p.plan != nullptr || p.n_split != 1 || p.o_part != nullptr) return false;
-    const int nblk = (p.Lk + kBlockN - 1) / kBlockN;
-    return nblk >= 2 * (dqk / 16) + 2 && nblk % 2 == 0;
-}
-
+// Non-causal launches run the chained sweep when the host set p.chain
+// (fwd_chained in attn_params.h states when).
 template <int DQK, int DV, bool DEBUG, bool FP16>
 hipError_t launch_noncausal(const FwdParams& p, hipStream_t stream) {
     if constexpr (DQK == DV) {
-        if (chained(p, DQK, DV))
-            return launch_one<DQK, DV, false, DEBUG, FP16, false, true>(p, stream);
+        if (p.chain) return launch_one<DQK, DV, false, DEBUG, FP16, false, true>(p, stream);
     }
     return launch_one<DQK, DV, false, DEBUG, FP16>(p, stream);
 }
@@ -1370,10 +1361,6 @@ hipError_t launch_dims(const FwdParams& p, bool causal, bool debug, bool fp16,
 }
 
 }  // namespace
-
-bool fwd_chained(const FwdParams& p, int dqk, int dv, bool causal) {
-    return !causal && chained(p, dqk, dv);
-}
 
 hipError_t launch_fwd(const FwdParams& p, int dqk, int dv, bool causal, bool debug, bool fp16,
                       hipStream_t stream) {

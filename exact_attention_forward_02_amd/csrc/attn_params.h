@@ -73,6 +73,7 @@ struct FwdParams {
     // the divisors of a tile's coordinates: sec_units * n_m, sec_units,
     // units_kv, n_hg, Hkv and Gp
     FastDiv div_sec, div_sec_units, div_units_kv, div_hg, div_hkv, div_gp;
+    int chain;      // 1: each workgroup's tiles run as one chained sweep (fwd_chained)
 
     long long q_sb, q_sh, k_sb, k_sh, v_sb, v_sh, o_sb, o_sh;  // batch and head strides
     int q_sr, k_sr, v_sr, o_sr;  // row strides (elements); one K or V head spans
@@ -88,10 +89,21 @@ struct FwdParams {
 hipError_t launch_fwd(const FwdParams& p, int dqk, int dv, bool causal, bool debug, bool fp16,
                       hipStream_t stream);
 
-// Whether launch_fwd runs the workgroups' tiles as one chained sweep (non-causal,
-// no key splits, equal head dims, an even number of at least 2 d / 16 + 2 key
-// blocks).
-bool fwd_chained(const FwdParams& p, int dqk, int dv, bool causal);
+// Whether a launch can run each workgroup's tiles as one chained sweep: non-causal,
+// one key split, equal head dims, and every tile's key range long enough for
+// its hand-offs (2 C + 2 blocks, C = d / 16 one-KiB chunks per wave slice) and
+// an even number of blocks (every tile then starts on the same stage buffers).
+// The sweep counts a workgroup's blocks, and twice that in phases, in ints.
+// Needs the schedule and grid filled in; the host stores the answer in p.chain.
+inline bool fwd_chained(const FwdParams& p, int dqk, int dv, bool causal) {
+    if (causal || dqk != dv || p.plan != nullptr || p.n_split != 1 || p.o_part != nullptr)
+        return false;
+    const long long nblk = (p.Lk + kBlockN - 1) / kBlockN;
+    const long long tiles = (long long)p.units * p.n_m;
+    const long long per_wg = (tiles + p.grid - 1) / p.grid + 1;
+    if (per_wg * nblk >= (1ll << 29)) return false;
+    return nblk >= 2 * (dqk / 16) + 2 && nblk % 2 == 0;
+}
 
 // Backward pass (contiguous [B, H, L, d] tensors, bf16 or fp16; q, k, dq, dk
 // rows of d_qk elements, v, o, dout, dv rows of d_v).

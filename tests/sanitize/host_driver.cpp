@@ -15,7 +15,6 @@
 
 namespace attn {
 hipError_t launch_fwd(const FwdParams&, int, int, bool, bool, bool, hipStream_t) { abort(); }
-bool fwd_chained(const FwdParams&, int, int, bool) { abort(); }
 hipError_t launch_bwd(const BwdParams&, int, int, bool, bool, hipStream_t) { abort(); }
 hipError_t launch_merge(const float*, const float*, uint16_t*, float*, int, long long, int,
                         hipStream_t) {
