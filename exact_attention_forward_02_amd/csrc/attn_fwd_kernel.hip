@@ -150,8 +150,9 @@ __device__ __forceinline__ u32x4 load16(const uint16_t* p) {
 
 // Copy 16 bytes per lane from global memory straight into LDS through a
 // buffer descriptor: lane l reads at byte soff + voff (soff wave-uniform) and
-// its data lands at lds_dst + 16 * l (one contiguous KiB per wave).  The buffer form (rather than the global-address form) lets
-// LDS reads issued after it wait for just the reads they need.  Offsets at or
+// its data lands at lds_dst + 16 * l (one contiguous KiB per wave).  The
+// buffer form (rather than the global-address form) lets LDS reads issued
+// after it wait for just the reads they need.  Offsets at or
 // past the descriptor's record count read as zero instead of faulting.
 typedef __attribute__((address_space(3))) void lds_void;
 __device__ __forceinline__ void copy_to_lds(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff,
@@ -699,7 +700,8 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
         }
     };
 
-    auto m_phase = [&](int j, const unsigned char* kl, const unsigned char* vl) __attribute__((always_inline)) {
+    auto m_phase = [&](int j, const unsigned char* kl, const unsigned char* vl)
+                       __attribute__((always_inline)) {
         constexpr bool kDown = CAUSAL && !VARLEN;  // launches that may sweep downward
         const bool do_pv = j >= (kDown ? jact0 : 0) && j < jact1;
         const bool do_s = (!kDown || j + 1 >= jact0) && j + 1 < jact1;
@@ -793,7 +795,8 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
                 // events count reference moves after the first one of a row
                 const unsigned long long ev = __ballot(moved && ref != kNegInf && qw + l32 < Lq_t);
                 if (lane == 0 && ev)
-                    atomicAdd(rescale_count, (unsigned long long)__builtin_popcountll(ev & 0xffffffffull));
+                    atomicAdd(rescale_count,
+                              (unsigned long long)__builtin_popcountll(ev & 0xffffffffull));
             }
             ref = moved ? cand : ref;
             const bool any_moved = __ballot(moved) != 0;
@@ -1035,176 +1038,175 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const FwdParams p) {
     // tile's descriptors.  Every wave computes every block, also a wave whose
     // rows lie past Lq (it stores nothing).
     if constexpr (CHAIN) {
-        static_assert(!CAUSAL && !VARLEN && kStage, "chained sweeps are for non-causal launches with slices");
-        {
-            const int nb = nblk;
-            const int n_mine = (n_local - slot + per_round - 1) / per_round;
-            const int total = n_mine * nb;
-            int tstart = 0;   // sweep index of this wave's current tile's block 0
-            int tile_n = -1;  // the tile after it, or -1
-            __amdgpu_buffer_rsrc_t nv_rsrc = vrsrc;
-            // the next tile's rows as set_tile would set them: the switch to
-            // it then only copies
-            int nx_qw = 0;
-            size_t nx_qrow0 = 0, nx_orow_w = 0;
-            auto prepare_next = [&]() __attribute__((always_inline)) {
-                tile_n = tile_of_round(round + 1);
-                nq_rows = 0;
-                if (tile_n >= 0) {
-                    const TileCoord c = tile_coord<CAUSAL, VARLEN>(p, tile_n, wave_t);
-                    nk_rsrc = make_rsrc(p.k + c.kbase, kv_bytes(c.Lk, k_rb, kRowK));
-                    nv_rsrc = make_rsrc(p.v + c.vbase, kv_bytes(c.Lk, v_rb, kRowV));
-                    nq_rows = max(0, min(kRowsPerWave, c.Lq - c.qw));
-                    nq_src = p.q + c.qbase + (size_t)(nq_rows > 0 ? c.qw : 0) * p.q_sr;
-                    nx_qw = c.qw;
-                    nx_qrow0 = c.qrow0;
-                    nx_orow_w = c.obase + (size_t)c.qw * p.o_sr;
+        static_assert(!CAUSAL && !VARLEN && kStage,
+                      "chained sweeps are for non-causal launches with slices");
+        const int nb = nblk;
+        const int n_mine = (n_local - slot + per_round - 1) / per_round;
+        const int total = n_mine * nb;
+        int tstart = 0;   // sweep index of this wave's current tile's block 0
+        int tile_n = -1;  // the tile after it, or -1
+        __amdgpu_buffer_rsrc_t nv_rsrc = vrsrc;
+        // the next tile's rows as set_tile would set them: the switch to
+        // it then only copies
+        int nx_qw = 0;
+        size_t nx_qrow0 = 0, nx_orow_w = 0;
+        auto prepare_next = [&]() __attribute__((always_inline)) {
+            tile_n = tile_of_round(round + 1);
+            nq_rows = 0;
+            if (tile_n >= 0) {
+                const TileCoord c = tile_coord<CAUSAL, VARLEN>(p, tile_n, wave_t);
+                nk_rsrc = make_rsrc(p.k + c.kbase, kv_bytes(c.Lk, k_rb, kRowK));
+                nv_rsrc = make_rsrc(p.v + c.vbase, kv_bytes(c.Lk, v_rb, kRowV));
+                nq_rows = max(0, min(kRowsPerWave, c.Lq - c.qw));
+                nq_src = p.q + c.qbase + (size_t)(nq_rows > 0 ? c.qw : 0) * p.q_sr;
+                nx_qw = c.qw;
+                nx_qrow0 = c.qrow0;
+                nx_orow_w = c.obase + (size_t)c.qw * p.o_sr;
+            }
+        };
+        prepare_next();
+        reset_state();
+        auto copy_k_at = [&](int J, unsigned char* dst) __attribute__((always_inline)) {
+            const int l = J - tstart;
+            if (l < nb)
+                copy_kblock(krsrc, l * kBlockN, dst);
+            else if (tile_n >= 0)
+                copy_kblock(nk_rsrc, (l - nb) * kBlockN, dst);
+        };
+        auto copy_v_at = [&](int J, unsigned char* dst) __attribute__((always_inline)) {
+            const int l = J - tstart;
+            if (l < nb)
+                copy_vblock(vrsrc, l * kBlockN, dst);
+            else if (tile_n >= 0)
+                copy_vblock(nv_rsrc, (l - nb) * kBlockN, dst);
+        };
+        auto hand_off = [&](int l) __attribute__((always_inline)) {
+            if (pend && l >= 1 && l <= kSliceChunks) store_o_chunk(l - 1);
+            __builtin_amdgcn_sched_barrier(0);
+            const int k = l - (nb - 1 - kSliceChunks);
+            if (nq_rows > 0 && k >= 0 && k < kSliceChunks) prefetch_q_chunk(k);
+        };
+        // V(J).  Only edge pairs (see below) hold a tile's first or last
+        // block for some wave, so only they test for the tile switch and
+        // for the load of the next tile's Q.
+        auto v_chain = [&](int J, auto edgec) __attribute__((always_inline)) {
+            constexpr bool kEdge = decltype(edgec)::value;
+            if constexpr (kEdge) {
+                if (J >= total) return;
+                if (J - tstart == nb) {  // the next tile's first block
+                    // (the previous tile's output is in the slice already:
+                    // the MFMA phase before wrote it, see tile_pairs)
+                    ++round;
+                    tile = tile_n;
+                    qw = nx_qw;
+                    qrow0 = nx_qrow0;
+                    orow_w = nx_orow_w;
+                    krsrc = nk_rsrc;
+                    vrsrc = nv_rsrc;
+                    tstart += nb;
+                    prepare_next();
+                    reset_rows();
                 }
+            }
+            softmax(J - tstart, kEdge && J == tstart);
+            if constexpr (kEdge) {
+                // the scores of the next tile's first block, in the coming
+                // MFMA phase, take the next tile's Q
+                if (J - tstart == nb - 1 && nq_rows > 0) load_q_slice();
+            }
+        };
+        // Pair t of the sweep (phases 2 t, 2 t + 1) reads stage t from the
+        // buffers kl, vl and fills stage t + 1 into kn, vn.  Group 0 runs
+        // M(t - 1) then V(t), group 1 V(t - 1) then M(t - 1).  MK selects
+        // the MFMA units of M(t - 1): 0 both products, 1 scores only (the
+        // first pair), 2 PV only (the last pair), 3 both with the PV
+        // product starting O from zero (M(t - 1) holds a tile's first PV),
+        // 4 both with the PV units first and the finished tile's output
+        // written into the slice in pieces beside the score units (M(t - 1)
+        // holds a tile's last PV and the next tile's first scores).
+        auto pair = [&](auto gc, auto mk, auto edgec, int t, const unsigned char* kl,
+                        const unsigned char* vl, unsigned char* kn, unsigned char* vn)
+                        __attribute__((always_inline)) {
+            constexpr int G = decltype(gc)::value;
+            constexpr int MK = decltype(mk)::value;
+            auto m = [&]() __attribute__((always_inline)) {
+                __builtin_amdgcn_s_setprio(2);
+                float inv = 0.0f;
+                int orow = 0;
+                m_units(MK != 1, MK != 2, kl, vl, std::integral_constant<bool, MK == 3>{},
+                        std::integral_constant<bool, MK == 4>{},
+                        [&](int k) __attribute__((always_inline)) {
+                            if (k < 0) {
+                                inv = out_head();
+                                orow = l32;
+                                asm volatile("" : "+v"(orow));
+                                pend = 1;
+                                pend_rows = max(0, min(kRowsPerWave, Lq_t - qw));
+                                pend_dst = o_out + orow_w;
+                            } else {
+                                out_piece(k, inv, orow);
+                            }
+                        });
             };
-            prepare_next();
-            reset_state();
-            auto copy_k_at = [&](int J, unsigned char* dst) __attribute__((always_inline)) {
-                const int l = J - tstart;
-                if (l < nb)
-                    copy_kblock(krsrc, l * kBlockN, dst);
-                else if (tile_n >= 0)
-                    copy_kblock(nk_rsrc, (l - nb) * kBlockN, dst);
-            };
-            auto copy_v_at = [&](int J, unsigned char* dst) __attribute__((always_inline)) {
-                const int l = J - tstart;
-                if (l < nb)
-                    copy_vblock(vrsrc, l * kBlockN, dst);
-                else if (tile_n >= 0)
-                    copy_vblock(nv_rsrc, (l - nb) * kBlockN, dst);
-            };
-            auto hand_off = [&](int l) __attribute__((always_inline)) {
-                if (pend && l >= 1 && l <= kSliceChunks) store_o_chunk(l - 1);
-                __builtin_amdgcn_sched_barrier(0);
-                const int k = l - (nb - 1 - kSliceChunks);
-                if (nq_rows > 0 && k >= 0 && k < kSliceChunks) prefetch_q_chunk(k);
-            };
-            // V(J).  Only edge pairs (see below) hold a tile's first or last
-            // block for some wave, so only they test for the tile switch and
-            // for the load of the next tile's Q.
-            auto v_chain = [&](int J, auto edgec) __attribute__((always_inline)) {
-                constexpr bool kEdge = decltype(edgec)::value;
-                if constexpr (kEdge) {
-                    if (J >= total) return;
-                    if (J - tstart == nb) {  // the next tile's first block
-                        // (the previous tile's output is in the slice already:
-                        // the MFMA phase before wrote it, see tile_pairs)
-                        ++round;
-                        tile = tile_n;
-                        qw = nx_qw;
-                        qrow0 = nx_qrow0;
-                        orow_w = nx_orow_w;
-                        krsrc = nk_rsrc;
-                        vrsrc = nv_rsrc;
-                        tstart += nb;
-                        prepare_next();
-                        reset_rows();
-                    }
+            if constexpr (G == 0) {
+                m();
+                hand_off(t - tstart);
+                if (MK != 2) {
+                    copy_v_at(t, vn);
+                    __builtin_amdgcn_s_setprio(0);
+                    v_chain(t, edgec);
                 }
-                softmax(J - tstart, kEdge && J == tstart);
-                if constexpr (kEdge) {
-                    // the scores of the next tile's first block, in the coming
-                    // MFMA phase, take the next tile's Q
-                    if (J - tstart == nb - 1 && nq_rows > 0) load_q_slice();
+            } else {
+                hand_off(t - 1 - tstart);
+                copy_k_at(t + 1, kn);
+                if (MK != 1) {
+                    __builtin_amdgcn_s_setprio(0);
+                    v_chain(t - 1, edgec);
                 }
-            };
-            // Pair t of the sweep (phases 2 t, 2 t + 1) reads stage t from the
-            // buffers kl, vl and fills stage t + 1 into kn, vn.  Group 0 runs
-            // M(t - 1) then V(t), group 1 V(t - 1) then M(t - 1).  MK selects
-            // the MFMA units of M(t - 1): 0 both products, 1 scores only (the
-            // first pair), 2 PV only (the last pair), 3 both with the PV
-            // product starting O from zero (M(t - 1) holds a tile's first PV),
-            // 4 both with the PV units first and the finished tile's output
-            // written into the slice in pieces beside the score units (M(t - 1)
-            // holds a tile's last PV and the next tile's first scores).
-            auto pair = [&](auto gc, auto mk, auto edgec, int t, const unsigned char* kl,
-                            const unsigned char* vl, unsigned char* kn, unsigned char* vn)
-                            __attribute__((always_inline)) {
-                constexpr int G = decltype(gc)::value;
-                constexpr int MK = decltype(mk)::value;
-                auto m = [&]() __attribute__((always_inline)) {
-                    __builtin_amdgcn_s_setprio(2);
-                    float inv = 0.0f;
-                    int orow = 0;
-                    m_units(MK != 1, MK != 2, kl, vl, std::integral_constant<bool, MK == 3>{},
-                            std::integral_constant<bool, MK == 4>{},
-                            [&](int k) __attribute__((always_inline)) {
-                                if (k < 0) {
-                                    inv = out_head();
-                                    orow = l32;
-                                    asm volatile("" : "+v"(orow));
-                                    pend = 1;
-                                    pend_rows = max(0, min(kRowsPerWave, Lq_t - qw));
-                                    pend_dst = o_out + orow_w;
-                                } else {
-                                    out_piece(k, inv, orow);
-                                }
-                            });
-                };
-                if constexpr (G == 0) {
-                    m();
-                    hand_off(t - tstart);
-                    if (MK != 2) {
-                        copy_v_at(t, vn);
-                        __builtin_amdgcn_s_setprio(0);
-                        v_chain(t, edgec);
-                    }
-                } else {
-                    hand_off(t - 1 - tstart);
-                    copy_k_at(t + 1, kn);
-                    if (MK != 1) {
-                        __builtin_amdgcn_s_setprio(0);
-                        v_chain(t - 1, edgec);
-                    }
-                    m();
-                }
-                __builtin_amdgcn_s_waitcnt(0);
-                __syncthreads();
-            };
-            // The pairs of the tile whose first block is tb (nblk is even, so
-            // every tile starts on stage buffers 0).  In pair tb both groups' MFMA
-            // phase holds the previous tile's last PV product, and writes that
-            // tile's output (MK 4); a wave's tile switch falls
-            // in pair tb (group 0) or tb + 1 (group 1), its load of the next Q
-            // in pair tb + nb - 1 (group 0) or the next tile's pair tb + nb
-            // (group 1): these are the edge pairs, and the loop between them
-            // holds only the steady form of a pair.
-            auto tile_pairs = [&](auto gc, auto firstc, int tb) __attribute__((always_inline)) {
-                using Both = std::integral_constant<int, 0>;
-                using SOnly = std::integral_constant<int, 1>;
-                using Finish = std::integral_constant<int, 4>;
-                using First = std::conditional_t<decltype(firstc)::value, SOnly, Finish>;
-                using Edge = std::true_type;
-                using Plain = std::false_type;
-                using PvFirst = std::integral_constant<int, 3>;
-                pair(gc, First{}, Edge{}, tb, lds_k0, lds_v0, lds_k1, lds_v1);
-                pair(gc, PvFirst{}, Edge{}, tb + 1, lds_k1, lds_v1, lds_k0, lds_v0);
-                for (int t = tb + 2; t < tb + nb - 2; t += 2) {
-                    pair(gc, Both{}, Plain{}, t, lds_k0, lds_v0, lds_k1, lds_v1);
-                    pair(gc, Both{}, Plain{}, t + 1, lds_k1, lds_v1, lds_k0, lds_v0);
-                }
-                pair(gc, Both{}, Plain{}, tb + nb - 2, lds_k0, lds_v0, lds_k1, lds_v1);
-                pair(gc, Both{}, Edge{}, tb + nb - 1, lds_k1, lds_v1, lds_k0, lds_v0);
-            };
-            auto chain_sweep = [&](auto gc) __attribute__((always_inline)) {
-                tile_pairs(gc, std::true_type{}, 0);
-                for (int tb = nb; tb < total; tb += nb) tile_pairs(gc, std::false_type{}, tb);
-                pair(gc, std::integral_constant<int, 2>{}, std::true_type{}, total, lds_k0,
-                     lds_v0, lds_k1, lds_v1);
-            };
-            if (grp == 0)
-                chain_sweep(std::integral_constant<int, 0>{});
-            else
-                chain_sweep(std::integral_constant<int, 1>{});
-            epilogue();
+                m();
+            }
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+        };
+        // The pairs of the tile whose first block is tb (nblk is even, so
+        // every tile starts on stage buffers 0).  In pair tb both groups' MFMA
+        // phase holds the previous tile's last PV product, and writes that
+        // tile's output (MK 4); a wave's tile switch falls
+        // in pair tb (group 0) or tb + 1 (group 1), its load of the next Q
+        // in pair tb + nb - 1 (group 0) or the next tile's pair tb + nb
+        // (group 1): these are the edge pairs, and the loop between them
+        // holds only the steady form of a pair.
+        auto tile_pairs = [&](auto gc, auto firstc, int tb) __attribute__((always_inline)) {
+            using Both = std::integral_constant<int, 0>;
+            using SOnly = std::integral_constant<int, 1>;
+            using Finish = std::integral_constant<int, 4>;
+            using First = std::conditional_t<decltype(firstc)::value, SOnly, Finish>;
+            using Edge = std::true_type;
+            using Plain = std::false_type;
+            using PvFirst = std::integral_constant<int, 3>;
+            pair(gc, First{}, Edge{}, tb, lds_k0, lds_v0, lds_k1, lds_v1);
+            pair(gc, PvFirst{}, Edge{}, tb + 1, lds_k1, lds_v1, lds_k0, lds_v0);
+            for (int t = tb + 2; t < tb + nb - 2; t += 2) {
+                pair(gc, Both{}, Plain{}, t, lds_k0, lds_v0, lds_k1, lds_v1);
+                pair(gc, Both{}, Plain{}, t + 1, lds_k1, lds_v1, lds_k0, lds_v0);
+            }
+            pair(gc, Both{}, Plain{}, tb + nb - 2, lds_k0, lds_v0, lds_k1, lds_v1);
+            pair(gc, Both{}, Edge{}, tb + nb - 1, lds_k1, lds_v1, lds_k0, lds_v0);
+        };
+        auto chain_sweep = [&](auto gc) __attribute__((always_inline)) {
+            tile_pairs(gc, std::true_type{}, 0);
+            for (int tb = nb; tb < total; tb += nb) tile_pairs(gc, std::false_type{}, tb);
+            pair(gc, std::integral_constant<int, 2>{}, std::true_type{}, total, lds_k0,
+                 lds_v0, lds_k1, lds_v1);
+        };
+        if (grp == 0)
+            chain_sweep(std::integral_constant<int, 0>{});
+        else
+            chain_sweep(std::integral_constant<int, 1>{});
+        epilogue();
 #pragma unroll 1
-            for (int k = 0; k < kSliceChunks; ++k) store_o_chunk(k);
-            return;
-        }
+        for (int k = 0; k < kSliceChunks; ++k) store_o_chunk(k);
+        return;
     }
 
     for (;;) {
@@ -1326,7 +1328,8 @@ hipError_t launch_one(const FwdParams& p, hipStream_t stream) {
     FwdParams arg = p;
     void* args[] = {&arg};
     return hipLaunchKernel(
-        reinterpret_cast<const void*>(&attn_fwd_kernel<DQK, DV, CAUSAL, DEBUG, FP16, VARLEN, CHAIN>),
+        reinterpret_cast<const void*>(
+            &attn_fwd_kernel<DQK, DV, CAUSAL, DEBUG, FP16, VARLEN, CHAIN>),
         grid, block, args, 0, stream);
 }
 
