@@ -202,6 +202,9 @@ CHAINED = [
     (3, 40, 8, 700, 1240, 128, 128, False, 1.0),     # GQA 5 (one query head per
                                                      # workgroup): 360 tiles
     (1, 300, 300, 256, 1152, 128, 128, False, 6.0),  # Q x 6, 300 units: plain tile order
+    (1, 200, 200, 700, 1089, 128, 128, False, 1.0),  # the fewest blocks at d = 128 (18), the
+                                                     # last holding one key; 600 tiles
+    (2, 100, 100, 333, 577, 64, 64, False, 1.0),     # the fewest at d = 64 (10), one-key tail
 ]
 
 
