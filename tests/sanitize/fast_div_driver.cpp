@@ -2,7 +2,9 @@
 // shift of attn::make_fast_div; this checks that quotient against plain
 // division for every divisor up to 5000 and a spread of larger ones, on all
 // numerators below 20000, on each divisor's largest multiples below 2^31 and
-// their neighbours, and on a sample across [0, 2^31).
+// their neighbours, and on a sample across [0, 2^31).  It also checks the
+// host's rule for the chained sweep (attn::fwd_chained) on launches at and
+// around each of its limits.
 #include <cstdint>
 #include <cstdio>
 
@@ -32,5 +34,45 @@ int main() {
     }
     std::printf("checked %llu quotients, %llu wrong\n", checked, bad);
     if (bad == 0) std::printf("all quotients exact\n");
-    return bad != 0;
+
+    // the chained-sweep rule: (causal, d_qk, d_v, Lk, tiles, grid, splits, split output)
+    struct Case {
+        bool causal;
+        int dqk, dv, Lk, units, n_m, grid, n_split, part;
+        bool want;
+    };
+    const Case cases[] = {
+        {false, 128, 128, 2048, 256, 8, 256, 1, 0, true},     // mha_l2k: 32 blocks
+        {true, 128, 128, 2048, 256, 8, 256, 1, 0, false},     // causal
+        {false, 192, 128, 2048, 256, 8, 256, 1, 0, false},    // unequal head dims
+        {false, 128, 128, 1152, 256, 8, 256, 1, 0, true},     // 18 blocks, the fewest at d = 128
+        {false, 128, 128, 1088, 256, 8, 256, 1, 0, false},    // 17 blocks
+        {false, 128, 128, 1090, 256, 8, 256, 1, 0, true},     // 18 blocks, the last with 2 keys
+        {false, 128, 128, 1216, 256, 8, 256, 1, 0, false},    // 19 blocks: odd
+        {false, 64, 64, 640, 256, 8, 256, 1, 0, true},        // 10 blocks, the fewest at d = 64
+        {false, 64, 64, 576, 256, 8, 256, 1, 0, false},       // 9 blocks
+        {false, 128, 128, 2048, 256, 8, 256, 4, 1, false},    // key splits into fp32 states
+        {false, 128, 128, 2048, 256, 8, 256, 1, 1, false},    // one split, fp32 state output
+        {false, 64, 64, 1 << 23, 1 << 20, 1, 256, 1, 0, false},  // the sweep's count past 2^29
+        {false, 64, 64, 1 << 16, 1 << 12, 1, 256, 1, 0, true},   // 17 tiles x 1024 blocks
+    };
+    int rule_bad = 0;
+    for (const Case& c : cases) {
+        attn::FwdParams p{};
+        p.Lk = c.Lk;
+        p.units = c.units;
+        p.n_m = c.n_m;
+        p.grid = c.grid;
+        p.n_split = c.n_split;
+        float part = 0.0f;
+        p.o_part = c.part ? &part : nullptr;
+        const bool got = attn::fwd_chained(p, c.dqk, c.dv, c.causal);
+        if (got != c.want) {
+            ++rule_bad;
+            std::printf("fwd_chained(causal %d, d %d/%d, Lk %d, units %d) = %d\n", c.causal, c.dqk,
+                        c.dv, c.Lk, c.units, got);
+        }
+    }
+    if (rule_bad == 0) std::printf("chained-sweep rule as stated\n");
+    return bad != 0 || rule_bad != 0;
 }

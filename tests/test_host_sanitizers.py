@@ -2,8 +2,8 @@
 the oracle (every entry point, tests/sanitize/oracle_driver.c), the C
 ABI's host side (validation, the varlen planner, split arithmetic;
 tests/sanitize/host_driver.cpp, with the kernel launchers stubbed) and the
-multiply-and-shift division the kernels use for tile coordinates
-(tests/sanitize/fast_div_driver.cpp).  Built with gcc / g++ on lines of their
+multiply-and-shift division the kernels use for tile coordinates and the
+rule that picks the chained sweep (tests/sanitize/fast_div_driver.cpp).  Built with gcc / g++ on lines of their
 own, no GPU code involved."""
 import os
 import shutil
@@ -63,3 +63,4 @@ def test_fast_division_is_exact(tmp_path):
                     "-o", exe, os.path.join(HERE, "fast_div_driver.cpp")], check=True)
     out = _run(exe, {"ASAN_OPTIONS": "detect_leaks=1"})
     assert "all quotients exact" in out
+    assert "chained-sweep rule as stated" in out
